@@ -1,0 +1,14 @@
+"""MI355X (gfx950) Attention Residuals (AttnRes) read, forward and backward.
+
+The compute lives in ``libattnres.so`` (hand-written HIP kernels behind the C ABI of
+``include/attnres.h``); this package marshals torch tensors into it. Build the library with
+``python -m attention_residuals_amd.build``. Nothing here falls back to a CPU implementation.
+"""
+from ._binding import (ATTNRES_BF16, ATTNRES_F32, EPS_DEFAULT, EXPORTS, AttnResError, Desc,
+                       Sources, attnres_bwd, attnres_fwd, load, make_desc, o32_elems,
+                       workspace_bytes)
+from .autograd import attnres
+
+__all__ = ["attnres", "attnres_fwd", "attnres_bwd", "o32_elems", "workspace_bytes", "make_desc",
+           "load", "Desc", "Sources", "AttnResError", "EXPORTS", "ATTNRES_BF16", "ATTNRES_F32",
+           "EPS_DEFAULT"]

@@ -1,0 +1,217 @@
+"""ctypes binding of ``libattnres.so`` (the C ABI declared in ``include/attnres.h``).
+
+Argument marshalling only: torch tensors are turned into device pointers, strides and a
+descriptor; every step of the computation runs in the library's HIP kernels. There is no
+fallback: if the library is missing or a call fails, this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattnres.so")
+
+ATTNRES_F32, ATTNRES_BF16 = 0, 1
+EPS_DEFAULT = 2.0 ** -23
+
+# Every function the header declares, with its ctypes signature.
+EXPORTS = ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd", "attnres_bwd",
+           "attnres_status_str", "attnres_last_error")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("N", ctypes.c_int64), ("eps", ctypes.c_float),
+                ("scale", ctypes.c_float), ("has_norm_weight", ctypes.c_int32),
+                ("out_norm", ctypes.c_int32), ("has_out_weight", ctypes.c_int32)]
+
+
+class Sources(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("src_stride", ctypes.c_int64),
+                ("list", ctypes.POINTER(ctypes.c_void_p)), ("row_stride", ctypes.c_int64)]
+
+
+class AttnResError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"attnres status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m attention_residuals_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64
+    pd, ps = ctypes.POINTER(Desc), ctypes.POINTER(Sources)
+    lib.attnres_o32_elems.argtypes = [pd, ctypes.POINTER(sz)]
+    lib.attnres_workspace_bytes.argtypes = [pd, ctypes.POINTER(sz)]
+    lib.attnres_fwd.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attnres_bwd.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, i64, ps, vp, vp, vp, vp, sz, vp]
+    for f in ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd", "attnres_bwd"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.attnres_status_str.argtypes = [ctypes.c_int]
+    lib.attnres_status_str.restype = ctypes.c_char_p
+    lib.attnres_last_error.argtypes = []
+    lib.attnres_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = load()
+        detail = lib.attnres_last_error().decode() or lib.attnres_status_str(status).decode()
+        raise AttnResError(status, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return ATTNRES_BF16
+    if dt == torch.float32:
+        return ATTNRES_F32
+    raise TypeError(f"AttnRes supports bfloat16 and float32 storage, not {dt}")
+
+
+def make_desc(S: int, N: int, D: int, R: int, dtype: torch.dtype, *, eps: float = EPS_DEFAULT,
+              scale: float = 1.0, has_norm_weight: bool = False, out_norm: bool = False,
+              has_out_weight: bool = False) -> Desc:
+    return Desc(S=S, D=D, R=R, dtype=_dtype_code(dtype), N=N, eps=eps, scale=scale,
+                has_norm_weight=int(has_norm_weight), out_norm=int(out_norm),
+                has_out_weight=int(has_out_weight))
+
+
+class _SourceView:
+    """Sources struct for a packed [S, N, D] tensor or a list of [N, D] tensors (kept alive)."""
+
+    def __init__(self, values: Union[torch.Tensor, Sequence[torch.Tensor]]):
+        if isinstance(values, torch.Tensor):
+            if values.dim() != 3 or values.stride(2) != 1:
+                raise ValueError("packed values must be [S, N, D] with unit stride in D")
+            self.S, self.N, self.D = values.shape
+            self.dtype, self.device = values.dtype, values.device
+            self.keep = [values]
+            self.ptrs = None
+            self.struct = Sources(packed=values.data_ptr(), src_stride=values.stride(0),
+                                  list=None, row_stride=values.stride(1))
+        else:
+            vs = list(values)
+            if not vs:
+                raise ValueError("need at least one source")
+            self.S = len(vs)
+            self.N, self.D = vs[0].shape
+            self.dtype, self.device = vs[0].dtype, vs[0].device
+            rs = vs[0].stride(0)
+            for v in vs:
+                if v.dim() != 2 or tuple(v.shape) != (self.N, self.D) or v.stride(1) != 1:
+                    raise ValueError("every source must be [N, D] with unit stride in D")
+                if v.dtype != self.dtype or v.device != self.device:
+                    raise ValueError("sources must share dtype and device")
+                if v.stride(0) != rs and self.N > 1:
+                    raise ValueError("sources must share one row stride")
+            self.keep = vs
+            self.ptrs = (ctypes.c_void_p * self.S)(*[v.data_ptr() for v in vs])
+            self.struct = Sources(packed=None, src_stride=0,
+                                  list=ctypes.cast(self.ptrs, ctypes.POINTER(ctypes.c_void_p)),
+                                  row_stride=rs if self.N > 1 else self.D)
+
+
+def o32_elems(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().attnres_o32_elems(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def workspace_bytes(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().attnres_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def attnres_fwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor] = None,
+                out_w: Optional[torch.Tensor] = None, *, eps: float = EPS_DEFAULT,
+                scale: float = 1.0, out_norm: bool = False,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                out_rstd: Optional[torch.Tensor] = None, o32: Optional[torch.Tensor] = None,
+                stream=None):
+    """Forward read. values: packed [S, N, D] or a list of [N, D] device tensors.
+    Returns (out [N, D], lse [N] f32, out_rstd [N] f32 or None, o32 [N, D] f32 or None);
+    output buffers are allocated with torch when not given."""
+    sv = _SourceView(values)
+    desc = make_desc(sv.S, sv.N, sv.D, query.numel(), sv.dtype, eps=eps, scale=scale,
+                     has_norm_weight=norm_w is not None, out_norm=out_norm,
+                     has_out_weight=out_w is not None)
+    dev = sv.device
+    if out is None:
+        out = torch.empty((sv.N, sv.D), dtype=sv.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((sv.N,), dtype=torch.float32, device=dev)
+    if out_norm and out_rstd is None:
+        out_rstd = torch.empty((sv.N,), dtype=torch.float32, device=dev)
+    if o32 is None and o32_elems(desc) > 0:
+        o32 = torch.empty((sv.N, sv.D), dtype=torch.float32, device=dev)
+    _check(load().attnres_fwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query),
+                              _ptr(norm_w), _ptr(out_w), _ptr(out), _ptr(lse), _ptr(out_rstd),
+                              _ptr(o32), _stream(stream)))
+    return out, lse, out_rstd, o32
+
+
+def attnres_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
+                out_w: Optional[torch.Tensor], lse: torch.Tensor,
+                out_rstd: Optional[torch.Tensor], o32: Optional[torch.Tensor],
+                dout: torch.Tensor, *, eps: float = EPS_DEFAULT, scale: float = 1.0,
+                out_norm: bool = False, dvalues=None, dq: Optional[torch.Tensor] = None,
+                dw: Optional[torch.Tensor] = None, dow: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward read. dvalues: packed [S, N, D] or list of [N, D] tensors to write (allocated
+    packed when None). Returns (dvalues, dq, dw or None, dow or None)."""
+    sv = _SourceView(values)
+    desc = make_desc(sv.S, sv.N, sv.D, query.numel(), sv.dtype, eps=eps, scale=scale,
+                     has_norm_weight=norm_w is not None, out_norm=out_norm,
+                     has_out_weight=out_w is not None)
+    dev = sv.device
+    if dout.dim() != 2 or dout.stride(1) != 1:
+        raise ValueError("dout must be [N, D] with unit stride in D")
+    if dvalues is None:
+        dvalues = torch.empty((sv.S, sv.N, sv.D), dtype=sv.dtype, device=dev)
+    dv = _SourceView(dvalues)
+    if dq is None:
+        dq = torch.empty((query.numel(),), dtype=sv.dtype, device=dev)
+    if norm_w is not None and dw is None:
+        dw = torch.empty((query.numel(),), dtype=sv.dtype, device=dev)
+    if out_w is not None and dow is None:
+        dow = torch.empty((sv.D,), dtype=sv.dtype, device=dev)
+    need = workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    dstride = dout.stride(0) if sv.N > 1 else sv.D
+    _check(load().attnres_bwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query),
+                              _ptr(norm_w), _ptr(out_w), _ptr(lse), _ptr(out_rstd), _ptr(o32),
+                              _ptr(dout), dstride, ctypes.byref(dv.struct), _ptr(dq), _ptr(dw),
+                              _ptr(dow), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dvalues, dq, dw, dow

@@ -1,0 +1,60 @@
+// attnres_args.hpp -- kernel argument blocks, shared by the kernels and the host dispatcher.
+#pragma once
+
+#include <stdint.h>
+
+namespace attnres {
+
+constexpr int kMaxSources = 64;
+
+struct FwdArgs {
+  const void* src[kMaxSources];  // base of source s ([N, D] rows, row_stride elements apart)
+  int64_t row_stride;
+  int64_t N;
+  int S, D, R, lo;               // lo = D - R: first column of the key slice
+  float eps, scale, inv_R, inv_D;
+  const void* query;             // [R]
+  const void* norm_w;            // [R] or nullptr
+  const void* out_w;             // [D] or nullptr
+  void* y;                       // [N, D] contiguous
+  float* lse;                    // [N]
+  float* o_rstd;                 // [N] or nullptr
+  float* o32;                    // [N, D] or nullptr
+  int out_norm;
+};
+
+struct BwdArgs {
+  const void* src[kMaxSources];
+  void* dsrc[kMaxSources];
+  int64_t row_stride, drow_stride, dout_stride;
+  int64_t N;
+  int S, D, R, lo;
+  float eps, scale, inv_R, inv_D;
+  const void* query;
+  const void* norm_w;
+  const void* out_w;
+  const float* lse;
+  const float* o_rstd;
+  const float* o32;
+  const void* dout;
+  float* part_du;                // [gridDim.x, R]
+  float* part_dow;               // [gridDim.x, D] or nullptr
+  uint32_t* counters;            // finaliser counters, zeroed here for the finaliser
+  int n_counters;
+  int out_norm;
+};
+
+struct FinArgs {
+  const float* part_du;          // [P, R]
+  const float* part_dow;         // [P, D] or nullptr
+  float* level2;                 // [G, cols]
+  uint32_t* counters;            // [ceil(cols / 256)]
+  int P, R, D, G, cols;
+  const void* query;
+  const void* norm_w;            // nullptr: dq = du and no dw
+  void* dq;
+  void* dw;
+  void* dow;
+};
+
+}  // namespace attnres

@@ -1,0 +1,30 @@
+// Instantiations of bwd_stream_kernel and finalize_kernel.
+#include "attnres_kernels.hpp"
+#include "attnres_internal.hpp"
+
+namespace attnres {
+
+#define ATTNRES_CASE(BF, CH, SB) \
+  case SB: return full ? (const void*)&bwd_stream_kernel<BF, CH, SB, true> \
+                       : (const void*)&bwd_stream_kernel<BF, CH, SB, false>;
+
+template <bool BF>
+static const void* stream_ptr(int ch, int sb, bool full) {
+  switch (ch) {
+    case 1: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE, BF, 1) default: break; } break;
+    case 2: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE, BF, 2) default: break; } break;
+    case 4: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE, BF, 4) default: break; } break;
+    default: break;
+  }
+  return nullptr;
+}
+
+const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full) {
+  return bf16 ? stream_ptr<true>(ch, sb, full) : stream_ptr<false>(ch, sb, full);
+}
+
+const void* finalize_kernel_ptr(bool bf16) {
+  return bf16 ? (const void*)&finalize_kernel<true> : (const void*)&finalize_kernel<false>;
+}
+
+}  // namespace attnres

@@ -1,0 +1,517 @@
+// attnres_host.cpp -- C ABI of the AttnRes read library: argument checks, launch planning and
+// kernel launches on the caller's stream. Declarations and contracts: include/attnres.h.
+//
+// Planning (everything derives from the descriptor and the current device):
+//   * a row of D elements is cut into 16-byte chunks; a workgroup of W <= 8 waves covers it with
+//     CH chunks per thread (CH = 1, 2 or 4, the smallest that keeps W <= 8);
+//   * the backward keeps a token's S rows in VGPRs when S fits a source-block bucket of that CH
+//     and no output norm is applied; otherwise it streams the sources and needs the forward's
+//     FP32 mixture o (attnres_o32_elems);
+//   * persistent grids: min(N, CUs x resident workgroups per CU from the occupancy calculator);
+//   * the backward writes one FP32 partial row per workgroup; the finaliser sums them over G row
+//     groups and merges the groups in a fixed order.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/attnres.h"
+#include "attnres_args.hpp"
+#include "attnres_internal.hpp"
+
+namespace {
+
+using namespace attnres;
+
+thread_local std::string g_err;
+
+attnres_status fail(attnres_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+attnres_status hip_fail(hipError_t e, const char* what) {
+  return fail(ATTNRES_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Optional tuning override read once from the environment: ATTNRES_CH forces chunks per thread
+// (1, 2 or 4) when the resulting workgroup still fits; ATTNRES_WG_PER_CU caps workgroups per CU.
+int env_int(const char* name) {
+  const char* v = std::getenv(name);
+  return v ? std::atoi(v) : 0;
+}
+
+// ------------------------------------------------------------------ shape (descriptor only)
+
+struct Shape {
+  bool bf16;
+  int vec, esz;
+  int ch, W, threads;
+  bool full;      // R == D
+  bool resident;  // backward keeps every source row of a token on chip
+  int sb_fwd, sb_bwd;
+};
+
+int bucket_at_least(int S, const int* b, int nb) {
+  for (int i = 0; i < nb; ++i)
+    if (b[i] >= S) return b[i];
+  return 0;
+}
+
+attnres_status check_desc(const attnres_desc* d) {
+  if (!d) return fail(ATTNRES_ERR_INVALID_ARG, "desc is NULL");
+  if (d->dtype != ATTNRES_F32 && d->dtype != ATTNRES_BF16)
+    return fail(ATTNRES_ERR_INVALID_ARG, "dtype %d is neither ATTNRES_F32 nor ATTNRES_BF16",
+                d->dtype);
+  if (d->S < 1 || d->S > kMaxSources)
+    return fail(ATTNRES_ERR_INVALID_ARG, "S=%d outside [1, %d]", d->S, kMaxSources);
+  if (d->D < 1 || d->R < 1 || d->R > d->D)
+    return fail(ATTNRES_ERR_INVALID_ARG, "need 1 <= R <= D (R=%d, D=%d)", d->R, d->D);
+  if (d->N < 0) return fail(ATTNRES_ERR_INVALID_ARG, "N=%lld is negative", (long long)d->N);
+  const int vec = d->dtype == ATTNRES_BF16 ? 8 : 4;
+  if (d->D % vec != 0)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "D=%d must be a multiple of %d for this dtype", d->D, vec);
+  const int dmax = d->dtype == ATTNRES_BF16 ? 16384 : 8192;
+  if (d->D < 8 || d->D > dmax)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "D=%d outside [8, %d] for this dtype", d->D, dmax);
+  if (!(d->eps >= 0.f) || d->eps > 3.0e38f)
+    return fail(ATTNRES_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!(d->scale == d->scale) || d->scale > 3.0e38f || d->scale < -3.0e38f)
+    return fail(ATTNRES_ERR_INVALID_ARG, "scale must be finite");
+  if (d->has_out_weight && !d->out_norm)
+    return fail(ATTNRES_ERR_INVALID_ARG, "has_out_weight requires out_norm");
+  return ATTNRES_OK;
+}
+
+attnres_status make_shape(const attnres_desc* d, Shape* sh) {
+  attnres_status st = check_desc(d);
+  if (st != ATTNRES_OK) return st;
+  sh->bf16 = d->dtype == ATTNRES_BF16;
+  sh->vec = sh->bf16 ? 8 : 4;
+  sh->esz = sh->bf16 ? 2 : 4;
+  const int chunks = d->D / sh->vec;
+  static const int forced = env_int("ATTNRES_CH");
+  int ch = 0;
+  if ((forced == 1 || forced == 2 || forced == 4) && (chunks + 64 * forced - 1) / (64 * forced) <= 8)
+    ch = forced;
+  if (!ch) {
+    for (int c : {1, 2, 4})
+      if ((chunks + 64 * c - 1) / (64 * c) <= 8) {
+        ch = c;
+        break;
+      }
+  }
+  if (!ch) return fail(ATTNRES_ERR_UNSUPPORTED, "D=%d too wide", d->D);
+  sh->ch = ch;
+  sh->W = (chunks + 64 * ch - 1) / (64 * ch);
+  sh->threads = 64 * sh->W;
+  sh->full = d->R == d->D;
+  const int* b = ch == 1 ? kSbCh1 : ch == 2 ? kSbCh2 : kSbCh4;
+  const int nb = ch == 1 ? (int)(sizeof kSbCh1 / sizeof(int))
+                 : ch == 2 ? (int)(sizeof kSbCh2 / sizeof(int))
+                           : (int)(sizeof kSbCh4 / sizeof(int));
+  const int fit = bucket_at_least(d->S, b, nb);
+  sh->resident = !d->out_norm && fit > 0;
+  // forward: one block when the sources fit a bucket, else blocks of the stream size
+  const int stream_max = ch == 4 ? 4 : 8;
+  sh->sb_fwd = fit > 0 ? fit : stream_max;
+  if (sh->resident) {
+    sh->sb_bwd = fit;
+  } else {
+    int s = bucket_at_least(d->S, kSbStream, (int)(sizeof kSbStream / sizeof(int)));
+    sh->sb_bwd = (s > 0 && s <= stream_max) ? s : stream_max;
+  }
+  return ATTNRES_OK;
+}
+
+const void* fwd_ptr(const Shape& sh) {
+  return sh.bf16 ? fwd_kernel_ptr_bf16(sh.ch, sh.sb_fwd, sh.full)
+                 : fwd_kernel_ptr_f32(sh.ch, sh.sb_fwd, sh.full);
+}
+
+const void* bwd_ptr(const Shape& sh) {
+  if (sh.resident)
+    return sh.bf16 ? bwd_resident_kernel_ptr_bf16(sh.ch, sh.sb_bwd, sh.full)
+                   : bwd_resident_kernel_ptr_f32(sh.ch, sh.sb_bwd, sh.full);
+  return bwd_stream_kernel_ptr(sh.bf16, sh.ch, sh.sb_bwd, sh.full);
+}
+
+size_t fwd_lds(const Shape& sh) { return 2u * (2u * sh.sb_fwd) * (4u * sh.W) * sizeof(float); }
+size_t bwd_lds(const Shape& sh) { return 2u * (3u * sh.sb_bwd) * (4u * sh.W) * sizeof(float); }
+
+// ------------------------------------------------------------------ device facts
+
+struct DevFacts {
+  int cus = 0;
+};
+
+attnres_status device_facts(DevFacts* f) {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(ATTNRES_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+    if (cus <= 0) return fail(ATTNRES_ERR_HIP, "device reports %d compute units", cus);
+    cached[dev] = cus;
+  }
+  f->cus = cached[dev];
+  return ATTNRES_OK;
+}
+
+attnres_status blocks_per_cu(const void* fn, int threads, size_t lds, int* out) {
+  int nb = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, lds);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  static const int cap = env_int("ATTNRES_WG_PER_CU");
+  if (cap > 0) nb = std::min(nb, cap);
+  if (nb <= 0) return fail(ATTNRES_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)");
+  *out = nb;
+  return ATTNRES_OK;
+}
+
+// ------------------------------------------------------------------ backward plan
+
+struct BwdPlan {
+  int P = 0;           // backward workgroups = partial rows
+  int G = 1;           // finaliser row groups
+  int cols = 0;        // R (+ D with the output-norm weight)
+  int n_counters = 0;  // one per 256 columns
+  size_t off_du = 0, off_dow = 0, off_l2 = 0, bytes = 0;
+};
+
+constexpr size_t kCounterBytes = 1024;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+attnres_status plan_bwd(const attnres_desc* d, const Shape& sh, BwdPlan* pl) {
+  const void* fn = bwd_ptr(sh);
+  if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no backward kernel for this shape");
+  DevFacts f;
+  attnres_status st = device_facts(&f);
+  if (st != ATTNRES_OK) return st;
+  int per_cu = 0;
+  st = blocks_per_cu(fn, sh.threads, bwd_lds(sh), &per_cu);
+  if (st != ATTNRES_OK) return st;
+  const int64_t cap = (int64_t)f.cus * per_cu;
+  pl->P = (int)std::min<int64_t>(d->N, cap);
+  pl->cols = d->R + (d->has_out_weight ? d->D : 0);
+  pl->n_counters = (pl->cols + 255) / 256;
+  int G = 1;
+  if (pl->P > 64) {
+    G = std::min(64, std::max(1, pl->P / 16));
+    while (G > 1 && (int64_t)pl->n_counters * G > 1024) G /= 2;
+  }
+  pl->G = G;
+  pl->off_du = kCounterBytes;
+  pl->off_dow = align256(pl->off_du + (size_t)pl->P * d->R * sizeof(float));
+  pl->off_l2 = align256(pl->off_dow +
+                        (d->has_out_weight ? (size_t)pl->P * d->D * sizeof(float) : 0));
+  pl->bytes = align256(pl->off_l2 + (G > 1 ? (size_t)G * pl->cols * sizeof(float) : 0));
+  return ATTNRES_OK;
+}
+
+// ------------------------------------------------------------------ pointer checks
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  const char* what;
+};
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Byte range of one [N, D] row block with the given row stride.
+Range rows_range(const void* p, int64_t N, int64_t rs, int D, int esz, const char* what) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  const uintptr_t len = N > 0 ? (uintptr_t)(((N - 1) * rs + D) * esz) : 0;
+  return Range{lo, lo + len, what};
+}
+
+attnres_status check_sources(const attnres_desc* d, const Shape& sh, const attnres_sources* src,
+                             const char* what, const void** out_ptrs) {
+  if (!src) return fail(ATTNRES_ERR_INVALID_ARG, "%s is NULL", what);
+  if ((src->packed == nullptr) == (src->list == nullptr))
+    return fail(ATTNRES_ERR_INVALID_ARG, "%s: exactly one of packed / list must be set", what);
+  if (src->row_stride < d->D)
+    return fail(ATTNRES_ERR_INVALID_ARG, "%s: row_stride %lld < D %d", what,
+                (long long)src->row_stride, d->D);
+  if ((src->row_stride * sh.esz) % 16 != 0)
+    return fail(ATTNRES_ERR_ALIGNMENT, "%s: row stride is not a multiple of 16 bytes", what);
+  for (int s = 0; s < d->S; ++s) {
+    const void* p;
+    if (src->packed) {
+      if ((src->src_stride * sh.esz) % 16 != 0)
+        return fail(ATTNRES_ERR_ALIGNMENT, "%s: src_stride is not a multiple of 16 bytes", what);
+      p = static_cast<const char*>(src->packed) + (int64_t)s * src->src_stride * sh.esz;
+    } else {
+      p = src->list[s];
+    }
+    if (!p) return fail(ATTNRES_ERR_INVALID_ARG, "%s: source %d is NULL", what, s);
+    if (!aligned(p, 16)) return fail(ATTNRES_ERR_ALIGNMENT, "%s: source %d not 16-byte aligned", what, s);
+    out_ptrs[s] = p;
+  }
+  return ATTNRES_OK;
+}
+
+attnres_status check_param(const void* p, bool want, int esz, const char* what) {
+  if (want && !p) return fail(ATTNRES_ERR_INVALID_ARG, "%s is required", what);
+  if (!want && p) return fail(ATTNRES_ERR_INVALID_ARG, "%s must be NULL for this descriptor", what);
+  if (p && !aligned(p, esz)) return fail(ATTNRES_ERR_ALIGNMENT, "%s is misaligned", what);
+  return ATTNRES_OK;
+}
+
+attnres_status check_disjoint(const std::vector<Range>& outs, const std::vector<Range>& ins) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    if (outs[i].lo == outs[i].hi) continue;
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(ATTNRES_ERR_INVALID_ARG, "output %s overlaps output %s", outs[i].what,
+                    outs[j].what);
+    for (const Range& r : ins)
+      if (overlap(outs[i], r))
+        return fail(ATTNRES_ERR_INVALID_ARG, "output %s overlaps input %s", outs[i].what, r.what);
+  }
+  return ATTNRES_OK;
+}
+
+attnres_status launch(const void* fn, unsigned grid_x, unsigned grid_y, int threads, size_t lds,
+                      void* args, void* stream, const char* what) {
+  void* kargs[] = {args};
+  hipError_t e = hipLaunchKernel(fn, dim3(grid_x, grid_y, 1), dim3(threads, 1, 1), kargs, lds,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, what);
+  return ATTNRES_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+const char* attnres_status_str(attnres_status s) {
+  switch (s) {
+    case ATTNRES_OK: return "ok";
+    case ATTNRES_ERR_INVALID_ARG: return "invalid argument";
+    case ATTNRES_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTNRES_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case ATTNRES_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTNRES_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* attnres_last_error(void) { return g_err.c_str(); }
+
+attnres_status attnres_o32_elems(const attnres_desc* d, size_t* elems) {
+  g_err.clear();
+  if (!elems) return fail(ATTNRES_ERR_INVALID_ARG, "elems is NULL");
+  Shape sh;
+  attnres_status st = make_shape(d, &sh);
+  if (st != ATTNRES_OK) return st;
+  *elems = sh.resident ? 0 : (size_t)d->N * d->D;
+  return ATTNRES_OK;
+}
+
+attnres_status attnres_workspace_bytes(const attnres_desc* d, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(ATTNRES_ERR_INVALID_ARG, "bytes is NULL");
+  Shape sh;
+  attnres_status st = make_shape(d, &sh);
+  if (st != ATTNRES_OK) return st;
+  BwdPlan pl;
+  st = plan_bwd(d, sh, &pl);
+  if (st != ATTNRES_OK) return st;
+  *bytes = pl.bytes;
+  return ATTNRES_OK;
+}
+
+attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
+                           const void* query, const void* norm_w, const void* out_w, void* out,
+                           float* lse, float* out_rstd, float* o32, void* stream) {
+  g_err.clear();
+  Shape sh;
+  attnres_status st = make_shape(d, &sh);
+  if (st != ATTNRES_OK) return st;
+  FwdArgs a;
+  std::memset(&a, 0, sizeof a);
+  st = check_sources(d, sh, values, "values", a.src);
+  if (st != ATTNRES_OK) return st;
+  if ((st = check_param(query, true, sh.esz, "query")) != ATTNRES_OK) return st;
+  if ((st = check_param(norm_w, d->has_norm_weight, sh.esz, "norm_w")) != ATTNRES_OK) return st;
+  if ((st = check_param(out_w, d->has_out_weight, sh.esz, "out_w")) != ATTNRES_OK) return st;
+  if (!out || !aligned(out, 16))
+    return fail(out ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "out NULL or misaligned");
+  if (!lse || !aligned(lse, 4))
+    return fail(lse ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "lse NULL or misaligned");
+  if ((st = check_param(out_rstd, d->out_norm, 4, "out_rstd")) != ATTNRES_OK) return st;
+  const bool need_o32 = !sh.resident;
+  if ((st = check_param(o32, need_o32, 16, "o32")) != ATTNRES_OK) return st;
+
+  const int64_t N = d->N;
+  std::vector<Range> ins, outs;
+  for (int s = 0; s < d->S; ++s)
+    ins.push_back(rows_range(a.src[s], N, values->row_stride, d->D, sh.esz, "values"));
+  outs.push_back(rows_range(out, N, d->D, d->D, sh.esz, "out"));
+  outs.push_back(rows_range(lse, N, 1, 1, 4, "lse"));
+  if (out_rstd) outs.push_back(rows_range(out_rstd, N, 1, 1, 4, "out_rstd"));
+  if (o32) outs.push_back(rows_range(o32, N, d->D, d->D, 4, "o32"));
+  if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
+  if (N == 0) return ATTNRES_OK;
+
+  const void* fn = fwd_ptr(sh);
+  if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no forward kernel for this shape");
+  DevFacts f;
+  if ((st = device_facts(&f)) != ATTNRES_OK) return st;
+  int per_cu = 0;
+  if ((st = blocks_per_cu(fn, sh.threads, fwd_lds(sh), &per_cu)) != ATTNRES_OK) return st;
+  const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
+
+  a.row_stride = values->row_stride;
+  a.N = N;
+  a.S = d->S;
+  a.D = d->D;
+  a.R = d->R;
+  a.lo = d->D - d->R;
+  a.eps = d->eps;
+  a.scale = d->scale;
+  a.inv_R = 1.0f / (float)d->R;
+  a.inv_D = 1.0f / (float)d->D;
+  a.query = query;
+  a.norm_w = norm_w;
+  a.out_w = out_w;
+  a.y = out;
+  a.lse = lse;
+  a.o_rstd = out_rstd;
+  a.o32 = o32;
+  a.out_norm = d->out_norm ? 1 : 0;
+  return launch(fn, grid, 1, sh.threads, fwd_lds(sh), &a, stream, "forward launch");
+}
+
+attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
+                           const void* query, const void* norm_w, const void* out_w,
+                           const float* lse, const float* out_rstd, const float* o32,
+                           const void* dout, int64_t dout_row_stride,
+                           const attnres_sources* dvalues, void* dq, void* dw, void* dow,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Shape sh;
+  attnres_status st = make_shape(d, &sh);
+  if (st != ATTNRES_OK) return st;
+  BwdArgs a;
+  std::memset(&a, 0, sizeof a);
+  st = check_sources(d, sh, values, "values", a.src);
+  if (st != ATTNRES_OK) return st;
+  const void* dptr[kMaxSources];
+  st = check_sources(d, sh, dvalues, "dvalues", dptr);
+  if (st != ATTNRES_OK) return st;
+  if ((st = check_param(query, true, sh.esz, "query")) != ATTNRES_OK) return st;
+  if ((st = check_param(norm_w, d->has_norm_weight, sh.esz, "norm_w")) != ATTNRES_OK) return st;
+  if ((st = check_param(out_w, d->has_out_weight, sh.esz, "out_w")) != ATTNRES_OK) return st;
+  if (!lse || !aligned(lse, 4))
+    return fail(lse ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "lse NULL or misaligned");
+  if ((st = check_param(out_rstd, d->out_norm, 4, "out_rstd")) != ATTNRES_OK) return st;
+  if ((st = check_param(o32, !sh.resident, 16, "o32")) != ATTNRES_OK) return st;
+  if (!dout || !aligned(dout, 16))
+    return fail(dout ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "dout NULL or misaligned");
+  if (dout_row_stride < d->D || (dout_row_stride * sh.esz) % 16 != 0)
+    return fail(ATTNRES_ERR_ALIGNMENT, "dout_row_stride must be >= D and a multiple of 16 bytes");
+  if ((st = check_param(dq, true, sh.esz, "dq")) != ATTNRES_OK) return st;
+  if ((st = check_param(dw, d->has_norm_weight, sh.esz, "dw")) != ATTNRES_OK) return st;
+  if ((st = check_param(dow, d->has_out_weight, sh.esz, "dow")) != ATTNRES_OK) return st;
+  if (!workspace) return fail(ATTNRES_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(ATTNRES_ERR_ALIGNMENT, "workspace not 256-byte aligned");
+
+  const int64_t N = d->N;
+  std::vector<Range> ins, outs;
+  for (int s = 0; s < d->S; ++s)
+    ins.push_back(rows_range(a.src[s], N, values->row_stride, d->D, sh.esz, "values"));
+  ins.push_back(rows_range(dout, N, dout_row_stride, d->D, sh.esz, "dout"));
+  ins.push_back(rows_range(lse, N, 1, 1, 4, "lse"));
+  if (o32) ins.push_back(rows_range(o32, N, d->D, d->D, 4, "o32"));
+  if (out_rstd) ins.push_back(rows_range(out_rstd, N, 1, 1, 4, "out_rstd"));
+  for (int s = 0; s < d->S; ++s)
+    outs.push_back(rows_range(dptr[s], N, dvalues->row_stride, d->D, sh.esz, "dvalues"));
+  outs.push_back(rows_range(dq, 1, d->R, d->R, sh.esz, "dq"));
+  if (dw) outs.push_back(rows_range(dw, 1, d->R, d->R, sh.esz, "dw"));
+  if (dow) outs.push_back(rows_range(dow, 1, d->D, d->D, sh.esz, "dow"));
+  if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
+
+  BwdPlan pl;
+  if ((st = plan_bwd(d, sh, &pl)) != ATTNRES_OK) return st;
+  if (workspace_bytes < pl.bytes)
+    return fail(ATTNRES_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                pl.bytes);
+  const void* fn = bwd_ptr(sh);
+  const void* fin = finalize_kernel_ptr(sh.bf16);
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
+
+  if (pl.P > 0) {
+    for (int s = 0; s < d->S; ++s) a.dsrc[s] = const_cast<void*>(dptr[s]);
+    a.row_stride = values->row_stride;
+    a.drow_stride = dvalues->row_stride;
+    a.dout_stride = dout_row_stride;
+    a.N = N;
+    a.S = d->S;
+    a.D = d->D;
+    a.R = d->R;
+    a.lo = d->D - d->R;
+    a.eps = d->eps;
+    a.scale = d->scale;
+    a.inv_R = 1.0f / (float)d->R;
+    a.inv_D = 1.0f / (float)d->D;
+    a.query = query;
+    a.norm_w = norm_w;
+    a.out_w = out_w;
+    a.lse = lse;
+    a.o_rstd = out_rstd;
+    a.o32 = o32;
+    a.dout = dout;
+    a.part_du = reinterpret_cast<float*>(ws + pl.off_du);
+    a.part_dow = d->has_out_weight ? reinterpret_cast<float*>(ws + pl.off_dow) : nullptr;
+    a.counters = counters;
+    a.n_counters = pl.n_counters;
+    a.out_norm = d->out_norm ? 1 : 0;
+    st = launch(fn, pl.P, 1, sh.threads, bwd_lds(sh), &a, stream, "backward launch");
+    if (st != ATTNRES_OK) return st;
+  }
+
+  FinArgs fa;
+  std::memset(&fa, 0, sizeof fa);
+  fa.part_du = reinterpret_cast<const float*>(ws + pl.off_du);
+  fa.part_dow = d->has_out_weight ? reinterpret_cast<const float*>(ws + pl.off_dow) : nullptr;
+  fa.level2 = reinterpret_cast<float*>(ws + pl.off_l2);
+  fa.counters = counters;
+  fa.P = pl.P;
+  fa.R = d->R;
+  fa.D = d->D;
+  fa.G = pl.G;
+  fa.cols = pl.cols;
+  fa.query = query;
+  fa.norm_w = norm_w;
+  fa.dq = dq;
+  fa.dw = dw;
+  fa.dow = dow;
+  return launch(fin, pl.n_counters, pl.G, 256, 0, &fa, stream, "finalize launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// attnres_internal.hpp -- host-side tables shared by the dispatcher and the instantiation files.
+#pragma once
+
+namespace attnres {
+
+// Source-block sizes instantiated per chunks-per-thread CH. A token's rows are kept on chip when
+// S <= the largest bucket of its CH (the register budget: SB * CH 16-byte chunks per thread).
+#define ATTNRES_SB_CH1(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 4) \
+  M(__VA_ARGS__, 8) M(__VA_ARGS__, 10) M(__VA_ARGS__, 12) M(__VA_ARGS__, 16)       \
+  M(__VA_ARGS__, 24)
+#define ATTNRES_SB_CH2(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 4) \
+  M(__VA_ARGS__, 8) M(__VA_ARGS__, 10) M(__VA_ARGS__, 12)
+#define ATTNRES_SB_CH4(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 4)
+// Streaming backward source blocks.
+#define ATTNRES_SB_STREAM(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 4) \
+  M(__VA_ARGS__, 8)
+
+inline constexpr int kSbCh1[] = {1, 2, 4, 8, 10, 12, 16, 24};
+inline constexpr int kSbCh2[] = {1, 2, 4, 8, 10, 12};
+inline constexpr int kSbCh4[] = {1, 2, 4};
+inline constexpr int kSbStream[] = {1, 2, 4, 8};
+
+// Largest workgroup any kernel is launched with (matches the kernels' launch bounds).
+inline constexpr int kMaxThreads = 512;
+
+// Kernel entry points by configuration; nullptr when that configuration is not built.
+const void* fwd_kernel_ptr_bf16(int ch, int sb, bool full);
+const void* fwd_kernel_ptr_f32(int ch, int sb, bool full);
+const void* bwd_resident_kernel_ptr_bf16(int ch, int sb, bool full);
+const void* bwd_resident_kernel_ptr_f32(int ch, int sb, bool full);
+const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full);
+const void* finalize_kernel_ptr(bool bf16);
+
+}  // namespace attnres

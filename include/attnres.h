@@ -1,0 +1,132 @@
+/*
+ * attnres.h -- C ABI of the MI355X (gfx950) Attention Residuals (AttnRes) read library.
+ *
+ * The operation ("Fast Attention Residuals" PyPI page, section "Equation"): for every token n and
+ * each of S ordered residual sources v_s[n, 0..D-1], the key is the final R coordinates
+ * t_s = v_s[n, D-R..D-1]; r_s = sqrt(mean(t_s^2) + eps); k_s = (t_s / r_s) * w (w = optional
+ * key-norm weight, 1 when absent); score_s = scale * <k_s, q>; p = softmax over the S sources;
+ * o = sum_s p_s v_s. Tokens are independent; the output keeps width D. Optionally
+ * ("[Perf] Parallelize AttnRes long-sequence reduction", FLA PR page, Summary) an output RMSNorm
+ * follows: y = o * rho_o * ow with rho_o = (mean_D(o^2) + eps)^(-1/2) saved per row (o_rstd) for
+ * the backward, ow optional. Without it y = o.
+ * The backward (same PR page: dq/dw/dow reduced over the flattened token dimension in FP32
+ * partials and finalised by a separate kernel) returns dvalues for every source row and the
+ * gradients of q, w and ow summed over all N tokens. It recomputes the routing weights from the
+ * saved per-row log-sum-exp.
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers of the current HIP device unless stated otherwise.
+ *     The caller owns every buffer; the library never allocates, frees or synchronises.
+ *   - Every kernel is enqueued on `stream` (a hipStream_t; NULL = the null stream). Calls return
+ *     once the work is enqueued. They record no memset or copy node, so they can be captured
+ *     into a HIP graph.
+ *   - Storage dtype (values, query, weights, outputs and gradients) is the descriptor's dtype;
+ *     all arithmetic is FP32; FP32 -> bfloat16 stores round to nearest even.
+ *   - Errors: argument checks run before anything is enqueued; on failure nothing is launched
+ *     or written and a nonzero status is returned. attnres_last_error() gives the calling
+ *     thread's detail text. No exception or abort crosses this boundary.
+ *   - Concurrency: calls on different streams may run concurrently as long as they share no
+ *     output buffer and no workspace.
+ */
+#ifndef ATTNRES_H
+#define ATTNRES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTNRES_OK = 0,
+  ATTNRES_ERR_INVALID_ARG = 1,   /* a size, pointer or flag is out of contract */
+  ATTNRES_ERR_UNSUPPORTED = 2,   /* within the math's domain but outside what is built */
+  ATTNRES_ERR_ALIGNMENT = 3,     /* a pointer or row stride is not 16-byte aligned */
+  ATTNRES_ERR_WORKSPACE = 4,     /* workspace missing or smaller than attnres_workspace_bytes */
+  ATTNRES_ERR_HIP = 5            /* a HIP runtime call failed (text in attnres_last_error) */
+} attnres_status;
+
+typedef enum { ATTNRES_F32 = 0, ATTNRES_BF16 = 1 } attnres_dtype;
+
+/* Problem descriptor, passed by pointer and validated on every call. */
+typedef struct {
+  int32_t S;               /* sources, 1 <= S <= 64 */
+  int32_t D;               /* width; D % 8 == 0 (bf16) or D % 4 == 0 (f32); 8 <= D <= 16384 */
+  int32_t R;               /* routing rank, 1 <= R <= D; key = final R coordinates */
+  int32_t dtype;           /* attnres_dtype */
+  int64_t N;               /* tokens, N >= 0 (N == 0 is a no-op apart from zeroed gradients) */
+  float eps;               /* inside both square roots; the pages' default is 2^-23 */
+  float scale;             /* score multiplier; default 1 */
+  int32_t has_norm_weight; /* key-norm weight w[R] present */
+  int32_t out_norm;        /* output RMSNorm after the mixture */
+  int32_t has_out_weight;  /* output-norm weight ow[D] present (requires out_norm) */
+} attnres_desc;
+
+/* S row blocks of shape [N, D]: either one packed [S, N, D] tensor or a list of S pointers.
+ * Exactly one of `packed` / `list` is non-NULL.
+ *   packed:     base of source 0; source s starts at packed + s * src_stride elements.
+ *   list:       HOST array of S device pointers (read during the call only). A list may repeat a
+ *               pointer when it describes inputs (a source read twice); for outputs every
+ *               pointer must be distinct.
+ *   row_stride: elements between token n and token n+1 inside a source (>= D); elements of a
+ *               row are contiguous. */
+typedef struct {
+  void* packed;
+  int64_t src_stride;
+  void* const* list;
+  int64_t row_stride;
+} attnres_sources;
+
+/* Number of FP32 elements of the saved mixture o32 that the forward must write for a later
+ * backward: N*D when the backward streams the sources (output RMSNorm on, or S*D too large to
+ * keep a token's rows on chip), else 0. */
+attnres_status attnres_o32_elems(const attnres_desc* desc, size_t* elems);
+
+/* Bytes of device workspace attnres_bwd needs on the CURRENT device (FP32 partial sums of the
+ * q/w/ow gradients, one row per workgroup of the backward, plus the finaliser's counters). The
+ * contents need no initialisation; the backward leaves them in a reusable state. */
+attnres_status attnres_workspace_bytes(const attnres_desc* desc, size_t* bytes);
+
+/* Forward.
+ *   values   [S][N, D] sources (read).
+ *   query    [R]; norm_w [R] iff has_norm_weight; out_w [D] iff has_out_weight.
+ *   out      [N, D] contiguous output y (written).
+ *   lse      [N] FP32 log-sum-exp of the scores (written; the backward's saved statistic).
+ *   out_rstd [N] FP32 rho_o (written iff out_norm, else must be NULL).
+ *   o32      [N, D] FP32 mixture o (written iff attnres_o32_elems > 0, else must be NULL).
+ * All device pointers 16-byte aligned; row strides multiples of 16 bytes. */
+attnres_status attnres_fwd(const attnres_desc* desc, const attnres_sources* values,
+                           const void* query, const void* norm_w, const void* out_w,
+                           void* out, float* lse, float* out_rstd, float* o32,
+                           void* stream);
+
+/* Backward, given the forward's inputs and saved statistics.
+ *   dout            [N, D] upstream gradient dL/dy with row stride dout_row_stride (read).
+ *   dvalues         [S][N, D] gradients of the sources (written, fully overwritten); must not
+ *                   alias values or each other.
+ *   dq [R]          gradient of the query, summed over tokens (written).
+ *   dw [R]          gradient of the key-norm weight (iff has_norm_weight, else NULL).
+ *   dow [D]         gradient of the output-norm weight (iff has_out_weight, else NULL).
+ *   workspace       at least attnres_workspace_bytes(desc) bytes, 256-byte aligned; not shared
+ *                   with any concurrent call.
+ * Reductions over tokens use a fixed order: repeated calls give bitwise-identical results. */
+attnres_status attnres_bwd(const attnres_desc* desc, const attnres_sources* values,
+                           const void* query, const void* norm_w, const void* out_w,
+                           const float* lse, const float* out_rstd, const float* o32,
+                           const void* dout, int64_t dout_row_stride,
+                           const attnres_sources* dvalues,
+                           void* dq, void* dw, void* dow,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* attnres_status_str(attnres_status status);
+
+/* Detail of the calling thread's most recent failure ("" if none). Valid until the thread's
+ * next call into this library. */
+const char* attnres_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTNRES_H */

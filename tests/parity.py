@@ -1,0 +1,192 @@
+"""Parity helpers: run the HIP path and the FP64 oracle on the same seeded inputs and compare.
+
+Tolerances (written here, applied in every GPU parity test):
+  * FP32 storage: max |gpu - ref| <= 1e-5 * rms(ref) for every output (y, dvalues, dq, dw, dow).
+  * BF16 storage, y and dvalues (and dow): the literal bound 2e-2 * rms(ref) applied to the error
+    beyond the rounding that any bf16 result must carry:
+        max_i (|gpu_i - ref_i| - half_ulp_bf16(max(|gpu_i|, |ref_i|))) <= 2e-2 * rms(ref).
+    Storing the exactly rounded oracle in bf16 alone already gives max |err| / rms of several
+    1e-2 on large-magnitude elements, so the literal bound without the half ulp rejects even the
+    correctly rounded answer. The literal ratio is reported alongside.
+  * BF16 dq and dw: relative L2 error ||gpu - ref|| / ||ref|| <= 1e-2.
+  * FP32 per-row statistics lse and o_rstd: |gpu - ref| <= 2e-5 * (1 + |ref|).
+rms(x) = sqrt(mean(x^2)) over the whole compared tensor.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+import attnres_workloads as W
+import oracle
+
+TOL_F32 = 1e-5
+TOL_BF16_ROWS = 2e-2
+TOL_BF16_VEC = 1e-2
+TOL_STAT = 2e-5
+
+
+def gpu_available() -> bool:
+    return torch.cuda.is_available()
+
+
+def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Half a bfloat16 ulp at |x| (8 significant bits): 2^(exponent - 8)."""
+    ax = np.abs(x)
+    _, k = np.frexp(np.where(ax > 0, ax, 1.0))  # ax = m 2^k, 0.5 <= m < 1
+    h = np.ldexp(1.0, k - 9)
+    return np.where(ax > 0, h, 0.0)
+
+
+def rms(x: np.ndarray) -> float:
+    return float(np.sqrt(np.mean(np.square(x, dtype=np.float64)))) if x.size else 0.0
+
+
+def compare_rows(g: np.ndarray, r: np.ndarray, dtype: str) -> dict:
+    """Element-by-element comparison of a row tensor (y, dvalues, dow)."""
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    scale = rms(r)
+    err = np.abs(g - r)
+    literal = float(err.max() / scale) if scale > 0 else float(err.max())
+    if dtype == "f32":
+        return {"literal": literal, "metric": literal, "tol": TOL_F32, "ok": literal <= TOL_F32,
+                "finite": bool(np.isfinite(g).all())}
+    excess = err - half_ulp_bf16(np.maximum(np.abs(g), np.abs(r)))
+    metric = float(max(excess.max(), 0.0) / scale) if scale > 0 else float(max(excess.max(), 0))
+    return {"literal": literal, "metric": metric, "tol": TOL_BF16_ROWS,
+            "ok": metric <= TOL_BF16_ROWS and bool(np.isfinite(g).all()),
+            "finite": bool(np.isfinite(g).all())}
+
+
+def compare_vec(g: np.ndarray, r: np.ndarray, dtype: str) -> dict:
+    """Comparison of a reduced gradient (dq, dw)."""
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    assert g.shape == r.shape
+    nr = float(np.linalg.norm(r))
+    rel = float(np.linalg.norm(g - r) / nr) if nr > 0 else float(np.linalg.norm(g))
+    if dtype == "f32":
+        scale = rms(r)
+        lit = float(np.abs(g - r).max() / scale) if scale > 0 else float(np.abs(g - r).max())
+        return {"literal": lit, "metric": lit, "rel_l2": rel, "tol": TOL_F32,
+                "ok": lit <= TOL_F32 or (scale == 0 and lit <= 1e-30)}
+    return {"rel_l2": rel, "metric": rel, "tol": TOL_BF16_VEC,
+            "ok": (rel <= TOL_BF16_VEC) if nr > 0 else (np.abs(g).max() <= 1e-30)}
+
+
+def compare_stat(g: np.ndarray, r: np.ndarray) -> dict:
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    err = np.abs(g - r) / (1.0 + np.abs(r))
+    m = float(err.max()) if err.size else 0.0
+    return {"metric": m, "tol": TOL_STAT, "ok": m <= TOL_STAT}
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def inputs_on(x: dict, device: str) -> dict:
+    return {k: (None if v is None else v.to(device)) for k, v in x.items()}
+
+
+def poison_(t: Optional[torch.Tensor]) -> None:
+    """Fills a freshly allocated output with NaN so unwritten elements cannot pass."""
+    if t is None:
+        return
+    if t.dtype in (torch.float32, torch.bfloat16, torch.float16):
+        t.fill_(float("nan"))
+    else:
+        t.fill_(0xFF)
+
+
+def run_gpu(w: W.Workload, xg: dict, *, packed: bool = True, poison: bool = True,
+            values=None, dvalues=None, dout=None, stream=None) -> dict:
+    """Forward + backward through the C ABI on the device tensors xg; returns device tensors."""
+    import attention_residuals_amd as A
+    v = xg["values"] if values is None else values
+    if values is None and not packed:
+        v = [xg["values"][s] for s in range(w.S)]
+    dev = xg["query"].device
+    N, D = w.N, w.D
+    desc = A.make_desc(w.S, N, D, w.R, w.torch_dtype, eps=w.eps, scale=w.scale,
+                       has_norm_weight=xg["norm_w"] is not None, out_norm=w.out_norm,
+                       has_out_weight=xg["out_w"] is not None)
+    y = torch.empty((N, D), dtype=w.torch_dtype, device=dev)
+    lse = torch.empty((N,), dtype=torch.float32, device=dev)
+    rstd = torch.empty((N,), dtype=torch.float32, device=dev) if w.out_norm else None
+    n32 = A.o32_elems(desc)
+    o32 = torch.empty((N, D), dtype=torch.float32, device=dev) if n32 else None
+    if dvalues is None:
+        dvalues = torch.empty((w.S, N, D), dtype=w.torch_dtype, device=dev)
+        if not packed:
+            dvalues = [dvalues[s] for s in range(w.S)]
+    dq = torch.empty((w.R,), dtype=w.torch_dtype, device=dev)
+    dw = torch.empty((w.R,), dtype=w.torch_dtype, device=dev) if xg["norm_w"] is not None else None
+    dow = torch.empty((D,), dtype=w.torch_dtype, device=dev) if xg["out_w"] is not None else None
+    ws = torch.empty((max(A.workspace_bytes(desc), 256),), dtype=torch.uint8, device=dev)
+    if poison:
+        for t in (y, lse, rstd, o32, dq, dw, dow):
+            poison_(t)
+        for t in (dvalues if isinstance(dvalues, list) else [dvalues]):
+            poison_(t)
+        ws.fill_(0xFF)
+    A.attnres_fwd(v, xg["query"], xg["norm_w"], xg["out_w"], eps=w.eps, scale=w.scale,
+                  out_norm=w.out_norm, out=y, lse=lse, out_rstd=rstd, o32=o32, stream=stream)
+    g = xg["dout"] if dout is None else dout
+    A.attnres_bwd(v, xg["query"], xg["norm_w"], xg["out_w"], lse, rstd, o32, g, eps=w.eps,
+                  scale=w.scale, out_norm=w.out_norm, dvalues=dvalues, dq=dq, dw=dw, dow=dow,
+                  workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    dv = torch.stack(dvalues) if isinstance(dvalues, list) else dvalues
+    return {"y": y, "lse": lse, "o_rstd": rstd, "o32": o32, "dvalues": dv, "dq": dq, "dw": dw,
+            "dow": dow}
+
+
+def run_oracle(w: W.Workload, xc: dict, tokens: Optional[Sequence[int]] = None,
+               reduce: bool = True, want=("y", "lse", "o_rstd", "dvalues")) -> dict:
+    return oracle.run(xc["values"], xc["query"], xc["norm_w"], xc["out_w"], xc["dout"],
+                      eps=w.eps, scale=w.scale, out_norm=w.out_norm, tokens=tokens,
+                      want=want, reduce=reduce)
+
+
+def check_all(w: W.Workload, got: dict, ref: dict, tokens: Optional[Sequence[int]] = None,
+              check_reduced: bool = True) -> dict:
+    """Compares GPU outputs (device tensors, all tokens) with oracle outputs (for `tokens`)."""
+    res = {}
+    idx = None if tokens is None else torch.as_tensor(np.asarray(tokens), dtype=torch.long,
+                                                      device=got["y"].device)
+
+    def rows(t, dim=0):
+        return t if idx is None else t.index_select(dim, idx)
+
+    res["y"] = compare_rows(to_f64(rows(got["y"])), ref["y"], w.dtype)
+    res["lse"] = compare_stat(to_f64(rows(got["lse"])), ref["lse"])
+    if w.out_norm:
+        res["o_rstd"] = compare_stat(to_f64(rows(got["o_rstd"])), ref["o_rstd"])
+    res["dvalues"] = compare_rows(to_f64(rows(got["dvalues"], 1)), ref["dvalues"], w.dtype)
+    if check_reduced:
+        res["dq"] = compare_vec(to_f64(got["dq"]), ref["dq"], w.dtype)
+        if got["dw"] is not None:
+            res["dw"] = compare_vec(to_f64(got["dw"]), ref["dw"], w.dtype)
+        if got["dow"] is not None:
+            res["dow"] = compare_rows(to_f64(got["dow"]), ref["dow"], w.dtype)
+    return res
+
+
+def assert_ok(res: dict, label: str) -> None:
+    bad = {k: v for k, v in res.items() if not v["ok"]}
+    summary = ", ".join(f"{k}={v['metric']:.3g}" for k, v in res.items())
+    print(f"[parity] {label}: {summary}", flush=True)
+    assert not bad, f"{label}: out of tolerance: {bad}"
+
+
+def sample_tokens(N: int, k: int, seed: int) -> list:
+    rng = np.random.default_rng(seed)
+    picks = set([0, N - 1, N // 2]) | set(rng.integers(0, N, size=k).tolist())
+    return sorted(t for t in picks if 0 <= t < N)
