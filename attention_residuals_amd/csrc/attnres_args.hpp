@@ -7,6 +7,10 @@ namespace attnres {
 
 constexpr int kMaxSources = 64;
 
+// Finaliser workgroup: 64 columns x 16 row phases.
+constexpr int kFinCols = 64;
+constexpr int kFinPhases = 16;
+
 struct FwdArgs {
   const void* src[kMaxSources];  // base of source s ([N, D] rows, row_stride elements apart)
   int64_t row_stride;
@@ -39,17 +43,13 @@ struct BwdArgs {
   const void* dout;
   float* part_du;                // [gridDim.x, R]
   float* part_dow;               // [gridDim.x, D] or nullptr
-  uint32_t* counters;            // finaliser counters, zeroed here for the finaliser
-  int n_counters;
   int out_norm;
 };
 
 struct FinArgs {
   const float* part_du;          // [P, R]
   const float* part_dow;         // [P, D] or nullptr
-  float* level2;                 // [G, cols]
-  uint32_t* counters;            // [ceil(cols / 256)]
-  int P, R, D, G, cols;
+  int P, R, D, cols;             // cols = R (+ D when dow is wanted)
   const void* query;
   const void* norm_w;            // nullptr: dq = du and no dw
   void* dq;

@@ -8,8 +8,8 @@
 //     and no output norm is applied; otherwise it streams the sources and needs the forward's
 //     FP32 mixture o (attnres_o32_elems);
 //   * persistent grids: min(N, CUs x resident workgroups per CU from the occupancy calculator);
-//   * the backward writes one FP32 partial row per workgroup; the finaliser sums them over G row
-//     groups and merges the groups in a fixed order.
+//   * the backward writes one FP32 partial row per workgroup; the finaliser sums each column's
+//     rows in a fixed order (64 columns per workgroup, 16 row phases merged through LDS).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -191,14 +191,10 @@ attnres_status blocks_per_cu(const void* fn, int threads, size_t lds, int* out) 
 // ------------------------------------------------------------------ backward plan
 
 struct BwdPlan {
-  int P = 0;           // backward workgroups = partial rows
-  int G = 1;           // finaliser row groups
-  int cols = 0;        // R (+ D with the output-norm weight)
-  int n_counters = 0;  // one per 256 columns
-  size_t off_du = 0, off_dow = 0, off_l2 = 0, bytes = 0;
+  int P = 0;     // backward workgroups = partial rows
+  int cols = 0;  // R (+ D with the output-norm weight)
+  size_t off_du = 0, off_dow = 0, bytes = 0;
 };
-
-constexpr size_t kCounterBytes = 1024;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -214,18 +210,11 @@ attnres_status plan_bwd(const attnres_desc* d, const Shape& sh, BwdPlan* pl) {
   const int64_t cap = (int64_t)f.cus * per_cu;
   pl->P = (int)std::min<int64_t>(d->N, cap);
   pl->cols = d->R + (d->has_out_weight ? d->D : 0);
-  pl->n_counters = (pl->cols + 255) / 256;
-  int G = 1;
-  if (pl->P > 64) {
-    G = std::min(64, std::max(1, pl->P / 16));
-    while (G > 1 && (int64_t)pl->n_counters * G > 1024) G /= 2;
-  }
-  pl->G = G;
-  pl->off_du = kCounterBytes;
-  pl->off_dow = align256(pl->off_du + (size_t)pl->P * d->R * sizeof(float));
-  pl->off_l2 = align256(pl->off_dow +
-                        (d->has_out_weight ? (size_t)pl->P * d->D * sizeof(float) : 0));
-  pl->bytes = align256(pl->off_l2 + (G > 1 ? (size_t)G * pl->cols * sizeof(float) : 0));
+  pl->off_du = 0;
+  pl->off_dow = align256((size_t)pl->P * d->R * sizeof(float));
+  pl->bytes = align256(pl->off_dow +
+                       (d->has_out_weight ? (size_t)pl->P * d->D * sizeof(float) : 0));
+  if (pl->bytes == 0) pl->bytes = 256;
   return ATTNRES_OK;
 }
 
@@ -463,7 +452,6 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
   const void* fn = bwd_ptr(sh);
   const void* fin = finalize_kernel_ptr(sh.bf16);
   char* ws = static_cast<char*>(workspace);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
 
   if (pl.P > 0) {
     for (int s = 0; s < d->S; ++s) a.dsrc[s] = const_cast<void*>(dptr[s]);
@@ -488,8 +476,6 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
     a.dout = dout;
     a.part_du = reinterpret_cast<float*>(ws + pl.off_du);
     a.part_dow = d->has_out_weight ? reinterpret_cast<float*>(ws + pl.off_dow) : nullptr;
-    a.counters = counters;
-    a.n_counters = pl.n_counters;
     a.out_norm = d->out_norm ? 1 : 0;
     st = launch(fn, pl.P, 1, sh.threads, bwd_lds(sh), &a, stream, "backward launch");
     if (st != ATTNRES_OK) return st;
@@ -499,19 +485,17 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
   std::memset(&fa, 0, sizeof fa);
   fa.part_du = reinterpret_cast<const float*>(ws + pl.off_du);
   fa.part_dow = d->has_out_weight ? reinterpret_cast<const float*>(ws + pl.off_dow) : nullptr;
-  fa.level2 = reinterpret_cast<float*>(ws + pl.off_l2);
-  fa.counters = counters;
   fa.P = pl.P;
   fa.R = d->R;
   fa.D = d->D;
-  fa.G = pl.G;
   fa.cols = pl.cols;
   fa.query = query;
   fa.norm_w = norm_w;
   fa.dq = dq;
   fa.dw = dw;
   fa.dow = dow;
-  return launch(fin, pl.n_counters, pl.G, 256, 0, &fa, stream, "finalize launch");
+  return launch(fin, (pl.cols + kFinCols - 1) / kFinCols, 1, kFinCols * kFinPhases, 0, &fa, stream,
+                "finalize launch");
 }
 
 }  // extern "C"

@@ -23,6 +23,7 @@ inline constexpr int kSbStream[] = {1, 2, 4, 8};
 // Largest workgroup any kernel is launched with (matches the kernels' launch bounds).
 inline constexpr int kMaxThreads = 512;
 
+
 // Kernel entry points by configuration; nullptr when that configuration is not built.
 const void* fwd_kernel_ptr_bf16(int ch, int sb, bool full);
 const void* fwd_kernel_ptr_f32(int ch, int sb, bool full);

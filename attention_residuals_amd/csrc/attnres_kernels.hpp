@@ -22,8 +22,8 @@
 //     the output y is never re-read. The streaming backward (output norm on, or S*D too large)
 //     reads the forward's FP32 mixture o instead and walks the sources in blocks.
 //   * q/w/ow gradients: every backward workgroup keeps its own FP32 partial in registers for the
-//     columns it owns and writes one row at the end; the finaliser sums the rows in a fixed
-//     order (deterministic), split over row groups with a last-arriver merge.
+//     columns it owns and writes one row at the end; the finaliser sums the rows of each column
+//     in a fixed order (deterministic), 64 columns x 16 row phases per workgroup.
 // No MFMA: per token this is a GEMV with a softmax over a handful of sources, bound by HBM.
 #pragma once
 
@@ -411,8 +411,6 @@ __global__ __launch_bounds__(512) void bwd_resident_kernel(const BwdArgs a) {
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
   const int R4 = nthr >> 4;
   const int xfl = K * R4;
-  if (blockIdx.x == 0)
-    for (int i = tid; i < a.n_counters; i += nthr) a.counters[i] = 0u;
 
   Cols<BF16, CH> cs;
   cs.init(tid, nthr, a.D, a.lo, a.query, a.norm_w);
@@ -518,8 +516,6 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
   const int R4 = nthr >> 4;
   const int xfl = K * R4;
-  if (blockIdx.x == 0)
-    for (int i = tid; i < a.n_counters; i += nthr) a.counters[i] = 0u;
 
   Cols<BF16, CH> cs;
   cs.init(tid, nthr, a.D, a.lo, a.query, a.norm_w);
@@ -670,47 +666,29 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
 
 // ------------------------------------------------------------------ finaliser
 
-// Sums the P partial rows in a fixed order. Block (x, g) sums rows [P*g/G, P*(g+1)/G) of 256
-// columns into level2[g]; the last block of each column group to arrive adds the G level-2 rows
-// in order g = 0..G-1 and writes dq = du*w (du without w), dw = du*q, dow.
+// Sums the P partial rows of every column in a fixed order and writes dq = du*w (du without w),
+// dw = du*q and dow. Thread (phase r, column c) adds rows r, r+16, r+32, ...; the 16 phase sums
+// are then added in phase order through LDS. No atomics and no inter-workgroup traffic.
 template <bool BF16>
-__global__ __launch_bounds__(256) void finalize_kernel(const FinArgs a) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  const int g = blockIdx.y;
+__global__ __launch_bounds__(kFinCols * kFinPhases) void finalize_kernel(const FinArgs a) {
+  __shared__ float red[kFinPhases][kFinCols];
+  const int cl = threadIdx.x % kFinCols, ph = threadIdx.x / kFinCols;
+  const int c = blockIdx.x * kFinCols + cl;
   const bool has = c < a.cols;
   const bool is_du = c < a.R;
-  const float* base = is_du ? a.part_du + c : a.part_dow + (c - a.R);
-  const int64_t stride = is_du ? a.R : a.D;
-
-  float total;
-  if (a.G == 1) {
-    float s = 0.f;
-    if (has)
-      for (int p = 0; p < a.P; ++p) s += base[p * stride];
-    total = s;
-  } else {
-    const int p0 = (int)((int64_t)a.P * g / a.G), p1 = (int)((int64_t)a.P * (g + 1) / a.G);
-    float s = 0.f;
-    if (has) {
-      for (int p = p0; p < p1; ++p) s += base[p * stride];
-      a.level2[(int64_t)g * a.cols + c] = s;
-    }
-    __threadfence();
-    __shared__ uint32_t is_last;
-    __syncthreads();
-    if (threadIdx.x == 0) is_last = (atomicAdd(&a.counters[blockIdx.x], 1u) == (uint32_t)(a.G - 1));
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    float t = 0.f;
-    if (has)
-      for (int gg = 0; gg < a.G; ++gg)
-        t += __hip_atomic_load(&a.level2[(int64_t)gg * a.cols + c], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    total = t;
-    if (threadIdx.x == 0) a.counters[blockIdx.x] = 0u;
+  float s = 0.f;
+  if (has) {
+    const float* base = is_du ? a.part_du + c : a.part_dow + (c - a.R);
+    const int64_t stride = is_du ? a.R : a.D;
+#pragma unroll 4
+    for (int p = ph; p < a.P; p += kFinPhases) s += base[p * stride];
   }
-  if (!has) return;
+  red[ph][cl] = s;
+  __syncthreads();
+  if (ph != 0 || !has) return;
+  float total = 0.f;
+#pragma unroll
+  for (int r = 0; r < kFinPhases; ++r) total += red[r][cl];
   if (is_du) {
     const float wv = a.norm_w ? load_param<BF16>(a.norm_w, c) : 1.f;
     store_param<BF16>(a.dq, c, total * wv);

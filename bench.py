@@ -1,0 +1,203 @@
+"""Benchmark of the AttnRes read, forward + backward, on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input resident in HBM:
+attnres_fwd (forward kernel) then attnres_bwd (backward kernel + finaliser), through the C ABI,
+on torch's current stream. Default workload: S=10 sources, N=32768 tokens, D=4096, R=D, bf16,
+key-norm weight, no output norm (the FLA PR page's L=10, T=32768, D=4096 benchmark row).
+
+Prints ONE JSON line. `value` is algorithmic HBM bytes per step / time per step (GB/s);
+algorithmic bytes = fwd reads V and writes y, bwd reads V and dY and writes dV, plus the FP32
+per-row statistics written once and read once. The `roofline` object is for the backward call
+(backward kernel + its finaliser, the dominant launch), timed with HIP events on the launch
+stream over the timed region. `cpu_baseline` times the FP64 CPU oracle (test infrastructure) on
+the same inputs.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+# B200 Triton fwdbwd median for this exact workload (FLA PR page, benchmark table, L=10,
+# T=32768, D=4096 bf16, candidate column): another machine's number, quoted as context.
+B200_MS = {"bf16_s10_n32768_d4096": 3.268607974052429,
+           "bf16_s8_n8192_d2048": 0.4638400077819824,
+           "bf16_s64_n8192_d8192_outnorm": 11.95311975479126}
+METRIC = "AttnRes fwd+bwd ms and HBM GB/s (% peak), S=10,N=32768,D=4096 bf16, 1 GPU"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_residuals_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, launches_bytes: int):
+    """HBM traffic of the backward call from committed rocprofv3 counter summaries, if they were
+    taken on the current kernel sources (same source hash); else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bwd_call_hbm_bytes")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bf16_s10_n32768_d4096")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--check", type=int, default=1, help="sampled-token parity check (0 = off)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the read "
+              "shards over tokens, so N GPUs run N independent copies of this step plus one "
+              "small all-reduce of the q/w gradients.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import attention_residuals_amd as A
+    import attnres_workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    x = W.generate(w, device=dev)
+    N, D, S, R = w.N, w.D, w.S, w.R
+    desc = A.make_desc(S, N, D, R, w.torch_dtype, eps=w.eps, scale=w.scale,
+                       has_norm_weight=x["norm_w"] is not None, out_norm=w.out_norm,
+                       has_out_weight=x["out_w"] is not None)
+    y = torch.empty((N, D), dtype=w.torch_dtype, device=dev)
+    lse = torch.empty((N,), dtype=torch.float32, device=dev)
+    rstd = torch.empty((N,), dtype=torch.float32, device=dev) if w.out_norm else None
+    o32 = torch.empty((N, D), dtype=torch.float32, device=dev) if A.o32_elems(desc) else None
+    dv = torch.empty((S, N, D), dtype=w.torch_dtype, device=dev)
+    dq = torch.empty((R,), dtype=w.torch_dtype, device=dev)
+    dw = torch.empty((R,), dtype=w.torch_dtype, device=dev) if x["norm_w"] is not None else None
+    dow = torch.empty((D,), dtype=w.torch_dtype, device=dev) if x["out_w"] is not None else None
+    ws = torch.empty((max(A.workspace_bytes(desc), 256),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        A.attnres_fwd(x["values"], x["query"], x["norm_w"], x["out_w"], eps=w.eps,
+                      scale=w.scale, out_norm=w.out_norm, out=y, lse=lse, out_rstd=rstd,
+                      o32=o32, stream=stream)
+
+    def bwd():
+        A.attnres_bwd(x["values"], x["query"], x["norm_w"], x["out_w"], lse, rstd, o32,
+                      x["dout"], eps=w.eps, scale=w.scale, out_norm=w.out_norm, dvalues=dv,
+                      dq=dq, dw=dw, dow=dow, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events between the two calls of every step
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        fwd()
+        ev[k][1].record(stream)
+        bwd()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)]
+    bwd_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(args.steps)]
+    ms_per_step = wall * 1e3 / args.steps
+    ev_step = [a + b for a, b in zip(fwd_ms, bwd_ms)]
+
+    algo = w.algorithmic_bytes()
+    b = w.elem_bytes
+    bwd_bytes = (2 * S + 1) * N * D * b + 4 * N * (2 if w.out_norm else 1)
+    fwd_bytes = (S + 1) * N * D * b + 4 * N * (2 if w.out_norm else 1)
+    bwd_avg = float(np.mean(bwd_ms))
+    fwd_avg = float(np.mean(fwd_ms))
+    achieved = bwd_bytes / (bwd_avg * 1e-3) / 1e9
+    value = algo / (ms_per_step * 1e-3) / 1e9
+
+    check = None
+    if args.check:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from parity import check_all, run_oracle, sample_tokens
+        toks = sample_tokens(N, 6, seed=7)
+        sel = torch.tensor(toks, device=dev)
+        xc = {"values": x["values"].index_select(1, sel).cpu(), "dout": x["dout"].index_select(0, sel).cpu()}
+        xc.update({k: (None if x[k] is None else x[k].cpu()) for k in ("query", "norm_w", "out_w")})
+        wt = w.with_(N=len(toks))
+        ref = run_oracle(wt, xc, reduce=False)
+        got = {"y": y, "lse": lse, "o_rstd": rstd, "dvalues": dv, "dq": dq, "dw": dw, "dow": dow}
+        res = check_all(w, got, ref, tokens=toks, check_reduced=False)
+        check = {k: {"metric": v["metric"], "ok": bool(v["ok"])} for k, v in res.items()}
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        xc = {k: (None if v is None else v.cpu()) for k, v in x.items()}
+        t1 = time.perf_counter()
+        oracle.run(xc["values"], xc["query"], xc["norm_w"], xc["out_w"], xc["dout"],
+                   eps=w.eps, scale=w.scale, out_norm=w.out_norm, want=(), reduce=True)
+        tc = time.perf_counter() - t1
+        cpu = {"value": round(algo / tc / 1e9, 3), "unit": "GB/s",
+               "cores": oracle.threads_used(), "kind": "oracle",
+               "ms_per_step": round(tc * 1e3, 1),
+               "sample": f"the full workload ({S} sources x {N} tokens x {D}), forward and "
+                         "backward with dq/dw reduction, FP64, OpenMP over tokens"}
+
+    traffic = load_traffic(w.name, bwd_bytes)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(B200_MS[w.name] / ms_per_step, 3) if w.name in B200_MS else None),
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "S": S, "N": N, "D": D, "R": R,
+                   "norm_weight": w.norm_weight, "out_norm": w.out_norm,
+                   "algorithmic_bytes": algo, "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 1),
+                   "fwd_ms": round(fwd_avg, 4), "bwd_ms": round(bwd_avg, 4),
+                   "event_ms_per_step": round(float(np.mean(ev_step)), 4),
+                   "b200_ms_context": B200_MS.get(w.name)},
+        "roofline": {"bound": "hbm", "kernel": "attnres_bwd (backward kernel + finaliser)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "fwd_achieved": round(fwd_bytes / (fwd_avg * 1e-3) / 1e9, 1)},
+        "cpu_baseline": cpu,
+        "parity_check": check,
+        "source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
