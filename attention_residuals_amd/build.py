@@ -22,8 +22,12 @@ OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattnres.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+# -amdgpu-atomic-optimizer-strategy=None: the backward takes its token ticket with a single-lane
+# atomic whose result is consumed after a whole pass of math; the optimizer's wave-reduced form
+# reads the result back immediately, which waits for every outstanding memory operation.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-I", os.path.join(ROOT, "include")]
 
 

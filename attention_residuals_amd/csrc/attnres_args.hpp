@@ -43,6 +43,7 @@ struct BwdArgs {
   const void* dout;
   float* part_du;                // [gridDim.x, R]
   float* part_dow;               // [gridDim.x, D] or nullptr
+  uint32_t* ticket;              // dynamic token counter, zero at launch (nullptr: static split)
   int out_norm;
 };
 

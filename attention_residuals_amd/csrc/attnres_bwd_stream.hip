@@ -1,4 +1,4 @@
-// Instantiations of bwd_stream_kernel and finalize_kernel.
+// Instantiations of bwd_stream_kernel and finalize_kernel, and the ticket reset kernel.
 #include "attnres_kernels.hpp"
 #include "attnres_internal.hpp"
 
@@ -22,6 +22,14 @@ static const void* stream_ptr(int ch, int sb, bool full) {
 const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full) {
   return bf16 ? stream_ptr<true>(ch, sb, full) : stream_ptr<false>(ch, sb, full);
 }
+
+// Zeroes the backward's token counter on the launch stream (a kernel store: no memset node, so
+// the call stays capturable into a HIP graph).
+__global__ __launch_bounds__(64) void ticket_reset_kernel(uint32_t* ticket) {
+  if (threadIdx.x == 0) *ticket = 0u;
+}
+
+const void* ticket_reset_kernel_ptr() { return (const void*)&ticket_reset_kernel; }
 
 const void* finalize_kernel_ptr(bool bf16) {
   return bf16 ? (const void*)&finalize_kernel<true> : (const void*)&finalize_kernel<false>;

@@ -1,14 +1,26 @@
-// Instantiations of fwd_kernel for bf16 storage.
+// Instantiations of fwd_kernel (single-block for every bucket, multi-block for the stream sizes) for bf16 storage.
 #include "attnres_kernels.hpp"
 #include "attnres_internal.hpp"
 
 namespace attnres {
 
 #define ATTNRES_CASE(CH, SB) \
-  case SB: return full ? (const void*)&fwd_kernel<true, CH, SB, true> \
-                       : (const void*)&fwd_kernel<true, CH, SB, false>;
+  case SB: return full ? (const void*)&fwd_kernel<true, CH, SB, true, true> \
+                       : (const void*)&fwd_kernel<true, CH, SB, false, true>;
+#define ATTNRES_CASE_MULTI(CH, SB) \
+  case SB: return full ? (const void*)&fwd_kernel<true, CH, SB, true, false> \
+                       : (const void*)&fwd_kernel<true, CH, SB, false, false>;
 
-const void* fwd_kernel_ptr_bf16(int ch, int sb, bool full) {
+const void* fwd_kernel_ptr_bf16(int ch, int sb, bool full, bool one_block) {
+  if (!one_block) {
+    switch (ch) {
+      case 1: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE_MULTI, 1) default: break; } break;
+      case 2: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE_MULTI, 2) default: break; } break;
+      case 4: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE_MULTI, 4) default: break; } break;
+      default: break;
+    }
+    return nullptr;
+  }
   switch (ch) {
     case 1: switch (sb) { ATTNRES_SB_CH1(ATTNRES_CASE, 1) default: break; } break;
     case 2: switch (sb) { ATTNRES_SB_CH2(ATTNRES_CASE, 2) default: break; } break;

@@ -47,8 +47,9 @@ attnres_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Optional tuning override read once from the environment: ATTNRES_CH forces chunks per thread
-// (1, 2 or 4) when the resulting workgroup still fits; ATTNRES_WG_PER_CU caps workgroups per CU.
+// Optional tuning overrides read once from the environment: ATTNRES_CH forces chunks per thread
+// (1, 2 or 4) when the resulting workgroup still fits; ATTNRES_WG_PER_CU caps workgroups per CU;
+// ATTNRES_FWD_GRID_MULT / ATTNRES_BWD_GRID_MULT multiply the resident-workgroup grid.
 int env_int(const char* name) {
   const char* v = std::getenv(name);
   return v ? std::atoi(v) : 0;
@@ -63,6 +64,7 @@ struct Shape {
   bool full;      // R == D
   bool resident;  // backward keeps every source row of a token on chip
   int sb_fwd, sb_bwd;
+  bool fwd_one;   // forward holds all S sources in one block
 };
 
 int bucket_at_least(int S, const int* b, int nb) {
@@ -107,6 +109,21 @@ attnres_status make_shape(const attnres_desc* d, Shape* sh) {
   int ch = 0;
   if ((forced == 1 || forced == 2 || forced == 4) && (chunks + 64 * forced - 1) / (64 * forced) <= 8)
     ch = forced;
+  // Resident shapes: 4-wave workgroups (CH = ceil(chunks / 256)) measured best on MI355X; the
+  // streaming path (output norm, or sources that do not fit a bucket) keeps CH <= 2 to leave
+  // registers for the FP32 mixture and do rows, with up to 8 waves.
+  auto fit_for = [&](int c) {
+    const int* b = c == 1 ? kSbCh1 : c == 2 ? kSbCh2 : kSbCh4;
+    const int nb = c == 1 ? (int)(sizeof kSbCh1 / sizeof(int))
+                   : c == 2 ? (int)(sizeof kSbCh2 / sizeof(int))
+                            : (int)(sizeof kSbCh4 / sizeof(int));
+    return bucket_at_least(d->S, b, nb);
+  };
+  if (!ch && !d->out_norm) {
+    const int c = std::min(4, std::max(1, (chunks + 255) / 256));
+    const int cc = c == 3 ? 4 : c;
+    if ((chunks + 64 * cc - 1) / (64 * cc) <= 8 && fit_for(cc) > 0) ch = cc;
+  }
   if (!ch) {
     for (int c : {1, 2, 4})
       if ((chunks + 64 * c - 1) / (64 * c) <= 8) {
@@ -119,15 +136,12 @@ attnres_status make_shape(const attnres_desc* d, Shape* sh) {
   sh->W = (chunks + 64 * ch - 1) / (64 * ch);
   sh->threads = 64 * sh->W;
   sh->full = d->R == d->D;
-  const int* b = ch == 1 ? kSbCh1 : ch == 2 ? kSbCh2 : kSbCh4;
-  const int nb = ch == 1 ? (int)(sizeof kSbCh1 / sizeof(int))
-                 : ch == 2 ? (int)(sizeof kSbCh2 / sizeof(int))
-                           : (int)(sizeof kSbCh4 / sizeof(int));
-  const int fit = bucket_at_least(d->S, b, nb);
+  const int fit = fit_for(ch);
   sh->resident = !d->out_norm && fit > 0;
   // forward: one block when the sources fit a bucket, else blocks of the stream size
   const int stream_max = ch == 4 ? 4 : 8;
   sh->sb_fwd = fit > 0 ? fit : stream_max;
+  sh->fwd_one = fit > 0;
   if (sh->resident) {
     sh->sb_bwd = fit;
   } else {
@@ -138,8 +152,8 @@ attnres_status make_shape(const attnres_desc* d, Shape* sh) {
 }
 
 const void* fwd_ptr(const Shape& sh) {
-  return sh.bf16 ? fwd_kernel_ptr_bf16(sh.ch, sh.sb_fwd, sh.full)
-                 : fwd_kernel_ptr_f32(sh.ch, sh.sb_fwd, sh.full);
+  return sh.bf16 ? fwd_kernel_ptr_bf16(sh.ch, sh.sb_fwd, sh.full, sh.fwd_one)
+                 : fwd_kernel_ptr_f32(sh.ch, sh.sb_fwd, sh.full, sh.fwd_one);
 }
 
 const void* bwd_ptr(const Shape& sh) {
@@ -149,8 +163,18 @@ const void* bwd_ptr(const Shape& sh) {
   return bwd_stream_kernel_ptr(sh.bf16, sh.ch, sh.sb_bwd, sh.full);
 }
 
-size_t fwd_lds(const Shape& sh) { return 2u * (2u * sh.sb_fwd) * (4u * sh.W) * sizeof(float); }
-size_t bwd_lds(const Shape& sh) { return 2u * (3u * sh.sb_bwd) * (4u * sh.W) * sizeof(float); }
+// LDS of every kernel: the per-thread parameter region (u = w*q as float4 slots, plus the
+// three-term bf16 split for bf16), then two exchange buffers (and the backward's ticket slots).
+size_t param_lds(const Shape& sh) {
+  const size_t slots = sh.ch * sh.vec / 4 + (sh.bf16 ? 3 * sh.ch : 0);
+  return slots * sh.threads * 16u;
+}
+size_t fwd_lds(const Shape& sh) {
+  return param_lds(sh) + 2u * (2u * sh.sb_fwd) * (4u * sh.W) * sizeof(float);
+}
+size_t bwd_lds(const Shape& sh) {
+  return param_lds(sh) + 2u * (3u * sh.sb_bwd) * (4u * sh.W) * sizeof(float) + 4 * sizeof(float);
+}
 
 // ------------------------------------------------------------------ device facts
 
@@ -177,10 +201,14 @@ attnres_status device_facts(DevFacts* f) {
   return ATTNRES_OK;
 }
 
-attnres_status blocks_per_cu(const void* fn, int threads, size_t lds, int* out) {
+// Workgroups per CU for a persistent grid: the occupancy limit, capped at `wave_cap` waves per
+// CU when wave_cap > 0 (two 4-wave token workgroups per CU measured best for the streaming
+// read/write mix on MI355X: more concurrent rows per CU lowered the achieved bandwidth).
+attnres_status blocks_per_cu(const void* fn, int threads, size_t lds, int* out, int wave_cap = 0) {
   int nb = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, lds);
   if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  if (wave_cap > 0) nb = std::min(nb, std::max(1, wave_cap / (threads / 64)));
   static const int cap = env_int("ATTNRES_WG_PER_CU");
   if (cap > 0) nb = std::min(nb, cap);
   if (nb <= 0) return fail(ATTNRES_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)");
@@ -193,7 +221,7 @@ attnres_status blocks_per_cu(const void* fn, int threads, size_t lds, int* out) 
 struct BwdPlan {
   int P = 0;     // backward workgroups = partial rows
   int cols = 0;  // R (+ D with the output-norm weight)
-  size_t off_du = 0, off_dow = 0, bytes = 0;
+  size_t off_ticket = 0, off_du = 0, off_dow = 0, bytes = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -205,13 +233,15 @@ attnres_status plan_bwd(const attnres_desc* d, const Shape& sh, BwdPlan* pl) {
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
   int per_cu = 0;
-  st = blocks_per_cu(fn, sh.threads, bwd_lds(sh), &per_cu);
+  st = blocks_per_cu(fn, sh.threads, bwd_lds(sh), &per_cu, sh.resident ? 8 : 0);
   if (st != ATTNRES_OK) return st;
-  const int64_t cap = (int64_t)f.cus * per_cu;
+  static const int mult = std::max(1, env_int("ATTNRES_BWD_GRID_MULT"));
+  const int64_t cap = (int64_t)f.cus * per_cu * mult;
   pl->P = (int)std::min<int64_t>(d->N, cap);
   pl->cols = d->R + (d->has_out_weight ? d->D : 0);
-  pl->off_du = 0;
-  pl->off_dow = align256((size_t)pl->P * d->R * sizeof(float));
+  pl->off_ticket = 0;
+  pl->off_du = 256;
+  pl->off_dow = align256(pl->off_du + (size_t)pl->P * d->R * sizeof(float));
   pl->bytes = align256(pl->off_dow +
                        (d->has_out_weight ? (size_t)pl->P * d->D * sizeof(float) : 0));
   if (pl->bytes == 0) pl->bytes = 256;
@@ -371,8 +401,13 @@ attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
   DevFacts f;
   if ((st = device_facts(&f)) != ATTNRES_OK) return st;
   int per_cu = 0;
-  if ((st = blocks_per_cu(fn, sh.threads, fwd_lds(sh), &per_cu)) != ATTNRES_OK) return st;
-  const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
+  if ((st = blocks_per_cu(fn, sh.threads, fwd_lds(sh), &per_cu, sh.fwd_one ? 8 : 0)) != ATTNRES_OK)
+    return st;
+  // the forward has no per-workgroup state: 8x the resident grid lets the hardware dispatcher
+  // balance workgroups over CUs (measured better than a one-pass persistent grid)
+  static const int env_mult = env_int("ATTNRES_FWD_GRID_MULT");
+  const int mult = env_mult > 0 ? env_mult : 8;
+  const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu * mult);
 
   a.row_stride = values->row_stride;
   a.N = N;
@@ -477,6 +512,12 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
     a.part_du = reinterpret_cast<float*>(ws + pl.off_du);
     a.part_dow = d->has_out_weight ? reinterpret_cast<float*>(ws + pl.off_dow) : nullptr;
     a.out_norm = d->out_norm ? 1 : 0;
+    if (sh.resident) {
+      a.ticket = reinterpret_cast<uint32_t*>(ws + pl.off_ticket);
+      void* targ = a.ticket;
+      st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");
+      if (st != ATTNRES_OK) return st;
+    }
     st = launch(fn, pl.P, 1, sh.threads, bwd_lds(sh), &a, stream, "backward launch");
     if (st != ATTNRES_OK) return st;
   }

@@ -25,11 +25,12 @@ inline constexpr int kMaxThreads = 512;
 
 
 // Kernel entry points by configuration; nullptr when that configuration is not built.
-const void* fwd_kernel_ptr_bf16(int ch, int sb, bool full);
-const void* fwd_kernel_ptr_f32(int ch, int sb, bool full);
+const void* fwd_kernel_ptr_bf16(int ch, int sb, bool full, bool one_block);
+const void* fwd_kernel_ptr_f32(int ch, int sb, bool full, bool one_block);
 const void* bwd_resident_kernel_ptr_bf16(int ch, int sb, bool full);
 const void* bwd_resident_kernel_ptr_f32(int ch, int sb, bool full);
 const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full);
 const void* finalize_kernel_ptr(bool bf16);
+const void* ticket_reset_kernel_ptr();
 
 }  // namespace attnres

@@ -13,11 +13,16 @@
 //     grid size). The D columns of a row are cut into 16-byte chunks (8 bf16 or 4 f32); thread
 //     `tid` owns chunks tid + j*blockDim for j < CH, so every load instruction of the workgroup
 //     reads one contiguous, fully coalesced span of the row.
+//   * Row addresses are a uniform (SGPR) base per source and token plus a loop-invariant 32-bit
+//     lane offset, so loads and stores use the scalar-base form with no per-lane address math.
 //   * A token's rows for a block of SB sources are held in VGPRs as packed 16-byte chunks.
 //     Per-source partial sums (sum t^2, <t, w*q>, <do, v_s>) are reduced across a 16-lane row
 //     with DPP, across rows and waves through a small double-buffered LDS exchange (one barrier
 //     per source block), and finished on lane s of every wave, which then computes source s's
 //     coefficients; v_readlane broadcasts them into SGPRs for the per-element FMAs.
+//   * bf16 sums of products use v_dot2_f32_bf16 on packed pairs (exact products, FP32
+//     accumulation), so t never needs widening for them. The FP32 vector u = w*q is split exactly
+//     into three bf16 terms (u = u1 + u2 + u3), which keeps <t, u> at FP32 accuracy.
 //   * The resident backward keeps all S rows of a token on chip, so delta is exact in FP32 and
 //     the output y is never re-read. The streaming backward (output norm on, or S*D too large)
 //     reads the forward's FP32 mixture o instead and walks the sources in blocks.
@@ -46,24 +51,34 @@ struct Fmt {
   static constexpr int ESZ = BF16 ? 2 : 4;   // bytes per element
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bits_f(uint32_t b) { return __builtin_bit_cast(float, b); }
 __device__ __forceinline__ uint32_t f_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
-// Element e of a chunk as FP32 (bf16 widening is exact: the 16 bits are the top half).
+// Low / high bf16 of a packed pair, widened exactly to FP32.
+__device__ __forceinline__ float lo_f(uint32_t w) { return bits_f(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return bits_f(w & 0xffff0000u); }
+
+// Element e of a chunk as FP32.
 template <bool BF16>
 __device__ __forceinline__ float elem(const Chunk& c, int e) {
   if constexpr (BF16) {
-    const uint32_t w = c.w[e >> 1];
-    return bits_f((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    return (e & 1) ? hi_f(c.w[e >> 1]) : lo_f(c.w[e >> 1]);
   } else {
     return bits_f(c.w[e]);
   }
 }
 
+// a.lo * b.lo + a.hi * b.hi + acc with exact bf16 products and FP32 accumulation.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
 // Two FP32 values to a packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -93,23 +108,44 @@ __device__ __forceinline__ float load_param(const void* p, int i) {
 template <bool BF16>
 __device__ __forceinline__ void store_param(void* p, int i, float v) {
   if constexpr (BF16) {
-    typedef __bf16 bf16x1;
-    static_cast<bf16x1*>(p)[i] = (bf16x1)v;
+    static_cast<__bf16*>(p)[i] = (__bf16)v;
   } else {
     static_cast<float*>(p)[i] = v;
   }
 }
 
-__device__ __forceinline__ Chunk ld_chunk(const void* base, int64_t byte_off) {
-  return *reinterpret_cast<const Chunk*>(static_cast<const char*>(base) + byte_off);
+// A row of `bytes` bytes at base + row_byte as a buffer resource: the 64-bit base lives in SGPRs,
+// every access adds a 32-bit per-lane offset, and accesses at or past `bytes` read 0 and drop
+// their writes (the hardware range check covers the chunks past D of the last waves).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc row_rsrc(const void* base, int64_t row_byte, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(base) + row_byte), 0, bytes, 0x00020000);
 }
 
-// Streaming store: the rows written here are not read again by this kernel.
-__device__ __forceinline__ void st_chunk(void* base, int64_t byte_off, const Chunk& c) {
-  uint32_t* p = reinterpret_cast<uint32_t*>(static_cast<char*>(base) + byte_off);
+// Streaming 16-byte load (non-temporal: every row is read once per kernel).
+// Row resource of source i of a block of `count` sources: empty (reads 0, writes dropped, no
+// memory traffic) for i >= count, so loops over a block need no per-source branches.
+__device__ __forceinline__ Rsrc src_rsrc(const void* base, int i, int count, int64_t row_byte,
+                                         uint32_t bytes) {
+  const bool live = i < count;
+  return row_rsrc(live ? base : nullptr, live ? row_byte : 0, live ? bytes : 0u);
+}
+
+__device__ __forceinline__ Chunk ld_row(Rsrc r, uint32_t voff) {
+  return __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2));
+}
+
+// Streaming 16-byte store (non-temporal: the rows written are not read again by the kernel).
+__device__ __forceinline__ void st_row(Rsrc r, uint32_t voff, const Chunk& c) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 v = {c.w[0], c.w[1], c.w[2], c.w[3]};
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, c), r, voff, 0, 2);
+}
+
+__device__ __forceinline__ void st_f32x4(float* p, float a, float b, float c, float d) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  f32x4 v = {a, b, c, d};
+  *reinterpret_cast<f32x4*>(p) = v;
 }
 
 // ------------------------------------------------------------------ cross-lane reductions
@@ -154,14 +190,32 @@ __device__ __forceinline__ float bcast(float x, int lane) {
       __builtin_amdgcn_readlane(static_cast<int>(f_bits(x)), lane)));
 }
 
-// Workgroup exchange of per-lane partials: every 16-lane row reduces value k with DPP and its
-// first lane writes the row sum to xb[k * R4 + row], R4 = 4 * waves = rows in the workgroup.
-__device__ __forceinline__ void xchg_put(float v, float* xb, int k, int R4, int tid) {
-  const float r = row_sum(v);
-  if ((tid & 15) == 0) xb[k * R4 + (tid >> 4)] = r;
+// Sources per exchange group: a group's partials are reduced and written before the next group is
+// computed, which bounds the live partial registers to NV * kGroup.
+constexpr int kGroup = 4;
+
+// Workgroup exchange of per-lane partials. Each 16-lane row reduces value v of group source g
+// with DPP (the NV * kGroup chains are independent, so their hazards overlap), then the row's
+// first lane writes it to xb[(v * SB + i0 + g) * R4 + row], R4 = 4 * waves = rows in the
+// workgroup (slots of sources past the block's count hold zeros and are never read).
+template <int NV, int SB>
+__device__ __forceinline__ void xchg_group(float (&v)[NV][kGroup], int i0, float* xb, int R4,
+                                           int tid) {
+#pragma unroll
+  for (int t = 0; t < NV; ++t)
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) v[t][g] = row_sum(v[t][g]);
+  if ((tid & 15) == 0) {
+    float* dst = xb + (tid >> 4);
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g)
+      if (i0 + g < SB)
+#pragma unroll
+        for (int t = 0; t < NV; ++t) dst[(t * SB + i0 + g) * R4] = v[t][g];
+  }
 }
 
-// Total of value k after the barrier that follows the xchg_put calls (fixed summation order).
+// Total of value k after the barrier that follows xchg_put (fixed summation order).
 __device__ __forceinline__ float xchg_total(const float* xb, int k, int R4) {
   const float* p = xb + k * R4;
   float s = 0.f;
@@ -172,26 +226,41 @@ __device__ __forceinline__ float xchg_total(const float* xb, int k, int R4) {
   return s;
 }
 
-// LDS floats one exchange buffer needs for K values and W waves (R4 = 4W, padded to 4).
-__host__ __device__ constexpr int xchg_floats(int K, int W) { return K * 4 * W; }
-
 // ------------------------------------------------------------------ per-lane column setup
 
-// For the CH chunks this thread owns: start column, validity, u = w*q (0 off the slice) and
-// whether each element lies in the key slice.
-template <bool BF16, int CH>
+// Columns of the CH chunks a thread owns: byte offset inside a row, validity and, for R < D with
+// bf16, a per-half mask of the key slice. The loop-invariant parameter vectors live in LDS rather
+// than VGPRs (each thread's slots are 16 bytes, lane-contiguous): u = w*q on the slice (0
+// elsewhere) in FP32 and, for bf16, its exact three-term split u = u1 + u2 + u3 in packed bf16
+// pairs. Kernels fetch them per token through a laundered offset, so the compiler cannot hoist
+// them back into registers.
+template <bool BF16, int CH, bool FULL>
 struct Cols {
   static constexpr int VEC = Fmt<BF16>::VEC;
+  static constexpr int ESZ = Fmt<BF16>::ESZ;
+  static constexpr int U_SLOTS = CH * VEC / 4;          // float4 slots of u
+  static constexpr int S_SLOTS = BF16 ? 3 * CH : 0;     // uint4 slots of the split
+  static constexpr int SLOTS = U_SLOTS + S_SLOTS;
   int col0[CH];
+  uint32_t voff[CH];
   bool valid[CH];
-  float u[CH][VEC];
+  uint32_t mk[CH][4];
+  char* params;  // this workgroup's parameter region in LDS
+  int nthr;
 
-  __device__ __forceinline__ void init(int tid, int nthr, int D, int lo, const void* query,
-                                       const void* norm_w) {
+  // LDS bytes of the parameter region for a workgroup of `threads` threads.
+  static constexpr uint32_t param_bytes(int threads) { return SLOTS * threads * 16u; }
+
+  __device__ __forceinline__ void init(int tid, int nthr_, int D, int lo, const void* query,
+                                       const void* norm_w, float* lds_params) {
+    nthr = nthr_;
+    params = reinterpret_cast<char*>(lds_params);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       col0[j] = (tid + j * nthr) * VEC;
+      voff[j] = static_cast<uint32_t>(col0[j] * ESZ);
       valid[j] = col0[j] < D;
+      float u[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const int idx = col0[j] + e - lo;
@@ -200,30 +269,250 @@ struct Cols {
           uv = load_param<BF16>(query, idx);
           if (norm_w) uv *= load_param<BF16>(norm_w, idx);
         }
-        u[j][e] = uv;
+        u[e] = uv;
+      }
+#pragma unroll
+      for (int h = 0; h < VEC / 4; ++h)
+        *reinterpret_cast<float4*>(params + ((j * (VEC / 4) + h) * nthr + tid) * 16) =
+            make_float4(u[4 * h], u[4 * h + 1], u[4 * h + 2], u[4 * h + 3]);
+      if constexpr (BF16) {
+        uint32_t us[3][4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float r0 = u[2 * k], r1 = u[2 * k + 1];
+#pragma unroll
+          for (int t = 0; t < 3; ++t) {  // u = u1 + u2 + u3; each remainder is exact in FP32
+            const __bf16 b0 = (__bf16)r0, b1 = (__bf16)r1;
+            us[t][k] = pack_bf16x2(b0, b1);
+            r0 -= (float)b0;
+            r1 -= (float)b1;
+          }
+          const bool in0 = col0[j] + 2 * k >= lo, in1 = col0[j] + 2 * k + 1 >= lo;
+          mk[j][k] = (in0 ? 0x0000ffffu : 0u) | (in1 ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+          *reinterpret_cast<uint4*>(params + ((U_SLOTS + t * CH + j) * nthr + tid) * 16) =
+              make_uint4(us[t][0], us[t][1], us[t][2], us[t][3]);
       }
     }
   }
+
+  // Per-token fetches (after the barrier that follows init). `lane_off` = tid * 16, laundered by
+  // the caller once per token.
+  __device__ __forceinline__ void fetch_u(uint32_t lane_off, float (&u)[CH][VEC]) const {
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int h = 0; h < VEC / 4; ++h) {
+        const float4 v = *reinterpret_cast<const float4*>(
+            params + (j * (VEC / 4) + h) * nthr * 16 + lane_off);
+        u[j][4 * h] = v.x;
+        u[j][4 * h + 1] = v.y;
+        u[j][4 * h + 2] = v.z;
+        u[j][4 * h + 3] = v.w;
+      }
+  }
+  __device__ __forceinline__ void fetch_us(uint32_t lane_off, uint32_t (&us)[3][CH][4]) const {
+    if constexpr (BF16) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const uint4 v = *reinterpret_cast<const uint4*>(
+              params + (U_SLOTS + t * CH + j) * nthr * 16 + lane_off);
+          us[t][j][0] = v.x;
+          us[t][j][1] = v.y;
+          us[t][j][2] = v.z;
+          us[t][j][3] = v.w;
+        }
+    }
+  }
+
   __device__ __forceinline__ bool in_slice(int j, int e, int lo) const {
-    return col0[j] + e >= lo;
+    return FULL || col0[j] + e >= lo;
   }
 };
 
+// Per-token per-lane LDS offset that the compiler cannot prove loop-invariant.
+__device__ __forceinline__ uint32_t laundered_lane_off(int tid) {
+  uint32_t off = static_cast<uint32_t>(tid) * 16u;
+  asm volatile("" : "+v"(off));
+  return off;
+}
+
+// sum over the slice of t^2 and <t, u> for one row (this thread's chunks).
+template <bool BF16, int CH, bool FULL>
+__device__ __forceinline__ void key_sums(const Chunk (&r)[CH], const Cols<BF16, CH, FULL>& cs,
+                                         const uint32_t (&us)[3][CH][4],
+                                         const float (&u)[CH][Fmt<BF16>::VEC], int lo, float& ss,
+                                         float& c) {
+  ss = 0.f;
+  c = 0.f;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t p = r[j].w[k];
+        const uint32_t pm = FULL ? p : (p & cs.mk[j][k]);
+        ss = dot2(pm, pm, ss);
+        c = dot2(p, us[0][j][k], c);
+        c = dot2(p, us[1][j][k], c);
+        c = dot2(p, us[2][j][k], c);
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = elem<false>(r[j], e);
+        const float tm = cs.in_slice(j, e, lo) ? t : 0.f;
+        ss = fmaf(tm, tm, ss);
+        c = fmaf(t, u[j][e], c);
+      }
+  }
+}
+
+// <g, v> over this thread's chunks, g and v both in storage format.
+template <bool BF16, int CH>
+__device__ __forceinline__ float dot_rows(const Chunk (&v)[CH], const Chunk (&g)[CH]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (BF16) {
+        acc = dot2(g[j].w[k], v[j].w[k], acc);
+      } else {
+        acc = fmaf(bits_f(g[j].w[k]), bits_f(v[j].w[k]), acc);
+      }
+    }
+  return acc;
+}
+
+// <g, v> with g in FP32.
+template <bool BF16, int CH>
+__device__ __forceinline__ float dot_f32(const Chunk (&v)[CH], const float (&g)[CH][Fmt<BF16>::VEC]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+#pragma unroll
+    for (int e = 0; e < Fmt<BF16>::VEC; ++e) acc = fmaf(g[j][e], elem<BF16>(v[j], e), acc);
+  return acc;
+}
+
+// dv = p*do + A*u + B*t (t masked to the slice) and du += A*t for one source row.
+template <bool BF16, int CH, bool FULL>
+__device__ __forceinline__ void grad_row(const Chunk (&r)[CH], const Cols<BF16, CH, FULL>& cs,
+                                         const float (&u)[CH][Fmt<BF16>::VEC],
+                                         const float (&dof)[CH][Fmt<BF16>::VEC], float p,
+                                         float A, float B, int lo,
+                                         float (&du)[CH][Fmt<BF16>::VEC], Chunk (&out)[CH]) {
+  constexpr int VEC = Fmt<BF16>::VEC;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    float dv[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float tm;
+      if constexpr (BF16) {
+        const uint32_t w = FULL ? r[j].w[e >> 1] : (r[j].w[e >> 1] & cs.mk[j][e >> 1]);
+        tm = (e & 1) ? hi_f(w) : lo_f(w);
+      } else {
+        const float t = elem<false>(r[j], e);
+        tm = cs.in_slice(j, e, lo) ? t : 0.f;
+      }
+      float d = p * dof[j][e];
+      d = fmaf(A, u[j][e], d);
+      dv[e] = fmaf(B, tm, d);
+      du[j][e] = fmaf(A, tm, du[j][e]);
+    }
+    out[j] = pack<BF16>(dv);
+  }
+}
+
+// ------------------------------------------------------------------ occupancy
+
+// Waves per SIMD the register allocator is asked to allow: three workgroups of a 4-wave token
+// (3 waves per SIMD, <= 168 VGPRs) keep more tokens' loads in flight per CU than two, and the
+// register budget allows it while a token's rows take at most 20 chunks per thread (12 with the
+// slice masks of R < D); larger slabs keep the default.
+constexpr int occupancy_hint(int ch, int sb, bool full) {
+  return ch * sb <= (full ? 20 : 12) ? 3 : 1;
+}
+
 // ------------------------------------------------------------------ forward
 
-// Forward. SB = sources held per block; S <= SB runs as one block (no rescaling).
-template <bool BF16, int CH, int SB, bool FULL>
-__global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
+// Output row: o (= acc / l already applied) to y, with the optional output RMSNorm, plus lse,
+// rho_o and the FP32 mixture when requested.
+template <bool BF16, int CH, bool FULL>
+__device__ __forceinline__ void fwd_emit(const FwdArgs& a, const Cols<BF16, CH, FULL>& cs,
+                                         float (&acc)[CH][Fmt<BF16>::VEC],
+                                         const float (&ow)[CH][Fmt<BF16>::VEC], int64_t n,
+                                         float lse, float* lds, int& buf, int xfl, int R4,
+                                         int tid, uint32_t row_bytes) {
+  constexpr int VEC = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  float rho_o = 1.f;
+  if (a.out_norm) {
+    float sq[1][kGroup] = {{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sq[0][0] = fmaf(acc[j][e], acc[j][e], sq[0][0]);
+    float* xb = lds + buf * xfl;
+    xchg_group<1, 1>(sq, 0, xb, R4, tid);
+    __syncthreads();
+    buf ^= 1;
+    rho_o = 1.f / sqrtf(xchg_total(xb, 0, R4) * a.inv_D + a.eps);
+  }
+  if (a.o32) {
+    const Rsrc ro = row_rsrc(a.o32, n * a.D * 4, static_cast<uint32_t>(a.D * 4));
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int h = 0; h < VEC; h += 4) {
+        Chunk c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c.w[e] = f_bits(acc[j][h + e]);
+        st_row(ro, static_cast<uint32_t>((cs.col0[j] + h) * 4), c);
+      }
+  }
+  const Rsrc ry = row_rsrc(a.y, n * a.D * ESZ, row_bytes);
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    float yv[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) yv[e] = a.out_norm ? acc[j][e] * rho_o * ow[j][e] : acc[j][e];
+    st_row(ry, cs.voff[j], pack<BF16>(yv));
+  }
+  if (tid == 0) {
+    a.lse[n] = lse;
+    if (a.out_norm && a.o_rstd) a.o_rstd[n] = rho_o;
+  }
+}
+
+// Forward. ONE: all S <= SB sources in one block, software-pipelined over tokens (the next
+// token's row i is loaded as soon as row i has been folded into the output, so the load overlaps
+// this token's remaining math and stores, and the next token's first wait covers only what was
+// issued before it; the vector-memory counter retires loads and stores in order).
+// !ONE: blocks of SB sources with an online softmax (running max and sum, rescaled output).
+template <bool BF16, int CH, int SB, bool FULL, bool ONE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(occupancy_hint(CH, SB, FULL), 8)))
+void fwd_kernel(const FwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
   constexpr int K = 2 * SB;
-  extern __shared__ float lds[];
+  extern __shared__ float lds_all[];
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
   const int R4 = nthr >> 4;
   const int xfl = K * R4;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.D * ESZ);
 
-  Cols<BF16, CH> cs;
-  cs.init(tid, nthr, a.D, a.lo, a.query, a.norm_w);
+  Cols<BF16, CH, FULL> cs;
+  cs.init(tid, nthr, a.D, a.lo, a.query, a.norm_w, lds_all);
+  float* lds = lds_all + Cols<BF16, CH, FULL>::param_bytes(nthr) / 4;  // exchange buffers
   float ow[CH][VEC];
 #pragma unroll
   for (int j = 0; j < CH; ++j)
@@ -232,9 +521,29 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
       ow[j][e] = (a.out_norm && a.out_w && cs.valid[j]) ? load_param<BF16>(a.out_w, cs.col0[j] + e)
                                                          : 1.f;
   int buf = 0;
+  // Every loop below runs over all SB slots of a block; slots past the block's source count use
+  // an empty resource (zero rows, dropped stores) and get routing weight 0, so there are no
+  // per-source branches and the wait counts stay exact across the token loop.
+  Chunk rows[SB][CH];
+
+  if constexpr (ONE) {
+    // issued in the loop body's order (rows 0..SB-1) so the wait counts at the loop head stay
+    // tight over both entry paths
+    const int live = (int64_t)blockIdx.x < a.N ? a.S : 0;
+    const int64_t row_byte = (int64_t)blockIdx.x * a.row_stride * ESZ;
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const Rsrc r = src_rsrc(a.src[i], i, live, row_byte, row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 
   for (int64_t n = blockIdx.x; n < a.N; n += gridDim.x) {
-    const int64_t row_off = n * a.row_stride * ESZ;
+    const int64_t row_byte = n * a.row_stride * ESZ;
+    const int64_t next = n + gridDim.x;
+    const int64_t next_byte = next * a.row_stride * ESZ;
     float acc[CH][VEC];
 #pragma unroll
     for (int j = 0; j < CH; ++j)
@@ -242,36 +551,31 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
       for (int e = 0; e < VEC; ++e) acc[j][e] = 0.f;
     float m = -INFINITY, l = 0.f;
 
-    for (int s0 = 0; s0 < a.S; s0 += SB) {
-      const int nb = min(SB, a.S - s0);
-      Chunk rows[SB][CH];
+    for (int s0 = 0; s0 < (ONE ? 1 : a.S); s0 += SB) {
+      const int nb = ONE ? a.S : min(SB, a.S - s0);
+      if constexpr (!ONE) {
 #pragma unroll
-      for (int i = 0; i < SB; ++i)
+        for (int i = 0; i < SB; ++i) {
+          const Rsrc r = src_rsrc(a.src[min(s0 + i, kMaxSources - 1)], i, nb, row_byte, row_bytes);
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          if (i < nb && cs.valid[j]) {
-            rows[i][j] = ld_chunk(a.src[s0 + i], row_off + (int64_t)cs.col0[j] * ESZ);
-          } else {
-            rows[i][j] = Chunk{{0u, 0u, 0u, 0u}};
-          }
+          for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
         }
+      }
       float* xb = lds + buf * xfl;
+      uint32_t us[3][CH][4];
+      float u[CH][VEC];
+      if constexpr (BF16) cs.fetch_us(laundered_lane_off(tid), us);
+      else cs.fetch_u(laundered_lane_off(tid), u);
 #pragma unroll
-      for (int i = 0; i < SB; ++i) {
-        if (i < nb) {
-          float ss = 0.f, c = 0.f;
+      for (int i0 = 0; i0 < SB; i0 += kGroup) {
+        float part[2][kGroup];
 #pragma unroll
-          for (int j = 0; j < CH; ++j)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              const float t = elem<BF16>(rows[i][j], e);
-              const float tm = (FULL || cs.in_slice(j, e, a.lo)) ? t : 0.f;
-              ss = fmaf(tm, tm, ss);
-              c = fmaf(t, cs.u[j][e], c);
-            }
-          xchg_put(ss, xb, i, R4, tid);
-          xchg_put(c, xb, SB + i, R4, tid);
+        for (int g = 0; g < kGroup; ++g) {
+          part[0][g] = part[1][g] = 0.f;
+          if (i0 + g < SB)
+            key_sums<BF16, CH, FULL>(rows[i0 + g], cs, us, u, a.lo, part[0][g], part[1][g]);
         }
+        xchg_group<2, SB>(part, i0, xb, R4, tid);
       }
       __syncthreads();
       buf ^= 1;
@@ -282,98 +586,57 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
         z = a.scale * c / sqrtf(ss * a.inv_R + a.eps);
       }
       const float m_new = fmaxf(m, wave_max(z));
-      const float ez = (lane < nb) ? expf(z - m_new) : 0.f;
+      float ez = (lane < nb) ? expf(z - m_new) : 0.f;
       const float lb = wave_sum(ez);
-      if (s0 > 0) {
-        const float alpha = expf(m - m_new);
-        l = l * alpha + lb;
-        if (alpha != 1.f) {
-#pragma unroll
-          for (int j = 0; j < CH; ++j)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[j][e] *= alpha;
-        }
-      } else {
+      if constexpr (ONE) {
         l = lb;
+        ez = ez / lb;  // the routing weight itself: acc becomes o directly
+      } else {
+        if (s0 > 0) {
+          const float alpha = expf(m - m_new);
+          l = l * alpha + lb;
+          if (alpha != 1.f) {
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+#pragma unroll
+              for (int e = 0; e < VEC; ++e) acc[j][e] *= alpha;
+          }
+        } else {
+          l = lb;
+        }
       }
       m = m_new;
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
-        if (i < nb) {
-          const float pi = bcast(ez, i);
+        const float pi = bcast(ez, i);
 #pragma unroll
-          for (int j = 0; j < CH; ++j)
+        for (int j = 0; j < CH; ++j)
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[j][e] = fmaf(pi, elem<BF16>(rows[i][j], e), acc[j][e]);
+          for (int e = 0; e < VEC; ++e) acc[j][e] = fmaf(pi, elem<BF16>(rows[i][j], e), acc[j][e]);
+        if constexpr (ONE) {
+          // the next token's row i (an empty resource past the last token)
+          const Rsrc r = src_rsrc(a.src[i], i, next < a.N ? a.S : 0, next_byte, row_bytes);
+#pragma unroll
+          for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
         }
       }
     }
-
-    const float inv_l = 1.f / l;
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[j][e] *= inv_l;  // acc now holds o
-
-    float rho_o = 1.f;
-    if (a.out_norm) {
-      float sq = 0.f;
+    if constexpr (!ONE) {
+      const float inv_l = 1.f / l;
 #pragma unroll
       for (int j = 0; j < CH; ++j)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) sq = fmaf(acc[j][e], acc[j][e], sq);
-      float* xb = lds + buf * xfl;
-      xchg_put(sq, xb, 0, R4, tid);
-      __syncthreads();
-      buf ^= 1;
-      rho_o = 1.f / sqrtf(xchg_total(xb, 0, R4) * a.inv_D + a.eps);
-      if (a.o32) {
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          if (!cs.valid[j]) continue;
-          float* dst = a.o32 + n * a.D + cs.col0[j];
-#pragma unroll
-          for (int h = 0; h < VEC; h += 4) {
-            typedef float f32x4 __attribute__((ext_vector_type(4)));
-            f32x4 v = {acc[j][h], acc[j][h + 1], acc[j][h + 2], acc[j][h + 3]};
-            *reinterpret_cast<f32x4*>(dst + h) = v;
-          }
-        }
-      }
-    } else if (a.o32) {
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        if (!cs.valid[j]) continue;
-        float* dst = a.o32 + n * a.D + cs.col0[j];
-#pragma unroll
-        for (int h = 0; h < VEC; h += 4) {
-          typedef float f32x4 __attribute__((ext_vector_type(4)));
-          f32x4 v = {acc[j][h], acc[j][h + 1], acc[j][h + 2], acc[j][h + 3]};
-          *reinterpret_cast<f32x4*>(dst + h) = v;
-        }
-      }
+        for (int e = 0; e < VEC; ++e) acc[j][e] *= inv_l;  // acc now holds o
     }
-
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      if (!cs.valid[j]) continue;
-      float yv[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) yv[e] = a.out_norm ? acc[j][e] * rho_o * ow[j][e] : acc[j][e];
-      st_chunk(a.y, (n * a.D + cs.col0[j]) * ESZ, pack<BF16>(yv));
-    }
-    if (tid == 0) {
-      a.lse[n] = m + logf(l);
-      if (a.out_norm && a.o_rstd) a.o_rstd[n] = rho_o;
-    }
+    fwd_emit<BF16, CH, FULL>(a, cs, acc, ow, n, m + logf(l), lds, buf, xfl, R4, tid, row_bytes);
   }
 }
 
 // ------------------------------------------------------------------ backward, shared tail
 
 // Writes this workgroup's partial sums of du (slice columns) and dow (all columns).
-template <bool BF16, int CH>
-__device__ __forceinline__ void write_partials(const BwdArgs& a, const Cols<BF16, CH>& cs,
+template <bool BF16, int CH, bool FULL>
+__device__ __forceinline__ void write_partials(const BwdArgs& a, const Cols<BF16, CH, FULL>& cs,
                                                const float (&du)[CH][Fmt<BF16>::VEC],
                                                const float (&dow)[CH][Fmt<BF16>::VEC]) {
   constexpr int VEC = Fmt<BF16>::VEC;
@@ -403,17 +666,20 @@ __device__ __forceinline__ void write_partials(const BwdArgs& a, const Cols<BF16
 // All S <= SB rows of a token stay in VGPRs: delta = sum_s p_s <dY, v_s> is exact in FP32.
 // No output norm on this path (dL/do = dY).
 template <bool BF16, int CH, int SB, bool FULL>
-__global__ __launch_bounds__(512) void bwd_resident_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(occupancy_hint(CH, SB, FULL), 8)))
+void bwd_resident_kernel(const BwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
   constexpr int K = 3 * SB;
-  extern __shared__ float lds[];
+  extern __shared__ float lds_all[];
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
   const int R4 = nthr >> 4;
   const int xfl = K * R4;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.D * ESZ);
 
-  Cols<BF16, CH> cs;
-  cs.init(tid, nthr, a.D, a.lo, a.query, a.norm_w);
+  Cols<BF16, CH, FULL> cs;
+  cs.init(tid, nthr, a.D, a.lo, a.query, a.norm_w, lds_all);
+  float* lds = lds_all + Cols<BF16, CH, FULL>::param_bytes(nthr) / 4;  // exchange buffers
   float du[CH][VEC], dow[CH][VEC];
 #pragma unroll
   for (int j = 0; j < CH; ++j)
@@ -422,46 +688,68 @@ __global__ __launch_bounds__(512) void bwd_resident_kernel(const BwdArgs a) {
   const int S = a.S;
   int buf = 0;
 
-  for (int64_t n = blockIdx.x; n < a.N; n += gridDim.x) {
-    const int64_t row_off = n * a.row_stride * ESZ;
-    Chunk rows[SB][CH];
-    Chunk gy[CH];
+  // Software pipeline over tokens: the next token's dY row is loaded once this token's has been
+  // widened, and its source row i once row i's gradient has been stored, so the loads overlap
+  // this token's math and stores, and the next token's first wait covers only what was issued
+  // before its own loads (the vector-memory counter retires loads and stores in order).
+  // Loops run over all SB slots; slots i >= S use an empty resource (zero rows, dropped stores)
+  // and get routing weight 0, so there are no per-source branches and the wait counts stay exact.
+  Chunk rows[SB][CH];
+  Chunk gy[CH];
+  // lse of the current token; the next one is loaded with the next token's rows (a vector load
+  // waited for at its use would otherwise also drain every store issued before it)
+  float lse = a.lse[min((int64_t)blockIdx.x, a.N - 1)];
+  {
+    // issued in the order the loop body issues the next token's loads (dY, then rows 0..SB-1):
+    // the wait counts at the loop head are the minimum over both entry paths
+    const int64_t n0 = blockIdx.x;
+    const int live = n0 < a.N ? S : 0;
+    const Rsrc rg = src_rsrc(a.dout, 0, live, n0 * a.dout_stride * ESZ, row_bytes);
 #pragma unroll
-    for (int j = 0; j < CH; ++j)
-      gy[j] = cs.valid[j] ? ld_chunk(a.dout, (n * a.dout_stride + cs.col0[j]) * ESZ)
-                          : Chunk{{0u, 0u, 0u, 0u}};
-#pragma unroll
-    for (int i = 0; i < SB; ++i)
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        if (i < S && cs.valid[j]) {
-          rows[i][j] = ld_chunk(a.src[i], row_off + (int64_t)cs.col0[j] * ESZ);
-        } else {
-          rows[i][j] = Chunk{{0u, 0u, 0u, 0u}};
-        }
-      }
-    const float lse = a.lse[n];
-    float* xb = lds + buf * xfl;
+    for (int j = 0; j < CH; ++j) gy[j] = ld_row(rg, cs.voff[j]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
-      if (i < S) {
-        float ss = 0.f, c = 0.f, dp = 0.f;
+      const Rsrc r = src_rsrc(a.src[i], i, live, n0 * a.row_stride * ESZ, row_bytes);
 #pragma unroll
-        for (int j = 0; j < CH; ++j)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const float t = elem<BF16>(rows[i][j], e);
-            const float tm = (FULL || cs.in_slice(j, e, a.lo)) ? t : 0.f;
-            ss = fmaf(tm, tm, ss);
-            c = fmaf(t, cs.u[j][e], c);
-            dp = fmaf(elem<BF16>(gy[j], e), t, dp);
-          }
-        xchg_put(ss, xb, i, R4, tid);
-        xchg_put(c, xb, SB + i, R4, tid);
-        xchg_put(dp, xb, 2 * SB + i, R4, tid);
-      }
+      for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  }
+
+  // Token schedule: the first token of workgroup g is g; later ones come from a device-wide
+  // ticket counter (token = grid + ticket), so workgroups that run faster take more tokens and
+  // all finish together. Thread 0 takes the ticket at the top of the loop; its latency hides
+  // behind pass 1, and it is published through LDS at the barrier pass 1 ends with.
+  uint32_t* tslot = reinterpret_cast<uint32_t*>(lds + 2 * xfl);
+  int64_t n = blockIdx.x;
+  while (n < a.N) {
+    uint32_t tk = 0;
+    if (a.ticket && tid == 0) tk = atomicAdd(a.ticket, 1u);
+    float* xb = lds + buf * xfl;
+    uint32_t us[3][CH][4];
+    float u[CH][VEC];
+    if constexpr (BF16) cs.fetch_us(laundered_lane_off(tid), us);
+    else cs.fetch_u(laundered_lane_off(tid), u);
+#pragma unroll
+    for (int i0 = 0; i0 < SB; i0 += kGroup) {
+      float part[3][kGroup];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        part[0][g] = part[1][g] = part[2][g] = 0.f;
+        if (i0 + g < SB) {
+          key_sums<BF16, CH, FULL>(rows[i0 + g], cs, us, u, a.lo, part[0][g], part[1][g]);
+          part[2][g] = dot_rows<BF16, CH>(rows[i0 + g], gy);
+        }
+      }
+      xchg_group<3, SB>(part, i0, xb, R4, tid);
+    }
+    if (tid == 0) tslot[buf] = tk;
     __syncthreads();
+    const int64_t next =
+        a.ticket ? (int64_t)gridDim.x + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf])
+                 : n + gridDim.x;
+    const bool has_next = next < a.N;
     buf ^= 1;
 
     // lane s finishes source s
@@ -477,30 +765,38 @@ __global__ __launch_bounds__(512) void bwd_resident_kernel(const BwdArgs a) {
     const float A = a.scale * p * (dp - delta) * rho;
     const float B = -A * rho * rho * c * a.inv_R;
 
+    float dof[CH][VEC];
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dof[j][e] = elem<BF16>(gy[j], e);
+    const int live_next = has_next ? S : 0;
+    const float lse_next = a.lse[has_next ? next : n];
+    {
+      // the next token's dY row (an empty resource past the last token)
+      const Rsrc rg = src_rsrc(a.dout, 0, live_next, next * a.dout_stride * ESZ, row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) gy[j] = ld_row(rg, cs.voff[j]);
+    }
+    const int64_t drow_byte = n * a.drow_stride * ESZ;
+    const int64_t next_byte = next * a.row_stride * ESZ;
+    cs.fetch_u(laundered_lane_off(tid), u);
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
-      if (i < S) {
-        const float pi = bcast(p, i), Ai = bcast(A, i), Bi = bcast(B, i);
+      Chunk out[CH];
+      grad_row<BF16, CH, FULL>(rows[i], cs, u, dof, bcast(p, i), bcast(A, i), bcast(B, i), a.lo,
+                               du, out);
+      const Rsrc rd = src_rsrc(a.dsrc[i], i, S, drow_byte, row_bytes);
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          float dv[VEC];
+      for (int j = 0; j < CH; ++j) st_row(rd, cs.voff[j], out[j]);
+      const Rsrc r = src_rsrc(a.src[i], i, live_next, next_byte, row_bytes);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const float t = elem<BF16>(rows[i][j], e);
-            const float tm = (FULL || cs.in_slice(j, e, a.lo)) ? t : 0.f;
-            float d = pi * elem<BF16>(gy[j], e);
-            d = fmaf(Ai, cs.u[j][e], d);
-            d = fmaf(Bi, tm, d);
-            dv[e] = d;
-            du[j][e] = fmaf(Ai, t, du[j][e]);
-          }
-          if (cs.valid[j])
-            st_chunk(a.dsrc[i], (n * a.drow_stride + cs.col0[j]) * ESZ, pack<BF16>(dv));
-        }
-      }
+      for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
     }
+    lse = lse_next;
+    n = next;
   }
-  write_partials<BF16, CH>(a, cs, du, dow);
+  write_partials<BF16, CH, FULL>(a, cs, du, dow);
 }
 
 // ------------------------------------------------------------------ backward, streaming
@@ -512,13 +808,15 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
   constexpr int K = 3 * SB;
-  extern __shared__ float lds[];
+  extern __shared__ float lds_all[];
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
   const int R4 = nthr >> 4;
   const int xfl = K * R4;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.D * ESZ);
 
-  Cols<BF16, CH> cs;
-  cs.init(tid, nthr, a.D, a.lo, a.query, a.norm_w);
+  Cols<BF16, CH, FULL> cs;
+  cs.init(tid, nthr, a.D, a.lo, a.query, a.norm_w, lds_all);
+  float* lds = lds_all + Cols<BF16, CH, FULL>::param_bytes(nthr) / 4;  // exchange buffers
   float du[CH][VEC], dow[CH][VEC], ow[CH][VEC];
 #pragma unroll
   for (int j = 0; j < CH; ++j)
@@ -531,44 +829,44 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
   int buf = 0;
 
   for (int64_t n = blockIdx.x; n < a.N; n += gridDim.x) {
-    const int64_t row_off = n * a.row_stride * ESZ;
+    const int64_t row_byte = n * a.row_stride * ESZ;
     float dov[CH][VEC], o[CH][VEC];
+    {
+      const Rsrc rg = row_rsrc(a.dout, n * a.dout_stride * ESZ, row_bytes);
+      const Rsrc ro = row_rsrc(a.o32, n * a.D * 4, static_cast<uint32_t>(a.D * 4));
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      Chunk g = cs.valid[j] ? ld_chunk(a.dout, (n * a.dout_stride + cs.col0[j]) * ESZ)
-                            : Chunk{{0u, 0u, 0u, 0u}};
+      for (int j = 0; j < CH; ++j) {
+        const Chunk g = ld_row(rg, cs.voff[j]);
 #pragma unroll
-      for (int h = 0; h < VEC; h += 4) {
-        Chunk oc = cs.valid[j] ? ld_chunk(a.o32, (n * a.D + cs.col0[j] + h) * 4)
-                               : Chunk{{0u, 0u, 0u, 0u}};
+        for (int h = 0; h < VEC; h += 4) {
+          const Chunk oc = ld_row(ro, static_cast<uint32_t>((cs.col0[j] + h) * 4));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[j][h + e] = bits_f(oc.w[e]);
+          for (int e = 0; e < 4; ++e) o[j][h + e] = bits_f(oc.w[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dov[j][e] = elem<BF16>(g, e);
       }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) dov[j][e] = elem<BF16>(g, e);
     }
     // do and delta = <do, o>
     float delta;
     {
-      float part[2] = {0.f, 0.f};
+      float part[2][kGroup] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
       if (a.out_norm) {
 #pragma unroll
         for (int j = 0; j < CH; ++j)
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
-            const float g = dov[j][e] * ow[j][e];
-            part[0] = fmaf(g, o[j][e], part[0]);          // <g, o>
-            part[1] = fmaf(o[j][e], o[j][e], part[1]);    // <o, o>
+            part[0][0] = fmaf(dov[j][e] * ow[j][e], o[j][e], part[0][0]);  // <g, o>
+            part[1][0] = fmaf(o[j][e], o[j][e], part[1][0]);                // <o, o>
           }
       } else {
 #pragma unroll
         for (int j = 0; j < CH; ++j)
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) part[0] = fmaf(dov[j][e], o[j][e], part[0]);
+          for (int e = 0; e < VEC; ++e) part[0][0] = fmaf(dov[j][e], o[j][e], part[0][0]);
       }
       float* xb = lds + buf * xfl;
-      xchg_put(part[0], xb, 0, R4, tid);
-      xchg_put(part[1], xb, 1, R4, tid);
+      xchg_group<2, 1>(part, 0, xb, R4, tid);
       __syncthreads();
       buf ^= 1;
       const float t0 = xchg_total(xb, 0, R4);
@@ -591,39 +889,34 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
       }
     }
     const float lse = a.lse[n];
+    const int64_t drow_byte = n * a.drow_stride * ESZ;
 
     for (int s0 = 0; s0 < a.S; s0 += SB) {
       const int nb = min(SB, a.S - s0);
-      Chunk rows[SB][CH];
-#pragma unroll
-      for (int i = 0; i < SB; ++i)
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          if (i < nb && cs.valid[j]) {
-            rows[i][j] = ld_chunk(a.src[s0 + i], row_off + (int64_t)cs.col0[j] * ESZ);
-          } else {
-            rows[i][j] = Chunk{{0u, 0u, 0u, 0u}};
-          }
-        }
-      float* xb = lds + buf * xfl;
+      Chunk rows[SB][CH];  // slots i >= nb: empty resource, zero rows, weight 0
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
-        if (i < nb) {
-          float ss = 0.f, c = 0.f, dp = 0.f;
+        const Rsrc r = src_rsrc(a.src[min(s0 + i, kMaxSources - 1)], i, nb, row_byte, row_bytes);
 #pragma unroll
-          for (int j = 0; j < CH; ++j)
+        for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+      }
+      float* xb = lds + buf * xfl;
+      uint32_t us[3][CH][4];
+      float u[CH][VEC];
+      if constexpr (BF16) cs.fetch_us(laundered_lane_off(tid), us);
+      else cs.fetch_u(laundered_lane_off(tid), u);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              const float t = elem<BF16>(rows[i][j], e);
-              const float tm = (FULL || cs.in_slice(j, e, a.lo)) ? t : 0.f;
-              ss = fmaf(tm, tm, ss);
-              c = fmaf(t, cs.u[j][e], c);
-              dp = fmaf(dov[j][e], t, dp);
-            }
-          xchg_put(ss, xb, i, R4, tid);
-          xchg_put(c, xb, SB + i, R4, tid);
-          xchg_put(dp, xb, 2 * SB + i, R4, tid);
+      for (int i0 = 0; i0 < SB; i0 += kGroup) {
+        float part[3][kGroup];
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+          part[0][g] = part[1][g] = part[2][g] = 0.f;
+          if (i0 + g < SB) {
+            key_sums<BF16, CH, FULL>(rows[i0 + g], cs, us, u, a.lo, part[0][g], part[1][g]);
+            part[2][g] = dot_f32<BF16, CH>(rows[i0 + g], dov);
+          }
         }
+        xchg_group<3, SB>(part, i0, xb, R4, tid);
       }
       __syncthreads();
       buf ^= 1;
@@ -637,31 +930,19 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
       }
       const float A = a.scale * p * (dp - delta) * rho;
       const float B = -A * rho * rho * c * a.inv_R;
+      cs.fetch_u(laundered_lane_off(tid), u);
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
-        if (i < nb) {
-          const float pi = bcast(p, i), Ai = bcast(A, i), Bi = bcast(B, i);
+        Chunk out[CH];
+        grad_row<BF16, CH, FULL>(rows[i], cs, u, dov, bcast(p, i), bcast(A, i), bcast(B, i), a.lo,
+                                 du, out);
+        const Rsrc rd = src_rsrc(a.dsrc[min(s0 + i, kMaxSources - 1)], i, nb, drow_byte, row_bytes);
 #pragma unroll
-          for (int j = 0; j < CH; ++j) {
-            float dv[VEC];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              const float t = elem<BF16>(rows[i][j], e);
-              const float tm = (FULL || cs.in_slice(j, e, a.lo)) ? t : 0.f;
-              float d = pi * dov[j][e];
-              d = fmaf(Ai, cs.u[j][e], d);
-              d = fmaf(Bi, tm, d);
-              dv[e] = d;
-              du[j][e] = fmaf(Ai, t, du[j][e]);
-            }
-            if (cs.valid[j])
-              st_chunk(a.dsrc[s0 + i], (n * a.drow_stride + cs.col0[j]) * ESZ, pack<BF16>(dv));
-          }
-        }
+        for (int j = 0; j < CH; ++j) st_row(rd, cs.voff[j], out[j]);
       }
     }
   }
-  write_partials<BF16, CH>(a, cs, du, dow);
+  write_partials<BF16, CH, FULL>(a, cs, du, dow);
 }
 
 // ------------------------------------------------------------------ finaliser
