@@ -18,11 +18,12 @@ from . import _binding as B
 
 class _AttnResFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, eps, scale, out_norm, packed, query, norm_w, out_w, *srcs):
+    def forward(ctx, eps, scale, out_norm, deterministic, packed, query, norm_w, out_w, *srcs):
         values = srcs[0] if packed else list(srcs)
         y, lse, rstd, o32 = B.attnres_fwd(values, query, norm_w, out_w, eps=eps, scale=scale,
                                           out_norm=out_norm)
         ctx.eps, ctx.scale, ctx.out_norm, ctx.packed = eps, scale, out_norm, packed
+        ctx.deterministic = deterministic
         ctx.save_for_backward(query, norm_w, out_w, lse, rstd, o32, *srcs)
         return y
 
@@ -39,16 +40,19 @@ class _AttnResFn(torch.autograd.Function):
             dvalues = [torch.empty(v.shape, dtype=v.dtype, device=v.device) for v in values]
         dvalues, dq, dw, dow = B.attnres_bwd(values, query, norm_w, out_w, lse, rstd, o32, dy,
                                              eps=ctx.eps, scale=ctx.scale,
-                                             out_norm=ctx.out_norm, dvalues=dvalues)
+                                             out_norm=ctx.out_norm,
+                                             deterministic=ctx.deterministic, dvalues=dvalues)
         dsrcs = (dvalues,) if ctx.packed else tuple(dvalues)
-        return (None, None, None, None, dq.view_as(query), dw, dow) + dsrcs
+        return (None, None, None, None, None, dq.view_as(query), dw, dow) + dsrcs
 
 
 def attnres(values: Union[torch.Tensor, Sequence[torch.Tensor]], query: torch.Tensor, *,
             eps: float = B.EPS_DEFAULT, scale: float = 1.0,
             norm_weight: Optional[torch.Tensor] = None, out_norm: bool = False,
-            out_weight: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """AttnRes read of S ordered sources with one learned query; returns [..., D]."""
+            out_weight: Optional[torch.Tensor] = None,
+            deterministic: bool = False) -> torch.Tensor:
+    """AttnRes read of S ordered sources with one learned query; returns [..., D].
+    deterministic=True makes the q/w/ow gradients bitwise reproducible (fixed token split)."""
     if out_weight is not None and not out_norm:
         raise ValueError("out_weight requires out_norm=True")
     if isinstance(values, torch.Tensor):
@@ -57,8 +61,8 @@ def attnres(values: Union[torch.Tensor, Sequence[torch.Tensor]], query: torch.Te
         flat = values.reshape(S, -1, D)
         if flat.stride(-1) != 1:
             flat = flat.contiguous()
-        y = _AttnResFn.apply(eps, scale, out_norm, True, query.reshape(-1), norm_weight,
-                             out_weight, flat)
+        y = _AttnResFn.apply(eps, scale, out_norm, deterministic, True, query.reshape(-1),
+                             norm_weight, out_weight, flat)
     else:
         vs = list(values)
         D = vs[0].shape[-1]
@@ -71,6 +75,6 @@ def attnres(values: Union[torch.Tensor, Sequence[torch.Tensor]], query: torch.Te
             flat.append(f)
         if len({f.stride(0) for f in flat}) > 1:
             flat = [f.contiguous() for f in flat]
-        y = _AttnResFn.apply(eps, scale, out_norm, False, query.reshape(-1), norm_weight,
-                             out_weight, *flat)
+        y = _AttnResFn.apply(eps, scale, out_norm, deterministic, False, query.reshape(-1),
+                             norm_weight, out_weight, *flat)
     return y.reshape(*lead, D)

@@ -95,6 +95,8 @@ attnres_status check_desc(const attnres_desc* d) {
     return fail(ATTNRES_ERR_INVALID_ARG, "scale must be finite");
   if (d->has_out_weight && !d->out_norm)
     return fail(ATTNRES_ERR_INVALID_ARG, "has_out_weight requires out_norm");
+  if (d->deterministic != 0 && d->deterministic != 1)
+    return fail(ATTNRES_ERR_INVALID_ARG, "deterministic must be 0 or 1");
   return ATTNRES_OK;
 }
 
@@ -166,6 +168,7 @@ const void* bwd_ptr(const Shape& sh) {
 // LDS of every kernel: the per-thread parameter region (u = w*q as float4 slots, plus the
 // three-term bf16 split for bf16), then two exchange buffers (and the backward's ticket slots).
 size_t param_lds(const Shape& sh) {
+  if (sh.ch > 2) return 0;  // CH == 4 keeps the parameter vectors in registers
   const size_t slots = sh.ch * sh.vec / 4 + (sh.bf16 ? 3 * sh.ch : 0);
   return slots * sh.threads * 16u;
 }
@@ -370,13 +373,14 @@ attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
   Shape sh;
   attnres_status st = make_shape(d, &sh);
   if (st != ATTNRES_OK) return st;
+  if ((st = check_param(query, true, sh.esz, "query")) != ATTNRES_OK) return st;
+  if ((st = check_param(norm_w, d->has_norm_weight, sh.esz, "norm_w")) != ATTNRES_OK) return st;
+  if ((st = check_param(out_w, d->has_out_weight, sh.esz, "out_w")) != ATTNRES_OK) return st;
+  if (d->N == 0) return ATTNRES_OK;  // nothing to read or write
   FwdArgs a;
   std::memset(&a, 0, sizeof a);
   st = check_sources(d, sh, values, "values", a.src);
   if (st != ATTNRES_OK) return st;
-  if ((st = check_param(query, true, sh.esz, "query")) != ATTNRES_OK) return st;
-  if ((st = check_param(norm_w, d->has_norm_weight, sh.esz, "norm_w")) != ATTNRES_OK) return st;
-  if ((st = check_param(out_w, d->has_out_weight, sh.esz, "out_w")) != ATTNRES_OK) return st;
   if (!out || !aligned(out, 16))
     return fail(out ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "out NULL or misaligned");
   if (!lse || !aligned(lse, 4))
@@ -394,7 +398,6 @@ attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
   if (out_rstd) outs.push_back(rows_range(out_rstd, N, 1, 1, 4, "out_rstd"));
   if (o32) outs.push_back(rows_range(o32, N, d->D, d->D, 4, "o32"));
   if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
-  if (N == 0) return ATTNRES_OK;
 
   const void* fn = fwd_ptr(sh);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no forward kernel for this shape");
@@ -442,38 +445,42 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
   if (st != ATTNRES_OK) return st;
   BwdArgs a;
   std::memset(&a, 0, sizeof a);
-  st = check_sources(d, sh, values, "values", a.src);
-  if (st != ATTNRES_OK) return st;
-  const void* dptr[kMaxSources];
-  st = check_sources(d, sh, dvalues, "dvalues", dptr);
-  if (st != ATTNRES_OK) return st;
+  const void* dptr[kMaxSources] = {nullptr};
+  const int64_t N = d->N;
   if ((st = check_param(query, true, sh.esz, "query")) != ATTNRES_OK) return st;
   if ((st = check_param(norm_w, d->has_norm_weight, sh.esz, "norm_w")) != ATTNRES_OK) return st;
   if ((st = check_param(out_w, d->has_out_weight, sh.esz, "out_w")) != ATTNRES_OK) return st;
-  if (!lse || !aligned(lse, 4))
-    return fail(lse ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "lse NULL or misaligned");
-  if ((st = check_param(out_rstd, d->out_norm, 4, "out_rstd")) != ATTNRES_OK) return st;
-  if ((st = check_param(o32, !sh.resident, 16, "o32")) != ATTNRES_OK) return st;
-  if (!dout || !aligned(dout, 16))
-    return fail(dout ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "dout NULL or misaligned");
-  if (dout_row_stride < d->D || (dout_row_stride * sh.esz) % 16 != 0)
-    return fail(ATTNRES_ERR_ALIGNMENT, "dout_row_stride must be >= D and a multiple of 16 bytes");
+  if (N > 0) {  // with N == 0 no per-token array is touched (they may be NULL)
+    st = check_sources(d, sh, values, "values", a.src);
+    if (st != ATTNRES_OK) return st;
+    st = check_sources(d, sh, dvalues, "dvalues", dptr);
+    if (st != ATTNRES_OK) return st;
+    if (!lse || !aligned(lse, 4))
+      return fail(lse ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "lse NULL or misaligned");
+    if ((st = check_param(out_rstd, d->out_norm, 4, "out_rstd")) != ATTNRES_OK) return st;
+    if ((st = check_param(o32, !sh.resident, 16, "o32")) != ATTNRES_OK) return st;
+    if (!dout || !aligned(dout, 16))
+      return fail(dout ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "dout NULL or misaligned");
+    if (dout_row_stride < d->D || (dout_row_stride * sh.esz) % 16 != 0)
+      return fail(ATTNRES_ERR_ALIGNMENT, "dout_row_stride must be >= D and a multiple of 16 bytes");
+  }
   if ((st = check_param(dq, true, sh.esz, "dq")) != ATTNRES_OK) return st;
   if ((st = check_param(dw, d->has_norm_weight, sh.esz, "dw")) != ATTNRES_OK) return st;
   if ((st = check_param(dow, d->has_out_weight, sh.esz, "dow")) != ATTNRES_OK) return st;
   if (!workspace) return fail(ATTNRES_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(ATTNRES_ERR_ALIGNMENT, "workspace not 256-byte aligned");
 
-  const int64_t N = d->N;
   std::vector<Range> ins, outs;
-  for (int s = 0; s < d->S; ++s)
-    ins.push_back(rows_range(a.src[s], N, values->row_stride, d->D, sh.esz, "values"));
-  ins.push_back(rows_range(dout, N, dout_row_stride, d->D, sh.esz, "dout"));
-  ins.push_back(rows_range(lse, N, 1, 1, 4, "lse"));
-  if (o32) ins.push_back(rows_range(o32, N, d->D, d->D, 4, "o32"));
-  if (out_rstd) ins.push_back(rows_range(out_rstd, N, 1, 1, 4, "out_rstd"));
-  for (int s = 0; s < d->S; ++s)
-    outs.push_back(rows_range(dptr[s], N, dvalues->row_stride, d->D, sh.esz, "dvalues"));
+  if (N > 0) {
+    for (int s = 0; s < d->S; ++s)
+      ins.push_back(rows_range(a.src[s], N, values->row_stride, d->D, sh.esz, "values"));
+    ins.push_back(rows_range(dout, N, dout_row_stride, d->D, sh.esz, "dout"));
+    ins.push_back(rows_range(lse, N, 1, 1, 4, "lse"));
+    if (o32) ins.push_back(rows_range(o32, N, d->D, d->D, 4, "o32"));
+    if (out_rstd) ins.push_back(rows_range(out_rstd, N, 1, 1, 4, "out_rstd"));
+    for (int s = 0; s < d->S; ++s)
+      outs.push_back(rows_range(dptr[s], N, dvalues->row_stride, d->D, sh.esz, "dvalues"));
+  }
   outs.push_back(rows_range(dq, 1, d->R, d->R, sh.esz, "dq"));
   if (dw) outs.push_back(rows_range(dw, 1, d->R, d->R, sh.esz, "dw"));
   if (dow) outs.push_back(rows_range(dow, 1, d->D, d->D, sh.esz, "dow"));
@@ -512,7 +519,7 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
     a.part_du = reinterpret_cast<float*>(ws + pl.off_du);
     a.part_dow = d->has_out_weight ? reinterpret_cast<float*>(ws + pl.off_dow) : nullptr;
     a.out_norm = d->out_norm ? 1 : 0;
-    if (sh.resident) {
+    if (sh.resident && !d->deterministic) {
       a.ticket = reinterpret_cast<uint32_t*>(ws + pl.off_ticket);
       void* targ = a.ticket;
       st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");

@@ -226,27 +226,57 @@ __device__ __forceinline__ float xchg_total(const float* xb, int k, int R4) {
   return s;
 }
 
+// ------------------------------------------------------------------ per-source scalars
+
+// Reciprocal key RMS and score of one source from its slice sums, each operation rounded on its
+// own: with contraction off here, no product below can be fused into an FMA with its neighbours or
+// with the caller's subtraction of lse, so the forward and both backwards compute bitwise-identical
+// scores and the backward's exp(score - lse) reproduces the forward's routing weights (exactly 1
+// for a single source). Division and square root are the correctly rounded HIP defaults.
+struct Score {
+  float rho, z;
+};
+__device__ __forceinline__ Score source_score(float ss, float c, float inv_R, float eps,
+                                              float scale) {
+#pragma clang fp contract(off)
+  Score r;
+  r.rho = 1.f / sqrtf(ss * inv_R + eps);
+  r.z = (scale * r.rho) * c;
+  return r;
+}
+
+// Routing weight of a source from its score and the token's log-sum-exp (no contraction).
+__device__ __forceinline__ float routing_weight(float z, float lse) {
+#pragma clang fp contract(off)
+  const float x = z - lse;
+  return expf(x);
+}
+
 // ------------------------------------------------------------------ per-lane column setup
 
 // Columns of the CH chunks a thread owns: byte offset inside a row, validity and, for R < D with
-// bf16, a per-half mask of the key slice. The loop-invariant parameter vectors live in LDS rather
-// than VGPRs (each thread's slots are 16 bytes, lane-contiguous): u = w*q on the slice (0
-// elsewhere) in FP32 and, for bf16, its exact three-term split u = u1 + u2 + u3 in packed bf16
-// pairs. Kernels fetch them per token through a laundered offset, so the compiler cannot hoist
-// them back into registers.
+// bf16, a per-half mask of the key slice. The loop-invariant parameter vectors are u = w*q on the
+// slice (0 elsewhere) in FP32 and, for bf16, its exact three-term split u = u1 + u2 + u3 in packed
+// bf16 pairs. With CH <= 2 they live in LDS rather than VGPRs (each thread's slots are 16 bytes,
+// lane-contiguous; 10 bytes per column for bf16) and kernels fetch them per token through a
+// laundered offset, so the compiler cannot hoist them back into registers. With CH == 4 (the
+// widest rows) the region would not fit a workgroup's LDS, and they stay in registers.
 template <bool BF16, int CH, bool FULL>
 struct Cols {
   static constexpr int VEC = Fmt<BF16>::VEC;
   static constexpr int ESZ = Fmt<BF16>::ESZ;
+  static constexpr bool IN_LDS = CH <= 2;
   static constexpr int U_SLOTS = CH * VEC / 4;          // float4 slots of u
   static constexpr int S_SLOTS = BF16 ? 3 * CH : 0;     // uint4 slots of the split
-  static constexpr int SLOTS = U_SLOTS + S_SLOTS;
+  static constexpr int SLOTS = IN_LDS ? U_SLOTS + S_SLOTS : 0;
   int col0[CH];
   uint32_t voff[CH];
   bool valid[CH];
   uint32_t mk[CH][4];
-  char* params;  // this workgroup's parameter region in LDS
+  char* params;  // this workgroup's parameter region in LDS (IN_LDS)
   int nthr;
+  float ureg[IN_LDS ? 1 : CH][VEC];       // registers otherwise
+  uint32_t usreg[IN_LDS ? 1 : 3][IN_LDS ? 1 : CH][4];
 
   // LDS bytes of the parameter region for a workgroup of `threads` threads.
   static constexpr uint32_t param_bytes(int threads) { return SLOTS * threads * 16u; }
@@ -271,10 +301,15 @@ struct Cols {
         }
         u[e] = uv;
       }
+      if constexpr (IN_LDS) {
 #pragma unroll
-      for (int h = 0; h < VEC / 4; ++h)
-        *reinterpret_cast<float4*>(params + ((j * (VEC / 4) + h) * nthr + tid) * 16) =
-            make_float4(u[4 * h], u[4 * h + 1], u[4 * h + 2], u[4 * h + 3]);
+        for (int h = 0; h < VEC / 4; ++h)
+          *reinterpret_cast<float4*>(params + ((j * (VEC / 4) + h) * nthr + tid) * 16) =
+              make_float4(u[4 * h], u[4 * h + 1], u[4 * h + 2], u[4 * h + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ureg[IN_LDS ? 0 : j][e] = u[e];
+      }
       if constexpr (BF16) {
         uint32_t us[3][4];
 #pragma unroll
@@ -290,10 +325,17 @@ struct Cols {
           const bool in0 = col0[j] + 2 * k >= lo, in1 = col0[j] + 2 * k + 1 >= lo;
           mk[j][k] = (in0 ? 0x0000ffffu : 0u) | (in1 ? 0xffff0000u : 0u);
         }
+        if constexpr (IN_LDS) {
 #pragma unroll
-        for (int t = 0; t < 3; ++t)
-          *reinterpret_cast<uint4*>(params + ((U_SLOTS + t * CH + j) * nthr + tid) * 16) =
-              make_uint4(us[t][0], us[t][1], us[t][2], us[t][3]);
+          for (int t = 0; t < 3; ++t)
+            *reinterpret_cast<uint4*>(params + ((U_SLOTS + t * CH + j) * nthr + tid) * 16) =
+                make_uint4(us[t][0], us[t][1], us[t][2], us[t][3]);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 3; ++t)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) usreg[IN_LDS ? 0 : t][IN_LDS ? 0 : j][k] = us[t][k];
+        }
       }
     }
   }
@@ -301,6 +343,13 @@ struct Cols {
   // Per-token fetches (after the barrier that follows init). `lane_off` = tid * 16, laundered by
   // the caller once per token.
   __device__ __forceinline__ void fetch_u(uint32_t lane_off, float (&u)[CH][VEC]) const {
+    if constexpr (!IN_LDS) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) u[j][e] = ureg[IN_LDS ? 0 : j][e];
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < CH; ++j)
 #pragma unroll
@@ -314,6 +363,15 @@ struct Cols {
       }
   }
   __device__ __forceinline__ void fetch_us(uint32_t lane_off, uint32_t (&us)[3][CH][4]) const {
+    if constexpr (BF16 && !IN_LDS) {
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) us[t][j][k] = usreg[IN_LDS ? 0 : t][IN_LDS ? 0 : j][k];
+      return;
+    }
     if constexpr (BF16) {
 #pragma unroll
       for (int t = 0; t < 3; ++t)
@@ -583,7 +641,7 @@ void fwd_kernel(const FwdArgs a) {
       if (lane < nb) {
         const float ss = xchg_total(xb, lane, R4);
         const float c = xchg_total(xb, SB + lane, R4);
-        z = a.scale * c / sqrtf(ss * a.inv_R + a.eps);
+        z = source_score(ss, c, a.inv_R, a.eps, a.scale).z;
       }
       const float m_new = fmaxf(m, wave_max(z));
       float ez = (lane < nb) ? expf(z - m_new) : 0.f;
@@ -758,8 +816,9 @@ void bwd_resident_kernel(const BwdArgs a) {
       const float ss = xchg_total(xb, lane, R4);
       c = xchg_total(xb, SB + lane, R4);
       dp = xchg_total(xb, 2 * SB + lane, R4);
-      rho = 1.f / sqrtf(ss * a.inv_R + a.eps);
-      p = expf(a.scale * rho * c - lse);
+      const Score sc = source_score(ss, c, a.inv_R, a.eps, a.scale);
+      rho = sc.rho;
+      p = routing_weight(sc.z, lse);
     }
     const float delta = wave_sum(p * dp);
     const float A = a.scale * p * (dp - delta) * rho;
@@ -925,8 +984,9 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
         const float ss = xchg_total(xb, lane, R4);
         c = xchg_total(xb, SB + lane, R4);
         dp = xchg_total(xb, 2 * SB + lane, R4);
-        rho = 1.f / sqrtf(ss * a.inv_R + a.eps);
-        p = expf(a.scale * rho * c - lse);
+        const Score sc = source_score(ss, c, a.inv_R, a.eps, a.scale);
+        rho = sc.rho;
+        p = routing_weight(sc.z, lse);
       }
       const float A = a.scale * p * (dp - delta) * rho;
       const float B = -A * rho * rho * c * a.inv_R;

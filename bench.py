@@ -66,6 +66,9 @@ def main() -> int:
     ap.add_argument("--workload", default="bf16_s10_n32768_d4096")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--check", type=int, default=1, help="sampled-token parity check (0 = off)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the read "
@@ -75,6 +78,16 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
+        return 0
 
     import attention_residuals_amd as A
     import attnres_workloads as W

@@ -55,12 +55,17 @@ typedef struct {
   int32_t D;               /* width; D % 8 == 0 (bf16) or D % 4 == 0 (f32); 8 <= D <= 16384 */
   int32_t R;               /* routing rank, 1 <= R <= D; key = final R coordinates */
   int32_t dtype;           /* attnres_dtype */
-  int64_t N;               /* tokens, N >= 0 (N == 0 is a no-op apart from zeroed gradients) */
+  int64_t N;               /* tokens, N >= 0. N == 0: nothing is read and the per-token arrays
+                              may be NULL; the backward still writes zero dq/dw/dow */
   float eps;               /* inside both square roots; the pages' default is 2^-23 */
   float scale;             /* score multiplier; default 1 */
   int32_t has_norm_weight; /* key-norm weight w[R] present */
   int32_t out_norm;        /* output RMSNorm after the mixture */
   int32_t has_out_weight;  /* output-norm weight ow[D] present (requires out_norm) */
+  int32_t deterministic;   /* 1: fixed token split, dq/dw/dow bitwise reproducible across calls;
+                              0: tokens handed out by a device-wide counter (faster: workgroups
+                              finish together), dq/dw/dow reproducible to FP32 rounding only.
+                              y, lse and dvalues are bitwise reproducible in both modes. */
 } attnres_desc;
 
 /* S row blocks of shape [N, D]: either one packed [S, N, D] tensor or a list of S pointers.
@@ -83,9 +88,9 @@ typedef struct {
  * keep a token's rows on chip), else 0. */
 attnres_status attnres_o32_elems(const attnres_desc* desc, size_t* elems);
 
-/* Bytes of device workspace attnres_bwd needs on the CURRENT device (FP32 partial sums of the
- * q/w/ow gradients, one row per workgroup of the backward, plus the finaliser's counters). The
- * contents need no initialisation; the backward leaves them in a reusable state. */
+/* Bytes of device workspace attnres_bwd needs on the CURRENT device (a token counter and FP32
+ * partial sums of the q/w/ow gradients, one row per workgroup of the backward). The contents need
+ * no initialisation. */
 attnres_status attnres_workspace_bytes(const attnres_desc* desc, size_t* bytes);
 
 /* Forward.
@@ -110,7 +115,8 @@ attnres_status attnres_fwd(const attnres_desc* desc, const attnres_sources* valu
  *   dow [D]         gradient of the output-norm weight (iff has_out_weight, else NULL).
  *   workspace       at least attnres_workspace_bytes(desc) bytes, 256-byte aligned; not shared
  *                   with any concurrent call.
- * Reductions over tokens use a fixed order: repeated calls give bitwise-identical results. */
+ * With desc->deterministic, the reductions over tokens use a fixed order and repeated calls give
+ * bitwise-identical results; otherwise only dq/dw/dow may differ in the last bits. */
 attnres_status attnres_bwd(const attnres_desc* desc, const attnres_sources* values,
                            const void* query, const void* norm_w, const void* out_w,
                            const float* lse, const float* out_rstd, const float* o32,

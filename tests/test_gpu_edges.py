@@ -1,0 +1,266 @@
+"""GPU edge cases of the AttnRes read against the FP64 oracle, through the C ABI.
+
+Covers the source counts of the FLA PR page's parity matrix (1, 3, 7, 10, 15, 29), routing ranks
+(fast-attnres page, "Sliced LR-AttnRes": powers of two, 384, 640, odd ranks), widths, tiny and empty
+token counts, packed vs list sources, repeated sources, strided rows, degenerate inputs (q = 0, zero
+rows, 1e-3..1e3 row scales), the output RMSNorm with and without its weight, determinism, the autograd
+wrapper, HIP-graph capture and replay, and error returns that launch nothing.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attnres_workloads as W
+from parity import (assert_ok, check_all, compare_rows, compare_vec, gpu_available, inputs_on,
+                    run_gpu, run_oracle, to_f64)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+
+def _wl(S, N, D, R, dtype="bf16", norm_weight=True, out_norm=False, out_weight=False, seed=7,
+        **kw):
+    return W.Workload(f"edge_s{S}_n{N}_d{D}_r{R}", S=S, N=N, D=D, R=R, dtype=dtype,
+                      norm_weight=norm_weight, out_norm=out_norm, out_weight=out_weight,
+                      seed=seed, **kw)
+
+
+def _check(w, xc, label, **kw):
+    got = run_gpu(w, inputs_on(xc, "cuda"), **kw)
+    ref = run_oracle(w, xc)
+    assert_ok(check_all(w, got, ref), label)
+    return got
+
+
+@pytest.mark.parametrize("S", [1, 3, 7, 10, 15, 29])
+def test_source_counts(S):
+    w = _wl(S, 333, 1024, 1024, seed=100 + S)
+    _check(w, W.generate(w), f"S={S}")
+
+
+@pytest.mark.parametrize("R", [1, 3, 16, 384, 512, 640, 2048])
+def test_routing_ranks(R):
+    w = _wl(5, 257, 2048, R, seed=200 + R, norm_weight=R % 2 == 0)
+    _check(w, W.generate(w), f"R={R}")
+
+
+@pytest.mark.parametrize("D,dtype", [(8, "bf16"), (256, "bf16"), (1024, "bf16"), (4096, "bf16"),
+                                     (8192, "bf16"), (16384, "bf16"), (8, "f32"), (1024, "f32"),
+                                     (4096, "f32"), (8192, "f32")])
+def test_widths(D, dtype):
+    w = _wl(6, 67, D, max(1, D // 2) if D > 8 else D, dtype=dtype, seed=300 + D)
+    _check(w, W.generate(w), f"D={D} {dtype}")
+
+
+@pytest.mark.parametrize("N", [1, 7, 511, 513])
+def test_token_counts(N):
+    w = _wl(10, N, 4096, 4096, seed=400 + N)
+    _check(w, W.generate(w), f"N={N}")
+
+
+def test_zero_tokens_gives_zero_gradients():
+    import attention_residuals_amd as A
+    w = _wl(4, 0, 256, 256, out_norm=True, out_weight=True, norm_weight=True)
+    x = inputs_on(W.generate(w), "cuda")
+    y, lse, rstd, o32 = A.attnres_fwd(x["values"], x["query"], x["norm_w"], x["out_w"],
+                                      out_norm=True)
+    dv, dq, dw, dow = A.attnres_bwd(x["values"], x["query"], x["norm_w"], x["out_w"], lse, rstd,
+                                    o32, x["dout"], out_norm=True)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and dv.numel() == 0
+    for t in (dq, dw, dow):
+        assert torch.all(t == 0), t
+
+
+@pytest.mark.parametrize("S,D,out_weight,dtype", [(4, 512, False, "bf16"), (5, 1024, True, "bf16"),
+                                                  (3, 256, True, "f32"), (40, 2048, True, "bf16"),
+                                                  (29, 4096, False, "bf16")])
+def test_output_norm(S, D, out_weight, dtype):
+    w = _wl(S, 129, D, D // 2, dtype=dtype, out_norm=True, out_weight=out_weight,
+            norm_weight=not out_weight, seed=500 + S)
+    _check(w, W.generate(w), f"out_norm S={S} D={D} ow={out_weight} {dtype}")
+
+
+def test_streaming_path_without_output_norm():
+    # 29 sources at D=4096 do not fit the register slab: the backward streams with the FP32 mixture
+    import attention_residuals_amd as A
+    w = _wl(29, 97, 4096, 4096, seed=601)
+    d = A.make_desc(w.S, w.N, w.D, w.R, w.torch_dtype, has_norm_weight=True)
+    assert A.o32_elems(d) == w.N * w.D
+    _check(w, W.generate(w), "stream S=29")
+
+
+def test_packed_and_list_sources_are_bitwise_identical():
+    w = _wl(7, 301, 2048, 2048, seed=701)
+    xg = inputs_on(W.generate(w), "cuda")
+    a = run_gpu(w, xg, packed=True)
+    b = run_gpu(w, xg, packed=False)
+    for k in ("y", "lse", "dvalues", "dq", "dw"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_repeated_source_pointer():
+    # a list may name the same source twice (a shared source read at two positions)
+    w = _wl(5, 123, 1024, 1024, seed=801)
+    xc = W.generate(w)
+    xc["values"][3].copy_(xc["values"][1])
+    xg = inputs_on(xc, "cuda")
+    srcs = [xg["values"][0], xg["values"][1], xg["values"][2], xg["values"][1], xg["values"][4]]
+    dvals = [torch.empty_like(s) for s in srcs]
+    got = run_gpu(w, xg, values=srcs, dvalues=dvals)
+    ref = run_oracle(w, xc)
+    assert_ok(check_all(w, got, ref), "repeated source")
+
+
+def test_strided_rows():
+    # values, dY and dvalues with row strides larger than D (views into wider buffers)
+    w = _wl(6, 211, 1024, 512, seed=901)
+    xc = W.generate(w)
+    xg = inputs_on(xc, "cuda")
+    wide = torch.zeros((w.S, w.N, w.D + 64), dtype=w.torch_dtype, device="cuda")
+    wide[:, :, 32:32 + w.D].copy_(xg["values"])
+    vals = [wide[s, :, 32:32 + w.D] for s in range(w.S)]
+    gw = torch.zeros((w.N, w.D + 128), dtype=w.torch_dtype, device="cuda")
+    gw[:, 64:64 + w.D].copy_(xg["dout"])
+    dwide = torch.full((w.S, w.N, w.D + 32), float("nan"), dtype=w.torch_dtype, device="cuda")
+    dvals = [dwide[s, :, 16:16 + w.D] for s in range(w.S)]
+    got = run_gpu(w, xg, values=vals, dvalues=dvals, dout=gw[:, 64:64 + w.D])
+    ref = run_oracle(w, xc)
+    assert_ok(check_all(w, got, ref), "strided rows")
+    # the padding around the written rows is untouched
+    assert torch.isnan(dwide[:, :, :16]).all() and torch.isnan(dwide[:, :, 16 + w.D:]).all()
+
+
+def test_zero_query_gives_uniform_mean():
+    w = _wl(6, 64, 512, 512, seed=1001)
+    xc = W.generate(w)
+    xc["query"].zero_()
+    got = _check(w, xc, "q=0")
+    np.testing.assert_allclose(to_f64(got["lse"]), math.log(6), rtol=1e-6)
+
+
+def test_zero_rows_and_row_scales():
+    w = _wl(5, 96, 1024, 1024, seed=1101)
+    xc = W.generate(w)
+    v = xc["values"]
+    v[2, :10].zero_()        # zero rows of one source
+    v[:, 10:20].zero_()      # tokens whose every source is zero
+    scales = torch.logspace(-3, 3, 96 - 20).to(v.dtype)
+    v[:, 20:] *= scales.view(1, -1, 1)
+    _check(w, xc, "zero rows / row scales")
+
+
+def test_deterministic_mode_repeats_bitwise():
+    w = _wl(10, 2000, 4096, 4096, seed=1201)
+    xg = inputs_on(W.generate(w), "cuda")
+    a = run_gpu(w, xg, deterministic=True)
+    b = run_gpu(w, xg, deterministic=True)
+    for k in ("y", "lse", "dvalues", "dq", "dw"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_ticket_schedule_matches_deterministic_mode():
+    # per-token outputs do not depend on which workgroup ran the token; the token reductions only
+    # differ by FP32 reassociation (bf16 storage: at most a few bf16 ulps of dq/dw)
+    w = _wl(10, 3001, 4096, 4096, seed=1202)
+    xg = inputs_on(W.generate(w), "cuda")
+    det = run_gpu(w, xg, deterministic=True)
+    for _ in range(3):
+        dyn = run_gpu(w, xg, deterministic=False)
+        for k in ("y", "lse", "dvalues"):
+            assert torch.equal(det[k], dyn[k]), k
+        for k in ("dq", "dw"):
+            a, b = to_f64(det[k]), to_f64(dyn[k])
+            assert np.linalg.norm(a - b) <= 4e-3 * np.linalg.norm(a), k
+
+
+def test_autograd_wrapper_matches_oracle():
+    import attention_residuals_amd as A
+    w = _wl(4, 2 * 37, 1024, 256, seed=1301)
+    xc = W.generate(w)
+    x = inputs_on(xc, "cuda")
+    vals = x["values"].view(w.S, 2, 37, w.D).clone().requires_grad_(True)
+    q = x["query"].clone().requires_grad_(True)
+    nw = x["norm_w"].clone().requires_grad_(True)
+    y = A.attnres(vals, q, norm_weight=nw)
+    assert y.shape == (2, 37, w.D)
+    y.backward(x["dout"].view(2, 37, w.D))
+    ref = run_oracle(w, xc)
+    assert compare_rows(to_f64(y.detach().reshape(-1, w.D)), ref["y"], "bf16")["ok"]
+    assert compare_rows(to_f64(vals.grad.reshape(w.S, -1, w.D)), ref["dvalues"], "bf16")["ok"]
+    assert compare_vec(to_f64(q.grad), ref["dq"], "bf16")["ok"]
+    assert compare_vec(to_f64(nw.grad), ref["dw"], "bf16")["ok"]
+    # list form: gradients flow back to each source tensor
+    srcs = [x["values"][s].clone().requires_grad_(True) for s in range(w.S)]
+    y2 = A.attnres(srcs, x["query"], norm_weight=x["norm_w"])
+    y2.backward(x["dout"])
+    assert torch.equal(y2.detach(), y.detach().reshape(-1, w.D))
+    for s in range(w.S):
+        assert torch.equal(srcs[s].grad, vals.grad[s].reshape(-1, w.D))
+
+
+@pytest.mark.parametrize("deterministic", [True, False])
+def test_graph_capture_and_replay_with_changed_inputs(deterministic):
+    import attention_residuals_amd as A
+    w = _wl(10, 1024, 4096, 4096, seed=1401)
+    x1 = inputs_on(W.generate(w), "cuda")
+    x2 = inputs_on(W.generate(w.with_(seed=1402)), "cuda")
+    buf = {k: (None if v is None else v.clone()) for k, v in x1.items()}
+    d = A.make_desc(w.S, w.N, w.D, w.R, w.torch_dtype, has_norm_weight=True,
+                    deterministic=deterministic)
+    y = torch.empty((w.N, w.D), dtype=w.torch_dtype, device="cuda")
+    lse = torch.empty((w.N,), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(buf["values"])
+    dq = torch.empty((w.R,), dtype=w.torch_dtype, device="cuda")
+    dw = torch.empty_like(dq)
+    ws = torch.empty((A.workspace_bytes(d),), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+
+    def step():
+        A.attnres_fwd(buf["values"], buf["query"], buf["norm_w"], None, out=y, lse=lse, stream=s)
+        A.attnres_bwd(buf["values"], buf["query"], buf["norm_w"], None, lse, None, None,
+                      buf["dout"], deterministic=deterministic, dvalues=dv, dq=dq, dw=dw,
+                      workspace=ws, stream=s)
+
+    with torch.cuda.stream(s):
+        step()  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for xin in (x1, x2, x1, x2):
+        for k in buf:
+            if buf[k] is not None:
+                buf[k].copy_(xin[k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = run_gpu(w, xin, deterministic=deterministic)
+        assert torch.equal(y, eager["y"]) and torch.equal(lse, eager["lse"])
+        assert torch.equal(dv, eager["dvalues"])
+        if deterministic:
+            assert torch.equal(dq, eager["dq"]) and torch.equal(dw, eager["dw"])
+        else:
+            for got, ref in ((dq, eager["dq"]), (dw, eager["dw"])):
+                a, b = to_f64(got), to_f64(ref)
+                assert np.linalg.norm(a - b) <= 4e-3 * np.linalg.norm(b)
+
+
+def test_workspace_too_small_is_an_error_and_launches_nothing():
+    import attention_residuals_amd as A
+    w = _wl(4, 300, 512, 512, seed=1501)
+    x = inputs_on(W.generate(w), "cuda")
+    y, lse, _, _ = A.attnres_fwd(x["values"], x["query"], x["norm_w"], None)
+    d = A.make_desc(w.S, w.N, w.D, w.R, w.torch_dtype, has_norm_weight=True)
+    need = A.workspace_bytes(d)
+    small = torch.empty((need - 256,), dtype=torch.uint8, device="cuda")
+    dv = torch.full_like(x["values"], 7.0)
+    with pytest.raises(A.AttnResError) as e:
+        A.attnres_bwd(x["values"], x["query"], x["norm_w"], None, lse, None, None, x["dout"],
+                      dvalues=dv, workspace=small)
+    assert e.value.status == 4
+    torch.cuda.synchronize()
+    assert torch.all(dv == 7.0)  # nothing was written

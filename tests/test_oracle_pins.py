@@ -328,3 +328,28 @@ def test_thread_count_does_not_change_results_beyond_rounding():
     np.testing.assert_array_equal(a["y"], b["y"])
     np.testing.assert_array_equal(a["dvalues"], b["dvalues"])
     np.testing.assert_allclose(a["dq"], b["dq"], rtol=1e-13)
+
+
+# ---------------------------------------------------------------- tolerance reading
+
+def test_bf16_tolerance_reading_is_well_posed():
+    # The stated bf16 bound (2e-2 * rms) taken literally rejects the correctly rounded answer;
+    # the reading used by the GPU parity tests (error beyond half a bf16 ulp) accepts it and still
+    # rejects an error of the size the bound is meant to catch.
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from parity import compare_rows
+    import attnres_workloads as W
+    w = W.small(W.WORKLOADS["bf16_s10_n32768_d4096"], 96)
+    x = W.generate(w)
+    r = oracle.run(x["values"], x["query"], x["norm_w"], None, x["dout"])
+    for key in ("y", "dvalues"):
+        exact = r[key]
+        rounded = torch.from_numpy(exact).to(torch.bfloat16).double().numpy()
+        res = compare_rows(rounded, exact, "bf16")
+        assert res["ok"] and res["metric"] < 1e-6, (key, res)
+        if key == "dvalues":
+            assert res["literal"] > 2e-2, res  # the literal reading would fail here
+        bad = rounded.copy()
+        bad.flat[7] += 0.05 * np.sqrt(np.mean(exact ** 2))
+        assert not compare_rows(bad, exact, "bf16")["ok"], key
