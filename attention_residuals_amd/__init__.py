@@ -5,10 +5,11 @@ The compute lives in ``libattnres.so`` (hand-written HIP kernels behind the C AB
 ``python -m attention_residuals_amd.build``. Nothing here falls back to a CPU implementation.
 """
 from ._binding import (ATTNRES_BF16, ATTNRES_F32, EPS_DEFAULT, EXPORTS, AttnResError, Desc,
-                       Sources, attnres_bwd, attnres_fwd, load, make_desc, o32_elems,
-                       workspace_bytes)
+                       Sources, attnres_bwd, attnres_fwd, fwd_workspace_bytes, load, make_desc,
+                       o32_elems, workspace_bytes)
 from .autograd import attnres
 
-__all__ = ["attnres", "attnres_fwd", "attnres_bwd", "o32_elems", "workspace_bytes", "make_desc",
+__all__ = ["attnres", "attnres_fwd", "attnres_bwd", "o32_elems", "workspace_bytes",
+           "fwd_workspace_bytes", "make_desc",
            "load", "Desc", "Sources", "AttnResError", "EXPORTS", "ATTNRES_BF16", "ATTNRES_F32",
            "EPS_DEFAULT"]

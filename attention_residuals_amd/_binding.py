@@ -19,8 +19,8 @@ ATTNRES_F32, ATTNRES_BF16 = 0, 1
 EPS_DEFAULT = 2.0 ** -23
 
 # Every function the header declares, with its ctypes signature.
-EXPORTS = ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd", "attnres_bwd",
-           "attnres_status_str", "attnres_last_error")
+EXPORTS = ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd_workspace_bytes",
+           "attnres_fwd", "attnres_bwd", "attnres_status_str", "attnres_last_error")
 
 
 class Desc(ctypes.Structure):
@@ -60,9 +60,11 @@ def load() -> ctypes.CDLL:
     pd, ps = ctypes.POINTER(Desc), ctypes.POINTER(Sources)
     lib.attnres_o32_elems.argtypes = [pd, ctypes.POINTER(sz)]
     lib.attnres_workspace_bytes.argtypes = [pd, ctypes.POINTER(sz)]
-    lib.attnres_fwd.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attnres_fwd_workspace_bytes.argtypes = [pd, ctypes.POINTER(sz)]
+    lib.attnres_fwd.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attnres_bwd.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, i64, ps, vp, vp, vp, vp, sz, vp]
-    for f in ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd", "attnres_bwd"):
+    for f in ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd_workspace_bytes",
+              "attnres_fwd", "attnres_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     lib.attnres_status_str.argtypes = [ctypes.c_int]
     lib.attnres_status_str.restype = ctypes.c_char_p
@@ -146,6 +148,12 @@ def workspace_bytes(desc: Desc) -> int:
     return int(n.value)
 
 
+def fwd_workspace_bytes(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().attnres_fwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -159,10 +167,11 @@ def attnres_fwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor] = No
                 scale: float = 1.0, out_norm: bool = False,
                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                 out_rstd: Optional[torch.Tensor] = None, o32: Optional[torch.Tensor] = None,
-                stream=None):
+                workspace: Optional[torch.Tensor] = None, dynamic: bool = True, stream=None):
     """Forward read. values: packed [S, N, D] or a list of [N, D] device tensors.
     Returns (out [N, D], lse [N] f32, out_rstd [N] f32 or None, o32 [N, D] f32 or None);
-    output buffers are allocated with torch when not given."""
+    output buffers are allocated with torch when not given. dynamic: hand tokens out through a
+    counter in `workspace` (allocated when not given); False: static token split, no workspace."""
     sv = _SourceView(values)
     desc = make_desc(sv.S, sv.N, sv.D, query.numel(), sv.dtype, eps=eps, scale=scale,
                      has_norm_weight=norm_w is not None, out_norm=out_norm,
@@ -176,9 +185,14 @@ def attnres_fwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor] = No
         out_rstd = torch.empty((sv.N,), dtype=torch.float32, device=dev)
     if o32 is None and o32_elems(desc) > 0:
         o32 = torch.empty((sv.N, sv.D), dtype=torch.float32, device=dev)
+    if not dynamic:
+        workspace = None
+    elif workspace is None:
+        workspace = torch.empty((fwd_workspace_bytes(desc),), dtype=torch.uint8, device=dev)
     _check(load().attnres_fwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query),
                               _ptr(norm_w), _ptr(out_w), _ptr(out), _ptr(lse), _ptr(out_rstd),
-                              _ptr(o32), _stream(stream)))
+                              _ptr(o32), _ptr(workspace),
+                              0 if workspace is None else workspace.numel(), _stream(stream)))
     return out, lse, out_rstd, o32
 
 

@@ -24,6 +24,8 @@ struct FwdArgs {
   float* lse;                    // [N]
   float* o_rstd;                 // [N] or nullptr
   float* o32;                    // [N, D] or nullptr
+  uint32_t* ticket;              // dynamic token counter, zero at launch (nullptr: static split)
+  int64_t tpt;                   // tokens per ticket (batch size of the dynamic schedule)
   int out_norm;
 };
 
@@ -44,6 +46,7 @@ struct BwdArgs {
   float* part_du;                // [gridDim.x, R]
   float* part_dow;               // [gridDim.x, D] or nullptr
   uint32_t* ticket;              // dynamic token counter, zero at launch (nullptr: static split)
+  int64_t tpt;                   // tokens per ticket (batch size of the dynamic schedule)
   int out_norm;
 };
 

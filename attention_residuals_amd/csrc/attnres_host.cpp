@@ -16,6 +16,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -173,7 +174,7 @@ size_t param_lds(const Shape& sh) {
   return slots * sh.threads * 16u;
 }
 size_t fwd_lds(const Shape& sh) {
-  return param_lds(sh) + 2u * (2u * sh.sb_fwd) * (4u * sh.W) * sizeof(float);
+  return param_lds(sh) + 2u * (2u * sh.sb_fwd) * (4u * sh.W) * sizeof(float) + 4 * sizeof(float);
 }
 size_t bwd_lds(const Shape& sh) {
   return param_lds(sh) + 2u * (3u * sh.sb_bwd) * (4u * sh.W) * sizeof(float) + 4 * sizeof(float);
@@ -217,6 +218,24 @@ attnres_status blocks_per_cu(const void* fn, int threads, size_t lds, int* out, 
   if (nb <= 0) return fail(ATTNRES_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)");
   *out = nb;
   return ATTNRES_OK;
+}
+
+// Tokens per ticket of the dynamic schedules (see the kernels). Two effects, measured on MI355X:
+//  - the device-wide counter serves its atomics one at a time; near ~70 tickets/us the queue
+//    stalls every workgroup, so a batch must keep the ticket rate below `max_rate` tickets per
+//    microsecond (the token rate is estimated at 5.6 TB/s over the kernel's bytes per token);
+//  - workgroups finish up to one batch apart, so the backward (16 tokens per workgroup at
+//    N = 8192) also keeps at least `min_batches` batches per workgroup.
+// The forward waits for its ticket behind one output row, the backward behind S gradient rows, so
+// the backward's ticket costs more and its rate bound is lower.
+int64_t tokens_per_ticket(int64_t N, int64_t grid, double bytes_per_token, double max_rate,
+                          int64_t min_batches) {
+  static const int forced = env_int("ATTNRES_TOKENS_PER_TICKET");
+  if (forced > 0) return forced;
+  const double rate = 5.6e6 / bytes_per_token;  // tokens per microsecond at 5.6 TB/s
+  int64_t b = std::max<int64_t>(1, (int64_t)std::ceil(rate / max_rate));
+  if (min_batches > 0) b = std::min(b, std::max<int64_t>(1, N / (grid * min_batches)));
+  return b;
 }
 
 // ------------------------------------------------------------------ backward plan
@@ -366,13 +385,30 @@ attnres_status attnres_workspace_bytes(const attnres_desc* d, size_t* bytes) {
   return ATTNRES_OK;
 }
 
+attnres_status attnres_fwd_workspace_bytes(const attnres_desc* d, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(ATTNRES_ERR_INVALID_ARG, "bytes is NULL");
+  Shape sh;
+  attnres_status st = make_shape(d, &sh);
+  if (st != ATTNRES_OK) return st;
+  *bytes = kFwdWorkspaceBytes;
+  return ATTNRES_OK;
+}
+
 attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
                            const void* query, const void* norm_w, const void* out_w, void* out,
-                           float* lse, float* out_rstd, float* o32, void* stream) {
+                           float* lse, float* out_rstd, float* o32, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   g_err.clear();
   Shape sh;
   attnres_status st = make_shape(d, &sh);
   if (st != ATTNRES_OK) return st;
+  if (workspace && (workspace_bytes < kFwdWorkspaceBytes || !aligned(workspace, 256)))
+    return fail(ATTNRES_ERR_WORKSPACE, "forward workspace: %zu bytes given, %zu (256-byte aligned) "
+                "needed", workspace_bytes, kFwdWorkspaceBytes);
+  if (!workspace && workspace_bytes)
+    return fail(ATTNRES_ERR_WORKSPACE, "forward workspace is NULL but workspace_bytes = %zu",
+                workspace_bytes);
   if ((st = check_param(query, true, sh.esz, "query")) != ATTNRES_OK) return st;
   if ((st = check_param(norm_w, d->has_norm_weight, sh.esz, "norm_w")) != ATTNRES_OK) return st;
   if ((st = check_param(out_w, d->has_out_weight, sh.esz, "out_w")) != ATTNRES_OK) return st;
@@ -404,13 +440,25 @@ attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
   DevFacts f;
   if ((st = device_facts(&f)) != ATTNRES_OK) return st;
   int per_cu = 0;
-  if ((st = blocks_per_cu(fn, sh.threads, fwd_lds(sh), &per_cu, sh.fwd_one ? 8 : 0)) != ATTNRES_OK)
+  static const int env_waves = env_int("ATTNRES_FWD_WAVES_PER_CU");
+  const int wave_cap = sh.fwd_one ? (env_waves > 0 ? env_waves : 8) : 0;
+  if ((st = blocks_per_cu(fn, sh.threads, fwd_lds(sh), &per_cu, wave_cap)) != ATTNRES_OK)
     return st;
-  // the forward has no per-workgroup state: 8x the resident grid lets the hardware dispatcher
-  // balance workgroups over CUs (measured better than a one-pass persistent grid)
+  // With the token counter (single-block path and a workspace) the grid is one resident pass and
+  // workgroups take tokens as they finish. Without it, 8x the resident grid lets the hardware
+  // dispatcher balance workgroups over CUs (measured better than a one-pass static grid).
+  const bool dyn = workspace != nullptr && sh.fwd_one && N < kMaxTicketTokens;
   static const int env_mult = env_int("ATTNRES_FWD_GRID_MULT");
-  const int mult = env_mult > 0 ? env_mult : 8;
-  const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu * mult);
+  const int mult = env_mult > 0 ? env_mult : (dyn ? 1 : 8);
+  const int64_t slots = (int64_t)f.cus * per_cu * mult;
+  a.tpt = dyn ? tokens_per_ticket(N, slots, (double)(d->S + 1) * d->D * sh.esz, 55.0, 0) : 1;
+  const int grid = (int)std::min<int64_t>((N + a.tpt - 1) / a.tpt, slots);
+  if (dyn) {
+    a.ticket = static_cast<uint32_t*>(workspace);
+    void* targ = a.ticket;
+    st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");
+    if (st != ATTNRES_OK) return st;
+  }
 
   a.row_stride = values->row_stride;
   a.N = N;
@@ -519,7 +567,9 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
     a.part_du = reinterpret_cast<float*>(ws + pl.off_du);
     a.part_dow = d->has_out_weight ? reinterpret_cast<float*>(ws + pl.off_dow) : nullptr;
     a.out_norm = d->out_norm ? 1 : 0;
-    if (sh.resident && !d->deterministic) {
+    a.tpt = 1;
+    if (sh.resident && !d->deterministic && N < kMaxTicketTokens) {
+      a.tpt = tokens_per_ticket(N, pl.P, (double)(2 * d->S + 1) * d->D * sh.esz, 30.0, 16);
       a.ticket = reinterpret_cast<uint32_t*>(ws + pl.off_ticket);
       void* targ = a.ticket;
       st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");

@@ -1,6 +1,9 @@
 // attnres_internal.hpp -- host-side tables shared by the dispatcher and the instantiation files.
 #pragma once
 
+#include <stddef.h>
+#include <stdint.h>
+
 namespace attnres {
 
 // Source-block sizes instantiated per chunks-per-thread CH. A token's rows are kept on chip when
@@ -22,6 +25,13 @@ inline constexpr int kSbStream[] = {1, 2, 4, 8};
 
 // Largest workgroup any kernel is launched with (matches the kernels' launch bounds).
 inline constexpr int kMaxThreads = 512;
+
+// Forward workspace: one token counter, padded to the 256-byte alignment the ABI asks for.
+inline constexpr size_t kFwdWorkspaceBytes = 256;
+
+// Token counters are 32-bit and a call takes at most N + 2 * grid tickets from them: larger
+// token counts use the static split.
+inline constexpr int64_t kMaxTicketTokens = int64_t(1) << 31;
 
 
 // Kernel entry points by configuration; nullptr when that configuration is not built.

@@ -584,11 +584,21 @@ void fwd_kernel(const FwdArgs a) {
   // per-source branches and the wait counts stay exact across the token loop.
   Chunk rows[SB][CH];
 
+  // Token schedule (single-block path with a counter): tokens go out in batches of B = a.tpt
+  // consecutive tokens. Workgroup g starts with batch g; each later batch is grid + a ticket from
+  // the device-wide counter, so workgroups that run faster take more batches and all finish
+  // together (B > 1 divides the counter's traffic, which is served one atomic at a time). Thread
+  // 0 takes the ticket at the top of a batch's last token and publishes it through LDS at the
+  // barrier that ends that token's exchange. Otherwise tokens are strided by the grid.
+  const bool dyn = ONE && a.ticket != nullptr;
+  const int64_t B = dyn ? a.tpt : 1;
+  const int64_t n0 = (int64_t)blockIdx.x * B;
+
   if constexpr (ONE) {
     // issued in the loop body's order (rows 0..SB-1) so the wait counts at the loop head stay
     // tight over both entry paths
-    const int live = (int64_t)blockIdx.x < a.N ? a.S : 0;
-    const int64_t row_byte = (int64_t)blockIdx.x * a.row_stride * ESZ;
+    const int live = n0 < a.N ? a.S : 0;
+    const int64_t row_byte = n0 * a.row_stride * ESZ;
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
       const Rsrc r = src_rsrc(a.src[i], i, live, row_byte, row_bytes);
@@ -596,12 +606,23 @@ void fwd_kernel(const FwdArgs a) {
       for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // as many dropped stores (empty resource) as the output row the loop body stores after its
+    // last row load: the wait for the last row at the loop head then lets the previous token's
+    // output stores stay in flight (the wait is the minimum over both entry paths)
+    const Rsrc none = row_rsrc(nullptr, 0, 0u);
+    const Chunk zero = {};
+#pragma unroll
+    for (int j = 0; j < CH; ++j) st_row(none, cs.voff[j], zero);
   }
 
-  for (int64_t n = blockIdx.x; n < a.N; n += gridDim.x) {
+  uint32_t* tslot = reinterpret_cast<uint32_t*>(lds + 2 * xfl);
+  int64_t n = n0, batch_end = n0 + B;
+  while (n < a.N) {
     const int64_t row_byte = n * a.row_stride * ESZ;
-    const int64_t next = n + gridDim.x;
-    const int64_t next_byte = next * a.row_stride * ESZ;
+    const bool take = dyn && n + 1 >= batch_end;  // last token of its batch
+    uint32_t tk = 0;
+    if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
+    int64_t next = dyn ? n + 1 : n + gridDim.x;
     float acc[CH][VEC];
 #pragma unroll
     for (int j = 0; j < CH; ++j)
@@ -635,7 +656,12 @@ void fwd_kernel(const FwdArgs a) {
         }
         xchg_group<2, SB>(part, i0, xb, R4, tid);
       }
+      if (take && tid == 0) tslot[buf] = tk;
       __syncthreads();
+      if (take) {
+        next = ((int64_t)gridDim.x + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf])) * B;
+        batch_end = next + B;
+      }
       buf ^= 1;
       float z = -INFINITY;
       if (lane < nb) {
@@ -673,7 +699,8 @@ void fwd_kernel(const FwdArgs a) {
           for (int e = 0; e < VEC; ++e) acc[j][e] = fmaf(pi, elem<BF16>(rows[i][j], e), acc[j][e]);
         if constexpr (ONE) {
           // the next token's row i (an empty resource past the last token)
-          const Rsrc r = src_rsrc(a.src[i], i, next < a.N ? a.S : 0, next_byte, row_bytes);
+          const Rsrc r = src_rsrc(a.src[i], i, next < a.N ? a.S : 0, next * a.row_stride * ESZ,
+                                  row_bytes);
 #pragma unroll
           for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
         }
@@ -687,6 +714,7 @@ void fwd_kernel(const FwdArgs a) {
         for (int e = 0; e < VEC; ++e) acc[j][e] *= inv_l;  // acc now holds o
     }
     fwd_emit<BF16, CH, FULL>(a, cs, acc, ow, n, m + logf(l), lds, buf, xfl, R4, tid, row_bytes);
+    n = next;
   }
 }
 
@@ -754,13 +782,22 @@ void bwd_resident_kernel(const BwdArgs a) {
   // and get routing weight 0, so there are no per-source branches and the wait counts stay exact.
   Chunk rows[SB][CH];
   Chunk gy[CH];
+  // Token schedule: tokens go out in batches of B = a.tpt consecutive tokens. Workgroup g starts
+  // with batch g; each later batch is grid + a ticket from the device-wide counter, so workgroups
+  // that run faster take more batches and all finish together (B > 1 divides the counter's
+  // traffic, which is served one atomic at a time). Thread 0 takes the ticket at the top of a
+  // batch's last token; its latency hides behind pass 1, and it is published through LDS at the
+  // barrier pass 1 ends with. Without a counter (deterministic mode) tokens are strided by the
+  // grid, so each workgroup's partial sums cover a fixed token set.
+  const bool dyn = a.ticket != nullptr;
+  const int64_t B = dyn ? a.tpt : 1;
+  const int64_t n0 = (int64_t)blockIdx.x * B;
   // lse of the current token; the next one is loaded with the next token's rows (a vector load
   // waited for at its use would otherwise also drain every store issued before it)
-  float lse = a.lse[min((int64_t)blockIdx.x, a.N - 1)];
+  float lse = a.lse[min(n0, a.N - 1)];
   {
     // issued in the order the loop body issues the next token's loads (dY, then rows 0..SB-1):
     // the wait counts at the loop head are the minimum over both entry paths
-    const int64_t n0 = blockIdx.x;
     const int live = n0 < a.N ? S : 0;
     const Rsrc rg = src_rsrc(a.dout, 0, live, n0 * a.dout_stride * ESZ, row_bytes);
 #pragma unroll
@@ -775,15 +812,12 @@ void bwd_resident_kernel(const BwdArgs a) {
     }
   }
 
-  // Token schedule: the first token of workgroup g is g; later ones come from a device-wide
-  // ticket counter (token = grid + ticket), so workgroups that run faster take more tokens and
-  // all finish together. Thread 0 takes the ticket at the top of the loop; its latency hides
-  // behind pass 1, and it is published through LDS at the barrier pass 1 ends with.
   uint32_t* tslot = reinterpret_cast<uint32_t*>(lds + 2 * xfl);
-  int64_t n = blockIdx.x;
+  int64_t n = n0, batch_end = n0 + B;
   while (n < a.N) {
+    const bool take = dyn && n + 1 >= batch_end;  // last token of its batch
     uint32_t tk = 0;
-    if (a.ticket && tid == 0) tk = atomicAdd(a.ticket, 1u);
+    if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
     float* xb = lds + buf * xfl;
     uint32_t us[3][CH][4];
     float u[CH][VEC];
@@ -802,11 +836,13 @@ void bwd_resident_kernel(const BwdArgs a) {
       }
       xchg_group<3, SB>(part, i0, xb, R4, tid);
     }
-    if (tid == 0) tslot[buf] = tk;
+    if (take && tid == 0) tslot[buf] = tk;
     __syncthreads();
-    const int64_t next =
-        a.ticket ? (int64_t)gridDim.x + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf])
-                 : n + gridDim.x;
+    int64_t next = dyn ? n + 1 : n + gridDim.x;
+    if (take) {
+      next = ((int64_t)gridDim.x + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf])) * B;
+      batch_end = next + B;
+    }
     const bool has_next = next < a.N;
     buf ^= 1;
 

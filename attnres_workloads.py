@@ -84,6 +84,19 @@ WORKLOADS = {
         norm_weight=False, out_norm=False, out_weight=False, seed=1005, query_over_rank=True),
 }
 
+# The FLA PR page's two other benchmark rows at D = 2048 / 4096 (same recipe): measured by the
+# benchmark for context and covered by the full-size parity tests.
+BENCH_ROWS = {
+    "bf16_s10_n8192_d4096": Workload(
+        "bf16_s10_n8192_d4096", S=10, N=8192, D=4096, R=4096, dtype="bf16",
+        norm_weight=True, out_norm=False, out_weight=False, seed=1006),
+    "bf16_s8_n32768_d2048": Workload(
+        "bf16_s8_n32768_d2048", S=8, N=32768, D=2048, R=2048, dtype="bf16",
+        norm_weight=True, out_norm=False, out_weight=False, seed=1007),
+}
+
+ALL = {**WORKLOADS, **BENCH_ROWS}
+
 HEADLINE = "bf16_s10_n32768_d4096"
 TINY = "tiny_f32_s4_n256_d256"
 

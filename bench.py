@@ -31,7 +31,9 @@ PEAK_HBM_GBPS = 8000.0
 # T=32768, D=4096 bf16, candidate column): another machine's number, quoted as context.
 B200_MS = {"bf16_s10_n32768_d4096": 3.268607974052429,
            "bf16_s8_n8192_d2048": 0.4638400077819824,
-           "bf16_s64_n8192_d8192_outnorm": 11.95311975479126}
+           "bf16_s64_n8192_d8192_outnorm": 11.95311975479126,
+           "bf16_s10_n8192_d4096": 0.9022,
+           "bf16_s8_n32768_d2048": 1.2953}
 METRIC = "AttnRes fwd+bwd ms and HBM GB/s (% peak), S=10,N=32768,D=4096 bf16, 1 GPU"
 
 
@@ -94,7 +96,7 @@ def main() -> int:
     import attention_residuals_amd as A
     import attnres_workloads as W
 
-    w = W.WORKLOADS[args.workload]
+    w = W.ALL[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
     x = W.generate(w, device=dev)
@@ -111,12 +113,13 @@ def main() -> int:
     dw = torch.empty((R,), dtype=w.torch_dtype, device=dev) if x["norm_w"] is not None else None
     dow = torch.empty((D,), dtype=w.torch_dtype, device=dev) if x["out_w"] is not None else None
     ws = torch.empty((max(A.workspace_bytes(desc), 256),), dtype=torch.uint8, device=dev)
+    fws = torch.empty((A.fwd_workspace_bytes(desc),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def fwd():
         A.attnres_fwd(x["values"], x["query"], x["norm_w"], x["out_w"], eps=w.eps,
                       scale=w.scale, out_norm=w.out_norm, out=y, lse=lse, out_rstd=rstd,
-                      o32=o32, stream=stream)
+                      o32=o32, workspace=fws, stream=stream)
 
     def bwd():
         A.attnres_bwd(x["values"], x["query"], x["norm_w"], x["out_w"], lse, rstd, o32,

@@ -93,6 +93,9 @@ attnres_status attnres_o32_elems(const attnres_desc* desc, size_t* elems);
  * no initialisation. */
 attnres_status attnres_workspace_bytes(const attnres_desc* desc, size_t* bytes);
 
+/* Bytes of the optional forward workspace (a device-wide token counter); currently 256. */
+attnres_status attnres_fwd_workspace_bytes(const attnres_desc* desc, size_t* bytes);
+
 /* Forward.
  *   values   [S][N, D] sources (read).
  *   query    [R]; norm_w [R] iff has_norm_weight; out_w [D] iff has_out_weight.
@@ -100,11 +103,16 @@ attnres_status attnres_workspace_bytes(const attnres_desc* desc, size_t* bytes);
  *   lse      [N] FP32 log-sum-exp of the scores (written; the backward's saved statistic).
  *   out_rstd [N] FP32 rho_o (written iff out_norm, else must be NULL).
  *   o32      [N, D] FP32 mixture o (written iff attnres_o32_elems > 0, else must be NULL).
+ *   workspace, workspace_bytes: optional. With a 256-byte aligned buffer of at least
+ *            attnres_fwd_workspace_bytes bytes (contents need no initialisation; not shared with a
+ *            concurrent call), workgroups take tokens from a counter kept there as they finish
+ *            (a one-thread kernel zeroes it first). NULL with 0 bytes: a static token split. The
+ *            outputs are bitwise identical either way.
  * All device pointers 16-byte aligned; row strides multiples of 16 bytes. */
 attnres_status attnres_fwd(const attnres_desc* desc, const attnres_sources* values,
                            const void* query, const void* norm_w, const void* out_w,
                            void* out, float* lse, float* out_rstd, float* o32,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward, given the forward's inputs and saved statistics.
  *   dout            [N, D] upstream gradient dL/dy with row stride dout_row_stride (read).

@@ -69,6 +69,13 @@ def test_descriptor_validation(kw, expect):
         assert A.load().attnres_last_error()
 
 
+def test_forward_workspace_size():
+    n = ctypes.c_size_t(0)
+    assert A.load().attnres_fwd_workspace_bytes(ctypes.byref(_desc()), ctypes.byref(n)) == OK
+    assert n.value == 256
+    assert A.load().attnres_fwd_workspace_bytes(ctypes.byref(_desc(S=0)), ctypes.byref(n)) == INVALID
+
+
 def test_o32_needed_only_when_backward_streams():
     assert _o32(_desc(S=10, N=32768, D=4096, R=4096)) == (OK, 0)
     assert _o32(_desc(S=24, N=16384, D=2048, R=512)) == (OK, 0)
@@ -82,10 +89,10 @@ def _fake(addr):
 
 
 def _call_fwd(desc, src, query=0x10000, norm_w=None, out_w=None, out=0x20000, lse=0x30000,
-              rstd=None, o32=None):
+              rstd=None, o32=None, ws=None, ws_bytes=0):
     lib = A.load()
     return lib.attnres_fwd(ctypes.byref(desc), ctypes.byref(src) if src is not None else None,
-                           query, norm_w, out_w, out, lse, rstd, o32, None)
+                           query, norm_w, out_w, out, lse, rstd, o32, ws, ws_bytes, None)
 
 
 def _packed(base=0x100000, src_stride=16 * 256, row_stride=256):
@@ -98,6 +105,8 @@ def _packed(base=0x100000, src_stride=16 * 256, row_stride=256):
     ("misaligned_base", ALIGN), ("odd_row_stride", ALIGN), ("null_query", INVALID),
     ("unwanted_norm_w", INVALID), ("missing_rstd", INVALID), ("null_out", INVALID),
     ("misaligned_out", ALIGN), ("out_overlaps_values", INVALID), ("unwanted_o32", INVALID),
+    ("workspace_too_small", WORKSPACE), ("workspace_misaligned", WORKSPACE),
+    ("workspace_bytes_without_pointer", WORKSPACE),
 ])
 def test_forward_argument_checks(case, expect):
     desc = _desc()
@@ -130,6 +139,12 @@ def test_forward_argument_checks(case, expect):
         kw["out"] = 0x100000 + 64 * 2
     elif case == "unwanted_o32":
         kw["o32"] = 0x900000
+    elif case == "workspace_too_small":
+        kw.update(ws=0xA00000, ws_bytes=128)
+    elif case == "workspace_misaligned":
+        kw.update(ws=0xA00010, ws_bytes=256)
+    elif case == "workspace_bytes_without_pointer":
+        kw.update(ws=None, ws_bytes=256)
     kw.pop("_keep", None)
     st = _call_fwd(desc, src, **kw)
     assert st == expect, (case, st, A.load().attnres_last_error())

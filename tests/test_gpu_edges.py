@@ -176,6 +176,45 @@ def test_ticket_schedule_matches_deterministic_mode():
             assert np.linalg.norm(a - b) <= 4e-3 * np.linalg.norm(a), k
 
 
+@pytest.mark.parametrize("S,N,D", [(8, 32768 + 5, 2048), (10, 32768 + 3, 4096)])
+def test_batched_ticket_schedules_match_static_split(S, N, D):
+    # long token counts where both dynamic schedules hand out batches of 2-3 tokens per ticket
+    # (ragged: N is not a multiple of the batch): every token's outputs must equal the static
+    # split's bit for bit, and the token reductions agree to FP32 reassociation
+    import attention_residuals_amd as A
+    w = _wl(S, N, D, D, seed=1260 + S)
+    xg = inputs_on(W.generate(w, device="cuda"), "cuda")
+    det = run_gpu(w, xg, deterministic=True, poison=False)
+    y_static, lse_static, _, _ = A.attnres_fwd(xg["values"], xg["query"], xg["norm_w"], None,
+                                               dynamic=False)
+    dyn = run_gpu(w, xg, deterministic=False, poison=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y_static, dyn["y"]) and torch.equal(lse_static, dyn["lse"])
+    assert torch.equal(det["y"], dyn["y"]) and torch.equal(det["dvalues"], dyn["dvalues"])
+    for k in ("dq", "dw"):
+        a, b = to_f64(det[k]), to_f64(dyn[k])
+        assert np.linalg.norm(a - b) <= 4e-3 * np.linalg.norm(a), k
+    del xg, det, dyn
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("S,N,D,out_norm", [(10, 3001, 4096, False), (4, 1000, 512, True),
+                                             (29, 301, 1024, False), (3, 5, 256, False)])
+def test_forward_counter_and_static_split_are_bitwise_identical(S, N, D, out_norm):
+    import attention_residuals_amd as A
+    w = _wl(S, N, D, D, out_norm=out_norm, seed=1250 + S)
+    x = inputs_on(W.generate(w), "cuda")
+    outs = []
+    for dyn in (False, True, True):
+        y, lse, rstd, o32 = A.attnres_fwd(x["values"], x["query"], x["norm_w"], None,
+                                          out_norm=out_norm, dynamic=dyn)
+        outs.append((y, lse, rstd, o32))
+    torch.cuda.synchronize()
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert (a is None and b is None) or torch.equal(a, b)
+
+
 def test_autograd_wrapper_matches_oracle():
     import attention_residuals_amd as A
     w = _wl(4, 2 * 37, 1024, 256, seed=1301)
@@ -216,10 +255,14 @@ def test_graph_capture_and_replay_with_changed_inputs(deterministic):
     dq = torch.empty((w.R,), dtype=w.torch_dtype, device="cuda")
     dw = torch.empty_like(dq)
     ws = torch.empty((A.workspace_bytes(d),), dtype=torch.uint8, device="cuda")
+    fws = torch.empty((A.fwd_workspace_bytes(d),), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
 
     def step():
-        A.attnres_fwd(buf["values"], buf["query"], buf["norm_w"], None, out=y, lse=lse, stream=s)
+        # deterministic: static forward schedule too; else the forward's token counter
+        A.attnres_fwd(buf["values"], buf["query"], buf["norm_w"], None, out=y, lse=lse,
+                      workspace=None if deterministic else fws, dynamic=not deterministic,
+                      stream=s)
         A.attnres_bwd(buf["values"], buf["query"], buf["norm_w"], None, lse, None, None,
                       buf["dout"], deterministic=deterministic, dvalues=dv, dq=dq, dw=dw,
                       workspace=ws, stream=s)

@@ -1,4 +1,5 @@
-"""GPU parity of the five workloads against the FP64 oracle, through the C ABI.
+"""GPU parity of the five workloads (and, at full size, the benchmark table's two other rows)
+against the FP64 oracle, through the C ABI.
 
 Reduced token counts: every output of every token is compared element by element (token counts
 are not multiples of the persistent grid, so workgroups end on a ragged tail). Full sizes, in
@@ -34,9 +35,9 @@ def test_workload_reduced_n(name):
     assert_ok(check_all(w, got, ref), f"{name} N={w.N}")
 
 
-@pytest.mark.parametrize("name", list(W.WORKLOADS))
+@pytest.mark.parametrize("name", list(W.ALL))
 def test_workload_full_size(name):
-    w = W.WORKLOADS[name]
+    w = W.ALL[name]
     print(f"[case] full {name}", flush=True)
     xg = W.generate(w, device="cuda")
     got = run_gpu(w, xg, poison=False)
