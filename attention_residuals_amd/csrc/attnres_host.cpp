@@ -224,8 +224,9 @@ attnres_status blocks_per_cu(const void* fn, int threads, size_t lds, int* out, 
 //  - the device-wide counter serves its atomics one at a time; near ~70 tickets/us the queue
 //    stalls every workgroup, so a batch must keep the ticket rate below `max_rate` tickets per
 //    microsecond (the token rate is estimated at 5.6 TB/s over the kernel's bytes per token);
-//  - workgroups finish up to one batch apart, so the backward (16 tokens per workgroup at
-//    N = 8192) also keeps at least `min_batches` batches per workgroup.
+//  - workgroups finish up to one batch apart, so every workgroup keeps at least `min_batches`
+//    batches (the backward asks for 16: at N = 8192 it has 16 tokens per workgroup), and the
+//    grid never shrinks below one batch per resident slot.
 // The forward waits for its ticket behind one output row, the backward behind S gradient rows, so
 // the backward's ticket costs more and its rate bound is lower.
 int64_t tokens_per_ticket(int64_t N, int64_t grid, double bytes_per_token, double max_rate,
@@ -234,7 +235,7 @@ int64_t tokens_per_ticket(int64_t N, int64_t grid, double bytes_per_token, doubl
   if (forced > 0) return forced;
   const double rate = 5.6e6 / bytes_per_token;  // tokens per microsecond at 5.6 TB/s
   int64_t b = std::max<int64_t>(1, (int64_t)std::ceil(rate / max_rate));
-  if (min_batches > 0) b = std::min(b, std::max<int64_t>(1, N / (grid * min_batches)));
+  b = std::min(b, std::max<int64_t>(1, N / (grid * std::max<int64_t>(1, min_batches))));
   return b;
 }
 
@@ -447,11 +448,13 @@ attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
   // With the token counter (single-block path and a workspace) the grid is one resident pass and
   // workgroups take tokens as they finish. Without it, 8x the resident grid lets the hardware
   // dispatcher balance workgroups over CUs (measured better than a one-pass static grid).
-  const bool dyn = workspace != nullptr && sh.fwd_one && N < kMaxTicketTokens;
+  // the counter pays off once every resident workgroup has at least two tokens
+  const int64_t resident = (int64_t)f.cus * per_cu;
+  const bool dyn = workspace != nullptr && sh.fwd_one && N >= 2 * resident && N < kMaxTicketTokens;
   static const int env_mult = env_int("ATTNRES_FWD_GRID_MULT");
   const int mult = env_mult > 0 ? env_mult : (dyn ? 1 : 8);
-  const int64_t slots = (int64_t)f.cus * per_cu * mult;
-  a.tpt = dyn ? tokens_per_ticket(N, slots, (double)(d->S + 1) * d->D * sh.esz, 55.0, 0) : 1;
+  const int64_t slots = resident * mult;
+  a.tpt = dyn ? tokens_per_ticket(N, slots, (double)(d->S + 1) * d->D * sh.esz, 55.0, 1) : 1;
   const int grid = (int)std::min<int64_t>((N + a.tpt - 1) / a.tpt, slots);
   if (dyn) {
     a.ticket = static_cast<uint32_t*>(workspace);
@@ -568,7 +571,7 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
     a.part_dow = d->has_out_weight ? reinterpret_cast<float*>(ws + pl.off_dow) : nullptr;
     a.out_norm = d->out_norm ? 1 : 0;
     a.tpt = 1;
-    if (sh.resident && !d->deterministic && N < kMaxTicketTokens) {
+    if (sh.resident && !d->deterministic && N >= 2 * (int64_t)pl.P && N < kMaxTicketTokens) {
       a.tpt = tokens_per_ticket(N, pl.P, (double)(2 * d->S + 1) * d->D * sh.esz, 30.0, 16);
       a.ticket = reinterpret_cast<uint32_t*>(ws + pl.off_ticket);
       void* targ = a.ticket;
