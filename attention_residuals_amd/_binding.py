@@ -28,7 +28,7 @@ class Desc(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("N", ctypes.c_int64), ("eps", ctypes.c_float),
                 ("scale", ctypes.c_float), ("has_norm_weight", ctypes.c_int32),
                 ("out_norm", ctypes.c_int32), ("has_out_weight", ctypes.c_int32),
-                ("deterministic", ctypes.c_int32)]
+                ("deterministic", ctypes.c_int32), ("accumulate_dvalues", ctypes.c_int32)]
 
 
 class Sources(ctypes.Structure):
@@ -95,10 +95,12 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 def make_desc(S: int, N: int, D: int, R: int, dtype: torch.dtype, *, eps: float = EPS_DEFAULT,
               scale: float = 1.0, has_norm_weight: bool = False, out_norm: bool = False,
-              has_out_weight: bool = False, deterministic: bool = False) -> Desc:
+              has_out_weight: bool = False, deterministic: bool = False,
+              accumulate_dvalues: bool = False) -> Desc:
     return Desc(S=S, D=D, R=R, dtype=_dtype_code(dtype), N=N, eps=eps, scale=scale,
                 has_norm_weight=int(has_norm_weight), out_norm=int(out_norm),
-                has_out_weight=int(has_out_weight), deterministic=int(deterministic))
+                has_out_weight=int(has_out_weight), deterministic=int(deterministic),
+                accumulate_dvalues=int(accumulate_dvalues))
 
 
 class _SourceView:
@@ -200,21 +202,26 @@ def attnres_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
                 out_w: Optional[torch.Tensor], lse: torch.Tensor,
                 out_rstd: Optional[torch.Tensor], o32: Optional[torch.Tensor],
                 dout: torch.Tensor, *, eps: float = EPS_DEFAULT, scale: float = 1.0,
-                out_norm: bool = False, deterministic: bool = False, dvalues=None,
+                out_norm: bool = False, deterministic: bool = False,
+                accumulate: bool = False, dvalues=None,
                 dq: Optional[torch.Tensor] = None,
                 dw: Optional[torch.Tensor] = None, dow: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None, stream=None):
     """Backward read. dvalues: packed [S, N, D] or list of [N, D] tensors to write (allocated
     packed when None). deterministic: fixed token split (bitwise-reproducible dq/dw/dow).
+    accumulate: add this read's gradient to the existing dvalues (which must then be given).
     Returns (dvalues, dq, dw or None, dow or None)."""
     sv = _SourceView(values)
     desc = make_desc(sv.S, sv.N, sv.D, query.numel(), sv.dtype, eps=eps, scale=scale,
                      has_norm_weight=norm_w is not None, out_norm=out_norm,
-                     has_out_weight=out_w is not None, deterministic=deterministic)
+                     has_out_weight=out_w is not None, deterministic=deterministic,
+                     accumulate_dvalues=accumulate)
     dev = sv.device
     if dout.dim() != 2 or dout.stride(1) != 1:
         raise ValueError("dout must be [N, D] with unit stride in D")
     if dvalues is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs the dvalues to add to")
         dvalues = torch.empty((sv.S, sv.N, sv.D), dtype=sv.dtype, device=dev)
     dv = _SourceView(dvalues)
     if dq is None:

@@ -4,23 +4,24 @@
 
 namespace attnres {
 
-#define ATTNRES_CASE(BF, CH, SB) \
-  case SB: return full ? (const void*)&bwd_stream_kernel<BF, CH, SB, true> \
-                       : (const void*)&bwd_stream_kernel<BF, CH, SB, false>;
+#define ATTNRES_CASE(BF, ACC, CH, SB) \
+  case SB: return full ? (const void*)&bwd_stream_kernel<BF, CH, SB, true, ACC> \
+                       : (const void*)&bwd_stream_kernel<BF, CH, SB, false, ACC>;
 
-template <bool BF>
+template <bool BF, bool ACC>
 static const void* stream_ptr(int ch, int sb, bool full) {
   switch (ch) {
-    case 1: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE, BF, 1) default: break; } break;
-    case 2: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE, BF, 2) default: break; } break;
-    case 4: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE, BF, 4) default: break; } break;
+    case 1: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE, BF, ACC, 1) default: break; } break;
+    case 2: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE, BF, ACC, 2) default: break; } break;
+    case 4: switch (sb) { ATTNRES_SB_STREAM(ATTNRES_CASE, BF, ACC, 4) default: break; } break;
     default: break;
   }
   return nullptr;
 }
 
-const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full) {
-  return bf16 ? stream_ptr<true>(ch, sb, full) : stream_ptr<false>(ch, sb, full);
+const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full, bool acc) {
+  if (acc) return bf16 ? stream_ptr<true, true>(ch, sb, full) : stream_ptr<false, true>(ch, sb, full);
+  return bf16 ? stream_ptr<true, false>(ch, sb, full) : stream_ptr<false, false>(ch, sb, full);
 }
 
 // Zeroes the backward's token counter on the launch stream (a kernel store: no memset node, so

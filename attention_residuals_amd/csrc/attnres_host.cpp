@@ -98,6 +98,8 @@ attnres_status check_desc(const attnres_desc* d) {
     return fail(ATTNRES_ERR_INVALID_ARG, "has_out_weight requires out_norm");
   if (d->deterministic != 0 && d->deterministic != 1)
     return fail(ATTNRES_ERR_INVALID_ARG, "deterministic must be 0 or 1");
+  if (d->accumulate_dvalues != 0 && d->accumulate_dvalues != 1)
+    return fail(ATTNRES_ERR_INVALID_ARG, "accumulate_dvalues must be 0 or 1");
   return ATTNRES_OK;
 }
 
@@ -142,7 +144,8 @@ attnres_status make_shape(const attnres_desc* d, Shape* sh) {
   const int fit = fit_for(ch);
   sh->resident = !d->out_norm && fit > 0;
   // forward: one block when the sources fit a bucket, else blocks of the stream size
-  const int stream_max = ch == 4 ? 4 : 8;
+  // (accumulating into dvalues holds a block's existing gradient rows too: half the block at CH = 2)
+  const int stream_max = ch == 4 ? 4 : (d->accumulate_dvalues && ch == 2) ? 4 : 8;
   sh->sb_fwd = fit > 0 ? fit : stream_max;
   sh->fwd_one = fit > 0;
   if (sh->resident) {
@@ -159,11 +162,15 @@ const void* fwd_ptr(const Shape& sh) {
                  : fwd_kernel_ptr_f32(sh.ch, sh.sb_fwd, sh.full, sh.fwd_one);
 }
 
-const void* bwd_ptr(const Shape& sh) {
-  if (sh.resident)
+const void* bwd_ptr(const Shape& sh, bool acc) {
+  if (sh.resident) {
+    if (acc)
+      return sh.bf16 ? bwd_resident_acc_kernel_ptr_bf16(sh.ch, sh.sb_bwd, sh.full)
+                     : bwd_resident_acc_kernel_ptr_f32(sh.ch, sh.sb_bwd, sh.full);
     return sh.bf16 ? bwd_resident_kernel_ptr_bf16(sh.ch, sh.sb_bwd, sh.full)
                    : bwd_resident_kernel_ptr_f32(sh.ch, sh.sb_bwd, sh.full);
-  return bwd_stream_kernel_ptr(sh.bf16, sh.ch, sh.sb_bwd, sh.full);
+  }
+  return bwd_stream_kernel_ptr(sh.bf16, sh.ch, sh.sb_bwd, sh.full, acc);
 }
 
 // LDS of every kernel: the per-thread parameter region (u = w*q as float4 slots, plus the
@@ -250,7 +257,7 @@ struct BwdPlan {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 attnres_status plan_bwd(const attnres_desc* d, const Shape& sh, BwdPlan* pl) {
-  const void* fn = bwd_ptr(sh);
+  const void* fn = bwd_ptr(sh, d->accumulate_dvalues != 0);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no backward kernel for this shape");
   DevFacts f;
   attnres_status st = device_facts(&f);
@@ -542,7 +549,7 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
   if (workspace_bytes < pl.bytes)
     return fail(ATTNRES_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
                 pl.bytes);
-  const void* fn = bwd_ptr(sh);
+  const void* fn = bwd_ptr(sh, d->accumulate_dvalues != 0);
   const void* fin = finalize_kernel_ptr(sh.bf16);
   char* ws = static_cast<char*>(workspace);
 

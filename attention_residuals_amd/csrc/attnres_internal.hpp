@@ -39,7 +39,9 @@ const void* fwd_kernel_ptr_bf16(int ch, int sb, bool full, bool one_block);
 const void* fwd_kernel_ptr_f32(int ch, int sb, bool full, bool one_block);
 const void* bwd_resident_kernel_ptr_bf16(int ch, int sb, bool full);
 const void* bwd_resident_kernel_ptr_f32(int ch, int sb, bool full);
-const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full);
+const void* bwd_resident_acc_kernel_ptr_bf16(int ch, int sb, bool full);
+const void* bwd_resident_acc_kernel_ptr_f32(int ch, int sb, bool full);
+const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full, bool acc);
 const void* finalize_kernel_ptr(bool bf16);
 const void* ticket_reset_kernel_ptr();
 

@@ -460,13 +460,15 @@ __device__ __forceinline__ float dot_f32(const Chunk (&v)[CH], const float (&g)[
   return acc;
 }
 
-// dv = p*do + A*u + B*t (t masked to the slice) and du += A*t for one source row.
-template <bool BF16, int CH, bool FULL>
+// dv = p*do + A*u + B*t (t masked to the slice) and du += A*t for one source row. With ACC the
+// row's existing gradient `old` is added in FP32 before the single rounding to storage.
+template <bool BF16, int CH, bool FULL, bool ACC = false>
 __device__ __forceinline__ void grad_row(const Chunk (&r)[CH], const Cols<BF16, CH, FULL>& cs,
                                          const float (&u)[CH][Fmt<BF16>::VEC],
                                          const float (&dof)[CH][Fmt<BF16>::VEC], float p,
                                          float A, float B, int lo,
-                                         float (&du)[CH][Fmt<BF16>::VEC], Chunk (&out)[CH]) {
+                                         float (&du)[CH][Fmt<BF16>::VEC], Chunk (&out)[CH],
+                                         const Chunk (&old)[CH]) {
   constexpr int VEC = Fmt<BF16>::VEC;
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
@@ -483,7 +485,9 @@ __device__ __forceinline__ void grad_row(const Chunk (&r)[CH], const Cols<BF16, 
       }
       float d = p * dof[j][e];
       d = fmaf(A, u[j][e], d);
-      dv[e] = fmaf(B, tm, d);
+      d = fmaf(B, tm, d);
+      if constexpr (ACC) d += elem<BF16>(old[j], e);
+      dv[e] = d;
       du[j][e] = fmaf(A, tm, du[j][e]);
     }
     out[j] = pack<BF16>(dv);
@@ -750,9 +754,10 @@ __device__ __forceinline__ void write_partials(const BwdArgs& a, const Cols<BF16
 // ------------------------------------------------------------------ backward, token-resident
 
 // All S <= SB rows of a token stay in VGPRs: delta = sum_s p_s <dY, v_s> is exact in FP32.
-// No output norm on this path (dL/do = dY).
-template <bool BF16, int CH, int SB, bool FULL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(occupancy_hint(CH, SB, FULL), 8)))
+// No output norm on this path (dL/do = dY). ACC: dvalues accumulate (the existing gradient rows
+// are prefetched one token ahead like the source rows and added before the store).
+template <bool BF16, int CH, int SB, bool FULL, bool ACC>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(occupancy_hint(CH, ACC ? 2 * SB : SB, FULL), 8)))
 void bwd_resident_kernel(const BwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
@@ -781,6 +786,7 @@ void bwd_resident_kernel(const BwdArgs a) {
   // Loops run over all SB slots; slots i >= S use an empty resource (zero rows, dropped stores)
   // and get routing weight 0, so there are no per-source branches and the wait counts stay exact.
   Chunk rows[SB][CH];
+  Chunk odv[ACC ? SB : 1][CH];  // ACC: the existing dvalues rows of the current token
   Chunk gy[CH];
   // Token schedule: tokens go out in batches of B = a.tpt consecutive tokens. Workgroup g starts
   // with batch g; each later batch is grid + a ticket from the device-wide counter, so workgroups
@@ -808,6 +814,11 @@ void bwd_resident_kernel(const BwdArgs a) {
       const Rsrc r = src_rsrc(a.src[i], i, live, n0 * a.row_stride * ESZ, row_bytes);
 #pragma unroll
       for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+      if constexpr (ACC) {
+        const Rsrc rd = src_rsrc(a.dsrc[i], i, live, n0 * a.drow_stride * ESZ, row_bytes);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) odv[i][j] = ld_row(rd, cs.voff[j]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -875,18 +886,25 @@ void bwd_resident_kernel(const BwdArgs a) {
     }
     const int64_t drow_byte = n * a.drow_stride * ESZ;
     const int64_t next_byte = next * a.row_stride * ESZ;
+    const int64_t next_dbyte = next * a.drow_stride * ESZ;
     cs.fetch_u(laundered_lane_off(tid), u);
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
       Chunk out[CH];
-      grad_row<BF16, CH, FULL>(rows[i], cs, u, dof, bcast(p, i), bcast(A, i), bcast(B, i), a.lo,
-                               du, out);
+      grad_row<BF16, CH, FULL, ACC>(rows[i], cs, u, dof, bcast(p, i), bcast(A, i), bcast(B, i),
+                                    a.lo, du, out, odv[ACC ? i : 0]);
       const Rsrc rd = src_rsrc(a.dsrc[i], i, S, drow_byte, row_bytes);
 #pragma unroll
       for (int j = 0; j < CH; ++j) st_row(rd, cs.voff[j], out[j]);
       const Rsrc r = src_rsrc(a.src[i], i, live_next, next_byte, row_bytes);
 #pragma unroll
       for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+      if constexpr (ACC) {
+        // the next token's existing gradient row i (issued after this token's row i is stored)
+        const Rsrc rn = src_rsrc(a.dsrc[i], i, live_next, next_dbyte, row_bytes);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) odv[i][j] = ld_row(rn, cs.voff[j]);
+      }
     }
     lse = lse_next;
     n = next;
@@ -897,8 +915,9 @@ void bwd_resident_kernel(const BwdArgs a) {
 // ------------------------------------------------------------------ backward, streaming
 
 // Sources walked in blocks of SB using the forward's FP32 mixture o (and rho_o with the output
-// norm): do and delta = <do, o> are known before the first source is read.
-template <bool BF16, int CH, int SB, bool FULL>
+// norm): do and delta = <do, o> are known before the first source is read. ACC: dvalues
+// accumulate (a block's existing gradient rows are loaded with its source rows).
+template <bool BF16, int CH, int SB, bool FULL, bool ACC>
 __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
@@ -989,11 +1008,21 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
     for (int s0 = 0; s0 < a.S; s0 += SB) {
       const int nb = min(SB, a.S - s0);
       Chunk rows[SB][CH];  // slots i >= nb: empty resource, zero rows, weight 0
+      Chunk odv[ACC ? SB : 1][CH];
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
         const Rsrc r = src_rsrc(a.src[min(s0 + i, kMaxSources - 1)], i, nb, row_byte, row_bytes);
 #pragma unroll
         for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+      }
+      if constexpr (ACC) {
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+          const Rsrc rd =
+              src_rsrc(a.dsrc[min(s0 + i, kMaxSources - 1)], i, nb, drow_byte, row_bytes);
+#pragma unroll
+          for (int j = 0; j < CH; ++j) odv[i][j] = ld_row(rd, cs.voff[j]);
+        }
       }
       float* xb = lds + buf * xfl;
       uint32_t us[3][CH][4];
@@ -1030,8 +1059,8 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
         Chunk out[CH];
-        grad_row<BF16, CH, FULL>(rows[i], cs, u, dov, bcast(p, i), bcast(A, i), bcast(B, i), a.lo,
-                                 du, out);
+        grad_row<BF16, CH, FULL, ACC>(rows[i], cs, u, dov, bcast(p, i), bcast(A, i), bcast(B, i),
+                                      a.lo, du, out, odv[ACC ? i : 0]);
         const Rsrc rd = src_rsrc(a.dsrc[min(s0 + i, kMaxSources - 1)], i, nb, drow_byte, row_bytes);
 #pragma unroll
         for (int j = 0; j < CH; ++j) st_row(rd, cs.voff[j], out[j]);

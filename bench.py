@@ -67,6 +67,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bf16_s10_n32768_d4096")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--accumulate", action="store_true",
+                    help="the backward adds into existing dvalues (reads them: +S*N*D elements)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time the oracle baseline repeats its pass for")
     ap.add_argument("--check", type=int, default=1, help="sampled-token parity check (0 = off)")
@@ -103,12 +105,12 @@ def main() -> int:
     N, D, S, R = w.N, w.D, w.S, w.R
     desc = A.make_desc(S, N, D, R, w.torch_dtype, eps=w.eps, scale=w.scale,
                        has_norm_weight=x["norm_w"] is not None, out_norm=w.out_norm,
-                       has_out_weight=x["out_w"] is not None)
+                       has_out_weight=x["out_w"] is not None, accumulate_dvalues=args.accumulate)
     y = torch.empty((N, D), dtype=w.torch_dtype, device=dev)
     lse = torch.empty((N,), dtype=torch.float32, device=dev)
     rstd = torch.empty((N,), dtype=torch.float32, device=dev) if w.out_norm else None
     o32 = torch.empty((N, D), dtype=torch.float32, device=dev) if A.o32_elems(desc) else None
-    dv = torch.empty((S, N, D), dtype=w.torch_dtype, device=dev)
+    dv = (torch.zeros if args.accumulate else torch.empty)((S, N, D), dtype=w.torch_dtype, device=dev)
     dq = torch.empty((R,), dtype=w.torch_dtype, device=dev)
     dw = torch.empty((R,), dtype=w.torch_dtype, device=dev) if x["norm_w"] is not None else None
     dow = torch.empty((D,), dtype=w.torch_dtype, device=dev) if x["out_w"] is not None else None
@@ -123,8 +125,9 @@ def main() -> int:
 
     def bwd():
         A.attnres_bwd(x["values"], x["query"], x["norm_w"], x["out_w"], lse, rstd, o32,
-                      x["dout"], eps=w.eps, scale=w.scale, out_norm=w.out_norm, dvalues=dv,
-                      dq=dq, dw=dw, dow=dow, workspace=ws, stream=stream)
+                      x["dout"], eps=w.eps, scale=w.scale, out_norm=w.out_norm,
+                      accumulate=args.accumulate, dvalues=dv, dq=dq, dw=dw, dow=dow,
+                      workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         fwd()
@@ -148,9 +151,9 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     ev_step = [a + b for a, b in zip(fwd_ms, bwd_ms)]
 
-    algo = w.algorithmic_bytes()
+    algo = w.algorithmic_bytes() + (S * N * D * w.elem_bytes if args.accumulate else 0)
     b = w.elem_bytes
-    bwd_bytes = (2 * S + 1) * N * D * b + 4 * N * (2 if w.out_norm else 1)
+    bwd_bytes = ((3 if args.accumulate else 2) * S + 1) * N * D * b + 4 * N * (2 if w.out_norm else 1)
     fwd_bytes = (S + 1) * N * D * b + 4 * N * (2 if w.out_norm else 1)
     bwd_avg = float(np.mean(bwd_ms))
     fwd_avg = float(np.mean(fwd_ms))
@@ -158,6 +161,12 @@ def main() -> int:
     value = algo / (ms_per_step * 1e-3) / 1e9
 
     check = None
+    if args.check and args.accumulate:
+        # the timed steps summed their gradients into dv: start from zero for the check
+        dv.zero_()
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
     if args.check:
         sys.path.insert(0, os.path.join(ROOT, "tests"))
         from parity import check_all, run_oracle, sample_tokens
@@ -190,7 +199,7 @@ def main() -> int:
                          f"{D}), forward and backward with the dq/dw reduction, FP64, OpenMP "
                          f"over tokens, {tc:.1f} s in total"}
 
-    traffic = load_traffic(w.name, bwd_bytes)
+    traffic = None if args.accumulate else load_traffic(w.name, bwd_bytes)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -206,6 +215,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "S": S, "N": N, "D": D, "R": R,
                    "norm_weight": w.norm_weight, "out_norm": w.out_norm,
+                   "accumulate_dvalues": args.accumulate,
                    "algorithmic_bytes": algo, "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 1),
                    "fwd_ms": round(fwd_avg, 4), "bwd_ms": round(bwd_avg, 4),
                    "event_ms_per_step": round(float(np.mean(ev_step)), 4),

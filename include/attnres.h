@@ -66,6 +66,11 @@ typedef struct {
                               0: tokens handed out by a device-wide counter (faster: workgroups
                               finish together), dq/dw/dow reproducible to FP32 rounding only.
                               y, lse and dvalues are bitwise reproducible in both modes. */
+  int32_t accumulate_dvalues; /* backward only. 0: dvalues are overwritten with this read's
+                              gradient. 1: the gradient is added to the existing dvalues (read,
+                              summed in FP32, rounded once to storage), so a source shared by
+                              several reads (the embedding and writer outputs of Full / Block
+                              schedules) collects all of them without a separate add pass. */
 } attnres_desc;
 
 /* S row blocks of shape [N, D]: either one packed [S, N, D] tensor or a list of S pointers.
@@ -116,8 +121,8 @@ attnres_status attnres_fwd(const attnres_desc* desc, const attnres_sources* valu
 
 /* Backward, given the forward's inputs and saved statistics.
  *   dout            [N, D] upstream gradient dL/dy with row stride dout_row_stride (read).
- *   dvalues         [S][N, D] gradients of the sources (written, fully overwritten); must not
- *                   alias values or each other.
+ *   dvalues         [S][N, D] gradients of the sources (written; with accumulate_dvalues read
+ *                   first and added to); must not alias values or each other.
  *   dq [R]          gradient of the query, summed over tokens (written).
  *   dw [R]          gradient of the key-norm weight (iff has_norm_weight, else NULL).
  *   dow [D]         gradient of the output-norm weight (iff has_out_weight, else NULL).

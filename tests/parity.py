@@ -106,8 +106,10 @@ def poison_(t: Optional[torch.Tensor]) -> None:
 
 
 def run_gpu(w: W.Workload, xg: dict, *, packed: bool = True, poison: bool = True,
-            values=None, dvalues=None, dout=None, stream=None, deterministic: bool = False) -> dict:
-    """Forward + backward through the C ABI on the device tensors xg; returns device tensors."""
+            values=None, dvalues=None, dout=None, stream=None, deterministic: bool = False,
+            accumulate: bool = False) -> dict:
+    """Forward + backward through the C ABI on the device tensors xg; returns device tensors.
+    accumulate: the backward adds into the given dvalues (never poisoned)."""
     import attention_residuals_amd as A
     v = xg["values"] if values is None else values
     if values is None and not packed:
@@ -116,7 +118,8 @@ def run_gpu(w: W.Workload, xg: dict, *, packed: bool = True, poison: bool = True
     N, D = w.N, w.D
     desc = A.make_desc(w.S, N, D, w.R, w.torch_dtype, eps=w.eps, scale=w.scale,
                        has_norm_weight=xg["norm_w"] is not None, out_norm=w.out_norm,
-                       has_out_weight=xg["out_w"] is not None, deterministic=deterministic)
+                       has_out_weight=xg["out_w"] is not None, deterministic=deterministic,
+                       accumulate_dvalues=accumulate)
     y = torch.empty((N, D), dtype=w.torch_dtype, device=dev)
     lse = torch.empty((N,), dtype=torch.float32, device=dev)
     rstd = torch.empty((N,), dtype=torch.float32, device=dev) if w.out_norm else None
@@ -133,15 +136,17 @@ def run_gpu(w: W.Workload, xg: dict, *, packed: bool = True, poison: bool = True
     if poison:
         for t in (y, lse, rstd, o32, dq, dw, dow):
             poison_(t)
-        for t in (dvalues if isinstance(dvalues, list) else [dvalues]):
-            poison_(t)
+        if not accumulate:
+            for t in (dvalues if isinstance(dvalues, list) else [dvalues]):
+                poison_(t)
         ws.fill_(0xFF)
     A.attnres_fwd(v, xg["query"], xg["norm_w"], xg["out_w"], eps=w.eps, scale=w.scale,
                   out_norm=w.out_norm, out=y, lse=lse, out_rstd=rstd, o32=o32, stream=stream)
     g = xg["dout"] if dout is None else dout
     A.attnres_bwd(v, xg["query"], xg["norm_w"], xg["out_w"], lse, rstd, o32, g, eps=w.eps,
                   scale=w.scale, out_norm=w.out_norm, deterministic=deterministic,
-                  dvalues=dvalues, dq=dq, dw=dw, dow=dow, workspace=ws, stream=stream)
+                  accumulate=accumulate, dvalues=dvalues, dq=dq, dw=dw, dow=dow, workspace=ws,
+                  stream=stream)
     torch.cuda.synchronize()
     dv = torch.stack(dvalues) if isinstance(dvalues, list) else dvalues
     return {"y": y, "lse": lse, "o_rstd": rstd, "o32": o32, "dvalues": dv, "dq": dq, "dw": dw,

@@ -60,7 +60,8 @@ def _o32(desc):
     (dict(D=12, R=12, dtype=torch.float32), OK), (dict(D=10, R=10, dtype=torch.float32), UNSUPPORTED),
     (dict(D=16384, R=16384, dtype=torch.float32), UNSUPPORTED),
     (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
-    (dict(has_out_weight=True), INVALID),
+    (dict(has_out_weight=True), INVALID), (dict(deterministic=2), INVALID),
+    (dict(accumulate_dvalues=2), INVALID), (dict(accumulate_dvalues=1), OK),
 ])
 def test_descriptor_validation(kw, expect):
     st, _ = _o32(_desc(**kw))

@@ -176,6 +176,28 @@ def test_ticket_schedule_matches_deterministic_mode():
             assert np.linalg.norm(a - b) <= 4e-3 * np.linalg.norm(a), k
 
 
+@pytest.mark.parametrize("S,N,D,R,dtype,out_norm,packed", [
+    (10, 701, 4096, 4096, "bf16", False, True),   # token-resident backward
+    (24, 257, 2048, 512, "bf16", False, False),   # resident, sliced key, list of sources
+    (5, 129, 1024, 1024, "bf16", True, True),     # streaming backward (output norm)
+    (29, 97, 4096, 4096, "bf16", False, True),    # streaming backward without the output norm
+    (6, 200, 1024, 512, "f32", False, True),
+])
+def test_accumulate_into_existing_dvalues(S, N, D, R, dtype, out_norm, packed):
+    # dvalues_out = dvalues_in + this read's gradient, summed in FP32 and rounded once
+    w = _wl(S, N, D, R, dtype=dtype, out_norm=out_norm, out_weight=out_norm, seed=1700 + S)
+    xc = W.generate(w)
+    gen = torch.Generator().manual_seed(1799 + S)
+    init = (3.0 * torch.randn((S, N, D), generator=gen)).to(w.torch_dtype)
+    dv = init.to("cuda")
+    if not packed:
+        dv = [dv[s].clone() for s in range(S)]
+    got = run_gpu(w, inputs_on(xc, "cuda"), packed=packed, dvalues=dv, accumulate=True)
+    ref = run_oracle(w, xc)
+    ref["dvalues"] = ref["dvalues"] + init.double().numpy()
+    assert_ok(check_all(w, got, ref), f"accumulate S={S} N={N} D={D} R={R} {dtype}")
+
+
 @pytest.mark.parametrize("S,N,D", [(8, 32768 + 5, 2048), (10, 32768 + 3, 4096)])
 def test_batched_ticket_schedules_match_static_split(S, N, D):
     # long token counts where both dynamic schedules hand out batches of 2-3 tokens per ticket
