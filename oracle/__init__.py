@@ -6,8 +6,10 @@ CPU-baseline leg of ``bench.py`` may import this package. It shares no code with
 
 The arithmetic lives in ``attnres_oracle.c`` (plain C, double precision): the forward follows the
 "Equation" section of the "Fast Attention Residuals" PyPI page in its own notation and order, and
-the backward is the reverse-mode derivative of those same steps. This module only marshals
-arguments (numpy or CPU torch arrays in, numpy float64 arrays out) and builds the C file with gcc.
+the backward is the reverse-mode derivative of those same steps. ``attnres_oracle_multi.c`` does
+the same for the page's multi-query read ("Multi-query AttnRes": M queries, each with its own
+routing weights and output). This module only marshals arguments (numpy or CPU torch arrays in,
+numpy float64 arrays out) and builds the C files with gcc.
 """
 from __future__ import annotations
 
@@ -20,6 +22,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attnres_oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "attnres_oracle_multi.c")]
 _LIB = os.path.join(_HERE, "libattnres_oracle.so")
 
 F32, BF16, F64 = 0, 1, 2
@@ -27,14 +30,21 @@ F32, BF16, F64 = 0, 1, 2
 
 def build(force: bool = True) -> str:
     """Compiles the oracle with gcc (IEEE double arithmetic: no fast-math) and returns the path."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if force or _stale():
         tmp = _LIB + ".tmp"
         subprocess.run(
             ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
-             "-ffp-contract=off", _SRC, "-o", tmp, "-lm"],
+             "-ffp-contract=off"] + _SRCS + ["-o", tmp, "-lm"],
             check=True)
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def _stale() -> bool:
+    if not os.path.exists(_LIB):
+        return True
+    t = os.path.getmtime(_LIB)
+    return any(os.path.getmtime(f) > t for f in _SRCS + [os.path.join(_HERE, "attnres_oracle.h")])
 
 
 class _Problem(ctypes.Structure):
@@ -52,13 +62,27 @@ class _Rows(ctypes.Structure):
                 for name in ("y", "lse", "o_rstd", "p", "score", "dvalues")]
 
 
+class _MultiProblem(ctypes.Structure):
+    _fields_ = [
+        ("S", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("M", ctypes.c_int32), ("N", ctypes.c_int64), ("dtype", ctypes.c_int32),
+        ("eps", ctypes.c_double), ("scale", ctypes.c_double),
+        ("values", ctypes.POINTER(ctypes.c_void_p)), ("queries", ctypes.c_void_p),
+        ("dout", ctypes.c_void_p),
+    ]
+
+
+class _MultiRows(ctypes.Structure):
+    _fields_ = [(name, ctypes.POINTER(ctypes.c_double)) for name in ("y", "lse", "dvalues")]
+
+
 _lib = None
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if _stale():
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         lib.attnres_oracle_run.restype = ctypes.c_int
@@ -66,6 +90,10 @@ def _load():
             ctypes.POINTER(_Problem), ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
             ctypes.POINTER(_Rows), ctypes.POINTER(ctypes.c_double),
             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+        lib.attnres_oracle_multi_run.restype = ctypes.c_int
+        lib.attnres_oracle_multi_run.argtypes = [
+            ctypes.POINTER(_MultiProblem), ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+            ctypes.POINTER(_MultiRows), ctypes.POINTER(ctypes.c_double), ctypes.c_int]
         lib.attnres_oracle_threads.restype = ctypes.c_int
         lib.attnres_oracle_threads.argtypes = [ctypes.c_int]
         _lib = lib
@@ -191,4 +219,71 @@ def run(values, query, norm_w=None, out_w=None, dout=None, *, eps: float = 2.0 *
         out["dw"] = dw
     if dow is not None:
         out["dow"] = dow
+    return out
+
+
+def _sources(values):
+    if isinstance(values, (list, tuple)):
+        vals = [_storage(v) for v in values]
+    else:
+        v3 = _storage(values)
+        if v3.ndim != 3:
+            raise ValueError("packed values must be [S, N, D]")
+        vals = [v3[s] for s in range(v3.shape[0])]
+    if not vals:
+        raise ValueError("need at least one source")
+    return [np.ascontiguousarray(v) for v in vals]
+
+
+def run_multi(values, queries, dout=None, *, eps: float = 2.0 ** -23, scale: float = 1.0,
+              tokens: Optional[Sequence[int]] = None, want: Sequence[str] = ("y", "lse", "dvalues"),
+              reduce: bool = True, threads: int = 0) -> dict:
+    """Evaluates the multi-query AttnRes read (and its backward when ``dout`` is given) in FP64.
+
+    values: [S, N, D] or S arrays [N, D]; queries [M, R]; dout [M, N, D] (query-major) or None;
+    one storage format for all. tokens / want / reduce as in ``run``. Returns float64 arrays:
+    y [M, T, D], lse [M, T], dvalues [S, T, D] (summed over the queries), dq [M, R].
+    """
+    lib = _load()
+    vals = _sources(values)
+    S = len(vals)
+    N, D = vals[0].shape
+    q = _storage(queries)
+    if q.ndim != 2:
+        raise ValueError("queries must be [M, R]")
+    q = np.ascontiguousarray(q)
+    M, R = q.shape
+    code = _code(vals[0])
+    g = None if dout is None else np.ascontiguousarray(_storage(dout).reshape(M, N, D))
+    for a in vals + [q] + ([g] if g is not None else []):
+        if _code(a) != code:
+            raise TypeError("all oracle inputs must share one storage format")
+    for v in vals:
+        if v.shape != (N, D):
+            raise ValueError("every source must be [N, D]")
+    ptrs = (ctypes.c_void_p * S)(*[v.ctypes.data for v in vals])
+    prob = _MultiProblem(S=S, D=D, R=R, M=M, N=N, dtype=code, eps=float(eps), scale=float(scale),
+                         values=ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)),
+                         queries=q.ctypes.data, dout=None if g is None else g.ctypes.data)
+    tok = None
+    T = N
+    if tokens is not None:
+        tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        T = tok.shape[0]
+    out = {}
+    shapes = {"y": (M, T, D), "lse": (M, T), "dvalues": (S, T, D)}
+    for name in want:
+        if name == "dvalues" and g is None:
+            continue
+        out[name] = np.zeros(shapes[name], dtype=np.float64)
+    rows = _MultiRows(**{k: _dptr(out.get(k)) for k in shapes})
+    dq = np.zeros((M, R), dtype=np.float64) if (reduce and g is not None) else None
+    rc = lib.attnres_oracle_multi_run(
+        ctypes.byref(prob),
+        None if tok is None else tok.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        T, ctypes.byref(rows), _dptr(dq), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"attnres_oracle_multi_run failed with code {rc}")
+    if dq is not None:
+        out["dq"] = dq
     return out

@@ -65,6 +65,30 @@ int attnres_oracle_run(const attnres_oracle_problem* prob, const int64_t* tokens
                        attnres_oracle_rows* rows, double* dq, double* dw, double* dow,
                        int threads);
 
+/* Multi-query read ("Fast Attention Residuals" PyPI page, section "Multi-query AttnRes"): M
+ * queries read the same sources, each with its own routing weights and output. No key-norm
+ * weight and no output norm (the page's operator as written). Layouts are query-major. */
+typedef struct {
+  int32_t S, D, R, M;     /* sources, width, routing rank, queries (M >= 1) */
+  int64_t N;
+  int32_t dtype;
+  double eps, scale;
+  const void* const* values;  /* host array of S pointers, each a contiguous [N, D] */
+  const void* queries;    /* [M, R] */
+  const void* dout;       /* [M, N, D] upstream gradients of the outputs, or NULL */
+} attnres_oracle_multi_problem;
+
+typedef struct {
+  double* y;        /* [M, T, D] outputs */
+  double* lse;      /* [M, T] */
+  double* dvalues;  /* [S, T, D], summed over the queries */
+} attnres_oracle_multi_rows;
+
+/* Like attnres_oracle_run; dq (optional) is [M, R], summed over the processed tokens. */
+int attnres_oracle_multi_run(const attnres_oracle_multi_problem* prob, const int64_t* tokens,
+                             int64_t T, attnres_oracle_multi_rows* rows, double* dq,
+                             int threads);
+
 /* Number of OpenMP threads a run with the given request would use (for reporting). */
 int attnres_oracle_threads(int threads);
 
