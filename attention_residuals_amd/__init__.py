@@ -5,11 +5,15 @@ The compute lives in ``libattnres.so`` (hand-written HIP kernels behind the C AB
 ``python -m attention_residuals_amd.build``. Nothing here falls back to a CPU implementation.
 """
 from ._binding import (ATTNRES_BF16, ATTNRES_F32, EPS_DEFAULT, EXPORTS, AttnResError, Desc,
-                       Sources, attnres_bwd, attnres_fwd, fwd_workspace_bytes, load, make_desc,
-                       o32_elems, workspace_bytes)
-from .autograd import attnres
+                       MultiDesc, Sources, attnres_bwd, attnres_fwd, attnres_multi_bwd,
+                       attnres_multi_fwd, fwd_workspace_bytes, load, make_desc, make_multi_desc,
+                       multi_fwd_workspace_bytes, multi_workspace_bytes, o32_elems,
+                       workspace_bytes)
+from .autograd import attnres, attnres_multi
 
-__all__ = ["attnres", "attnres_fwd", "attnres_bwd", "o32_elems", "workspace_bytes",
-           "fwd_workspace_bytes", "make_desc",
+__all__ = ["attnres", "attnres_multi", "attnres_fwd", "attnres_bwd", "attnres_multi_fwd",
+           "attnres_multi_bwd", "o32_elems", "workspace_bytes", "fwd_workspace_bytes",
+           "multi_workspace_bytes", "multi_fwd_workspace_bytes", "make_desc", "make_multi_desc",
+           "MultiDesc",
            "load", "Desc", "Sources", "AttnResError", "EXPORTS", "ATTNRES_BF16", "ATTNRES_F32",
            "EPS_DEFAULT"]

@@ -20,7 +20,12 @@ EPS_DEFAULT = 2.0 ** -23
 
 # Every function the header declares, with its ctypes signature.
 EXPORTS = ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd_workspace_bytes",
-           "attnres_fwd", "attnres_bwd", "attnres_status_str", "attnres_last_error")
+           "attnres_fwd", "attnres_bwd", "attnres_multi_fwd_workspace_bytes",
+           "attnres_multi_workspace_bytes", "attnres_multi_fwd", "attnres_multi_bwd",
+           "attnres_status_str", "attnres_last_error")
+
+QUERY_MAJOR, TOKEN_MAJOR = 0, 1
+LAYOUTS = {"query_major": QUERY_MAJOR, "token_major": TOKEN_MAJOR}
 
 
 class Desc(ctypes.Structure):
@@ -28,6 +33,13 @@ class Desc(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("N", ctypes.c_int64), ("eps", ctypes.c_float),
                 ("scale", ctypes.c_float), ("has_norm_weight", ctypes.c_int32),
                 ("out_norm", ctypes.c_int32), ("has_out_weight", ctypes.c_int32),
+                ("deterministic", ctypes.c_int32), ("accumulate_dvalues", ctypes.c_int32)]
+
+
+class MultiDesc(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
+                ("M", ctypes.c_int32), ("dtype", ctypes.c_int32), ("N", ctypes.c_int64),
+                ("eps", ctypes.c_float), ("scale", ctypes.c_float), ("layout", ctypes.c_int32),
                 ("deterministic", ctypes.c_int32), ("accumulate_dvalues", ctypes.c_int32)]
 
 
@@ -63,8 +75,14 @@ def load() -> ctypes.CDLL:
     lib.attnres_fwd_workspace_bytes.argtypes = [pd, ctypes.POINTER(sz)]
     lib.attnres_fwd.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attnres_bwd.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, i64, ps, vp, vp, vp, vp, sz, vp]
+    pm = ctypes.POINTER(MultiDesc)
+    lib.attnres_multi_fwd_workspace_bytes.argtypes = [pm, ctypes.POINTER(sz)]
+    lib.attnres_multi_workspace_bytes.argtypes = [pm, ctypes.POINTER(sz)]
+    lib.attnres_multi_fwd.argtypes = [pm, ps, vp, vp, vp, vp, sz, vp]
+    lib.attnres_multi_bwd.argtypes = [pm, ps, vp, vp, vp, ps, vp, vp, sz, vp]
     for f in ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd_workspace_bytes",
-              "attnres_fwd", "attnres_bwd"):
+              "attnres_fwd", "attnres_bwd", "attnres_multi_fwd_workspace_bytes",
+              "attnres_multi_workspace_bytes", "attnres_multi_fwd", "attnres_multi_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     lib.attnres_status_str.argtypes = [ctypes.c_int]
     lib.attnres_status_str.restype = ctypes.c_char_p
@@ -239,3 +257,91 @@ def attnres_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
                               _ptr(dout), dstride, ctypes.byref(dv.struct), _ptr(dq), _ptr(dw),
                               _ptr(dow), _ptr(workspace), workspace.numel(), _stream(stream)))
     return dvalues, dq, dw, dow
+
+
+# ---------------------------------------------------------------- multi-query read
+
+def make_multi_desc(S: int, N: int, D: int, R: int, M: int, dtype: torch.dtype, *,
+                    eps: float = EPS_DEFAULT, scale: float = 1.0, layout: str = "query_major",
+                    deterministic: bool = False, accumulate_dvalues: bool = False) -> MultiDesc:
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    return MultiDesc(S=S, D=D, R=R, M=M, dtype=_dtype_code(dtype), N=N, eps=eps, scale=scale,
+                     layout=LAYOUTS[layout], deterministic=int(deterministic),
+                     accumulate_dvalues=int(accumulate_dvalues))
+
+
+def multi_workspace_bytes(desc: MultiDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().attnres_multi_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def multi_fwd_workspace_bytes(desc: MultiDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().attnres_multi_fwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _rows_shape(layout: str, M: int, N: int, D: Optional[int] = None):
+    base = (M, N) if layout == "query_major" else (N, M)
+    return base if D is None else base + (D,)
+
+
+def attnres_multi_fwd(values, queries: torch.Tensor, *, eps: float = EPS_DEFAULT,
+                      scale: float = 1.0, layout: str = "query_major",
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, dynamic: bool = True,
+                      stream=None):
+    """Multi-query forward. values: packed [S, N, D] or a list of [N, D]; queries [M, R].
+    Returns (y, lse): y [M, N, D] (query_major) or [N, M, D] (token_major), lse [M, N] or [N, M]
+    in FP32, allocated with torch when not given."""
+    sv = _SourceView(values)
+    if queries.dim() != 2 or not queries.is_contiguous():
+        raise ValueError("queries must be a contiguous [M, R] tensor")
+    M, R = queries.shape
+    desc = make_multi_desc(sv.S, sv.N, sv.D, R, M, sv.dtype, eps=eps, scale=scale, layout=layout)
+    dev = sv.device
+    if out is None:
+        out = torch.empty(_rows_shape(layout, M, sv.N, sv.D), dtype=sv.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(_rows_shape(layout, M, sv.N), dtype=torch.float32, device=dev)
+    if not dynamic:
+        workspace = None
+    elif workspace is None:
+        workspace = torch.empty((multi_fwd_workspace_bytes(desc),), dtype=torch.uint8, device=dev)
+    _check(load().attnres_multi_fwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(queries),
+                                    _ptr(out), _ptr(lse), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(),
+                                    _stream(stream)))
+    return out, lse
+
+
+def attnres_multi_bwd(values, queries: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, *,
+                      eps: float = EPS_DEFAULT, scale: float = 1.0, layout: str = "query_major",
+                      deterministic: bool = False, accumulate: bool = False, dvalues=None,
+                      dq: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Multi-query backward. dout like the forward's y (contiguous, same layout). Returns
+    (dvalues, dq [M, R]); dvalues are allocated packed when not given (accumulate needs them)."""
+    sv = _SourceView(values)
+    M, R = queries.shape
+    desc = make_multi_desc(sv.S, sv.N, sv.D, R, M, sv.dtype, eps=eps, scale=scale, layout=layout,
+                           deterministic=deterministic, accumulate_dvalues=accumulate)
+    dev = sv.device
+    if not dout.is_contiguous():
+        raise ValueError("dout must be contiguous")
+    if dvalues is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs the dvalues to add to")
+        dvalues = torch.empty((sv.S, sv.N, sv.D), dtype=sv.dtype, device=dev)
+    dv = _SourceView(dvalues)
+    if dq is None:
+        dq = torch.empty((M, R), dtype=sv.dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(multi_workspace_bytes(desc), 256),), dtype=torch.uint8,
+                                device=dev)
+    _check(load().attnres_multi_bwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(queries),
+                                    _ptr(lse), _ptr(dout), ctypes.byref(dv.struct), _ptr(dq),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+    return dvalues, dq

@@ -78,3 +78,61 @@ def attnres(values: Union[torch.Tensor, Sequence[torch.Tensor]], query: torch.Te
         y = _AttnResFn.apply(eps, scale, out_norm, deterministic, False, query.reshape(-1),
                              norm_weight, out_weight, *flat)
     return y.reshape(*lead, D)
+
+
+class _AttnResMultiFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, eps, scale, layout, deterministic, packed, queries, *srcs):
+        values = srcs[0] if packed else list(srcs)
+        y, lse = B.attnres_multi_fwd(values, queries, eps=eps, scale=scale, layout=layout)
+        ctx.eps, ctx.scale, ctx.layout, ctx.packed = eps, scale, layout, packed
+        ctx.deterministic = deterministic
+        ctx.save_for_backward(queries, lse, *srcs)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        queries, lse, *srcs = ctx.saved_tensors
+        dy = dy.contiguous()
+        if ctx.packed:
+            values = srcs[0]
+            dvalues = torch.empty_like(values, memory_format=torch.contiguous_format)
+        else:
+            values = list(srcs)
+            dvalues = [torch.empty(v.shape, dtype=v.dtype, device=v.device) for v in values]
+        dvalues, dq = B.attnres_multi_bwd(values, queries, lse, dy, eps=ctx.eps, scale=ctx.scale,
+                                          layout=ctx.layout, deterministic=ctx.deterministic,
+                                          dvalues=dvalues)
+        dsrcs = (dvalues,) if ctx.packed else tuple(dvalues)
+        return (None, None, None, None, None, dq) + dsrcs
+
+
+def attnres_multi(values: Union[torch.Tensor, Sequence[torch.Tensor]], queries: torch.Tensor, *,
+                  eps: float = B.EPS_DEFAULT, scale: float = 1.0,
+                  output_layout: str = "query_major", deterministic: bool = False) -> torch.Tensor:
+    """Multi-query AttnRes read ("Fast Attention Residuals" page, Multi-query AttnRes): queries
+    [M, R], 1 <= M <= 16, each with its own routing weights and full-width output. Returns
+    [M, ..., D] (query_major) or [..., M, D] (token_major)."""
+    if queries.dim() != 2:
+        raise ValueError("queries must be [M, R]")
+    q = queries.contiguous()
+    M = q.shape[0]
+    if isinstance(values, torch.Tensor):
+        S, D = values.shape[0], values.shape[-1]
+        lead = values.shape[1:-1]
+        flat = values.reshape(S, -1, D)
+        if flat.stride(-1) != 1:
+            flat = flat.contiguous()
+        y = _AttnResMultiFn.apply(eps, scale, output_layout, deterministic, True, q, flat)
+    else:
+        vs = list(values)
+        D = vs[0].shape[-1]
+        lead = vs[0].shape[:-1]
+        flat = [v.reshape(-1, D) for v in vs]
+        flat = [f if f.stride(-1) == 1 else f.contiguous() for f in flat]
+        if len({f.stride(0) for f in flat}) > 1:
+            flat = [f.contiguous() for f in flat]
+        y = _AttnResMultiFn.apply(eps, scale, output_layout, deterministic, False, q, *flat)
+    if output_layout == "query_major":
+        return y.reshape(M, *lead, D)
+    return y.reshape(*lead, M, D)

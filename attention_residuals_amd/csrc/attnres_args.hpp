@@ -61,4 +61,40 @@ struct FinArgs {
   void* dow;
 };
 
+// Multi-query read: queries per launch group (the largest instantiated MQ).
+constexpr int kMaxGroupQueries = 4;
+
+struct MultiFwdArgs {
+  const void* src[kMaxSources];
+  int64_t row_stride;
+  int64_t N;
+  int S, D, R, lo, M;            // M <= MQ: queries of this group
+  float eps, scale, inv_R;
+  const void* query;             // [M, R] rows of this group (row stride R)
+  void* y;                       // output of query 0 of the group, token 0
+  int64_t y_sm, y_sn;            // element strides between queries / tokens
+  float* lse;
+  int64_t l_sm, l_sn;
+  uint32_t* ticket;              // dynamic token counter, zero at launch (nullptr: static split)
+  int64_t tpt;                   // tokens per ticket
+};
+
+struct MultiBwdArgs {
+  const void* src[kMaxSources];
+  void* dsrc[kMaxSources];
+  int64_t row_stride, drow_stride;
+  int64_t N;
+  int S, D, R, lo, M;
+  float eps, scale, inv_R;
+  const void* query;             // [M, R]
+  const float* lse;              // of query 0 of the group
+  int64_t l_sm, l_sn;
+  const void* dout;              // dY of query 0 of the group, token 0
+  int64_t g_sm, g_sn;
+  float* part;                   // [gridDim.x, Mtot * R] partial du rows; this group's columns
+  int64_t part_stride;           //   start at part, row stride part_stride floats
+  uint32_t* ticket;
+  int64_t tpt;
+};
+
 }  // namespace attnres

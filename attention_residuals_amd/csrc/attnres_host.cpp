@@ -607,3 +607,371 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
 }
 
 }  // extern "C"
+
+// ====================================================================== multi-query read
+
+namespace {
+
+constexpr int kMaxQueries = 16;
+
+struct MultiShape {
+  Shape base;     // dtype facts (bf16, esz, vec) for the shared argument checks
+  int ch = 0, W = 0, threads = 0, sb = 0;
+  bool full = false;
+  int mq_max = 2;  // queries per launch group (see make_multi_shape)
+};
+
+struct Group {
+  int m0, cnt, mq;  // queries m0 .. m0 + cnt - 1, served by the MQ = mq kernel
+};
+
+attnres_desc single_desc(const attnres_multi_desc* m) {
+  attnres_desc d;
+  std::memset(&d, 0, sizeof d);
+  d.S = m->S;
+  d.D = m->D;
+  d.R = m->R;
+  d.dtype = m->dtype;
+  d.N = m->N;
+  d.eps = m->eps;
+  d.scale = m->scale;
+  d.deterministic = m->deterministic;
+  d.accumulate_dvalues = m->accumulate_dvalues;
+  return d;
+}
+
+// The multi-query kernels keep a token's S rows in VGPRs with workgroups of up to 8 waves and the
+// fewest chunks per thread that allow it (registers also hold the group's query slices and sums).
+attnres_status make_multi_shape(const attnres_multi_desc* m, MultiShape* ms) {
+  if (!m) return fail(ATTNRES_ERR_INVALID_ARG, "desc is NULL");
+  const attnres_desc d = single_desc(m);
+  attnres_status st = check_desc(&d);
+  if (st != ATTNRES_OK) return st;
+  if (m->M < 1 || m->M > kMaxQueries)
+    return fail(ATTNRES_ERR_INVALID_ARG, "M=%d outside [1, %d]", m->M, kMaxQueries);
+  if (m->layout != ATTNRES_QUERY_MAJOR && m->layout != ATTNRES_TOKEN_MAJOR)
+    return fail(ATTNRES_ERR_INVALID_ARG, "layout %d is neither query- nor token-major", m->layout);
+  ms->base.bf16 = d.dtype == ATTNRES_BF16;
+  ms->base.vec = ms->base.bf16 ? 8 : 4;
+  ms->base.esz = ms->base.bf16 ? 2 : 4;
+  const int chunks = d.D / ms->base.vec;
+  for (int c : {1, 2, 4})
+    if ((chunks + 64 * c - 1) / (64 * c) <= 8) {
+      ms->ch = c;
+      break;
+    }
+  if (!ms->ch) return fail(ATTNRES_ERR_UNSUPPORTED, "D=%d too wide", d.D);
+  ms->W = (chunks + 64 * ms->ch - 1) / (64 * ms->ch);
+  ms->threads = 64 * ms->W;
+  ms->full = d.R == d.D;
+  const int* b = ms->ch == 1 ? kSbCh1 : ms->ch == 2 ? kSbCh2 : kSbCh4;
+  const int nb = ms->ch == 1 ? (int)(sizeof kSbCh1 / sizeof(int))
+                 : ms->ch == 2 ? (int)(sizeof kSbCh2 / sizeof(int))
+                               : (int)(sizeof kSbCh4 / sizeof(int));
+  ms->sb = bucket_at_least(d.S, b, nb);
+  if (ms->sb <= 0)
+    return fail(ATTNRES_ERR_UNSUPPORTED,
+                "the multi-query read keeps a token's rows on chip: S=%d sources of D=%d is too "
+                "many (at most %d)", d.S, d.D, b[nb - 1]);
+  // Four queries share one launch with one chunk per thread and at most 12 sources (fewer passes
+  // over the sources and, for M > 4, fewer intermediate roundings of dvalues); groups that also
+  // hold the existing gradient rows spill a few registers there. Otherwise groups of two.
+  ms->mq_max = (ms->ch == 1 && ms->sb <= 12) ? kMaxGroupQueries : 2;
+  return ATTNRES_OK;
+}
+
+std::vector<Group> plan_groups(const attnres_multi_desc* m, const MultiShape& ms) {
+  std::vector<Group> g;
+  for (int m0 = 0; m0 < m->M;) {
+    const int cnt = std::min(m->M - m0, ms.mq_max);
+    g.push_back(Group{m0, cnt, cnt <= 2 ? 2 : 4});
+    m0 += cnt;
+  }
+  return g;
+}
+
+size_t multi_fwd_lds(const MultiShape& ms, int mq) {
+  return 2u * (size_t)(1 + mq) * ms.sb * (4u * ms.W) * sizeof(float) + 4 * sizeof(float);
+}
+size_t multi_bwd_lds(const MultiShape& ms, int mq) {
+  return 2u * (size_t)(1 + 2 * mq) * ms.sb * (4u * ms.W) * sizeof(float) + 4 * sizeof(float);
+}
+
+const void* multi_bwd_ptr(const MultiShape& ms, int mq, bool acc) {
+  if (acc)
+    return ms.base.bf16 ? multi_bwd_kernel_ptr_acc_bf16(ms.ch, ms.sb, ms.full, mq)
+                        : multi_bwd_kernel_ptr_acc_f32(ms.ch, ms.sb, ms.full, mq);
+  return ms.base.bf16 ? multi_bwd_kernel_ptr_bf16(ms.ch, ms.sb, ms.full, mq)
+                      : multi_bwd_kernel_ptr_f32(ms.ch, ms.sb, ms.full, mq);
+}
+
+// Element strides of y / dout rows and of lse between queries and between tokens.
+void multi_strides(const attnres_multi_desc* m, int64_t* row_sm, int64_t* row_sn, int64_t* l_sm,
+                   int64_t* l_sn) {
+  if (m->layout == ATTNRES_QUERY_MAJOR) {
+    *row_sm = m->N * (int64_t)m->D;
+    *row_sn = m->D;
+    *l_sm = m->N;
+    *l_sn = 1;
+  } else {
+    *row_sm = m->D;
+    *row_sn = (int64_t)m->M * m->D;
+    *l_sm = 1;
+    *l_sn = m->M;
+  }
+}
+
+// A single query is the single-query read without a key-norm weight: its resident kernels serve it.
+bool single_query_fast_path(const attnres_multi_desc* m, attnres_desc* d) {
+  if (m->M != 1) return false;
+  *d = single_desc(m);
+  Shape sh;
+  if (make_shape(d, &sh) != ATTNRES_OK) return false;
+  g_err.clear();
+  return sh.resident;
+}
+
+struct MultiBwdPlan {
+  int P = 0;
+  size_t off_part = 256, bytes = 256;
+};
+
+attnres_status plan_multi_bwd(const attnres_multi_desc* m, const MultiShape& ms,
+                              MultiBwdPlan* pl) {
+  const std::vector<Group> groups = plan_groups(m, ms);
+  const void* fn = multi_bwd_ptr(ms, groups[0].mq, m->accumulate_dvalues != 0);
+  if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no multi-query backward kernel for this shape");
+  DevFacts f;
+  attnres_status st = device_facts(&f);
+  if (st != ATTNRES_OK) return st;
+  int per_cu = 0;
+  st = blocks_per_cu(fn, ms.threads, multi_bwd_lds(ms, groups[0].mq), &per_cu, 8);
+  if (st != ATTNRES_OK) return st;
+  pl->P = (int)std::min<int64_t>(m->N, (int64_t)f.cus * per_cu);
+  pl->off_part = 256;
+  pl->bytes = align256(pl->off_part + (size_t)pl->P * m->M * m->R * sizeof(float));
+  return ATTNRES_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attnres_status attnres_multi_fwd_workspace_bytes(const attnres_multi_desc* m, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(ATTNRES_ERR_INVALID_ARG, "bytes is NULL");
+  MultiShape ms;
+  attnres_status st = make_multi_shape(m, &ms);
+  if (st != ATTNRES_OK) return st;
+  *bytes = kFwdWorkspaceBytes;
+  return ATTNRES_OK;
+}
+
+attnres_status attnres_multi_workspace_bytes(const attnres_multi_desc* m, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(ATTNRES_ERR_INVALID_ARG, "bytes is NULL");
+  MultiShape ms;
+  attnres_status st = make_multi_shape(m, &ms);
+  if (st != ATTNRES_OK) return st;
+  attnres_desc d;
+  if (single_query_fast_path(m, &d)) return attnres_workspace_bytes(&d, bytes);
+  MultiBwdPlan pl;
+  if ((st = plan_multi_bwd(m, ms, &pl)) != ATTNRES_OK) return st;
+  *bytes = pl.bytes;
+  return ATTNRES_OK;
+}
+
+attnres_status attnres_multi_fwd(const attnres_multi_desc* m, const attnres_sources* values,
+                                 const void* queries, void* y, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  MultiShape ms;
+  attnres_status st = make_multi_shape(m, &ms);
+  if (st != ATTNRES_OK) return st;
+  if (workspace && (workspace_bytes < kFwdWorkspaceBytes || !aligned(workspace, 256)))
+    return fail(ATTNRES_ERR_WORKSPACE, "forward workspace: %zu bytes given, %zu (256-byte aligned) "
+                "needed", workspace_bytes, kFwdWorkspaceBytes);
+  if (!workspace && workspace_bytes)
+    return fail(ATTNRES_ERR_WORKSPACE, "forward workspace is NULL but workspace_bytes = %zu",
+                workspace_bytes);
+  const attnres_desc d = single_desc(m);
+  if ((st = check_param(queries, true, ms.base.esz, "queries")) != ATTNRES_OK) return st;
+  if (m->N == 0) return ATTNRES_OK;
+  MultiFwdArgs a;
+  std::memset(&a, 0, sizeof a);
+  if ((st = check_sources(&d, ms.base, values, "values", a.src)) != ATTNRES_OK) return st;
+  if (!y || !aligned(y, 16))
+    return fail(y ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "y NULL or misaligned");
+  if (!lse || !aligned(lse, 4))
+    return fail(lse ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "lse NULL or misaligned");
+  const int64_t N = m->N, M = m->M;
+  std::vector<Range> ins, outs;
+  for (int s = 0; s < m->S; ++s)
+    ins.push_back(rows_range(a.src[s], N, values->row_stride, m->D, ms.base.esz, "values"));
+  ins.push_back(rows_range(queries, M, m->R, m->R, ms.base.esz, "queries"));
+  outs.push_back(rows_range(y, M * N, m->D, m->D, ms.base.esz, "y"));
+  outs.push_back(rows_range(lse, M * N, 1, 1, 4, "lse"));
+  if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
+
+  attnres_desc d1;
+  if (single_query_fast_path(m, &d1))
+    return attnres_fwd(&d1, values, queries, nullptr, nullptr, y, lse, nullptr, nullptr, workspace,
+                       workspace_bytes, stream);
+
+  DevFacts f;
+  if ((st = device_facts(&f)) != ATTNRES_OK) return st;
+  int64_t y_sm, y_sn, l_sm, l_sn;
+  multi_strides(m, &y_sm, &y_sn, &l_sm, &l_sn);
+  a.row_stride = values->row_stride;
+  a.N = N;
+  a.S = m->S;
+  a.D = m->D;
+  a.R = m->R;
+  a.lo = m->D - m->R;
+  a.eps = m->eps;
+  a.scale = m->scale;
+  a.inv_R = 1.0f / (float)m->R;
+  a.y_sm = y_sm;
+  a.y_sn = y_sn;
+  a.l_sm = l_sm;
+  a.l_sn = l_sn;
+  for (const Group& g : plan_groups(m, ms)) {
+    const void* fn = multi_fwd_kernel_ptr(ms.base.bf16, ms.ch, ms.sb, ms.full, g.mq);
+    if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no multi-query forward kernel for this shape");
+    const size_t lds = multi_fwd_lds(ms, g.mq);
+    int per_cu = 0;
+    if ((st = blocks_per_cu(fn, ms.threads, lds, &per_cu, 8)) != ATTNRES_OK) return st;
+    const int64_t resident = (int64_t)f.cus * per_cu;
+    const bool dyn = workspace != nullptr && N >= 2 * resident && N < kMaxTicketTokens;
+    const int64_t slots = resident * (dyn ? 1 : 8);
+    a.tpt = dyn ? tokens_per_ticket(N, slots, (double)(m->S + g.mq) * m->D * ms.base.esz, 55.0, 1)
+                : 1;
+    a.ticket = nullptr;
+    if (dyn) {
+      a.ticket = static_cast<uint32_t*>(workspace);
+      void* targ = a.ticket;
+      st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");
+      if (st != ATTNRES_OK) return st;
+    }
+    a.M = g.cnt;
+    a.query = static_cast<const char*>(queries) + (int64_t)g.m0 * m->R * ms.base.esz;
+    a.y = static_cast<char*>(y) + g.m0 * y_sm * ms.base.esz;
+    a.lse = lse + g.m0 * l_sm;
+    const int grid = (int)std::min<int64_t>((N + a.tpt - 1) / a.tpt, slots);
+    st = launch(fn, grid, 1, ms.threads, lds, &a, stream, "multi-query forward launch");
+    if (st != ATTNRES_OK) return st;
+  }
+  return ATTNRES_OK;
+}
+
+attnres_status attnres_multi_bwd(const attnres_multi_desc* m, const attnres_sources* values,
+                                 const void* queries, const float* lse, const void* dout,
+                                 const attnres_sources* dvalues, void* dq, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  MultiShape ms;
+  attnres_status st = make_multi_shape(m, &ms);
+  if (st != ATTNRES_OK) return st;
+  const attnres_desc d = single_desc(m);
+  const int64_t N = m->N, M = m->M;
+  MultiBwdArgs a;
+  std::memset(&a, 0, sizeof a);
+  const void* dptr[kMaxSources] = {nullptr};
+  if ((st = check_param(queries, true, ms.base.esz, "queries")) != ATTNRES_OK) return st;
+  if ((st = check_param(dq, true, ms.base.esz, "dq")) != ATTNRES_OK) return st;
+  if (N > 0) {
+    if ((st = check_sources(&d, ms.base, values, "values", a.src)) != ATTNRES_OK) return st;
+    if ((st = check_sources(&d, ms.base, dvalues, "dvalues", dptr)) != ATTNRES_OK) return st;
+    if (!lse || !aligned(lse, 4))
+      return fail(lse ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "lse NULL or misaligned");
+    if (!dout || !aligned(dout, 16))
+      return fail(dout ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "dout NULL or misaligned");
+  }
+  if (!workspace) return fail(ATTNRES_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(ATTNRES_ERR_ALIGNMENT, "workspace not 256-byte aligned");
+  std::vector<Range> ins, outs;
+  if (N > 0) {
+    for (int s = 0; s < m->S; ++s)
+      ins.push_back(rows_range(a.src[s], N, values->row_stride, m->D, ms.base.esz, "values"));
+    ins.push_back(rows_range(dout, M * N, m->D, m->D, ms.base.esz, "dout"));
+    ins.push_back(rows_range(lse, M * N, 1, 1, 4, "lse"));
+    for (int s = 0; s < m->S; ++s)
+      outs.push_back(rows_range(dptr[s], N, dvalues->row_stride, m->D, ms.base.esz, "dvalues"));
+  }
+  ins.push_back(rows_range(queries, M, m->R, m->R, ms.base.esz, "queries"));
+  outs.push_back(rows_range(dq, M, m->R, m->R, ms.base.esz, "dq"));
+  if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
+
+  attnres_desc d1;
+  if (single_query_fast_path(m, &d1))
+    return attnres_bwd(&d1, values, queries, nullptr, nullptr, lse, nullptr, nullptr, dout, m->D,
+                       dvalues, dq, nullptr, nullptr, workspace, workspace_bytes, stream);
+
+  MultiBwdPlan pl;
+  if ((st = plan_multi_bwd(m, ms, &pl)) != ATTNRES_OK) return st;
+  if (workspace_bytes < pl.bytes)
+    return fail(ATTNRES_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                pl.bytes);
+  char* ws = static_cast<char*>(workspace);
+  if (pl.P > 0) {
+    int64_t g_sm, g_sn, l_sm, l_sn;
+    multi_strides(m, &g_sm, &g_sn, &l_sm, &l_sn);
+    for (int s = 0; s < m->S; ++s) a.dsrc[s] = const_cast<void*>(dptr[s]);
+    a.row_stride = values->row_stride;
+    a.drow_stride = dvalues->row_stride;
+    a.N = N;
+    a.S = m->S;
+    a.D = m->D;
+    a.R = m->R;
+    a.lo = m->D - m->R;
+    a.eps = m->eps;
+    a.scale = m->scale;
+    a.inv_R = 1.0f / (float)m->R;
+    a.l_sm = l_sm;
+    a.l_sn = l_sn;
+    a.g_sm = g_sm;
+    a.g_sn = g_sn;
+    a.part_stride = M * m->R;
+    const std::vector<Group> groups = plan_groups(m, ms);
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const Group& g = groups[gi];
+      // later groups add to the gradient rows the first group wrote
+      const bool acc = m->accumulate_dvalues != 0 || gi > 0;
+      const void* fn = multi_bwd_ptr(ms, g.mq, acc);
+      if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no multi-query backward kernel for this shape");
+      a.tpt = 1;
+      a.ticket = nullptr;
+      if (!m->deterministic && N >= 2 * (int64_t)pl.P && N < kMaxTicketTokens) {
+        a.tpt = tokens_per_ticket(N, pl.P,
+                                  (double)((acc ? 3 : 2) * m->S + g.mq) * m->D * ms.base.esz,
+                                  30.0, 16);
+        a.ticket = reinterpret_cast<uint32_t*>(ws);
+        void* targ = a.ticket;
+        st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");
+        if (st != ATTNRES_OK) return st;
+      }
+      a.M = g.cnt;
+      a.query = static_cast<const char*>(queries) + (int64_t)g.m0 * m->R * ms.base.esz;
+      a.lse = lse + g.m0 * l_sm;
+      a.dout = static_cast<const char*>(dout) + g.m0 * g_sm * ms.base.esz;
+      a.part = reinterpret_cast<float*>(ws + pl.off_part) + (int64_t)g.m0 * m->R;
+      st = launch(fn, pl.P, 1, ms.threads, multi_bwd_lds(ms, g.mq), &a, stream,
+                  "multi-query backward launch");
+      if (st != ATTNRES_OK) return st;
+    }
+  }
+  // dq [M, R]: the partial rows are [P, M * R]; the finaliser sums them as one long row
+  FinArgs fa;
+  std::memset(&fa, 0, sizeof fa);
+  fa.part_du = reinterpret_cast<const float*>(ws + pl.off_part);
+  fa.P = pl.P;
+  fa.R = (int)(M * m->R);
+  fa.D = 0;
+  fa.cols = (int)(M * m->R);
+  fa.query = queries;
+  fa.dq = dq;
+  return launch(finalize_kernel_ptr(ms.base.bf16), (fa.cols + kFinCols - 1) / kFinCols, 1,
+                kFinCols * kFinPhases, 0, &fa, stream, "finalize launch");
+}
+
+}  // extern "C"

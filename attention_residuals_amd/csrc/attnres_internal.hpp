@@ -43,6 +43,11 @@ const void* bwd_resident_acc_kernel_ptr_bf16(int ch, int sb, bool full);
 const void* bwd_resident_acc_kernel_ptr_f32(int ch, int sb, bool full);
 const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full, bool acc);
 const void* finalize_kernel_ptr(bool bf16);
+const void* multi_fwd_kernel_ptr(bool bf16, int ch, int sb, bool full, int mq);
+const void* multi_bwd_kernel_ptr_bf16(int ch, int sb, bool full, int mq);
+const void* multi_bwd_kernel_ptr_f32(int ch, int sb, bool full, int mq);
+const void* multi_bwd_kernel_ptr_acc_bf16(int ch, int sb, bool full, int mq);
+const void* multi_bwd_kernel_ptr_acc_f32(int ch, int sb, bool full, int mq);
 const void* ticket_reset_kernel_ptr();
 
 }  // namespace attnres

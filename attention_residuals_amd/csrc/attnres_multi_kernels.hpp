@@ -1,0 +1,437 @@
+// attnres_multi_kernels.hpp -- gfx950 kernels of the multi-query AttnRes read.
+//
+// "Fast Attention Residuals" PyPI page, section "Multi-query AttnRes": M queries q_m read the same
+// S sources; each has its own routing weights p_{m,s} = softmax_s(scale * <t_s / r_s, q_m>) and
+// its own full-width output y_m = sum_s p_{m,s} v_s. The keys t_s / r_s are shared. No key-norm
+// weight and no output norm (the page's operator as written).
+//
+// One launch serves a group of MQ <= 4 queries (the host runs larger M as several groups). The
+// structure is the single-query resident path's: a workgroup holds a token's S rows in VGPRs, one
+// exchange per token reduces all per-source sums (1 + MQ in the forward, 1 + 2 MQ in the backward),
+// lane s finishes source s, and tokens come from the same batched ticket schedule with the next
+// token's rows prefetched as the current ones are consumed. The group's query slices sit in VGPRs
+// for the whole kernel (zero outside the key slice, so <t, q> needs no mask).
+//
+// Backward, per token, with dz_{m,s} = p_{m,s} (<dY_m, v_s> - delta_m), delta_m = sum_s p dp:
+//   a_{m,s} = scale dz_{m,s} / r_s,   B_s = -sum_m a_{m,s} c_{m,s} / (R r_s^2)   (c = <t_s, q_m>)
+//   dV_s = sum_m p_{m,s} dY_m + sum_m a_{m,s} q_m + B_s t_s   (q, t zero outside the slice)
+//   du_m += sum_s a_{m,s} t_s   ->  dq_m (summed over tokens by the finaliser).
+#pragma once
+
+#include "attnres_kernels.hpp"
+
+namespace attnres {
+
+// A thread's columns and the group's query slices (zero outside the slice and past D).
+template <bool BF16, int CH, bool FULL, int MQ>
+struct MultiCols {
+  static constexpr int VEC = Fmt<BF16>::VEC;
+  static constexpr int ESZ = Fmt<BF16>::ESZ;
+  int col0[CH];
+  uint32_t voff[CH];
+  uint32_t mk[CH][4];  // bf16, R < D: per-half mask of the key slice
+  Chunk q[MQ][CH];     // storage-format query values at this thread's columns
+
+  __device__ __forceinline__ void init(int tid, int nthr, int D, int lo, int M,
+                                       const void* query, int R) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      col0[j] = (tid + j * nthr) * VEC;
+      voff[j] = static_cast<uint32_t>(col0[j] * ESZ);
+      const bool valid = col0[j] < D;
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) {
+        float v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int idx = col0[j] + e - lo;
+          v[e] = (valid && m < M && idx >= 0)
+                     ? load_param<BF16>(static_cast<const char*>(query) + (int64_t)m * R * ESZ, idx)
+                     : 0.f;
+        }
+        q[m][j] = pack<BF16>(v);  // exact: the values came from this format
+      }
+      if constexpr (BF16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const bool in0 = col0[j] + 2 * k >= lo, in1 = col0[j] + 2 * k + 1 >= lo;
+          mk[j][k] = (in0 ? 0x0000ffffu : 0u) | (in1 ? 0xffff0000u : 0u);
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ bool in_slice(int j, int e, int lo) const {
+    return FULL || col0[j] + e >= lo;
+  }
+};
+
+// Sum of t^2 over the slice for one row (this thread's chunks).
+template <bool BF16, int CH, bool FULL, int MQ>
+__device__ __forceinline__ float slice_sumsq(const Chunk (&r)[CH],
+                                             const MultiCols<BF16, CH, FULL, MQ>& cs, int lo) {
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    if constexpr (BF16) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t pm = FULL ? r[j].w[k] : (r[j].w[k] & cs.mk[j][k]);
+        ss = dot2(pm, pm, ss);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = elem<false>(r[j], e);
+        const float tm = cs.in_slice(j, e, lo) ? t : 0.f;
+        ss = fmaf(tm, tm, ss);
+      }
+    }
+  }
+  return ss;
+}
+
+// Multi-query forward: all S <= SB sources of a token in one block.
+template <bool BF16, int CH, int SB, bool FULL, int MQ>
+__global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
+  constexpr int VEC = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  constexpr int NV = 1 + MQ;  // per source: sum t^2, then <t, q_m>
+  constexpr int K = NV * SB;
+  extern __shared__ float lds[];
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
+  const int R4 = nthr >> 4;
+  const int xfl = K * R4;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.D * ESZ);
+
+  MultiCols<BF16, CH, FULL, MQ> cs;
+  cs.init(tid, nthr, a.D, a.lo, a.M, a.query, a.R);
+  int buf = 0;
+  Chunk rows[SB][CH];
+
+  // token schedule: batches of B tokens, later batches from the counter (as the single-query
+  // kernels: the ticket is taken at the top of a batch's last token and published through LDS at
+  // that token's exchange barrier)
+  const bool dyn = a.ticket != nullptr;
+  const int64_t B = dyn ? a.tpt : 1;
+  const int64_t n0 = (int64_t)blockIdx.x * B;
+  {
+    const int live = n0 < a.N ? a.S : 0;
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const Rsrc r = src_rsrc(a.src[i], i, live, n0 * a.row_stride * ESZ, row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dropped stores matching the output rows the loop body stores after its last row load
+    const Rsrc none = row_rsrc(nullptr, 0, 0u);
+    const Chunk zero = {};
+#pragma unroll
+    for (int m = 0; m < MQ; ++m)
+#pragma unroll
+      for (int j = 0; j < CH; ++j) st_row(none, cs.voff[j], zero);
+  }
+
+  uint32_t* tslot = reinterpret_cast<uint32_t*>(lds + 2 * xfl);
+  int64_t n = n0, batch_end = n0 + B;
+  while (n < a.N) {
+    const bool take = dyn && n + 1 >= batch_end;
+    uint32_t tk = 0;
+    if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
+    int64_t next = dyn ? n + 1 : n + gridDim.x;
+
+    float* xb = lds + buf * xfl;
+#pragma unroll
+    for (int i0 = 0; i0 < SB; i0 += kGroup) {
+      float part[NV][kGroup];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) part[v][g] = 0.f;
+        if (i0 + g < SB) {
+          part[0][g] = slice_sumsq<BF16, CH, FULL, MQ>(rows[i0 + g], cs, a.lo);
+#pragma unroll
+          for (int m = 0; m < MQ; ++m) part[1 + m][g] = dot_rows<BF16, CH>(rows[i0 + g], cs.q[m]);
+        }
+      }
+      xchg_group<NV, SB>(part, i0, xb, R4, tid);
+    }
+    if (take && tid == 0) tslot[buf] = tk;
+    __syncthreads();
+    if (take) {
+      next = ((int64_t)gridDim.x + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf])) * B;
+      batch_end = next + B;
+    }
+    buf ^= 1;
+
+    // lane s finishes source s for every query of the group
+    float pw[MQ], lse[MQ];
+    {
+      float ss = 0.f;
+      if (lane < a.S) ss = xchg_total(xb, lane, R4);
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) {
+        float z = -INFINITY;
+        if (lane < a.S) {
+          const float c = xchg_total(xb, (1 + m) * SB + lane, R4);
+          z = source_score(ss, c, a.inv_R, a.eps, a.scale).z;
+        }
+        const float mx = wave_max(z);
+        const float ez = (lane < a.S) ? expf(z - mx) : 0.f;
+        const float l = wave_sum(ez);
+        pw[m] = ez / l;
+        lse[m] = mx + logf(l);
+      }
+    }
+
+    float acc[MQ][CH][VEC];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m)
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[m][j][e] = 0.f;
+    const int64_t next_byte = next * a.row_stride * ESZ;
+    const int live_next = next < a.N ? a.S : 0;
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      float pi[MQ];
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) pi[m] = bcast(pw[m], i);
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float v = elem<BF16>(rows[i][j], e);
+#pragma unroll
+          for (int m = 0; m < MQ; ++m) acc[m][j][e] = fmaf(pi[m], v, acc[m][j][e]);
+        }
+      // the next token's row i (an empty resource past the last token)
+      const Rsrc r = src_rsrc(a.src[i], i, live_next, next_byte, row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+    }
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      // queries past the group's count store through an empty resource (dropped)
+      const Rsrc ry = src_rsrc(a.y, m, a.M, (m * a.y_sm + n * a.y_sn) * ESZ, row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) st_row(ry, cs.voff[j], pack<BF16>(acc[m][j]));
+    }
+    if (tid < MQ && tid < a.M) {
+      float v = lse[0];
+#pragma unroll
+      for (int m = 1; m < MQ; ++m) v = (tid == m) ? lse[m] : v;
+      a.lse[tid * a.l_sm + n * a.l_sn] = v;
+    }
+    n = next;
+  }
+}
+
+// Multi-query backward, token-resident. ACC: dvalues accumulate (existing rows prefetched one
+// token ahead like the source rows).
+template <bool BF16, int CH, int SB, bool FULL, int MQ, bool ACC>
+__global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
+  constexpr int VEC = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+  constexpr int NV = 1 + 2 * MQ;  // per source: sum t^2, <t, q_m>, <dY_m, v>
+  constexpr int K = NV * SB;
+  extern __shared__ float lds[];
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
+  const int R4 = nthr >> 4;
+  const int xfl = K * R4;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.D * ESZ);
+  const int S = a.S;
+
+  MultiCols<BF16, CH, FULL, MQ> cs;
+  cs.init(tid, nthr, a.D, a.lo, a.M, a.query, a.R);
+  float du[MQ][CH][VEC];
+#pragma unroll
+  for (int m = 0; m < MQ; ++m)
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) du[m][j][e] = 0.f;
+  int buf = 0;
+
+  Chunk rows[SB][CH];
+  Chunk odv[ACC ? SB : 1][CH];
+  Chunk gy[MQ][CH];
+  const bool dyn = a.ticket != nullptr;
+  const int64_t B = dyn ? a.tpt : 1;
+  const int64_t n0 = (int64_t)blockIdx.x * B;
+  // lse of the current token per query (lane m holds query m); the next token's is loaded with
+  // its rows
+  float lse_l = 0.f;
+  if (lane < a.M && n0 < a.N) lse_l = a.lse[lane * a.l_sm + n0 * a.l_sn];
+  {
+    const int live = n0 < a.N ? S : 0;
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      const Rsrc rg = src_rsrc(a.dout, m, live ? a.M : 0, (m * a.g_sm + n0 * a.g_sn) * ESZ,
+                               row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) gy[m][j] = ld_row(rg, cs.voff[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const Rsrc r = src_rsrc(a.src[i], i, live, n0 * a.row_stride * ESZ, row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+      if constexpr (ACC) {
+        const Rsrc rd = src_rsrc(a.dsrc[i], i, live, n0 * a.drow_stride * ESZ, row_bytes);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) odv[i][j] = ld_row(rd, cs.voff[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  uint32_t* tslot = reinterpret_cast<uint32_t*>(lds + 2 * xfl);
+  int64_t n = n0, batch_end = n0 + B;
+  while (n < a.N) {
+    const bool take = dyn && n + 1 >= batch_end;
+    uint32_t tk = 0;
+    if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
+    float* xb = lds + buf * xfl;
+#pragma unroll
+    for (int i0 = 0; i0 < SB; i0 += kGroup) {
+      float part[NV][kGroup];
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) part[v][g] = 0.f;
+        if (i0 + g < SB) {
+          part[0][g] = slice_sumsq<BF16, CH, FULL, MQ>(rows[i0 + g], cs, a.lo);
+#pragma unroll
+          for (int m = 0; m < MQ; ++m) {
+            part[1 + m][g] = dot_rows<BF16, CH>(rows[i0 + g], cs.q[m]);
+            part[1 + MQ + m][g] = dot_rows<BF16, CH>(rows[i0 + g], gy[m]);
+          }
+        }
+      }
+      xchg_group<NV, SB>(part, i0, xb, R4, tid);
+    }
+    if (take && tid == 0) tslot[buf] = tk;
+    __syncthreads();
+    int64_t next = dyn ? n + 1 : n + gridDim.x;
+    if (take) {
+      next = ((int64_t)gridDim.x + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf])) * B;
+      batch_end = next + B;
+    }
+    const bool has_next = next < a.N;
+    buf ^= 1;
+
+    // lane s finishes source s
+    float pw[MQ], aw[MQ], Bs = 0.f;
+    {
+      float ss = 0.f, rho = 0.f;
+      if (lane < S) ss = xchg_total(xb, lane, R4);
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) {
+        const float lse_m = bcast(lse_l, m);
+        float p = 0.f, dp = 0.f, c = 0.f;
+        if (lane < S) {
+          c = xchg_total(xb, (1 + m) * SB + lane, R4);
+          dp = xchg_total(xb, (1 + MQ + m) * SB + lane, R4);
+          const Score sc = source_score(ss, c, a.inv_R, a.eps, a.scale);
+          rho = sc.rho;
+          p = routing_weight(sc.z, lse_m);
+        }
+        const float delta = wave_sum(p * dp);
+        const float am = a.scale * p * (dp - delta) * rho;
+        Bs -= am * rho * rho * c * a.inv_R;
+        pw[m] = p;
+        aw[m] = am;
+      }
+    }
+    // queries past the group's count have dY = 0 (empty resource) and q = 0, so p dY, a q and
+    // a t all vanish for them: dp = 0 = delta gives a = 0
+
+    float dof[MQ][CH][VEC];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m)
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) dof[m][j][e] = elem<BF16>(gy[m][j], e);
+    const int live_next = has_next ? S : 0;
+    if (lane < a.M && has_next) lse_l = a.lse[lane * a.l_sm + next * a.l_sn];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      // the next token's dY rows (empty resources past the last token or the group's count)
+      const Rsrc rg = src_rsrc(a.dout, m, has_next ? a.M : 0,
+                               (m * a.g_sm + next * a.g_sn) * ESZ, row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) gy[m][j] = ld_row(rg, cs.voff[j]);
+    }
+    const int64_t drow_byte = n * a.drow_stride * ESZ;
+    const int64_t next_byte = next * a.row_stride * ESZ;
+    const int64_t next_dbyte = next * a.drow_stride * ESZ;
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      float pi[MQ], ai[MQ];
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) {
+        pi[m] = bcast(pw[m], i);
+        ai[m] = bcast(aw[m], i);
+      }
+      const float bi = bcast(Bs, i);
+      Chunk out[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        float dv[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float tm;
+          if constexpr (BF16) {
+            const uint32_t w = FULL ? rows[i][j].w[e >> 1] : (rows[i][j].w[e >> 1] & cs.mk[j][e >> 1]);
+            tm = (e & 1) ? hi_f(w) : lo_f(w);
+          } else {
+            const float t = elem<false>(rows[i][j], e);
+            tm = cs.in_slice(j, e, a.lo) ? t : 0.f;
+          }
+          float d = bi * tm;
+#pragma unroll
+          for (int m = 0; m < MQ; ++m) {
+            d = fmaf(pi[m], dof[m][j][e], d);
+            d = fmaf(ai[m], elem<BF16>(cs.q[m][j], e), d);
+            du[m][j][e] = fmaf(ai[m], tm, du[m][j][e]);
+          }
+          if constexpr (ACC) d += elem<BF16>(odv[i][j], e);
+          dv[e] = d;
+        }
+        out[j] = pack<BF16>(dv);
+      }
+      const Rsrc rd = src_rsrc(a.dsrc[i], i, S, drow_byte, row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) st_row(rd, cs.voff[j], out[j]);
+      const Rsrc r = src_rsrc(a.src[i], i, live_next, next_byte, row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+      if constexpr (ACC) {
+        const Rsrc rn = src_rsrc(a.dsrc[i], i, live_next, next_dbyte, row_bytes);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) odv[i][j] = ld_row(rn, cs.voff[j]);
+      }
+    }
+    n = next;
+  }
+
+  // this workgroup's partial du rows of the group's queries (slice columns only)
+  float* prow = a.part + (int64_t)blockIdx.x * a.part_stride;
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) {
+    if (m >= a.M) break;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const int col = cs.col0[j] + e;
+        if (col < a.D && col >= a.lo) prow[m * a.R + (col - a.lo)] = du[m][j][e];
+      }
+  }
+}
+
+}  // namespace attnres

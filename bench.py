@@ -69,6 +69,11 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--accumulate", action="store_true",
                     help="the backward adds into existing dvalues (reads them: +S*N*D elements)")
+    ap.add_argument("--queries", type=int, default=0, metavar="M",
+                    help="time the multi-query read with M queries on the workload's sources "
+                         "(no key-norm weight, no output norm)")
+    ap.add_argument("--layout", default="query_major", choices=["query_major", "token_major"],
+                    help="output layout of the multi-query read")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time the oracle baseline repeats its pass for")
     ap.add_argument("--check", type=int, default=1, help="sampled-token parity check (0 = off)")
@@ -101,6 +106,8 @@ def main() -> int:
     w = W.ALL[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.queries:
+        return run_multi(args, w)
     x = W.generate(w, device=dev)
     N, D, S, R = w.N, w.D, w.S, w.R
     desc = A.make_desc(S, N, D, R, w.torch_dtype, eps=w.eps, scale=w.scale,
@@ -225,6 +232,128 @@ def main() -> int:
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "fwd_achieved": round(fwd_bytes / (fwd_avg * 1e-3) / 1e9, 1)},
         "cpu_baseline": cpu,
+        "parity_check": check,
+        "source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _timed(args, fwd, bwd, stream):
+    """Warm-up, then K timed steps with HIP events between the calls (on the launch stream)."""
+    import numpy as np
+    import torch
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        fwd()
+        ev[k][1].record(stream)
+        bwd()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)]))
+    bwd_ms = float(np.mean([ev[k][1].elapsed_time(ev[k][2]) for k in range(args.steps)]))
+    return wall * 1e3 / args.steps, fwd_ms, bwd_ms
+
+
+def run_multi(args, w) -> int:
+    """The multi-query read ("Fast Attention Residuals" page, Multi-query AttnRes) with M queries
+    over the workload's sources; one JSON line like the default mode."""
+    import math
+    import numpy as np
+    import torch
+    import attention_residuals_amd as A
+    import attnres_workloads as W
+
+    dev = "cuda:0"
+    M, S, N, D, R = args.queries, w.S, w.N, w.D, w.R
+    x = W.generate(w, device=dev, with_dout=False)
+    values = x["values"]
+    del x
+    g = torch.Generator(device=dev).manual_seed(w.seed + 100 * M)
+    qs = (torch.randn((M, R), generator=g, device=dev) / math.sqrt(R if w.query_over_rank else D))
+    queries = qs.to(w.torch_dtype)
+    shape = (M, N, D) if args.layout == "query_major" else (N, M, D)
+    dout = torch.randn(shape, generator=g, device=dev).to(w.torch_dtype)
+    desc = A.make_multi_desc(S, N, D, R, M, w.torch_dtype, eps=w.eps, scale=w.scale,
+                             layout=args.layout, accumulate_dvalues=args.accumulate)
+    y = torch.empty(shape, dtype=w.torch_dtype, device=dev)
+    lse = torch.empty(shape[:2], dtype=torch.float32, device=dev)
+    dv = (torch.zeros if args.accumulate else torch.empty)((S, N, D), dtype=w.torch_dtype,
+                                                           device=dev)
+    dq = torch.empty((M, R), dtype=w.torch_dtype, device=dev)
+    ws = torch.empty((max(A.multi_workspace_bytes(desc), 256),), dtype=torch.uint8, device=dev)
+    fws = torch.empty((A.multi_fwd_workspace_bytes(desc),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        A.attnres_multi_fwd(values, queries, eps=w.eps, scale=w.scale, layout=args.layout,
+                            out=y, lse=lse, workspace=fws, stream=stream)
+
+    def bwd():
+        A.attnres_multi_bwd(values, queries, lse, dout, eps=w.eps, scale=w.scale,
+                            layout=args.layout, accumulate=args.accumulate, dvalues=dv, dq=dq,
+                            workspace=ws, stream=stream)
+
+    ms, fwd_ms, bwd_ms = _timed(args, fwd, bwd, stream)
+    b = w.elem_bytes
+    acc = S * N * D * b if args.accumulate else 0
+    fwd_bytes = (S + M) * N * D * b + 4 * M * N
+    bwd_bytes = (2 * S + M) * N * D * b + 4 * M * N + acc
+    algo = fwd_bytes + bwd_bytes
+    value = algo / (ms * 1e-3) / 1e9
+
+    check = None
+    if args.check:
+        if args.accumulate:
+            dv.zero_()
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
+        import oracle
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from parity import compare_rows, compare_stat, sample_tokens
+        toks = sample_tokens(N, 6, seed=7)
+        sel = torch.tensor(toks, device=dev)
+        gq = dout if args.layout == "query_major" else dout.transpose(0, 1)
+        yq = y if args.layout == "query_major" else y.transpose(0, 1)
+        lq = lse if args.layout == "query_major" else lse.transpose(0, 1)
+        ref = oracle.run_multi(values.index_select(1, sel).cpu(), queries.cpu(),
+                               gq.index_select(1, sel).cpu(), eps=w.eps, scale=w.scale,
+                               reduce=False)
+        f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
+        groups = -(-M // (4 if (D // (8 if w.dtype == "bf16" else 4) <= 512 and S <= 12) else 2))
+        res = {"y": compare_rows(f64(yq.index_select(1, sel)).reshape(-1, D),
+                                 ref["y"].reshape(-1, D), w.dtype),
+               "lse": compare_stat(f64(lq.index_select(1, sel)), ref["lse"]),
+               "dvalues": compare_rows(f64(dv.index_select(1, sel)), ref["dvalues"], w.dtype,
+                                       roundings=groups)}
+        check = {k: {"metric": v["metric"], "ok": bool(v["ok"])} for k, v in res.items()}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}_multi_m{M}_{args.layout}", "S": S, "N": N, "D": D,
+                   "R": R, "M": M, "layout": args.layout, "accumulate_dvalues": args.accumulate,
+                   "algorithmic_bytes": algo,
+                   "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 1),
+                   "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4)},
+        "roofline": {"bound": "hbm", "kernel": "attnres_multi_bwd (backward kernels + finaliser)",
+                     "achieved": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "traffic": None,
+                     "fwd_achieved": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1)},
+        "cpu_baseline": None,
         "parity_check": check,
         "source_hash": kernel_source_hash(),
     }

@@ -138,6 +138,51 @@ attnres_status attnres_bwd(const attnres_desc* desc, const attnres_sources* valu
                            void* dq, void* dw, void* dow,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- multi-query read
+ * "Fast Attention Residuals" PyPI page, section "Multi-query AttnRes": M queries q_m (1 <= M <= 16)
+ * read the same S sources; each has its own routing weights
+ * p_{m,s} = softmax_s(scale * <t_s / r_s, q_m>) and its own full-width output
+ * y_m = sum_s p_{m,s} v_s (t_s, r_s as in the single-query read). The operator is the page's as
+ * written: no key-norm weight and no output norm. The backward returns dvalues summed over the
+ * queries and dq [M, R], each row summed over all tokens.
+ * Token-resident only: a token's S rows must fit on chip (attnres_multi_*_workspace_bytes and the
+ * entry points return ATTNRES_ERR_UNSUPPORTED otherwise; at D = 4096, bf16, S <= 24). M > 4 runs as
+ * groups of at most four queries, each reading the sources again.
+ * Layout of y, dout [.., D] and lse: ATTNRES_QUERY_MAJOR = [M, N] rows (the page's default),
+ * ATTNRES_TOKEN_MAJOR = [N, M] rows (the page's output_layout="token_major"). */
+typedef enum { ATTNRES_QUERY_MAJOR = 0, ATTNRES_TOKEN_MAJOR = 1 } attnres_layout;
+
+typedef struct {
+  int32_t S, D, R;         /* as in attnres_desc */
+  int32_t M;               /* queries, 1 <= M <= 16 */
+  int32_t dtype;
+  int64_t N;
+  float eps, scale;
+  int32_t layout;          /* attnres_layout of y, dout and lse */
+  int32_t deterministic;   /* as in attnres_desc (backward) */
+  int32_t accumulate_dvalues; /* as in attnres_desc (backward) */
+} attnres_multi_desc;
+
+/* Bytes of the optional forward workspace (a token counter): 256. */
+attnres_status attnres_multi_fwd_workspace_bytes(const attnres_multi_desc* desc, size_t* bytes);
+
+/* Bytes of the backward workspace (a token counter and FP32 partial dq rows). No initialisation
+ * needed. */
+attnres_status attnres_multi_workspace_bytes(const attnres_multi_desc* desc, size_t* bytes);
+
+/* Forward. queries [M, R] contiguous; y [M, N, D] or [N, M, D] contiguous (layout); lse [M, N] or
+ * [N, M] FP32 (written). workspace / workspace_bytes: optional, as for attnres_fwd. */
+attnres_status attnres_multi_fwd(const attnres_multi_desc* desc, const attnres_sources* values,
+                                 const void* queries, void* y, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Backward. lse as written by the forward; dout like y (contiguous, same layout); dvalues as for
+ * attnres_bwd (overwritten, or added to with accumulate_dvalues); dq [M, R] (written). */
+attnres_status attnres_multi_bwd(const attnres_multi_desc* desc, const attnres_sources* values,
+                                 const void* queries, const float* lse, const void* dout,
+                                 const attnres_sources* dvalues, void* dq, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* attnres_status_str(attnres_status status);
 

@@ -8,6 +8,10 @@ Tolerances (written here, applied in every GPU parity test):
     Storing the exactly rounded oracle in bf16 alone already gives max |err| / rms of several
     1e-2 on large-magnitude elements, so the literal bound without the half ulp rejects even the
     correctly rounded answer. The literal ratio is reported alongside.
+  * A bf16 result built by k passes that each round it to storage (the multi-query backward with
+    more than four queries adds every group of queries into dvalues, so dvalues carry one rounding
+    per group) may differ from the reference by k half ulps beyond the bound above: the same
+    reading with half_ulp replaced by k * half_ulp.
   * BF16 dq and dw: relative L2 error ||gpu - ref|| / ||ref|| <= 1e-2.
   * FP32 per-row statistics lse and o_rstd: |gpu - ref| <= 2e-5 * (1 + |ref|).
 rms(x) = sqrt(mean(x^2)) over the whole compared tensor.
@@ -45,8 +49,9 @@ def rms(x: np.ndarray) -> float:
     return float(np.sqrt(np.mean(np.square(x, dtype=np.float64)))) if x.size else 0.0
 
 
-def compare_rows(g: np.ndarray, r: np.ndarray, dtype: str) -> dict:
-    """Element-by-element comparison of a row tensor (y, dvalues, dow)."""
+def compare_rows(g: np.ndarray, r: np.ndarray, dtype: str, roundings: int = 1) -> dict:
+    """Element-by-element comparison of a row tensor (y, dvalues, dow); `roundings` = how many
+    times the result was rounded to bf16 storage on its way (1 for every single pass)."""
     g = np.asarray(g, dtype=np.float64)
     r = np.asarray(r, dtype=np.float64)
     assert g.shape == r.shape, (g.shape, r.shape)
@@ -56,7 +61,7 @@ def compare_rows(g: np.ndarray, r: np.ndarray, dtype: str) -> dict:
     if dtype == "f32":
         return {"literal": literal, "metric": literal, "tol": TOL_F32, "ok": literal <= TOL_F32,
                 "finite": bool(np.isfinite(g).all())}
-    excess = err - half_ulp_bf16(np.maximum(np.abs(g), np.abs(r)))
+    excess = err - roundings * half_ulp_bf16(np.maximum(np.abs(g), np.abs(r)))
     metric = float(max(excess.max(), 0.0) / scale) if scale > 0 else float(max(excess.max(), 0))
     return {"literal": literal, "metric": metric, "tol": TOL_BF16_ROWS,
             "ok": metric <= TOL_BF16_ROWS and bool(np.isfinite(g).all()),

@@ -187,3 +187,27 @@ def test_backward_argument_checks_before_device():
 def test_python_binding_rejects_bad_dtype():
     with pytest.raises(TypeError):
         B.make_desc(2, 4, 64, 64, torch.float16)
+
+
+def _multi_status(**kw):
+    base = dict(S=4, N=16, D=256, R=256, M=2, dtype=torch.bfloat16)
+    base.update(kw)
+    extra = {k: base.pop(k) for k in list(base) if k not in ("S", "N", "D", "R", "M", "dtype")}
+    layout = extra.pop("layout_code", None)
+    d = B.make_multi_desc(base["S"], base["N"], base["D"], base["R"], base["M"], base["dtype"],
+                          **extra)
+    if layout is not None:
+        d.layout = layout
+    n = ctypes.c_size_t(0)
+    return A.load().attnres_multi_fwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), OK), (dict(M=16), OK), (dict(M=0), INVALID), (dict(M=17), INVALID),
+    (dict(layout_code=2), INVALID), (dict(S=0), INVALID), (dict(R=300), INVALID),
+    (dict(S=64, D=8192, R=8192), UNSUPPORTED), (dict(S=24, D=4096, R=4096), OK),
+    (dict(S=25, D=4096, R=4096), UNSUPPORTED), (dict(accumulate_dvalues=True), OK),
+])
+def test_multi_descriptor_validation(kw, expect):
+    st = _multi_status(**kw)
+    assert st == expect, (kw, st, A.load().attnres_last_error())

@@ -1,0 +1,164 @@
+"""GPU parity of the multi-query read ("Fast Attention Residuals" PyPI page, Multi-query AttnRes)
+against the FP64 multi-query oracle, through the C ABI.
+
+Tolerances are the single-query read's (tests/parity.py), applied to every query's output rows,
+to dvalues (summed over the queries), and per query to dq_m (relative L2 for bf16).
+Covered: M = 1 (served by the single-query kernels), 2, 3 (a padded group of four), 4, 5 and 16
+(several groups: later groups accumulate into dvalues), both output layouts, sliced keys, bf16 and
+FP32, accumulation into existing dvalues, the widest rows (two query groups per launch), list
+sources, ragged token counts, determinism and the static schedule, the autograd wrapper, N = 0,
+and the unsupported (non-resident) shapes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (assert_ok, compare_rows, compare_stat, compare_vec, gpu_available, to_f64)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+
+def _inputs(S, N, D, R, M, dtype, seed, device="cpu"):
+    g = torch.Generator(device=device).manual_seed(seed)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    V = torch.empty((S, N, D), dtype=dt, device=device)
+    for s in range(S):
+        V[s].copy_(torch.randn((N, D), generator=g, device=device) * math.sqrt(1.0 + s))
+    Q = (torch.randn((M, R), generator=g, device=device) / math.sqrt(R)).to(dt)
+    G = torch.randn((M, N, D), generator=g, device=device).to(dt)   # query-major dY
+    return V, Q, G
+
+
+def _to_layout(x, layout):
+    """[M, N, ...] query-major -> the layout's order."""
+    return x.contiguous() if layout == "query_major" else x.transpose(0, 1).contiguous()
+
+
+def _from_layout(x, layout):
+    return x if layout == "query_major" else x.transpose(0, 1)
+
+
+def _run(V, Q, G, layout="query_major", dvalues=None, accumulate=False, deterministic=False,
+         dynamic=True, packed=True):
+    import attention_residuals_amd as A
+    vals = V if packed else [V[s] for s in range(V.shape[0])]
+    y, lse = A.attnres_multi_fwd(vals, Q, layout=layout, dynamic=dynamic)
+    dv, dq = A.attnres_multi_bwd(vals, Q, lse, _to_layout(G, layout), layout=layout,
+                                 deterministic=deterministic, accumulate=accumulate,
+                                 dvalues=dvalues)
+    torch.cuda.synchronize()
+    dv = torch.stack(dv) if isinstance(dv, list) else dv
+    return _from_layout(y, layout), _from_layout(lse, layout), dv, dq
+
+
+def _groups(S, D, M, dtype):
+    """Query groups the library runs (one launch each); each after the first adds into dvalues,
+    which then carry one bf16 rounding per group. Four queries share a launch with one 16-byte
+    chunk per thread (D <= 512 chunks of 8 bf16 / 4 f32 at eight waves) and S <= 12."""
+    chunks = D // (8 if dtype == "bf16" else 4)
+    per_launch = 4 if (chunks <= 512 and S <= 12) else 2
+    return -(-M // per_launch)
+
+
+def _check(V, Q, G, label, dtype, init=None, **kw):
+    Vg, Qg, Gg = V.cuda(), Q.cuda(), G.cuda()
+    dvalues = None
+    if init is not None:
+        dvalues = init.cuda()
+        if not kw.get("packed", True):
+            dvalues = [dvalues[s].clone() for s in range(V.shape[0])]
+    y, lse, dv, dq = _run(Vg, Qg, Gg, dvalues=dvalues, **kw)
+    ref = oracle.run_multi(V, Q, G)
+    if init is not None:
+        ref["dvalues"] = ref["dvalues"] + init.double().numpy()
+    M = Q.shape[0]
+    res = {}
+    res["y"] = compare_rows(to_f64(y).reshape(-1, V.shape[2]), ref["y"].reshape(-1, V.shape[2]),
+                            dtype)
+    res["lse"] = compare_stat(to_f64(lse), ref["lse"])
+    S, D = V.shape[0], V.shape[2]
+    res["dvalues"] = compare_rows(to_f64(dv), ref["dvalues"], dtype,
+                                  roundings=_groups(S, D, M, dtype))
+    for m in range(M):
+        res[f"dq{m}"] = compare_vec(to_f64(dq[m]), ref["dq"][m], dtype)
+    assert_ok(res, label)
+    return y, lse, dv, dq
+
+
+@pytest.mark.parametrize("S,N,D,R,M,dtype,layout", [
+    (10, 701, 4096, 4096, 2, "bf16", "query_major"),
+    (8, 513, 2048, 512, 3, "bf16", "token_major"),
+    (6, 257, 1024, 1024, 4, "bf16", "query_major"),
+    (5, 300, 2048, 2048, 5, "bf16", "token_major"),
+    (4, 129, 256, 256, 16, "f32", "query_major"),
+    (5, 333, 1024, 1024, 1, "bf16", "token_major"),
+    (4, 211, 8192, 8192, 4, "bf16", "query_major"),
+    (24, 199, 2048, 640, 2, "bf16", "query_major"),
+    # FP32 with a 3-wide key: the slice gradient's terms scale with <dY, v> ~ sqrt(D) and nearly
+    # cancel, so any FP32 evaluation errs by ~eps32 * sqrt(D) relative to the row's rms (measured:
+    # 1.8e-5 rms at D = 1024, 9.5e-6 at D = 256); D = 64 keeps a margin to the literal 1e-5 bound
+    (3, 97, 64, 3, 3, "f32", "token_major"),
+])
+def test_multi_query_parity(S, N, D, R, M, dtype, layout):
+    V, Q, G = _inputs(S, N, D, R, M, dtype, seed=2000 + S * M + D)
+    print(f"[case] S={S} N={N} D={D} R={R} M={M} {dtype} {layout}", flush=True)
+    _check(V, Q, G, f"multi S={S} N={N} D={D} R={R} M={M} {dtype} {layout}", dtype,
+           layout=layout)
+
+
+@pytest.mark.parametrize("M,packed", [(2, True), (6, False)])
+def test_multi_query_accumulate_into_dvalues(M, packed):
+    S, N, D, R = 6, 301, 2048, 2048
+    V, Q, G = _inputs(S, N, D, R, M, "bf16", seed=2100 + M)
+    init = (2.0 * torch.randn((S, N, D), generator=torch.Generator().manual_seed(5))).to(V.dtype)
+    _check(V, Q, G, f"multi accumulate M={M}", "bf16", init=init, accumulate=True, packed=packed)
+
+
+def test_multi_query_schedules_and_determinism():
+    S, N, D, R, M = 10, 3001, 4096, 4096, 2
+    V, Q, G = (t.cuda() for t in _inputs(S, N, D, R, M, "bf16", seed=2200))
+    det1 = _run(V, Q, G, deterministic=True, dynamic=False)
+    det2 = _run(V, Q, G, deterministic=True, dynamic=False)
+    dyn = _run(V, Q, G)
+    for a, b in zip(det1, det2):
+        assert torch.equal(a, b)
+    for k in range(3):  # y, lse, dvalues: per token, independent of the schedule
+        assert torch.equal(det1[k], dyn[k])
+    a, b = to_f64(det1[3]), to_f64(dyn[3])
+    assert np.linalg.norm(a - b) <= 4e-3 * np.linalg.norm(a)
+
+
+def test_multi_query_autograd_wrapper():
+    import attention_residuals_amd as A
+    S, N, D, R, M = 4, 2 * 37, 1024, 256, 3
+    V, Q, G = _inputs(S, N, D, R, M, "bf16", seed=2300)
+    v = V.cuda().view(S, 2, 37, D).clone().requires_grad_(True)
+    q = Q.cuda().clone().requires_grad_(True)
+    y = A.attnres_multi(v, q, output_layout="token_major")
+    assert y.shape == (2, 37, M, D)
+    y.backward(G.cuda().permute(1, 0, 2).reshape(2, 37, M, D))
+    ref = oracle.run_multi(V, Q, G)
+    got_y = to_f64(y.detach().reshape(N, M, D)).transpose(1, 0, 2)
+    assert compare_rows(got_y.reshape(-1, D), ref["y"].reshape(-1, D), "bf16")["ok"]
+    assert compare_rows(to_f64(v.grad.reshape(S, N, D)), ref["dvalues"], "bf16")["ok"]
+    for m in range(M):
+        assert compare_vec(to_f64(q.grad[m]), ref["dq"][m], "bf16")["ok"]
+
+
+def test_multi_query_zero_tokens_and_unsupported_shape():
+    import attention_residuals_amd as A
+    V = torch.empty((3, 0, 256), dtype=torch.bfloat16, device="cuda")
+    Q = torch.randn((2, 256), device="cuda").to(torch.bfloat16)
+    y, lse = A.attnres_multi_fwd(V, Q)
+    dv, dq = A.attnres_multi_bwd(V, Q, lse, torch.empty((2, 0, 256), dtype=torch.bfloat16,
+                                                         device="cuda"))
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and torch.all(dq == 0)
+    big = torch.empty((64, 4, 8192), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(A.AttnResError) as e:
+        A.attnres_multi_fwd(big, torch.zeros((2, 8192), dtype=torch.bfloat16, device="cuda"))
+    assert e.value.status == 2
