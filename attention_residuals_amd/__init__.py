@@ -9,7 +9,7 @@ from ._binding import (ATTNRES_BF16, ATTNRES_F32, EPS_DEFAULT, EXPORTS, AttnResE
                        attnres_multi_fwd, fwd_workspace_bytes, load, make_desc, make_multi_desc,
                        multi_fwd_workspace_bytes, multi_workspace_bytes, o32_elems,
                        workspace_bytes)
-from .autograd import attnres, attnres_multi
+from .ops import attnres, attnres_multi
 
 __all__ = ["attnres", "attnres_multi", "attnres_fwd", "attnres_bwd", "attnres_multi_fwd",
            "attnres_multi_bwd", "o32_elems", "workspace_bytes", "fwd_workspace_bytes",
