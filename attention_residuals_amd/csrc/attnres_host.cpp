@@ -640,8 +640,10 @@ attnres_desc single_desc(const attnres_multi_desc* m) {
   return d;
 }
 
-// The multi-query kernels keep a token's S rows in VGPRs with workgroups of up to 8 waves and the
-// fewest chunks per thread that allow it (registers also hold the group's query slices and sums).
+// The multi-query kernels keep a token's S rows in VGPRs. With M <= 2 the single-query read's
+// 4-wave workgroups (CH = ceil(chunks / 256)) measured best when the sources fit their bucket; with
+// more queries (and otherwise) the fewest chunks per thread with at most 8 waves, which leaves
+// registers for four queries per launch.
 attnres_status make_multi_shape(const attnres_multi_desc* m, MultiShape* ms) {
   if (!m) return fail(ATTNRES_ERR_INVALID_ARG, "desc is NULL");
   const attnres_desc d = single_desc(m);
@@ -655,8 +657,23 @@ attnres_status make_multi_shape(const attnres_multi_desc* m, MultiShape* ms) {
   ms->base.vec = ms->base.bf16 ? 8 : 4;
   ms->base.esz = ms->base.bf16 ? 2 : 4;
   const int chunks = d.D / ms->base.vec;
+  auto bucket = [&](int c) {
+    const int* b = c == 1 ? kSbCh1 : c == 2 ? kSbCh2 : kSbCh4;
+    const int nb = c == 1 ? (int)(sizeof kSbCh1 / sizeof(int))
+                   : c == 2 ? (int)(sizeof kSbCh2 / sizeof(int))
+                            : (int)(sizeof kSbCh4 / sizeof(int));
+    return bucket_at_least(d.S, b, nb);
+  };
+  static const int forced = env_int("ATTNRES_MULTI_CH");
+  if ((forced == 1 || forced == 2 || forced == 4) && (chunks + 64 * forced - 1) / (64 * forced) <= 8)
+    ms->ch = forced;
+  if (!ms->ch && m->M <= 2) {
+    const int c = std::min(4, std::max(1, (chunks + 255) / 256));
+    const int cc = c == 3 ? 4 : c;
+    if ((chunks + 64 * cc - 1) / (64 * cc) <= 8 && bucket(cc) > 0) ms->ch = cc;
+  }
   for (int c : {1, 2, 4})
-    if ((chunks + 64 * c - 1) / (64 * c) <= 8) {
+    if (!ms->ch && (chunks + 64 * c - 1) / (64 * c) <= 8) {
       ms->ch = c;
       break;
     }
@@ -664,15 +681,11 @@ attnres_status make_multi_shape(const attnres_multi_desc* m, MultiShape* ms) {
   ms->W = (chunks + 64 * ms->ch - 1) / (64 * ms->ch);
   ms->threads = 64 * ms->W;
   ms->full = d.R == d.D;
-  const int* b = ms->ch == 1 ? kSbCh1 : ms->ch == 2 ? kSbCh2 : kSbCh4;
-  const int nb = ms->ch == 1 ? (int)(sizeof kSbCh1 / sizeof(int))
-                 : ms->ch == 2 ? (int)(sizeof kSbCh2 / sizeof(int))
-                               : (int)(sizeof kSbCh4 / sizeof(int));
-  ms->sb = bucket_at_least(d.S, b, nb);
+  ms->sb = bucket(ms->ch);
   if (ms->sb <= 0)
     return fail(ATTNRES_ERR_UNSUPPORTED,
                 "the multi-query read keeps a token's rows on chip: S=%d sources of D=%d is too "
-                "many (at most %d)", d.S, d.D, b[nb - 1]);
+                "many for %d chunks per thread", d.S, d.D, ms->ch);
   // Four queries share one launch with one chunk per thread and at most 12 sources (fewer passes
   // over the sources and, for M > 4, fewer intermediate roundings of dvalues); groups that also
   // hold the existing gradient rows spill a few registers there. Otherwise groups of two.
