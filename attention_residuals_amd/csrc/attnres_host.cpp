@@ -144,15 +144,18 @@ attnres_status make_shape(const attnres_desc* d, Shape* sh) {
   const int fit = fit_for(ch);
   sh->resident = !d->out_norm && fit > 0;
   // forward: one block when the sources fit a bucket, else blocks of the stream size
-  // (accumulating into dvalues holds a block's existing gradient rows too: half the block at CH = 2)
-  const int stream_max = ch == 4 ? 4 : (d->accumulate_dvalues && ch == 2) ? 4 : 8;
-  sh->sb_fwd = fit > 0 ? fit : stream_max;
+  // Source blocks of the streaming kernels: the forward holds one block, the backward two (it
+  // double-buffers them) and, accumulating into dvalues, their existing gradient rows too: the
+  // largest blocks that stay in registers.
+  const int fwd_stream_max = ch == 4 ? 4 : 8;
+  const int bwd_stream_max = ch == 4 ? 2 : (d->accumulate_dvalues && ch == 2) ? 2 : 4;
+  sh->sb_fwd = fit > 0 ? fit : fwd_stream_max;
   sh->fwd_one = fit > 0;
   if (sh->resident) {
     sh->sb_bwd = fit;
   } else {
     int s = bucket_at_least(d->S, kSbStream, (int)(sizeof kSbStream / sizeof(int)));
-    sh->sb_bwd = (s > 0 && s <= stream_max) ? s : stream_max;
+    sh->sb_bwd = (s > 0 && s <= bwd_stream_max) ? s : bwd_stream_max;
   }
   return ATTNRES_OK;
 }
@@ -578,8 +581,11 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
     a.part_dow = d->has_out_weight ? reinterpret_cast<float*>(ws + pl.off_dow) : nullptr;
     a.out_norm = d->out_norm ? 1 : 0;
     a.tpt = 1;
-    if (sh.resident && !d->deterministic && N >= 2 * (int64_t)pl.P && N < kMaxTicketTokens) {
-      a.tpt = tokens_per_ticket(N, pl.P, (double)(2 * d->S + 1) * d->D * sh.esz, 30.0, 16);
+    if (!d->deterministic && N >= 2 * (int64_t)pl.P && N < kMaxTicketTokens) {
+      const double row_bytes = (double)d->D * sh.esz;
+      const double per_token =
+          ((d->accumulate_dvalues ? 3 : 2) * d->S + 1) * row_bytes + (sh.resident ? 0 : 4.0 * d->D);
+      a.tpt = tokens_per_ticket(N, pl.P, per_token, 30.0, 16);
       a.ticket = reinterpret_cast<uint32_t*>(ws + pl.off_ticket);
       void* targ = a.ticket;
       st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");

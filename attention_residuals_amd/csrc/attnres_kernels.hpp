@@ -915,18 +915,24 @@ void bwd_resident_kernel(const BwdArgs a) {
 // ------------------------------------------------------------------ backward, streaming
 
 // Sources walked in blocks of SB using the forward's FP32 mixture o (and rho_o with the output
-// norm): do and delta = <do, o> are known before the first source is read. ACC: dvalues
-// accumulate (a block's existing gradient rows are loaded with its source rows).
+// norm): do and delta = <do, o> are known before the first source is read. Blocks are
+// double-buffered: block b+1's rows (and, during a token's last block, the next token's dY, o and
+// block 0) are loaded while block b is reduced and its gradients stored; every block issues the
+// same loads (empty resources where there is nothing to load), so the wait counts are the same
+// on every path. Tokens come in batches from the device-wide counter like the resident kernels.
+// ACC: dvalues accumulate (a block's existing gradient rows are loaded with its source rows).
 template <bool BF16, int CH, int SB, bool FULL, bool ACC>
 __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
   constexpr int K = 3 * SB;
+  constexpr int OC = VEC / 4;  // 16-byte chunks of the FP32 mixture per row chunk
   extern __shared__ float lds_all[];
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
   const int R4 = nthr >> 4;
   const int xfl = K * R4;
   const uint32_t row_bytes = static_cast<uint32_t>(a.D * ESZ);
+  const uint32_t o_bytes = static_cast<uint32_t>(a.D * 4);
 
   Cols<BF16, CH, FULL> cs;
   cs.init(tid, nthr, a.D, a.lo, a.query, a.norm_w, lds_all);
@@ -941,27 +947,66 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
                                                          : 1.f;
     }
   int buf = 0;
+  const int nblk = (a.S + SB - 1) / SB;
 
-  for (int64_t n = blockIdx.x; n < a.N; n += gridDim.x) {
-    const int64_t row_byte = n * a.row_stride * ESZ;
-    float dov[CH][VEC], o[CH][VEC];
-    {
-      const Rsrc rg = row_rsrc(a.dout, n * a.dout_stride * ESZ, row_bytes);
-      const Rsrc ro = row_rsrc(a.o32, n * a.D * 4, static_cast<uint32_t>(a.D * 4));
+  const bool dyn = a.ticket != nullptr;
+  const int64_t B = dyn ? a.tpt : 1;
+  const int64_t n0 = (int64_t)blockIdx.x * B;
+
+  // a token's head (dY row and FP32 mixture row) and one source block's rows (+ existing grads)
+  Chunk g[CH], oc[CH][OC];
+  Chunk cur[SB][CH], nxt[SB][CH];
+  Chunk odc[ACC ? SB : 1][CH], odn[ACC ? SB : 1][CH];
+  auto load_head = [&](int64_t tok, bool live) {
+    const Rsrc rg = row_rsrc(live ? a.dout : nullptr, live ? tok * a.dout_stride * ESZ : 0,
+                             live ? row_bytes : 0u);
+    const Rsrc ro = row_rsrc(live ? a.o32 : nullptr, live ? tok * a.D * 4 : 0, live ? o_bytes : 0u);
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const Chunk g = ld_row(rg, cs.voff[j]);
+    for (int j = 0; j < CH; ++j) {
+      g[j] = ld_row(rg, cs.voff[j]);
 #pragma unroll
-        for (int h = 0; h < VEC; h += 4) {
-          const Chunk oc = ld_row(ro, static_cast<uint32_t>((cs.col0[j] + h) * 4));
+      for (int h = 0; h < OC; ++h)
+        oc[j][h] = ld_row(ro, static_cast<uint32_t>((cs.col0[j] + 4 * h) * 4));
+    }
+  };
+  auto load_block = [&](Chunk (&rows)[SB][CH], Chunk (&od)[ACC ? SB : 1][CH], int64_t tok,
+                        int s0, bool live) {
+    const int nb = live ? min(SB, a.S - s0) : 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[j][h + e] = bits_f(oc.w[e]);
-        }
+    for (int i = 0; i < SB; ++i) {
+      const int s = min(s0 + i, kMaxSources - 1);
+      const Rsrc r = src_rsrc(a.src[s], i, nb, tok * a.row_stride * ESZ, row_bytes);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) dov[j][e] = elem<BF16>(g, e);
+      for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+      if constexpr (ACC) {
+        const Rsrc rd = src_rsrc(a.dsrc[s], i, nb, tok * a.drow_stride * ESZ, row_bytes);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) od[i][j] = ld_row(rd, cs.voff[j]);
       }
     }
-    // do and delta = <do, o>
+  };
+  load_head(n0, n0 < a.N);
+  load_block(cur, odc, n0, 0, n0 < a.N);
+
+  uint32_t* tslot = reinterpret_cast<uint32_t*>(lds + 2 * xfl);
+  int64_t n = n0, batch_end = n0 + B;
+  while (n < a.N) {
+    const bool take = dyn && n + 1 >= batch_end;
+    uint32_t tk = 0;
+    if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
+    int64_t next = dyn ? n + 1 : n + gridDim.x;
+
+    float dov[CH][VEC], o[CH][VEC];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+#pragma unroll
+      for (int h = 0; h < OC; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[j][4 * h + e] = bits_f(oc[j][h].w[e]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dov[j][e] = elem<BF16>(g[j], e);
+    }
+    // do and delta = <do, o>; the ticket rides on this exchange's barrier
     float delta;
     {
       float part[2][kGroup] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -981,7 +1026,12 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
       }
       float* xb = lds + buf * xfl;
       xchg_group<2, 1>(part, 0, xb, R4, tid);
+      if (take && tid == 0) tslot[buf] = tk;
       __syncthreads();
+      if (take) {
+        next = ((int64_t)gridDim.x + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf])) * B;
+        batch_end = next + B;
+      }
       buf ^= 1;
       const float t0 = xchg_total(xb, 0, R4);
       if (a.out_norm) {
@@ -1004,26 +1054,16 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
     }
     const float lse = a.lse[n];
     const int64_t drow_byte = n * a.drow_stride * ESZ;
+    const bool live_next = next < a.N;
 
-    for (int s0 = 0; s0 < a.S; s0 += SB) {
+    for (int b = 0; b < nblk; ++b) {
+      const int s0 = b * SB;
       const int nb = min(SB, a.S - s0);
-      Chunk rows[SB][CH];  // slots i >= nb: empty resource, zero rows, weight 0
-      Chunk odv[ACC ? SB : 1][CH];
-#pragma unroll
-      for (int i = 0; i < SB; ++i) {
-        const Rsrc r = src_rsrc(a.src[min(s0 + i, kMaxSources - 1)], i, nb, row_byte, row_bytes);
-#pragma unroll
-        for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
-      }
-      if constexpr (ACC) {
-#pragma unroll
-        for (int i = 0; i < SB; ++i) {
-          const Rsrc rd =
-              src_rsrc(a.dsrc[min(s0 + i, kMaxSources - 1)], i, nb, drow_byte, row_bytes);
-#pragma unroll
-          for (int j = 0; j < CH; ++j) odv[i][j] = ld_row(rd, cs.voff[j]);
-        }
-      }
+      const bool last = b + 1 == nblk;
+      // the following block: this token's next one, or the next token's first (with its head)
+      load_head(next, last && live_next);
+      load_block(nxt, odn, last ? next : n, last ? 0 : s0 + SB, last ? live_next : true);
+
       float* xb = lds + buf * xfl;
       uint32_t us[3][CH][4];
       float u[CH][VEC];
@@ -1033,11 +1073,11 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
       for (int i0 = 0; i0 < SB; i0 += kGroup) {
         float part[3][kGroup];
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g) {
-          part[0][g] = part[1][g] = part[2][g] = 0.f;
-          if (i0 + g < SB) {
-            key_sums<BF16, CH, FULL>(rows[i0 + g], cs, us, u, a.lo, part[0][g], part[1][g]);
-            part[2][g] = dot_f32<BF16, CH>(rows[i0 + g], dov);
+        for (int gi = 0; gi < kGroup; ++gi) {
+          part[0][gi] = part[1][gi] = part[2][gi] = 0.f;
+          if (i0 + gi < SB) {
+            key_sums<BF16, CH, FULL>(cur[i0 + gi], cs, us, u, a.lo, part[0][gi], part[1][gi]);
+            part[2][gi] = dot_f32<BF16, CH>(cur[i0 + gi], dov);
           }
         }
         xchg_group<3, SB>(part, i0, xb, R4, tid);
@@ -1054,18 +1094,27 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
         p = routing_weight(sc.z, lse);
       }
       const float A = a.scale * p * (dp - delta) * rho;
-      const float B = -A * rho * rho * c * a.inv_R;
+      const float Bc = -A * rho * rho * c * a.inv_R;
       cs.fetch_u(laundered_lane_off(tid), u);
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
         Chunk out[CH];
-        grad_row<BF16, CH, FULL, ACC>(rows[i], cs, u, dov, bcast(p, i), bcast(A, i), bcast(B, i),
-                                      a.lo, du, out, odv[ACC ? i : 0]);
-        const Rsrc rd = src_rsrc(a.dsrc[min(s0 + i, kMaxSources - 1)], i, nb, drow_byte, row_bytes);
+        grad_row<BF16, CH, FULL, ACC>(cur[i], cs, u, dov, bcast(p, i), bcast(A, i), bcast(Bc, i),
+                                      a.lo, du, out, odc[ACC ? i : 0]);
+        const Rsrc rd =
+            src_rsrc(a.dsrc[min(s0 + i, kMaxSources - 1)], i, nb, drow_byte, row_bytes);
 #pragma unroll
         for (int j = 0; j < CH; ++j) st_row(rd, cs.voff[j], out[j]);
       }
+#pragma unroll
+      for (int i = 0; i < SB; ++i)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          cur[i][j] = nxt[i][j];
+          if constexpr (ACC) odc[i][j] = odn[i][j];
+        }
     }
+    n = next;
   }
   write_partials<BF16, CH, FULL>(a, cs, du, dow);
 }
