@@ -561,7 +561,7 @@ __device__ __forceinline__ void fwd_emit(const FwdArgs& a, const Cols<BF16, CH, 
 // issued before it; the vector-memory counter retires loads and stores in order).
 // !ONE: blocks of SB sources with an online softmax (running max and sum, rescaled output).
 template <bool BF16, int CH, int SB, bool FULL, bool ONE>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(occupancy_hint(CH, SB, FULL), 8)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(occupancy_hint(CH, ONE ? SB : 2 * SB, FULL), 8)))
 void fwd_kernel(const FwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
@@ -597,6 +597,17 @@ void fwd_kernel(const FwdArgs a) {
   const bool dyn = ONE && a.ticket != nullptr;
   const int64_t B = dyn ? a.tpt : 1;
   const int64_t n0 = (int64_t)blockIdx.x * B;
+  // multi-block path: the following block's rows, loaded while the current block is processed
+  Chunk nxt[ONE ? 1 : SB][CH];
+  if constexpr (!ONE) {
+    const int nb0 = n0 < a.N ? min(SB, a.S) : 0;
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const Rsrc r = src_rsrc(a.src[i], i, nb0, n0 * a.row_stride * ESZ, row_bytes);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+    }
+  }
 
   if constexpr (ONE) {
     // issued in the loop body's order (rows 0..SB-1) so the wait counts at the loop head stay
@@ -622,7 +633,6 @@ void fwd_kernel(const FwdArgs a) {
   uint32_t* tslot = reinterpret_cast<uint32_t*>(lds + 2 * xfl);
   int64_t n = n0, batch_end = n0 + B;
   while (n < a.N) {
-    const int64_t row_byte = n * a.row_stride * ESZ;
     const bool take = dyn && n + 1 >= batch_end;  // last token of its batch
     uint32_t tk = 0;
     if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
@@ -637,11 +647,18 @@ void fwd_kernel(const FwdArgs a) {
     for (int s0 = 0; s0 < (ONE ? 1 : a.S); s0 += SB) {
       const int nb = ONE ? a.S : min(SB, a.S - s0);
       if constexpr (!ONE) {
+        // the following block: this token's next one, or the next token's first (static split:
+        // the next token is known); the same loads on every path (empty past the last token)
+        const bool last = s0 + SB >= a.S;
+        const int64_t tok = last ? next : n;
+        const int f0 = last ? 0 : s0 + SB;
+        const int nbf = (tok < a.N) ? min(SB, a.S - f0) : 0;
 #pragma unroll
         for (int i = 0; i < SB; ++i) {
-          const Rsrc r = src_rsrc(a.src[min(s0 + i, kMaxSources - 1)], i, nb, row_byte, row_bytes);
+          const Rsrc r = src_rsrc(a.src[min(f0 + i, kMaxSources - 1)], i, nbf,
+                                  tok * a.row_stride * ESZ, row_bytes);
 #pragma unroll
-          for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
+          for (int j = 0; j < CH; ++j) nxt[i][j] = ld_row(r, cs.voff[j]);
         }
       }
       float* xb = lds + buf * xfl;
@@ -708,6 +725,12 @@ void fwd_kernel(const FwdArgs a) {
 #pragma unroll
           for (int j = 0; j < CH; ++j) rows[i][j] = ld_row(r, cs.voff[j]);
         }
+      }
+      if constexpr (!ONE) {
+#pragma unroll
+        for (int i = 0; i < SB; ++i)
+#pragma unroll
+          for (int j = 0; j < CH; ++j) rows[i][j] = nxt[i][j];
       }
     }
     if constexpr (!ONE) {
