@@ -76,6 +76,16 @@ class _MultiRows(ctypes.Structure):
     _fields_ = [(name, ctypes.POINTER(ctypes.c_double)) for name in ("y", "lse", "dvalues")]
 
 
+class _SelectedProblem(ctypes.Structure):
+    _fields_ = [
+        ("S", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("N", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("eps", ctypes.c_double), ("scale", ctypes.c_double),
+        ("values", ctypes.POINTER(ctypes.c_void_p)), ("bank", ctypes.c_void_p),
+        ("ids", ctypes.POINTER(ctypes.c_int64)), ("dout", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -93,6 +103,10 @@ def _load():
         lib.attnres_oracle_multi_run.restype = ctypes.c_int
         lib.attnres_oracle_multi_run.argtypes = [
             ctypes.POINTER(_MultiProblem), ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+            ctypes.POINTER(_MultiRows), ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+        lib.attnres_oracle_selected_run.restype = ctypes.c_int
+        lib.attnres_oracle_selected_run.argtypes = [
+            ctypes.POINTER(_SelectedProblem), ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
             ctypes.POINTER(_MultiRows), ctypes.POINTER(ctypes.c_double), ctypes.c_int]
         lib.attnres_oracle_threads.restype = ctypes.c_int
         lib.attnres_oracle_threads.argtypes = [ctypes.c_int]
@@ -286,4 +300,64 @@ def run_multi(values, queries, dout=None, *, eps: float = 2.0 ** -23, scale: flo
         raise RuntimeError(f"attnres_oracle_multi_run failed with code {rc}")
     if dq is not None:
         out["dq"] = dq
+    return out
+
+
+def run_selected(values, bank, ids, dout=None, *, eps: float = 2.0 ** -23, scale: float = 1.0,
+                 tokens: Optional[Sequence[int]] = None,
+                 want: Sequence[str] = ("y", "lse", "dvalues"), reduce: bool = True,
+                 threads: int = 0) -> dict:
+    """Evaluates the selected-query AttnRes read in FP64: token n reads with the K queries
+    bank[ids[n, k]]. values: [S, N, D] or S arrays [N, D]; bank [E, R]; ids [N, K] integers;
+    dout [N, K, D] or None. Returns y [T, K, D], lse [T, K], dvalues [S, T, D] and, with
+    reduce, dbank [E, R]."""
+    lib = _load()
+    vals = _sources(values)
+    S = len(vals)
+    N, D = vals[0].shape
+    b = np.ascontiguousarray(_storage(bank))
+    if b.ndim != 2:
+        raise ValueError("bank must be [E, R]")
+    E, R = b.shape
+    try:
+        import torch
+        if isinstance(ids, torch.Tensor):
+            ids = ids.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    idx = np.ascontiguousarray(np.asarray(ids, dtype=np.int64).reshape(N, -1))
+    K = idx.shape[1]
+    code = _code(vals[0])
+    g = None if dout is None else np.ascontiguousarray(_storage(dout).reshape(N, K, D))
+    for a in vals + [b] + ([g] if g is not None else []):
+        if _code(a) != code:
+            raise TypeError("all oracle inputs must share one storage format")
+    ptrs = (ctypes.c_void_p * S)(*[v.ctypes.data for v in vals])
+    prob = _SelectedProblem(S=S, D=D, R=R, E=E, K=K, N=N, dtype=code, eps=float(eps),
+                            scale=float(scale),
+                            values=ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)),
+                            bank=b.ctypes.data,
+                            ids=idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                            dout=None if g is None else g.ctypes.data)
+    tok = None
+    T = N
+    if tokens is not None:
+        tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        T = tok.shape[0]
+    out = {}
+    shapes = {"y": (T, K, D), "lse": (T, K), "dvalues": (S, T, D)}
+    for name in want:
+        if name == "dvalues" and g is None:
+            continue
+        out[name] = np.zeros(shapes[name], dtype=np.float64)
+    rows = _MultiRows(**{k: _dptr(out.get(k)) for k in shapes})
+    dbank = np.zeros((E, R), dtype=np.float64) if (reduce and g is not None) else None
+    rc = lib.attnres_oracle_selected_run(
+        ctypes.byref(prob),
+        None if tok is None else tok.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        T, ctypes.byref(rows), _dptr(dbank), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"attnres_oracle_selected_run failed with code {rc}")
+    if dbank is not None:
+        out["dbank"] = dbank
     return out

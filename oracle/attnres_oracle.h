@@ -89,6 +89,25 @@ int attnres_oracle_multi_run(const attnres_oracle_multi_problem* prob, const int
                              int64_t T, attnres_oracle_multi_rows* rows, double* dq,
                              int threads);
 
+/* Selected-query read (same section: per-token query selection): token n reads with the K queries
+ * bank[ids[n, k]]; outputs are token-major [T, K, D] and lse [T, K]; dbank [E, R] sums the query
+ * gradients of every (n, k) by id. S <= 64. */
+typedef struct {
+  int32_t S, D, R, E, K;  /* sources, width, rank, bank rows, queries per token */
+  int64_t N;
+  int32_t dtype;
+  double eps, scale;
+  const void* const* values;  /* S pointers, each a contiguous [N, D] */
+  const void* bank;       /* [E, R] */
+  const int64_t* ids;     /* [N, K], each in [0, E) */
+  const void* dout;       /* [N, K, D] or NULL */
+} attnres_oracle_selected_problem;
+
+/* rows->y is [T, K, D], rows->lse [T, K], rows->dvalues [S, T, D]; dbank (optional) [E, R]. */
+int attnres_oracle_selected_run(const attnres_oracle_selected_problem* prob,
+                                const int64_t* tokens, int64_t T, attnres_oracle_multi_rows* rows,
+                                double* dbank, int threads);
+
 /* Number of OpenMP threads a run with the given request would use (for reporting). */
 int attnres_oracle_threads(int threads);
 

@@ -203,3 +203,99 @@ int attnres_oracle_multi_run(const attnres_oracle_multi_problem* P, const int64_
   free(ws);
   return 0;
 }
+
+/* ---------------------------------------------------------------- selected-query read
+ * "Fast Attention Residuals" PyPI page, section "Multi-query AttnRes" (per-token query selection):
+ * token n reads the sources with the K queries bank[ids[n, k]]; everything else is the
+ * multi-query read of that token. The bank's gradient sums, for every bank row e, the query
+ * gradients of all (n, k) with ids[n, k] = e. This reuses the multi-query steps above, one token
+ * at a time, with the token's own query list. */
+int attnres_oracle_selected_run(const attnres_oracle_selected_problem* P, const int64_t* tokens,
+                                int64_t T, attnres_oracle_multi_rows* rows, double* dbank,
+                                int threads) {
+  if (!P || P->S < 1 || P->D < 1 || P->R < 1 || P->R > P->D || P->N < 0 || P->K < 1 || P->E < 1)
+    return -1;
+  if (P->dtype != ORACLE_F32 && P->dtype != ORACLE_BF16 && P->dtype != ORACLE_F64) return -2;
+  if (!P->values || !P->bank || !P->ids) return -3;
+  for (int s = 0; s < P->S; ++s) if (!P->values[s]) return -3;
+  if (!tokens) T = P->N;
+  if (T < 0) return -4;
+  if (tokens)
+    for (int64_t t = 0; t < T; ++t) if (tokens[t] < 0 || tokens[t] >= P->N) return -5;
+  for (int64_t i = 0; i < P->N * (int64_t)P->K; ++i)
+    if (P->ids[i] < 0 || P->ids[i] >= P->E) return -9;
+  if ((dbank || (rows && rows->dvalues)) && !P->dout) return -6;
+  const int S = P->S, D = P->D, R = P->R, K = P->K;
+  const int esz = P->dtype == ORACLE_F32 ? 4 : P->dtype == ORACLE_BF16 ? 2 : 8;
+  const int nth = attnres_oracle_threads(threads);
+  double* part = dbank ? calloc((size_t)nth * P->E * R, sizeof(double)) : NULL;
+  if (dbank && !part) return -100;
+  int bad = 0;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nth) reduction(| : bad)
+#endif
+  {
+#ifdef _OPENMP
+    const int me = omp_get_thread_num();
+    const int cnt = omp_get_num_threads();
+#else
+    const int me = 0, cnt = 1;
+#endif
+    /* the token's own queries [K, R] (copied in storage format) and its dY rows [K, 1, D] */
+    char* q = malloc((size_t)K * R * esz);
+    char* g = P->dout ? malloc((size_t)K * D * esz) : NULL;
+    double* dq = calloc((size_t)K * R, sizeof(double));
+    double *y = NULL, *lse = NULL, *dv = NULL;
+    if (rows && rows->y) y = malloc((size_t)K * D * sizeof(double));
+    if (rows && rows->lse) lse = malloc((size_t)K * sizeof(double));
+    if (rows && rows->dvalues) dv = malloc((size_t)S * D * sizeof(double));
+    if (!q || (P->dout && !g) || !dq || (rows && rows->y && !y) || (rows && rows->lse && !lse) ||
+        (rows && rows->dvalues && !dv))
+      bad = 1;
+    const int64_t lo = T * me / cnt, hi = T * (me + 1) / cnt;
+    for (int64_t row = lo; row < hi && !bad; ++row) {
+      const int64_t n = tokens ? tokens[row] : row;
+      const void* src[64];
+      for (int s = 0; s < S; ++s)
+        src[s] = (const char*)P->values[s] + (size_t)n * D * esz;
+      for (int k = 0; k < K; ++k) {
+        memcpy(q + (size_t)k * R * esz, (const char*)P->bank + (size_t)P->ids[n * K + k] * R * esz,
+               (size_t)R * esz);
+        if (g)
+          memcpy(g + (size_t)k * D * esz, (const char*)P->dout + ((size_t)n * K + k) * D * esz,
+                 (size_t)D * esz);
+      }
+      /* one-token multi-query problem over this token's rows and queries */
+      attnres_oracle_multi_problem mp = {S, D, R, K, 1, P->dtype, P->eps, P->scale,
+                                         (const void* const*)src, q, g};
+      attnres_oracle_multi_rows mr = {y, lse, dv};
+      if (attnres_oracle_multi_run(&mp, NULL, 1, &mr, dbank ? dq : NULL, 1) != 0) {
+        bad = 1;
+        break;
+      }
+      if (rows && rows->y)
+        for (int k = 0; k < K; ++k)
+          memcpy(rows->y + ((size_t)row * K + k) * D, y + (size_t)k * D, (size_t)D * sizeof(double));
+      if (rows && rows->lse)
+        for (int k = 0; k < K; ++k) rows->lse[(size_t)row * K + k] = lse[k];
+      if (rows && rows->dvalues)
+        for (int s = 0; s < S; ++s)
+          memcpy(rows->dvalues + ((size_t)s * T + row) * D, dv + (size_t)s * D,
+                 (size_t)D * sizeof(double));
+      if (dbank)
+        for (int k = 0; k < K; ++k) {
+          double* pe = part + ((size_t)me * P->E + P->ids[n * K + k]) * R;
+          for (int j = 0; j < R; ++j) pe[j] += dq[(size_t)k * R + j];
+        }
+    }
+    free(q); free(g); free(dq); free(y); free(lse); free(dv);
+  }
+  if (!bad && dbank) {
+    const size_t er = (size_t)P->E * R;
+    for (size_t j = 0; j < er; ++j) dbank[j] = 0.0;
+    for (int i = 0; i < nth; ++i)
+      for (size_t j = 0; j < er; ++j) dbank[j] += part[(size_t)i * er + j];
+  }
+  free(part);
+  return bad ? -100 : 0;
+}

@@ -11,6 +11,9 @@ with the wrong key) fail at least one:
     tests/test_oracle_pins.py): outputs and dq_m per query, source gradients summed;
   * special cases: M = 1 is the single-query read; equal queries give equal outputs; a zero query
     gives the mean of the sources.
+The selected-query read (per-token queries bank[ids[n, k]]) is pinned by torch.autograd over a
+gather of the bank, finite differences on the bank, and equality with the multi-query read when
+every token selects the same rows (a repeated row collects both query gradients).
 """
 import math
 
@@ -132,3 +135,78 @@ def test_token_subset_and_bf16_storage():
     f = oracle.run_multi(tV.double().numpy(), tQ.double().numpy(), tG.double().numpy())
     for k in ("y", "lse", "dvalues", "dq"):
         np.testing.assert_array_equal(b[k], f[k])
+
+
+# ---------------------------------------------------------------- selected-query read
+
+def _selected_problem(seed, S, N, D, R, E, K):
+    rng = np.random.default_rng(seed)
+    V = rng.standard_normal((S, N, D)) * np.sqrt(1.0 + np.arange(S))[:, None, None]
+    bank = rng.standard_normal((E, R)) / math.sqrt(R)
+    ids = rng.integers(0, E, size=(N, K))
+    G = rng.standard_normal((N, K, D))
+    return V, bank, ids, G
+
+
+SEL_CASES = [  # S, N, D, R, E, K, eps, scale
+    (3, 4, 8, 8, 3, 2, 2.0 ** -23, 1.0),
+    (4, 5, 16, 5, 6, 3, 1e-3, 0.7),
+    (2, 3, 8, 3, 1, 4, 0.25, 1.3),
+]
+
+
+@pytest.mark.parametrize("case", SEL_CASES)
+def test_selected_torch_autograd_f64(case):
+    S, N, D, R, E, K, eps, scale = case
+    V, bank, ids, G = _selected_problem(51 + S + K, S, N, D, R, E, K)
+    out = oracle.run_selected(V, bank, ids, G, eps=eps, scale=scale)
+    tV = torch.tensor(V, requires_grad=True)
+    tB = torch.tensor(bank, requires_grad=True)
+    t = tV[:, :, D - R:]
+    k = t / torch.sqrt((t * t).mean(-1, keepdim=True) + eps)       # [S, N, R]
+    q = tB[torch.tensor(ids)]                                        # [N, K, R]
+    score = scale * torch.einsum("snr,nkr->nks", k, q)               # [N, K, S]
+    p = torch.softmax(score, dim=-1)
+    y = torch.einsum("nks,snd->nkd", p, tV)
+    (y * torch.tensor(G)).sum().backward()
+    np.testing.assert_allclose(out["y"], y.detach().numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(out["lse"], torch.logsumexp(score, -1).detach().numpy(),
+                               rtol=1e-12, atol=1e-13)
+    gV, gB = tV.grad.numpy(), tB.grad.numpy()
+    np.testing.assert_allclose(out["dvalues"], gV, rtol=1e-10, atol=1e-12 * np.abs(gV).max())
+    np.testing.assert_allclose(out["dbank"], gB, rtol=1e-10, atol=1e-12 * np.abs(gB).max())
+
+
+def test_selected_finite_differences_on_the_bank():
+    S, N, D, R, E, K = 3, 4, 8, 4, 3, 2
+    V, bank, ids, G = _selected_problem(61, S, N, D, R, E, K)
+    out = oracle.run_selected(V, bank, ids, G)
+    h = 1e-6
+    num = np.zeros_like(bank)
+    for idx in np.ndindex(bank.shape):
+        old = bank[idx]
+        bank[idx] = old + h
+        lp = float(np.sum(oracle.run_selected(V, bank, ids, want=("y",), reduce=False)["y"] * G))
+        bank[idx] = old - h
+        lm = float(np.sum(oracle.run_selected(V, bank, ids, want=("y",), reduce=False)["y"] * G))
+        bank[idx] = old
+        num[idx] = (lp - lm) / (2 * h)
+    err = np.abs(out["dbank"] - num).max() / np.abs(num).max()
+    assert err <= 1e-6, err
+
+
+def test_selected_with_fixed_ids_is_the_multi_query_read():
+    # every token selecting rows (2, 0, 2) of the bank is the multi-query read with those queries;
+    # the repeated row's gradient is the sum of its two query gradients
+    S, N, D, R, E = 4, 6, 16, 8, 3
+    V, bank, _, _ = _selected_problem(71, S, N, D, R, E, 3)
+    ids = np.tile(np.array([2, 0, 2]), (N, 1))
+    G = np.random.default_rng(72).standard_normal((N, 3, D))
+    sel = oracle.run_selected(V, bank, ids, G)
+    mq = oracle.run_multi(V, bank[[2, 0, 2]], G.transpose(1, 0, 2))
+    np.testing.assert_array_equal(sel["y"], mq["y"].transpose(1, 0, 2))
+    np.testing.assert_array_equal(sel["lse"], mq["lse"].T)
+    np.testing.assert_allclose(sel["dvalues"], mq["dvalues"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(sel["dbank"][2], mq["dq"][0] + mq["dq"][2], rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(sel["dbank"][0], mq["dq"][1], rtol=1e-11, atol=1e-14)
+    np.testing.assert_array_equal(sel["dbank"][1], 0.0)
