@@ -5,15 +5,19 @@ The compute lives in ``libattnres.so`` (hand-written HIP kernels behind the C AB
 ``python -m attention_residuals_amd.build``. Nothing here falls back to a CPU implementation.
 """
 from ._binding import (ATTNRES_BF16, ATTNRES_F32, EPS_DEFAULT, EXPORTS, AttnResError, Desc,
-                       MultiDesc, Sources, attnres_bwd, attnres_fwd, attnres_multi_bwd,
-                       attnres_multi_fwd, fwd_workspace_bytes, load, make_desc, make_multi_desc,
-                       multi_fwd_workspace_bytes, multi_workspace_bytes, o32_elems,
-                       workspace_bytes)
-from .ops import attnres, attnres_multi
+                       MultiDesc, SelectedDesc, Sources, attnres_bwd, attnres_fwd,
+                       attnres_multi_bwd, attnres_multi_fwd, attnres_selected_bwd,
+                       attnres_selected_fwd, fwd_workspace_bytes, load, make_desc,
+                       make_multi_desc, make_selected_desc, multi_fwd_workspace_bytes,
+                       multi_workspace_bytes, o32_elems, selected_fwd_workspace_bytes,
+                       selected_workspace_bytes, workspace_bytes)
+from .ops import attnres, attnres_multi, attnres_selected
 
-__all__ = ["attnres", "attnres_multi", "attnres_fwd", "attnres_bwd", "attnres_multi_fwd",
-           "attnres_multi_bwd", "o32_elems", "workspace_bytes", "fwd_workspace_bytes",
-           "multi_workspace_bytes", "multi_fwd_workspace_bytes", "make_desc", "make_multi_desc",
-           "MultiDesc",
+__all__ = ["attnres", "attnres_multi", "attnres_selected", "attnres_fwd", "attnres_bwd",
+           "attnres_multi_fwd", "attnres_multi_bwd", "attnres_selected_fwd",
+           "attnres_selected_bwd", "o32_elems", "workspace_bytes", "fwd_workspace_bytes",
+           "multi_workspace_bytes", "multi_fwd_workspace_bytes", "selected_workspace_bytes",
+           "selected_fwd_workspace_bytes", "make_desc", "make_multi_desc", "make_selected_desc",
+           "MultiDesc", "SelectedDesc",
            "load", "Desc", "Sources", "AttnResError", "EXPORTS", "ATTNRES_BF16", "ATTNRES_F32",
            "EPS_DEFAULT"]

@@ -22,6 +22,8 @@ EPS_DEFAULT = 2.0 ** -23
 EXPORTS = ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd_workspace_bytes",
            "attnres_fwd", "attnres_bwd", "attnres_multi_fwd_workspace_bytes",
            "attnres_multi_workspace_bytes", "attnres_multi_fwd", "attnres_multi_bwd",
+           "attnres_selected_fwd_workspace_bytes", "attnres_selected_workspace_bytes",
+           "attnres_selected_fwd", "attnres_selected_bwd",
            "attnres_status_str", "attnres_last_error")
 
 QUERY_MAJOR, TOKEN_MAJOR = 0, 1
@@ -40,6 +42,13 @@ class MultiDesc(ctypes.Structure):
     _fields_ = [("S", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
                 ("M", ctypes.c_int32), ("dtype", ctypes.c_int32), ("N", ctypes.c_int64),
                 ("eps", ctypes.c_float), ("scale", ctypes.c_float), ("layout", ctypes.c_int32),
+                ("deterministic", ctypes.c_int32), ("accumulate_dvalues", ctypes.c_int32)]
+
+
+class SelectedDesc(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("K", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("N", ctypes.c_int64), ("eps", ctypes.c_float), ("scale", ctypes.c_float),
                 ("deterministic", ctypes.c_int32), ("accumulate_dvalues", ctypes.c_int32)]
 
 
@@ -80,10 +89,14 @@ def load() -> ctypes.CDLL:
     lib.attnres_multi_workspace_bytes.argtypes = [pm, ctypes.POINTER(sz)]
     lib.attnres_multi_fwd.argtypes = [pm, ps, vp, vp, vp, vp, sz, vp]
     lib.attnres_multi_bwd.argtypes = [pm, ps, vp, vp, vp, ps, vp, vp, sz, vp]
-    for f in ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd_workspace_bytes",
-              "attnres_fwd", "attnres_bwd", "attnres_multi_fwd_workspace_bytes",
-              "attnres_multi_workspace_bytes", "attnres_multi_fwd", "attnres_multi_bwd"):
-        getattr(lib, f).restype = ctypes.c_int
+    pe = ctypes.POINTER(SelectedDesc)
+    lib.attnres_selected_fwd_workspace_bytes.argtypes = [pe, ctypes.POINTER(sz)]
+    lib.attnres_selected_workspace_bytes.argtypes = [pe, ctypes.POINTER(sz)]
+    lib.attnres_selected_fwd.argtypes = [pe, ps, vp, vp, vp, vp, vp, sz, vp]
+    lib.attnres_selected_bwd.argtypes = [pe, ps, vp, vp, vp, vp, ps, vp, vp, sz, vp]
+    for f in EXPORTS:
+        if f not in ("attnres_status_str", "attnres_last_error"):
+            getattr(lib, f).restype = ctypes.c_int
     lib.attnres_status_str.argtypes = [ctypes.c_int]
     lib.attnres_status_str.restype = ctypes.c_char_p
     lib.attnres_last_error.argtypes = []
@@ -345,3 +358,92 @@ def attnres_multi_bwd(values, queries: torch.Tensor, lse: torch.Tensor, dout: to
                                     _ptr(lse), _ptr(dout), ctypes.byref(dv.struct), _ptr(dq),
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
     return dvalues, dq
+
+
+# ---------------------------------------------------------------- selected-query read
+
+def make_selected_desc(S: int, N: int, D: int, R: int, E: int, K: int, dtype: torch.dtype, *,
+                       eps: float = EPS_DEFAULT, scale: float = 1.0, deterministic: bool = False,
+                       accumulate_dvalues: bool = False) -> SelectedDesc:
+    return SelectedDesc(S=S, D=D, R=R, E=E, K=K, dtype=_dtype_code(dtype), N=N, eps=eps,
+                        scale=scale, deterministic=int(deterministic),
+                        accumulate_dvalues=int(accumulate_dvalues))
+
+
+def selected_workspace_bytes(desc: SelectedDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().attnres_selected_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def selected_fwd_workspace_bytes(desc: SelectedDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().attnres_selected_fwd_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _check_ids(ids: torch.Tensor, N: int) -> int:
+    if ids.dtype != torch.int64 or ids.dim() != 2 or ids.shape[0] != N or not ids.is_contiguous():
+        raise ValueError(f"ids must be a contiguous int64 [N={N}, K] tensor")
+    return int(ids.shape[1])
+
+
+def attnres_selected_fwd(values, bank: torch.Tensor, ids: torch.Tensor, *,
+                         eps: float = EPS_DEFAULT, scale: float = 1.0,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, dynamic: bool = True,
+                         stream=None):
+    """Selected-query forward. values: packed [S, N, D] or a list of [N, D]; bank [E, R]; ids
+    [N, K] int64. Returns (y [N, K, D], lse [N, K] FP32)."""
+    sv = _SourceView(values)
+    if bank.dim() != 2 or not bank.is_contiguous():
+        raise ValueError("bank must be a contiguous [E, R] tensor")
+    E, R = bank.shape
+    K = _check_ids(ids, sv.N)
+    desc = make_selected_desc(sv.S, sv.N, sv.D, R, E, K, sv.dtype, eps=eps, scale=scale)
+    dev = sv.device
+    if out is None:
+        out = torch.empty((sv.N, K, sv.D), dtype=sv.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((sv.N, K), dtype=torch.float32, device=dev)
+    if not dynamic:
+        workspace = None
+    elif workspace is None:
+        workspace = torch.empty((selected_fwd_workspace_bytes(desc),), dtype=torch.uint8,
+                                device=dev)
+    _check(load().attnres_selected_fwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(bank),
+                                       _ptr(ids), _ptr(out), _ptr(lse), _ptr(workspace),
+                                       0 if workspace is None else workspace.numel(),
+                                       _stream(stream)))
+    return out, lse
+
+
+def attnres_selected_bwd(values, bank: torch.Tensor, ids: torch.Tensor, lse: torch.Tensor,
+                         dout: torch.Tensor, *, eps: float = EPS_DEFAULT, scale: float = 1.0,
+                         deterministic: bool = False, accumulate: bool = False, dvalues=None,
+                         dbank: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """Selected-query backward. dout [N, K, D] contiguous. Returns (dvalues, dbank [E, R])."""
+    sv = _SourceView(values)
+    E, R = bank.shape
+    K = _check_ids(ids, sv.N)
+    desc = make_selected_desc(sv.S, sv.N, sv.D, R, E, K, sv.dtype, eps=eps, scale=scale,
+                              deterministic=deterministic, accumulate_dvalues=accumulate)
+    dev = sv.device
+    if not dout.is_contiguous():
+        raise ValueError("dout must be contiguous")
+    if dvalues is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs the dvalues to add to")
+        dvalues = torch.empty((sv.S, sv.N, sv.D), dtype=sv.dtype, device=dev)
+    dv = _SourceView(dvalues)
+    if dbank is None:
+        dbank = torch.empty((E, R), dtype=sv.dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty((max(selected_workspace_bytes(desc), 256),), dtype=torch.uint8,
+                                device=dev)
+    _check(load().attnres_selected_bwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(bank),
+                                       _ptr(ids), _ptr(lse), _ptr(dout), ctypes.byref(dv.struct),
+                                       _ptr(dbank), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)))
+    return dvalues, dbank

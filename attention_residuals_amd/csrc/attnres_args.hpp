@@ -64,6 +64,16 @@ struct FinArgs {
 // Multi-query read: queries per launch group (the largest instantiated MQ).
 constexpr int kMaxGroupQueries = 4;
 
+// Selected-query read: per-token queries bank[ids[n * K + m0 + m]] (m0 = the group's first
+// query slot); ids outside [0, E) read a zero query and drop their bank gradient.
+struct SelArgs {
+  const void* bank;              // [E, R]
+  const int64_t* ids;            // [N, K]
+  int E, K, m0;
+  int first;                     // backward: the first query group (its partial rows start at 0)
+  int lds_bank;                  // backward: the partial bank rows live in LDS
+};
+
 struct MultiFwdArgs {
   const void* src[kMaxSources];
   int64_t row_stride;
@@ -77,6 +87,7 @@ struct MultiFwdArgs {
   int64_t l_sm, l_sn;
   uint32_t* ticket;              // dynamic token counter, zero at launch (nullptr: static split)
   int64_t tpt;                   // tokens per ticket
+  SelArgs sel;                   // selected-query kernels only
 };
 
 struct MultiBwdArgs {
@@ -93,8 +104,10 @@ struct MultiBwdArgs {
   int64_t g_sm, g_sn;
   float* part;                   // [gridDim.x, Mtot * R] partial du rows; this group's columns
   int64_t part_stride;           //   start at part, row stride part_stride floats
+                                 // (selected-query: [gridDim.x, E * R] partial bank rows)
   uint32_t* ticket;
   int64_t tpt;
+  SelArgs sel;
 };
 
 }  // namespace attnres

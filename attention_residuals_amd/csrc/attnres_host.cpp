@@ -194,11 +194,13 @@ size_t bwd_lds(const Shape& sh) {
 
 struct DevFacts {
   int cus = 0;
+  int lds_per_block = 0;  // bytes of LDS one workgroup may allocate
 };
 
 attnres_status device_facts(DevFacts* f) {
   static std::mutex mu;
   static int cached[64] = {0};
+  static int cached_lds[64] = {0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -209,9 +211,14 @@ attnres_status device_facts(DevFacts* f) {
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
     if (cus <= 0) return fail(ATTNRES_ERR_HIP, "device reports %d compute units", cus);
+    int lds = 0;
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock)");
     cached[dev] = cus;
+    cached_lds[dev] = lds;
   }
   f->cus = cached[dev];
+  f->lds_per_block = cached_lds[dev];
   return ATTNRES_OK;
 }
 
@@ -650,7 +657,8 @@ attnres_desc single_desc(const attnres_multi_desc* m) {
 // 4-wave workgroups (CH = ceil(chunks / 256)) measured best when the sources fit their bucket; with
 // more queries (and otherwise) the fewest chunks per thread with at most 8 waves, which leaves
 // registers for four queries per launch.
-attnres_status make_multi_shape(const attnres_multi_desc* m, MultiShape* ms) {
+attnres_status make_multi_shape(const attnres_multi_desc* m, MultiShape* ms,
+                                bool fewest_chunks = false) {
   if (!m) return fail(ATTNRES_ERR_INVALID_ARG, "desc is NULL");
   const attnres_desc d = single_desc(m);
   attnres_status st = check_desc(&d);
@@ -673,7 +681,7 @@ attnres_status make_multi_shape(const attnres_multi_desc* m, MultiShape* ms) {
   static const int forced = env_int("ATTNRES_MULTI_CH");
   if ((forced == 1 || forced == 2 || forced == 4) && (chunks + 64 * forced - 1) / (64 * forced) <= 8)
     ms->ch = forced;
-  if (!ms->ch && m->M <= 2) {
+  if (!ms->ch && m->M <= 2 && !fewest_chunks) {
     const int c = std::min(4, std::max(1, (chunks + 255) / 256));
     const int cc = c == 3 ? 4 : c;
     if ((chunks + 64 * cc - 1) / (64 * cc) <= 8 && bucket(cc) > 0) ms->ch = cc;
@@ -989,6 +997,310 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* m, const attnres_sour
   fa.cols = (int)(M * m->R);
   fa.query = queries;
   fa.dq = dq;
+  return launch(finalize_kernel_ptr(ms.base.bf16), (fa.cols + kFinCols - 1) / kFinCols, 1,
+                kFinCols * kFinPhases, 0, &fa, stream, "finalize launch");
+}
+
+}  // extern "C"
+
+// ====================================================================== selected-query read
+
+namespace {
+
+constexpr size_t kMaxSelPartialBytes = size_t(1) << 30;  // cap on the partial bank rows
+
+attnres_multi_desc multi_of(const attnres_selected_desc* d) {
+  attnres_multi_desc m;
+  std::memset(&m, 0, sizeof m);
+  m.S = d->S;
+  m.D = d->D;
+  m.R = d->R;
+  m.M = d->K;
+  m.dtype = d->dtype;
+  m.N = d->N;
+  m.eps = d->eps;
+  m.scale = d->scale;
+  m.layout = ATTNRES_TOKEN_MAJOR;
+  m.deterministic = d->deterministic;
+  m.accumulate_dvalues = d->accumulate_dvalues;
+  return m;
+}
+
+// The selected-query kernels are the multi-query kernels with per-token queries, built for groups
+// of two queries and one or two chunks per thread.
+attnres_status make_sel_shape(const attnres_selected_desc* d, MultiShape* ms) {
+  if (!d) return fail(ATTNRES_ERR_INVALID_ARG, "desc is NULL");
+  if (d->E < 1) return fail(ATTNRES_ERR_INVALID_ARG, "E=%d: the bank needs a row", d->E);
+  if (d->R >= 1 && (int64_t)d->E * d->R * 4 > (int64_t(1) << 31))
+    return fail(ATTNRES_ERR_UNSUPPORTED, "bank of %d x %d: over 2 GiB of FP32 partial rows", d->E,
+                d->R);
+  // eight-wave workgroups with the fewest chunks per thread: registers for the next token's bank
+  // rows beside the sources
+  const attnres_multi_desc m = multi_of(d);
+  attnres_status st = make_multi_shape(&m, ms, true);
+  if (st != ATTNRES_OK) return st;
+  if (ms->ch > 2)
+    return fail(ATTNRES_ERR_UNSUPPORTED, "selected-query read: D=%d is too wide", d->D);
+  ms->mq_max = 2;
+  return ATTNRES_OK;
+}
+
+// The backward's partial bank rows: in LDS when the whole [E, R] FP32 bank fits beside the exchange
+// buffers (kept to 64 KiB per workgroup, so two workgroups still share a CU), else per-workgroup
+// global blocks. Either way the workspace holds P blocks of E * R floats for the finaliser.
+constexpr size_t kSelLdsCap = 64 * 1024;
+
+struct SelBwdPlan {
+  int P = 0;
+  bool lds_bank = false;
+  size_t lds = 0;
+  size_t off_part = 256, bytes = 256;
+};
+
+attnres_status plan_sel_bwd(const attnres_selected_desc* d, const MultiShape& ms,
+                            SelBwdPlan* pl) {
+  const bool acc = d->accumulate_dvalues != 0;
+  const void* fn = ms.base.bf16 ? sel_bwd_kernel_ptr_bf16(ms.ch, ms.sb, ms.full, acc)
+                                : sel_bwd_kernel_ptr_f32(ms.ch, ms.sb, ms.full, acc);
+  if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query backward kernel for this shape");
+  DevFacts f;
+  attnres_status st = device_facts(&f);
+  if (st != ATTNRES_OK) return st;
+  const size_t row = (size_t)d->E * d->R * sizeof(float);
+  const size_t base = multi_bwd_lds(ms, 2);
+  pl->lds_bank = base + row <= std::min<size_t>(kSelLdsCap, (size_t)f.lds_per_block);
+  pl->lds = pl->lds_bank ? base + row : base;
+  int per_cu = 0;
+  st = blocks_per_cu(fn, ms.threads, pl->lds, &per_cu, 8);
+  if (st != ATTNRES_OK) return st;
+  const int64_t cap = std::max<int64_t>(1, (int64_t)(kMaxSelPartialBytes / row));
+  pl->P = (int)std::min<int64_t>(std::min<int64_t>(d->N, (int64_t)f.cus * per_cu), cap);
+  pl->off_part = 256;
+  pl->bytes = align256(pl->off_part + (size_t)pl->P * row);
+  return ATTNRES_OK;
+}
+
+attnres_status check_ids(const int64_t* ids, int64_t N, int K) {
+  if (N > 0 && (!ids || !aligned(ids, 8)))
+    return fail(ids ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "ids NULL or misaligned");
+  (void)K;
+  return ATTNRES_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attnres_status attnres_selected_fwd_workspace_bytes(const attnres_selected_desc* d,
+                                                    size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(ATTNRES_ERR_INVALID_ARG, "bytes is NULL");
+  MultiShape ms;
+  attnres_status st = make_sel_shape(d, &ms);
+  if (st != ATTNRES_OK) return st;
+  *bytes = kFwdWorkspaceBytes;
+  return ATTNRES_OK;
+}
+
+attnres_status attnres_selected_workspace_bytes(const attnres_selected_desc* d, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(ATTNRES_ERR_INVALID_ARG, "bytes is NULL");
+  MultiShape ms;
+  attnres_status st = make_sel_shape(d, &ms);
+  if (st != ATTNRES_OK) return st;
+  SelBwdPlan pl;
+  if ((st = plan_sel_bwd(d, ms, &pl)) != ATTNRES_OK) return st;
+  *bytes = pl.bytes;
+  return ATTNRES_OK;
+}
+
+attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnres_sources* values,
+                                    const void* bank, const int64_t* ids, void* y, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  MultiShape ms;
+  attnres_status st = make_sel_shape(d, &ms);
+  if (st != ATTNRES_OK) return st;
+  if (workspace && (workspace_bytes < kFwdWorkspaceBytes || !aligned(workspace, 256)))
+    return fail(ATTNRES_ERR_WORKSPACE, "forward workspace: %zu bytes given, %zu (256-byte aligned) "
+                "needed", workspace_bytes, kFwdWorkspaceBytes);
+  if (!workspace && workspace_bytes)
+    return fail(ATTNRES_ERR_WORKSPACE, "forward workspace is NULL but workspace_bytes = %zu",
+                workspace_bytes);
+  const attnres_multi_desc m = multi_of(d);
+  const attnres_desc d1 = single_desc(&m);
+  if ((st = check_param(bank, true, ms.base.esz, "bank")) != ATTNRES_OK) return st;
+  if ((st = check_ids(ids, d->N, d->K)) != ATTNRES_OK) return st;
+  if (d->N == 0) return ATTNRES_OK;
+  MultiFwdArgs a;
+  std::memset(&a, 0, sizeof a);
+  if ((st = check_sources(&d1, ms.base, values, "values", a.src)) != ATTNRES_OK) return st;
+  if (!y || !aligned(y, 16))
+    return fail(y ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "y NULL or misaligned");
+  if (!lse || !aligned(lse, 4))
+    return fail(lse ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "lse NULL or misaligned");
+  const int64_t N = d->N, K = d->K;
+  std::vector<Range> ins, outs;
+  for (int s = 0; s < d->S; ++s)
+    ins.push_back(rows_range(a.src[s], N, values->row_stride, d->D, ms.base.esz, "values"));
+  ins.push_back(rows_range(bank, d->E, d->R, d->R, ms.base.esz, "bank"));
+  ins.push_back(rows_range(ids, N, K, (int)K, 8, "ids"));
+  outs.push_back(rows_range(y, N * K, d->D, d->D, ms.base.esz, "y"));
+  outs.push_back(rows_range(lse, N * K, 1, 1, 4, "lse"));
+  if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
+
+  DevFacts f;
+  if ((st = device_facts(&f)) != ATTNRES_OK) return st;
+  const void* fn = sel_fwd_kernel_ptr(ms.base.bf16, ms.ch, ms.sb, ms.full);
+  if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query forward kernel for this shape");
+  const size_t lds = multi_fwd_lds(ms, 2);
+  int per_cu = 0;
+  if ((st = blocks_per_cu(fn, ms.threads, lds, &per_cu, 8)) != ATTNRES_OK) return st;
+  const int64_t resident = (int64_t)f.cus * per_cu;
+  const bool dyn = workspace != nullptr && N >= 2 * resident && N < kMaxTicketTokens;
+  const int64_t slots = resident * (dyn ? 1 : 8);
+  a.row_stride = values->row_stride;
+  a.N = N;
+  a.S = d->S;
+  a.D = d->D;
+  a.R = d->R;
+  a.lo = d->D - d->R;
+  a.eps = d->eps;
+  a.scale = d->scale;
+  a.inv_R = 1.0f / (float)d->R;
+  a.y_sm = d->D;
+  a.y_sn = K * d->D;
+  a.l_sm = 1;
+  a.l_sn = K;
+  a.sel.bank = bank;
+  a.sel.ids = ids;
+  a.sel.E = d->E;
+  a.sel.K = (int)K;
+  for (const Group& g : plan_groups(&m, ms)) {
+    a.tpt = dyn ? tokens_per_ticket(N, slots, (double)(d->S + 2) * d->D * ms.base.esz, 55.0, 1) : 1;
+    a.ticket = nullptr;
+    if (dyn) {
+      a.ticket = static_cast<uint32_t*>(workspace);
+      void* targ = a.ticket;
+      st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");
+      if (st != ATTNRES_OK) return st;
+    }
+    a.M = g.cnt;
+    a.sel.m0 = g.m0;
+    a.y = static_cast<char*>(y) + (int64_t)g.m0 * d->D * ms.base.esz;
+    a.lse = lse + g.m0;
+    const int grid = (int)std::min<int64_t>((N + a.tpt - 1) / a.tpt, slots);
+    st = launch(fn, grid, 1, ms.threads, lds, &a, stream, "selected-query forward launch");
+    if (st != ATTNRES_OK) return st;
+  }
+  return ATTNRES_OK;
+}
+
+attnres_status attnres_selected_bwd(const attnres_selected_desc* d, const attnres_sources* values,
+                                    const void* bank, const int64_t* ids, const float* lse,
+                                    const void* dout, const attnres_sources* dvalues, void* dbank,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  MultiShape ms;
+  attnres_status st = make_sel_shape(d, &ms);
+  if (st != ATTNRES_OK) return st;
+  const attnres_multi_desc m = multi_of(d);
+  const attnres_desc d1 = single_desc(&m);
+  const int64_t N = d->N, K = d->K;
+  MultiBwdArgs a;
+  std::memset(&a, 0, sizeof a);
+  const void* dptr[kMaxSources] = {nullptr};
+  if ((st = check_param(bank, true, ms.base.esz, "bank")) != ATTNRES_OK) return st;
+  if ((st = check_param(dbank, true, ms.base.esz, "dbank")) != ATTNRES_OK) return st;
+  if ((st = check_ids(ids, N, (int)K)) != ATTNRES_OK) return st;
+  if (N > 0) {
+    if ((st = check_sources(&d1, ms.base, values, "values", a.src)) != ATTNRES_OK) return st;
+    if ((st = check_sources(&d1, ms.base, dvalues, "dvalues", dptr)) != ATTNRES_OK) return st;
+    if (!lse || !aligned(lse, 4))
+      return fail(lse ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "lse NULL or misaligned");
+    if (!dout || !aligned(dout, 16))
+      return fail(dout ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "dout NULL or misaligned");
+  }
+  if (!workspace) return fail(ATTNRES_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(ATTNRES_ERR_ALIGNMENT, "workspace not 256-byte aligned");
+  std::vector<Range> ins, outs;
+  if (N > 0) {
+    for (int s = 0; s < d->S; ++s)
+      ins.push_back(rows_range(a.src[s], N, values->row_stride, d->D, ms.base.esz, "values"));
+    ins.push_back(rows_range(dout, N * K, d->D, d->D, ms.base.esz, "dout"));
+    ins.push_back(rows_range(lse, N * K, 1, 1, 4, "lse"));
+    ins.push_back(rows_range(ids, N, K, (int)K, 8, "ids"));
+    for (int s = 0; s < d->S; ++s)
+      outs.push_back(rows_range(dptr[s], N, dvalues->row_stride, d->D, ms.base.esz, "dvalues"));
+  }
+  ins.push_back(rows_range(bank, d->E, d->R, d->R, ms.base.esz, "bank"));
+  outs.push_back(rows_range(dbank, d->E, d->R, d->R, ms.base.esz, "dbank"));
+  if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
+
+  SelBwdPlan pl;
+  if ((st = plan_sel_bwd(d, ms, &pl)) != ATTNRES_OK) return st;
+  if (workspace_bytes < pl.bytes)
+    return fail(ATTNRES_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                pl.bytes);
+  char* ws = static_cast<char*>(workspace);
+  if (pl.P > 0) {
+    for (int s = 0; s < d->S; ++s) a.dsrc[s] = const_cast<void*>(dptr[s]);
+    a.row_stride = values->row_stride;
+    a.drow_stride = dvalues->row_stride;
+    a.N = N;
+    a.S = d->S;
+    a.D = d->D;
+    a.R = d->R;
+    a.lo = d->D - d->R;
+    a.eps = d->eps;
+    a.scale = d->scale;
+    a.inv_R = 1.0f / (float)d->R;
+    a.l_sm = 1;
+    a.l_sn = K;
+    a.g_sm = d->D;
+    a.g_sn = K * d->D;
+    a.part = reinterpret_cast<float*>(ws + pl.off_part);
+    a.part_stride = (int64_t)d->E * d->R;
+    a.sel.bank = bank;
+    a.sel.ids = ids;
+    a.sel.E = d->E;
+    a.sel.K = (int)K;
+    const std::vector<Group> groups = plan_groups(&m, ms);
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const Group& g = groups[gi];
+      const bool acc = d->accumulate_dvalues != 0 || gi > 0;
+      const void* fn = ms.base.bf16 ? sel_bwd_kernel_ptr_bf16(ms.ch, ms.sb, ms.full, acc)
+                                    : sel_bwd_kernel_ptr_f32(ms.ch, ms.sb, ms.full, acc);
+      if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query backward kernel");
+      a.tpt = 1;
+      a.ticket = nullptr;
+      if (!d->deterministic && N >= 2 * (int64_t)pl.P && N < kMaxTicketTokens) {
+        a.tpt = tokens_per_ticket(N, pl.P, (double)((acc ? 3 : 2) * d->S + 2) * d->D * ms.base.esz,
+                                  30.0, 16);
+        a.ticket = reinterpret_cast<uint32_t*>(ws);
+        void* targ = a.ticket;
+        st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");
+        if (st != ATTNRES_OK) return st;
+      }
+      a.M = g.cnt;
+      a.sel.m0 = g.m0;
+      a.sel.first = gi == 0 ? 1 : 0;
+      a.sel.lds_bank = pl.lds_bank ? 1 : 0;
+      a.lse = lse + g.m0;
+      a.dout = static_cast<const char*>(dout) + (int64_t)g.m0 * d->D * ms.base.esz;
+      st = launch(fn, pl.P, 1, ms.threads, pl.lds, &a, stream, "selected-query backward launch");
+      if (st != ATTNRES_OK) return st;
+    }
+  }
+  FinArgs fa;
+  std::memset(&fa, 0, sizeof fa);
+  fa.part_du = reinterpret_cast<const float*>(ws + pl.off_part);
+  fa.P = pl.P;
+  fa.R = d->E * d->R;
+  fa.D = 0;
+  fa.cols = d->E * d->R;
+  fa.query = bank;
+  fa.dq = dbank;
   return launch(finalize_kernel_ptr(ms.base.bf16), (fa.cols + kFinCols - 1) / kFinCols, 1,
                 kFinCols * kFinPhases, 0, &fa, stream, "finalize launch");
 }

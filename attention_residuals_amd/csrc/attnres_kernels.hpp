@@ -142,6 +142,24 @@ __device__ __forceinline__ void st_row(Rsrc r, uint32_t voff, const Chunk& c) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, c), r, voff, 0, 2);
 }
 
+// Loads and stores that go to L2 (sc0: no stale vector-L1 line), for rows a thread rewrites.
+__device__ __forceinline__ Chunk ld_row_cached(Rsrc r, uint32_t voff) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 1));
+}
+__device__ __forceinline__ void st_row_cached(Rsrc r, uint32_t voff, const Chunk& c) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, c), r, voff, 0, 1);
+}
+
+// (the 4-byte forms move integer words: FP32 values go through bit casts)
+__device__ __forceinline__ float ld_f32_cached(Rsrc r, uint32_t voff) {
+  return bits_f(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 1)));
+}
+__device__ __forceinline__ void st_f32_cached(Rsrc r, uint32_t voff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(f_bits(v), r, voff, 0, 1);
+}
+
 __device__ __forceinline__ void st_f32x4(float* p, float a, float b, float c, float d) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   f32x4 v = {a, b, c, d};

@@ -5,8 +5,8 @@
 namespace attnres {
 
 #define ATTNRES_CASE(MQ, CH, SB) \
-  case SB: return full ? (const void*)&multi_bwd_kernel<false, CH, SB, true, MQ, true> \
-                       : (const void*)&multi_bwd_kernel<false, CH, SB, false, MQ, true>;
+  case SB: return full ? (const void*)&multi_bwd_kernel<false, CH, SB, true, MQ, true, false> \
+                       : (const void*)&multi_bwd_kernel<false, CH, SB, false, MQ, true, false>;
 
 template <int MQ>
 static const void* bwd_ptr(int ch, int sb, bool full) {

@@ -5,8 +5,8 @@
 namespace attnres {
 
 #define ATTNRES_CASE(MQ, CH, SB) \
-  case SB: return full ? (const void*)&multi_bwd_kernel<false, CH, SB, true, MQ, false> \
-                       : (const void*)&multi_bwd_kernel<false, CH, SB, false, MQ, false>;
+  case SB: return full ? (const void*)&multi_bwd_kernel<false, CH, SB, true, MQ, false, false> \
+                       : (const void*)&multi_bwd_kernel<false, CH, SB, false, MQ, false, false>;
 
 template <int MQ>
 static const void* bwd_ptr(int ch, int sb, bool full) {

@@ -6,8 +6,8 @@
 namespace attnres {
 
 #define ATTNRES_CASE(BF, MQ, CH, SB) \
-  case SB: return full ? (const void*)&multi_fwd_kernel<BF, CH, SB, true, MQ> \
-                       : (const void*)&multi_fwd_kernel<BF, CH, SB, false, MQ>;
+  case SB: return full ? (const void*)&multi_fwd_kernel<BF, CH, SB, true, MQ, false> \
+                       : (const void*)&multi_fwd_kernel<BF, CH, SB, false, MQ, false>;
 
 template <bool BF, int MQ>
 static const void* fwd_ptr(int ch, int sb, bool full) {

@@ -65,6 +65,124 @@ struct MultiCols {
   }
 };
 
+// Selected-query read: the group's query slices for token `tok` (bank rows ids[tok, m0 + m]), zero
+// for padded slots, dead tokens and ids outside [0, E). With R % VEC == 0 a chunk lies wholly
+// inside or before the slice; each row is read through a resource of exactly R elements and a
+// chunk before the slice is given the offset R (out of range: reads zero). Otherwise the chunks
+// straddle the slice start and are gathered element by element.
+template <bool BF16, int CH, bool FULL, int MQ>
+__device__ __forceinline__ void load_sel_queries(const SelArgs& sa, int M, int R, int lo, int D,
+                                                 int64_t tok, bool live,
+                                                 const MultiCols<BF16, CH, FULL, MQ>& cs,
+                                                 Chunk (&q)[MQ][CH]) {
+  constexpr int VEC = Fmt<BF16>::VEC;
+  constexpr int ESZ = Fmt<BF16>::ESZ;
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) {
+    const int64_t id = (live && m < M) ? sa.ids[tok * sa.K + sa.m0 + m] : -1;
+    const bool ok = id >= 0 && id < sa.E;
+    const char* row = static_cast<const char*>(sa.bank) + (ok ? id : 0) * (int64_t)R * ESZ;
+    if (R % VEC == 0) {
+      const Rsrc rq = row_rsrc(ok ? row : nullptr, 0, ok ? static_cast<uint32_t>(R * ESZ) : 0u);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int idx = cs.col0[j] - lo;
+        q[m][j] = ld_row(rq, static_cast<uint32_t>((idx >= 0 ? idx : R) * ESZ));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        float v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const int idx = cs.col0[j] + e - lo;
+          v[e] = (ok && idx >= 0 && cs.col0[j] + e < D) ? load_param<BF16>(row, idx) : 0.f;
+        }
+        q[m][j] = pack<BF16>(v);
+      }
+    }
+  }
+}
+
+// Selected-query backward: a thread's columns [col, col + VEC) of one FP32 partial bank row, at
+// byte `row` of the workgroup's global block (a resource) or at float `row` of its LDS block. Only
+// columns inside the key slice [lo, D) are touched (global: the others read 0 and drop their
+// writes). With the slice start a multiple of 4 the columns go as 16-byte chunks (a chunk is then
+// wholly inside or outside the slice), else element by element.
+__device__ __forceinline__ uint32_t part_off(uint32_t row, int col, int lo, int D, uint32_t end) {
+  return (col >= lo && col < D) ? row + static_cast<uint32_t>((col - lo) * 4) : end;
+}
+
+template <int VEC>
+__device__ __forceinline__ void part_load(Rsrc rp, uint32_t row, int col, int lo, int D,
+                                          uint32_t end, bool al4, float (&v)[VEC]) {
+  if (al4) {
+#pragma unroll
+    for (int h = 0; h < VEC; h += 4) {
+      const Chunk c = ld_row_cached(rp, part_off(row, col + h, lo, D, end));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[h + k] = bits_f(c.w[k]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) v[e] = ld_f32_cached(rp, part_off(row, col + e, lo, D, end));
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void part_store(Rsrc rp, uint32_t row, int col, int lo, int D,
+                                           uint32_t end, bool al4, const float (&v)[VEC]) {
+  if (al4) {
+#pragma unroll
+    for (int h = 0; h < VEC; h += 4) {
+      Chunk c;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c.w[k] = f_bits(v[h + k]);
+      st_row_cached(rp, part_off(row, col + h, lo, D, end), c);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) st_f32_cached(rp, part_off(row, col + e, lo, D, end), v[e]);
+  }
+}
+
+// LDS block: v (+)= row[col - lo ...] over the slice; columns outside it read 0 / are skipped.
+template <int VEC>
+__device__ __forceinline__ void lds_part_load(const float* blk, int col, int lo, int D, bool al4,
+                                              float (&v)[VEC]) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  if (al4) {
+#pragma unroll
+    for (int h = 0; h < VEC; h += 4) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (col + h >= lo && col + h < D) x = *reinterpret_cast<const f32x4*>(blk + (col + h - lo));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[h + k] = x[k];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) v[e] = (col + e >= lo && col + e < D) ? blk[col + e - lo] : 0.f;
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void lds_part_store(float* blk, int col, int lo, int D, bool al4,
+                                               const float (&v)[VEC]) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  if (al4) {
+#pragma unroll
+    for (int h = 0; h < VEC; h += 4)
+      if (col + h >= lo && col + h < D) {
+        const f32x4 x = {v[h], v[h + 1], v[h + 2], v[h + 3]};
+        *reinterpret_cast<f32x4*>(blk + (col + h - lo)) = x;
+      }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      if (col + e >= lo && col + e < D) blk[col + e - lo] = v[e];
+  }
+}
+
 // Sum of t^2 over the slice for one row (this thread's chunks).
 template <bool BF16, int CH, bool FULL, int MQ>
 __device__ __forceinline__ float slice_sumsq(const Chunk (&r)[CH],
@@ -90,8 +208,9 @@ __device__ __forceinline__ float slice_sumsq(const Chunk (&r)[CH],
   return ss;
 }
 
-// Multi-query forward: all S <= SB sources of a token in one block.
-template <bool BF16, int CH, int SB, bool FULL, int MQ>
+// Multi-query forward: all S <= SB sources of a token in one block. SEL: the selected-query read
+// (each token's queries come from the bank; the next token's are loaded once it is known).
+template <bool BF16, int CH, int SB, bool FULL, int MQ, bool SEL>
 __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
@@ -104,9 +223,10 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
   const uint32_t row_bytes = static_cast<uint32_t>(a.D * ESZ);
 
   MultiCols<BF16, CH, FULL, MQ> cs;
-  cs.init(tid, nthr, a.D, a.lo, a.M, a.query, a.R);
+  cs.init(tid, nthr, a.D, a.lo, SEL ? 0 : a.M, a.query, a.R);
   int buf = 0;
   Chunk rows[SB][CH];
+  Chunk qn[SEL ? MQ : 1][CH];  // SEL: the next token's query slices
 
   // token schedule: batches of B tokens, later batches from the counter (as the single-query
   // kernels: the ticket is taken at the top of a batch's last token and published through LDS at
@@ -114,6 +234,7 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
   const bool dyn = a.ticket != nullptr;
   const int64_t B = dyn ? a.tpt : 1;
   const int64_t n0 = (int64_t)blockIdx.x * B;
+  if constexpr (SEL) load_sel_queries(a.sel, a.M, a.R, a.lo, a.D, n0, n0 < a.N, cs, cs.q);
   {
     const int live = n0 < a.N ? a.S : 0;
 #pragma unroll
@@ -163,6 +284,7 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
       batch_end = next + B;
     }
     buf ^= 1;
+    if constexpr (SEL) load_sel_queries(a.sel, a.M, a.R, a.lo, a.D, next, next < a.N, cs, qn);
 
     // lane s finishes source s for every query of the group
     float pw[MQ], lse[MQ];
@@ -224,13 +346,22 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
       for (int m = 1; m < MQ; ++m) v = (tid == m) ? lse[m] : v;
       a.lse[tid * a.l_sm + n * a.l_sn] = v;
     }
+    if constexpr (SEL) {
+#pragma unroll
+      for (int m = 0; m < MQ; ++m)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) cs.q[m][j] = qn[SEL ? m : 0][j];
+    }
     n = next;
   }
 }
 
 // Multi-query backward, token-resident. ACC: dvalues accumulate (existing rows prefetched one
-// token ahead like the source rows).
-template <bool BF16, int CH, int SB, bool FULL, int MQ, bool ACC>
+// token ahead like the source rows). SEL: the selected-query read; each token's query gradients
+// are added into this workgroup's FP32 partial rows of the bank rows it selected (zeroed at the
+// start; each thread only touches its own columns, read at the top of the token and written back
+// at its end), summed over workgroups by the finaliser.
+template <bool BF16, int CH, int SB, bool FULL, int MQ, bool ACC, bool SEL>
 __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
@@ -244,7 +375,30 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
   const int S = a.S;
 
   MultiCols<BF16, CH, FULL, MQ> cs;
-  cs.init(tid, nthr, a.D, a.lo, a.M, a.query, a.R);
+  cs.init(tid, nthr, a.D, a.lo, SEL ? 0 : a.M, a.query, a.R);
+  Chunk qn[SEL ? MQ : 1][CH];
+  // SEL: this workgroup's FP32 partial rows of the whole bank [E, R]: in LDS after the exchange
+  // buffers when they fit (a.sel.lds_bank; added into the global block once, at the end), else its
+  // global block, read-modify-written per token through L2. Each thread only touches its own
+  // columns, so no barrier guards them.
+  const uint32_t pend = SEL ? static_cast<uint32_t>(a.sel.E * a.R * 4) : 0u;
+  const bool al4 = (a.lo & 3) == 0;
+  const Rsrc rpart = row_rsrc(SEL ? a.part + (int64_t)blockIdx.x * a.part_stride : nullptr, 0, pend);
+  float* lbank = lds + 2 * xfl + 4;
+  if (SEL && (a.sel.lds_bank || a.sel.first)) {
+    float zero[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) zero[e] = 0.f;
+    for (int e = 0; e < a.sel.E; ++e)
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        if (a.sel.lds_bank)
+          lds_part_store<VEC>(lbank + e * a.R, cs.col0[j], a.lo, a.D, al4, zero);
+        else
+          part_store<VEC>(rpart, static_cast<uint32_t>(e * a.R * 4), cs.col0[j], a.lo, a.D, pend,
+                          al4, zero);
+      }
+  }
   float du[MQ][CH][VEC];
 #pragma unroll
   for (int m = 0; m < MQ; ++m)
@@ -264,6 +418,7 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
   // its rows
   float lse_l = 0.f;
   if (lane < a.M && n0 < a.N) lse_l = a.lse[lane * a.l_sm + n0 * a.l_sn];
+  if constexpr (SEL) load_sel_queries(a.sel, a.M, a.R, a.lo, a.D, n0, n0 < a.N, cs, cs.q);
   {
     const int live = n0 < a.N ? S : 0;
 #pragma unroll
@@ -294,6 +449,19 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
     const bool take = dyn && n + 1 >= batch_end;
     uint32_t tk = 0;
     if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
+    // SEL: the bank rows this token's slots selected (-1: an invalid id or a padded slot)
+    int bid[SEL ? MQ : 1];
+    if constexpr (SEL) {
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) {
+        const int64_t id = (m < a.M) ? a.sel.ids[n * a.sel.K + a.sel.m0 + m] : -1;
+        bid[m] = (id >= 0 && id < a.sel.E) ? static_cast<int>(id) : -1;
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) du[m][j][e] = 0.f;
+      }
+    }
     float* xb = lds + buf * xfl;
 #pragma unroll
     for (int i0 = 0; i0 < SB; i0 += kGroup) {
@@ -322,6 +490,7 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
     }
     const bool has_next = next < a.N;
     buf ^= 1;
+    if constexpr (SEL) load_sel_queries(a.sel, a.M, a.R, a.lo, a.D, next, has_next, cs, qn);
 
     // lane s finishes source s
     float pw[MQ], aw[MQ], Bs = 0.f;
@@ -416,7 +585,56 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
         for (int j = 0; j < CH; ++j) odv[i][j] = ld_row(rn, cs.voff[j]);
       }
     }
+    if constexpr (SEL) {
+      // this token's query gradients into the partial bank rows it selected, slot by slot (two
+      // slots naming one row add in order: the thread reads back its own earlier write)
+#pragma unroll
+      for (int m = 0; m < MQ; ++m) {
+        if (bid[m] < 0) continue;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          float v[VEC];
+          if (a.sel.lds_bank) {
+            float* blk = lbank + bid[m] * a.R;
+            lds_part_load<VEC>(blk, cs.col0[j], a.lo, a.D, al4, v);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] += du[m][j][e];
+            lds_part_store<VEC>(blk, cs.col0[j], a.lo, a.D, al4, v);
+          } else {
+            const uint32_t row = static_cast<uint32_t>(bid[m] * a.R * 4);
+            part_load<VEC>(rpart, row, cs.col0[j], a.lo, a.D, pend, al4, v);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] += du[m][j][e];
+            part_store<VEC>(rpart, row, cs.col0[j], a.lo, a.D, pend, al4, v);
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MQ; ++m)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) cs.q[m][j] = qn[SEL ? m : 0][j];
+    }
     n = next;
+  }
+  if constexpr (SEL) {
+    // LDS partial rows into the global block: stored by the first query group, added by later ones
+    if (a.sel.lds_bank) {
+      for (int e = 0; e < a.sel.E; ++e)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          float v[VEC];
+          lds_part_load<VEC>(lbank + e * a.R, cs.col0[j], a.lo, a.D, al4, v);
+          const uint32_t row = static_cast<uint32_t>(e * a.R * 4);
+          if (!a.sel.first) {
+            float g[VEC];
+            part_load<VEC>(rpart, row, cs.col0[j], a.lo, a.D, pend, al4, g);
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) v[k] += g[k];
+          }
+          part_store<VEC>(rpart, row, cs.col0[j], a.lo, a.D, pend, al4, v);
+        }
+    }
+    return;
   }
 
   // this workgroup's partial du rows of the group's queries (slice columns only)

@@ -237,6 +237,86 @@ multi_fwd_packed.register_autograd(_backward_multi, setup_context=_setup_multi)
 multi_fwd_list.register_autograd(_backward_multi, setup_context=_setup_multi)
 
 
+# ---------------------------------------------------------------- selected-query read
+
+@torch.library.custom_op("attnres_amd::selected_fwd_packed", mutates_args=(), device_types="cuda")
+def selected_fwd_packed(values: Tensor, bank: Tensor, ids: Tensor, eps: float, scale: float,
+                        deterministic: bool) -> Tuple[Tensor, Tensor]:
+    return B.attnres_selected_fwd(values, bank, ids, eps=eps, scale=scale)
+
+
+@selected_fwd_packed.register_fake
+def _(values, bank, ids, eps, scale, deterministic):
+    _, N, D = values.shape
+    K = ids.shape[1]
+    return values.new_empty((N, K, D)), values.new_empty((N, K), dtype=torch.float32)
+
+
+@torch.library.custom_op("attnres_amd::selected_fwd_list", mutates_args=(), device_types="cuda")
+def selected_fwd_list(values: List[Tensor], bank: Tensor, ids: Tensor, eps: float, scale: float,
+                      deterministic: bool) -> Tuple[Tensor, Tensor]:
+    return B.attnres_selected_fwd(list(values), bank, ids, eps=eps, scale=scale)
+
+
+@selected_fwd_list.register_fake
+def _(values, bank, ids, eps, scale, deterministic):
+    N, D = values[0].shape
+    K = ids.shape[1]
+    return values[0].new_empty((N, K, D)), values[0].new_empty((N, K), dtype=torch.float32)
+
+
+@torch.library.custom_op("attnres_amd::selected_bwd_packed", mutates_args=(), device_types="cuda")
+def selected_bwd_packed(values: Tensor, bank: Tensor, ids: Tensor, lse: Tensor, dy: Tensor,
+                        eps: float, scale: float, deterministic: bool) -> Tuple[Tensor, Tensor]:
+    return B.attnres_selected_bwd(values, bank, ids, lse, dy.contiguous(), eps=eps, scale=scale,
+                                  deterministic=deterministic)
+
+
+@selected_bwd_packed.register_fake
+def _(values, bank, ids, lse, dy, eps, scale, deterministic):
+    return values.new_empty(values.shape), bank.new_empty(bank.shape)
+
+
+@torch.library.custom_op("attnres_amd::selected_bwd_list", mutates_args=(), device_types="cuda")
+def selected_bwd_list(values: List[Tensor], bank: Tensor, ids: Tensor, lse: Tensor, dy: Tensor,
+                      eps: float, scale: float,
+                      deterministic: bool) -> Tuple[List[Tensor], Tensor]:
+    vals = list(values)
+    dvalues = [torch.empty(v.shape, dtype=v.dtype, device=v.device) for v in vals]
+    _, dbank = B.attnres_selected_bwd(vals, bank, ids, lse, dy.contiguous(), eps=eps, scale=scale,
+                                      deterministic=deterministic, dvalues=dvalues)
+    return dvalues, dbank
+
+
+@selected_bwd_list.register_fake
+def _(values, bank, ids, lse, dy, eps, scale, deterministic):
+    return [v.new_empty(v.shape) for v in values], bank.new_empty(bank.shape)
+
+
+def _setup_selected(ctx, inputs, output):
+    values, bank, ids, eps, scale, deterministic = inputs
+    _, lse = output
+    ctx.packed = isinstance(values, Tensor)
+    vals = [values] if ctx.packed else list(values)
+    ctx.args = (eps, scale, deterministic)
+    ctx.save_for_backward(bank, ids, lse, *vals)
+
+
+def _backward_selected(ctx, gy, glse):
+    bank, ids, lse, *vals = ctx.saved_tensors
+    eps, scale, deterministic = ctx.args
+    if ctx.packed:
+        dvalues, dbank = selected_bwd_packed(vals[0], bank, ids, lse, gy, eps, scale,
+                                             deterministic)
+    else:
+        dvalues, dbank = selected_bwd_list(vals, bank, ids, lse, gy, eps, scale, deterministic)
+    return dvalues, dbank, None, None, None, None
+
+
+selected_fwd_packed.register_autograd(_backward_selected, setup_context=_setup_selected)
+selected_fwd_list.register_autograd(_backward_selected, setup_context=_setup_selected)
+
+
 # ---------------------------------------------------------------- user-facing calls
 
 def _flatten_sources(values, D_last: bool = True):
@@ -290,3 +370,22 @@ def attnres_multi(values, queries: Tensor, *, eps: float = B.EPS_DEFAULT, scale:
     if output_layout == "query_major":
         return y.reshape(M, *lead, D)
     return y.reshape(*lead, M, D)
+
+
+def attnres_selected(values, query_bank: Tensor, ids: Tensor, *, eps: float = B.EPS_DEFAULT,
+                     scale: float = 1.0, deterministic: bool = False) -> Tensor:
+    """Selected-query AttnRes read ("Fast Attention Residuals" page, Multi-query AttnRes: per-token
+    query selection): token t reads the sources with the K queries query_bank[ids[t, k]] of an
+    [E, R] bank. ids: integer [..., K] over the sources' leading shape. Returns [..., K, D]. An id
+    outside [0, E) reads a zero query (uniform weights) and adds nothing to the bank's gradient."""
+    if query_bank.dim() != 2:
+        raise ValueError("query_bank must be [E, R]")
+    packed, flat, lead, D = _flatten_sources(values)
+    if tuple(ids.shape[:-1]) != tuple(lead):
+        raise ValueError(f"ids must be [..., K] over the sources' leading shape {tuple(lead)}")
+    K = ids.shape[-1]
+    flat_ids = ids.reshape(-1, K).to(torch.int64).contiguous()
+    op = selected_fwd_packed if packed else selected_fwd_list
+    y, _ = op(flat, query_bank.contiguous(), flat_ids, float(eps), float(scale),
+              bool(deterministic))
+    return y.reshape(*lead, K, D)

@@ -183,6 +183,45 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* desc, const attnres_s
                                  const attnres_sources* dvalues, void* dq, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- selected-query read
+ * Same section, per-token query selection: token n reads the sources with the K queries
+ * bank[ids[n, k]] (1 <= K <= 16) of an [E, R] bank; outputs are token-major y [N, K, D] and lse
+ * [N, K]. The backward returns dvalues (summed over the K reads) and dbank [E, R]: for every bank
+ * row e, the sum of the query gradients of all (n, k) with ids[n, k] = e. ids are int64 on the
+ * device; an id outside [0, E) reads a zero query and its bank gradient is dropped. Token-resident
+ * with one or two chunks per thread (D <= 8192 bf16 / 4096 f32); queries run in groups of two.
+ * The bank gradient goes through per-workgroup FP32 partial rows of the whole bank (the workspace
+ * is 256 + P * E * R * 4 bytes, P = backward workgroups), so a large bank costs workspace and
+ * traffic. */
+typedef struct {
+  int32_t S, D, R;
+  int32_t E;               /* bank rows, >= 1 */
+  int32_t K;               /* queries per token, 1 <= K <= 16 */
+  int32_t dtype;
+  int64_t N;
+  float eps, scale;
+  int32_t deterministic;   /* as in attnres_desc (backward) */
+  int32_t accumulate_dvalues;
+} attnres_selected_desc;
+
+attnres_status attnres_selected_fwd_workspace_bytes(const attnres_selected_desc* desc,
+                                                    size_t* bytes);
+attnres_status attnres_selected_workspace_bytes(const attnres_selected_desc* desc, size_t* bytes);
+
+/* Forward. bank [E, R]; ids [N, K] int64 (device); y [N, K, D] and lse [N, K] FP32 (written);
+ * workspace optional as for attnres_fwd. */
+attnres_status attnres_selected_fwd(const attnres_selected_desc* desc,
+                                    const attnres_sources* values, const void* bank,
+                                    const int64_t* ids, void* y, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Backward. dout [N, K, D] (contiguous); dbank [E, R] (written). */
+attnres_status attnres_selected_bwd(const attnres_selected_desc* desc,
+                                    const attnres_sources* values, const void* bank,
+                                    const int64_t* ids, const float* lse, const void* dout,
+                                    const attnres_sources* dvalues, void* dbank, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* attnres_status_str(attnres_status status);
 

@@ -211,3 +211,24 @@ def _multi_status(**kw):
 def test_multi_descriptor_validation(kw, expect):
     st = _multi_status(**kw)
     assert st == expect, (kw, st, A.load().attnres_last_error())
+
+
+def _selected_status(**kw):
+    base = dict(S=4, N=16, D=256, R=256, E=8, K=2, dtype=torch.bfloat16)
+    base.update(kw)
+    d = B.make_selected_desc(base["S"], base["N"], base["D"], base["R"], base["E"], base["K"],
+                             base["dtype"])
+    n = ctypes.c_size_t(0)
+    return A.load().attnres_selected_fwd_workspace_bytes(ctypes.byref(d), ctypes.byref(n))
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), OK), (dict(K=16), OK), (dict(K=0), INVALID), (dict(K=17), INVALID),
+    (dict(E=0), INVALID), (dict(R=300), INVALID), (dict(R=5), OK),
+    (dict(S=24, D=4096, R=4096), OK), (dict(S=12, D=8192, R=8192), OK),
+    (dict(S=13, D=8192, R=8192), UNSUPPORTED), (dict(D=16384, R=16384), UNSUPPORTED),
+    (dict(E=1 << 18, D=4096, R=4096), UNSUPPORTED),
+])
+def test_selected_descriptor_validation(kw, expect):
+    st = _selected_status(**kw)
+    assert st == expect, (kw, st, A.load().attnres_last_error())

@@ -65,3 +65,23 @@ def test_multi_query_ops_shapes(layout):
                                      False)
         assert lse.shape == ((3, 14) if layout == "query_major" else (14, 3))
         assert lse.dtype == torch.float32
+
+
+def test_selected_query_ops_shapes():
+    with FakeTensorMode():
+        v = _t(5, 3, 4, 1024)
+        bank = _t(6, 512)
+        ids = torch.empty((3, 4, 2), dtype=torch.int64, device="cuda")
+        y = A.attnres_selected(v, bank, ids)
+        assert y.shape == (3, 4, 2, 1024) and y.dtype == BF
+        flat = v.reshape(5, 12, 1024)
+        fids = ids.reshape(12, 2)
+        yk, lse = ops.selected_fwd_packed(flat, bank, fids, 1e-6, 1.0, False)
+        assert yk.shape == (12, 2, 1024) and lse.shape == (12, 2) and lse.dtype == torch.float32
+        dv, db = ops.selected_bwd_packed(flat, bank, fids, lse, yk, 1e-6, 1.0, False)
+        assert dv.shape == flat.shape and db.shape == bank.shape
+        dvs, db2 = ops.selected_bwd_list([flat[s] for s in range(5)], bank, fids, lse, yk, 1e-6,
+                                         1.0, False)
+        assert [d.shape for d in dvs] == [(12, 1024)] * 5 and db2.shape == bank.shape
+        with pytest.raises(ValueError):
+            A.attnres_selected(v, bank, torch.empty((3, 2), dtype=torch.int64, device="cuda"))
