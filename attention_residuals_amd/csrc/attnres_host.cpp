@@ -1027,17 +1027,23 @@ attnres_multi_desc multi_of(const attnres_selected_desc* d) {
 }
 
 // The selected-query kernels are the multi-query kernels with per-token queries, built for groups
-// of two queries and one or two chunks per thread.
-attnres_status make_sel_shape(const attnres_selected_desc* d, MultiShape* ms) {
+// of two queries and one or two chunks per thread. The forward takes the two-query read's
+// workgroup shape (four waves when the sources fit their bucket: most bytes in flight per CU). The
+// backward takes eight waves with the fewest chunks per thread: its per-token bank update keeps
+// the query gradients and their partial rows live beside the sources, which at two chunks per
+// thread spills heavily (measured 2.9x slower at S = 10, D = 4096 bf16).
+attnres_status make_sel_shape(const attnres_selected_desc* d, MultiShape* ms, bool backward) {
   if (!d) return fail(ATTNRES_ERR_INVALID_ARG, "desc is NULL");
   if (d->E < 1) return fail(ATTNRES_ERR_INVALID_ARG, "E=%d: the bank needs a row", d->E);
   if (d->R >= 1 && (int64_t)d->E * d->R * 4 > (int64_t(1) << 31))
     return fail(ATTNRES_ERR_UNSUPPORTED, "bank of %d x %d: over 2 GiB of FP32 partial rows", d->E,
                 d->R);
-  // eight-wave workgroups with the fewest chunks per thread: registers for the next token's bank
-  // rows beside the sources
   const attnres_multi_desc m = multi_of(d);
-  attnres_status st = make_multi_shape(&m, ms, true);
+  attnres_status st = make_multi_shape(&m, ms, backward);
+  if (st == ATTNRES_OK && ms->ch > 2) {  // four-chunk rows: the eight-wave shape
+    *ms = MultiShape();
+    st = make_multi_shape(&m, ms, true);
+  }
   if (st != ATTNRES_OK) return st;
   if (ms->ch > 2)
     return fail(ATTNRES_ERR_UNSUPPORTED, "selected-query read: D=%d is too wide", d->D);
@@ -1046,9 +1052,11 @@ attnres_status make_sel_shape(const attnres_selected_desc* d, MultiShape* ms) {
 }
 
 // The backward's partial bank rows: in LDS when the whole [E, R] FP32 bank fits beside the exchange
-// buffers (kept to 64 KiB per workgroup, so two workgroups still share a CU), else per-workgroup
-// global blocks. Either way the workspace holds P blocks of E * R floats for the finaliser.
-constexpr size_t kSelLdsCap = 64 * 1024;
+// buffers within one workgroup's LDS allocation, else per-workgroup global blocks. Either way the
+// workspace holds P blocks of E * R floats for the finaliser. (The eight-wave backward holds one
+// workgroup per CU for its registers, so a large LDS block costs no occupancy there; the host
+// takes the occupancy with the LDS size into account either way.)
+constexpr size_t kSelLdsCap = 160 * 1024;
 
 struct SelBwdPlan {
   int P = 0;
@@ -1096,7 +1104,7 @@ attnres_status attnres_selected_fwd_workspace_bytes(const attnres_selected_desc*
   g_err.clear();
   if (!bytes) return fail(ATTNRES_ERR_INVALID_ARG, "bytes is NULL");
   MultiShape ms;
-  attnres_status st = make_sel_shape(d, &ms);
+  attnres_status st = make_sel_shape(d, &ms, false);
   if (st != ATTNRES_OK) return st;
   *bytes = kFwdWorkspaceBytes;
   return ATTNRES_OK;
@@ -1106,7 +1114,7 @@ attnres_status attnres_selected_workspace_bytes(const attnres_selected_desc* d, 
   g_err.clear();
   if (!bytes) return fail(ATTNRES_ERR_INVALID_ARG, "bytes is NULL");
   MultiShape ms;
-  attnres_status st = make_sel_shape(d, &ms);
+  attnres_status st = make_sel_shape(d, &ms, true);
   if (st != ATTNRES_OK) return st;
   SelBwdPlan pl;
   if ((st = plan_sel_bwd(d, ms, &pl)) != ATTNRES_OK) return st;
@@ -1119,7 +1127,7 @@ attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnre
                                     void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   MultiShape ms;
-  attnres_status st = make_sel_shape(d, &ms);
+  attnres_status st = make_sel_shape(d, &ms, false);
   if (st != ATTNRES_OK) return st;
   if (workspace && (workspace_bytes < kFwdWorkspaceBytes || !aligned(workspace, 256)))
     return fail(ATTNRES_ERR_WORKSPACE, "forward workspace: %zu bytes given, %zu (256-byte aligned) "
@@ -1202,7 +1210,7 @@ attnres_status attnres_selected_bwd(const attnres_selected_desc* d, const attnre
                                     void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   MultiShape ms;
-  attnres_status st = make_sel_shape(d, &ms);
+  attnres_status st = make_sel_shape(d, &ms, true);
   if (st != ATTNRES_OK) return st;
   const attnres_multi_desc m = multi_of(d);
   const attnres_desc d1 = single_desc(&m);

@@ -65,23 +65,33 @@ struct MultiCols {
   }
 };
 
-// Selected-query read: the group's query slices for token `tok` (bank rows ids[tok, m0 + m]), zero
-// for padded slots, dead tokens and ids outside [0, E). With R % VEC == 0 a chunk lies wholly
+// Selected-query read: the bank rows a token's slots select (ids[tok, m0 + m]); -1 for padded slots,
+// dead tokens and ids outside [0, E).
+template <int MQ>
+__device__ __forceinline__ void load_sel_ids(const SelArgs& sa, int M, int64_t tok, bool live,
+                                             int (&id)[MQ]) {
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) {
+    const int64_t v = (live && m < M) ? sa.ids[tok * sa.K + sa.m0 + m] : -1;
+    id[m] = (v >= 0 && v < sa.E) ? static_cast<int>(v) : -1;
+  }
+}
+
+// The query slices of bank rows `id` (zero for id < 0). With R % VEC == 0 a chunk lies wholly
 // inside or before the slice; each row is read through a resource of exactly R elements and a
 // chunk before the slice is given the offset R (out of range: reads zero). Otherwise the chunks
 // straddle the slice start and are gathered element by element.
 template <bool BF16, int CH, bool FULL, int MQ>
-__device__ __forceinline__ void load_sel_queries(const SelArgs& sa, int M, int R, int lo, int D,
-                                                 int64_t tok, bool live,
+__device__ __forceinline__ void load_sel_queries(const SelArgs& sa, int R, int lo, int D,
+                                                 const int (&id)[MQ],
                                                  const MultiCols<BF16, CH, FULL, MQ>& cs,
                                                  Chunk (&q)[MQ][CH]) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
 #pragma unroll
   for (int m = 0; m < MQ; ++m) {
-    const int64_t id = (live && m < M) ? sa.ids[tok * sa.K + sa.m0 + m] : -1;
-    const bool ok = id >= 0 && id < sa.E;
-    const char* row = static_cast<const char*>(sa.bank) + (ok ? id : 0) * (int64_t)R * ESZ;
+    const bool ok = id[m] >= 0;
+    const char* row = static_cast<const char*>(sa.bank) + (ok ? id[m] : 0) * (int64_t)R * ESZ;
     if (R % VEC == 0) {
       const Rsrc rq = row_rsrc(ok ? row : nullptr, 0, ok ? static_cast<uint32_t>(R * ESZ) : 0u);
 #pragma unroll
@@ -226,7 +236,6 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
   cs.init(tid, nthr, a.D, a.lo, SEL ? 0 : a.M, a.query, a.R);
   int buf = 0;
   Chunk rows[SB][CH];
-  Chunk qn[SEL ? MQ : 1][CH];  // SEL: the next token's query slices
 
   // token schedule: batches of B tokens, later batches from the counter (as the single-query
   // kernels: the ticket is taken at the top of a batch's last token and published through LDS at
@@ -234,7 +243,11 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
   const bool dyn = a.ticket != nullptr;
   const int64_t B = dyn ? a.tpt : 1;
   const int64_t n0 = (int64_t)blockIdx.x * B;
-  if constexpr (SEL) load_sel_queries(a.sel, a.M, a.R, a.lo, a.D, n0, n0 < a.N, cs, cs.q);
+  if constexpr (SEL) {
+    int id[MQ];
+    load_sel_ids<MQ>(a.sel, a.M, n0, n0 < a.N, id);
+    load_sel_queries<BF16, CH, FULL, MQ>(a.sel, a.R, a.lo, a.D, id, cs, cs.q);
+  }
   {
     const int live = n0 < a.N ? a.S : 0;
 #pragma unroll
@@ -284,7 +297,12 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
       batch_end = next + B;
     }
     buf ^= 1;
-    if constexpr (SEL) load_sel_queries(a.sel, a.M, a.R, a.lo, a.D, next, next < a.N, cs, qn);
+    // SEL: the queries are not used again for this token: load the next token's in their place
+    if constexpr (SEL) {
+      int nid[MQ];
+      load_sel_ids<MQ>(a.sel, a.M, next, next < a.N, nid);
+      load_sel_queries<BF16, CH, FULL, MQ>(a.sel, a.R, a.lo, a.D, nid, cs, cs.q);
+    }
 
     // lane s finishes source s for every query of the group
     float pw[MQ], lse[MQ];
@@ -346,12 +364,6 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
       for (int m = 1; m < MQ; ++m) v = (tid == m) ? lse[m] : v;
       a.lse[tid * a.l_sm + n * a.l_sn] = v;
     }
-    if constexpr (SEL) {
-#pragma unroll
-      for (int m = 0; m < MQ; ++m)
-#pragma unroll
-        for (int j = 0; j < CH; ++j) cs.q[m][j] = qn[SEL ? m : 0][j];
-    }
     n = next;
   }
 }
@@ -376,7 +388,6 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
 
   MultiCols<BF16, CH, FULL, MQ> cs;
   cs.init(tid, nthr, a.D, a.lo, SEL ? 0 : a.M, a.query, a.R);
-  Chunk qn[SEL ? MQ : 1][CH];
   // SEL: this workgroup's FP32 partial rows of the whole bank [E, R]: in LDS after the exchange
   // buffers when they fit (a.sel.lds_bank; added into the global block once, at the end), else its
   // global block, read-modify-written per token through L2. Each thread only touches its own
@@ -418,7 +429,14 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
   // its rows
   float lse_l = 0.f;
   if (lane < a.M && n0 < a.N) lse_l = a.lse[lane * a.l_sm + n0 * a.l_sn];
-  if constexpr (SEL) load_sel_queries(a.sel, a.M, a.R, a.lo, a.D, n0, n0 < a.N, cs, cs.q);
+  // SEL: the current token's bank rows, and the next token's rows and query slices (loaded right
+  // after the exchange barrier, in flight during the dV loop)
+  int bid[SEL ? MQ : 1], nid[SEL ? MQ : 1];
+  Chunk qn[SEL ? MQ : 1][CH];
+  if constexpr (SEL) {
+    load_sel_ids<MQ>(a.sel, a.M, n0, n0 < a.N, bid);
+    load_sel_queries<BF16, CH, FULL, MQ>(a.sel, a.R, a.lo, a.D, bid, cs, cs.q);
+  }
   {
     const int live = n0 < a.N ? S : 0;
 #pragma unroll
@@ -449,18 +467,20 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
     const bool take = dyn && n + 1 >= batch_end;
     uint32_t tk = 0;
     if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
-    // SEL: the bank rows this token's slots selected (-1: an invalid id or a padded slot)
-    int bid[SEL ? MQ : 1];
+    // SEL: this token's query gradients start from zero; with global partial blocks the rows they
+    // add into are read now (the thread's own stores of earlier tokens precede these loads)
+    float pold[SEL ? MQ : 1][CH][SEL ? VEC : 1];
     if constexpr (SEL) {
 #pragma unroll
-      for (int m = 0; m < MQ; ++m) {
-        const int64_t id = (m < a.M) ? a.sel.ids[n * a.sel.K + a.sel.m0 + m] : -1;
-        bid[m] = (id >= 0 && id < a.sel.E) ? static_cast<int>(id) : -1;
+      for (int m = 0; m < MQ; ++m)
 #pragma unroll
-        for (int j = 0; j < CH; ++j)
+        for (int j = 0; j < CH; ++j) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) du[m][j][e] = 0.f;
-      }
+          if (!a.sel.lds_bank && bid[m] >= 0)
+            part_load<VEC>(rpart, static_cast<uint32_t>(bid[m] * a.R * 4), cs.col0[j], a.lo, a.D,
+                           pend, al4, pold[m][j]);
+        }
     }
     float* xb = lds + buf * xfl;
 #pragma unroll
@@ -490,7 +510,10 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
     }
     const bool has_next = next < a.N;
     buf ^= 1;
-    if constexpr (SEL) load_sel_queries(a.sel, a.M, a.R, a.lo, a.D, next, has_next, cs, qn);
+    if constexpr (SEL) {
+      load_sel_ids<MQ>(a.sel, a.M, next, has_next, nid);
+      load_sel_queries<BF16, CH, FULL, MQ>(a.sel, a.R, a.lo, a.D, nid, cs, qn);
+    }
 
     // lane s finishes source s
     float pw[MQ], aw[MQ], Bs = 0.f;
@@ -586,8 +609,8 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
       }
     }
     if constexpr (SEL) {
-      // this token's query gradients into the partial bank rows it selected, slot by slot (two
-      // slots naming one row add in order: the thread reads back its own earlier write)
+      // this token's query gradients into the partial bank rows it selected, slot by slot (a row
+      // named by two slots adds both: the later slot starts from the earlier one's result)
 #pragma unroll
       for (int m = 0; m < MQ; ++m) {
         if (bid[m] < 0) continue;
@@ -601,18 +624,24 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
             for (int e = 0; e < VEC; ++e) v[e] += du[m][j][e];
             lds_part_store<VEC>(blk, cs.col0[j], a.lo, a.D, al4, v);
           } else {
-            const uint32_t row = static_cast<uint32_t>(bid[m] * a.R * 4);
-            part_load<VEC>(rpart, row, cs.col0[j], a.lo, a.D, pend, al4, v);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) v[e] += du[m][j][e];
-            part_store<VEC>(rpart, row, cs.col0[j], a.lo, a.D, pend, al4, v);
+            for (int e = 0; e < VEC; ++e) v[e] = pold[m][j][e] + du[m][j][e];
+            part_store<VEC>(rpart, static_cast<uint32_t>(bid[m] * a.R * 4), cs.col0[j], a.lo, a.D,
+                            pend, al4, v);
+#pragma unroll
+            for (int m2 = m + 1; m2 < MQ; ++m2)
+              if (bid[m2] == bid[m])
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) pold[m2][j][e] = v[e];
           }
         }
       }
 #pragma unroll
-      for (int m = 0; m < MQ; ++m)
+      for (int m = 0; m < MQ; ++m) {
+        bid[m] = nid[m];
 #pragma unroll
         for (int j = 0; j < CH; ++j) cs.q[m][j] = qn[SEL ? m : 0][j];
+      }
     }
     n = next;
   }

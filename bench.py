@@ -38,9 +38,14 @@ METRIC = "AttnRes fwd+bwd ms and HBM GB/s (% peak), S=10,N=32768,D=4096 bf16, 1 
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources the single-query read is built from (its kernels, their instantiations,
+    the shared argument structs and the host planner); the multi- and selected-query kernels'
+    own files are left out, since the default workload never runs them."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_residuals_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name.startswith(("attnres_multi_", "attnres_sel_")):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -74,6 +79,11 @@ def main() -> int:
                          "(no key-norm weight, no output norm)")
     ap.add_argument("--layout", default="query_major", choices=["query_major", "token_major"],
                     help="output layout of the multi-query read")
+    ap.add_argument("--bank", type=int, default=0, metavar="E",
+                    help="time the selected-query read: per-token queries from an [E, R] bank "
+                         "(with --slots K ids per token, uniform over the bank)")
+    ap.add_argument("--slots", type=int, default=2, metavar="K",
+                    help="queries per token of the selected-query read")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time the oracle baseline repeats its pass for")
     ap.add_argument("--check", type=int, default=1, help="sampled-token parity check (0 = off)")
@@ -106,6 +116,8 @@ def main() -> int:
     w = W.ALL[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.bank:
+        return run_selected(args, w)
     if args.queries:
         return run_multi(args, w)
     x = W.generate(w, device=dev)
@@ -348,6 +360,101 @@ def run_multi(args, w) -> int:
                    "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 1),
                    "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4)},
         "roofline": {"bound": "hbm", "kernel": "attnres_multi_bwd (backward kernels + finaliser)",
+                     "achieved": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "traffic": None,
+                     "fwd_achieved": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1)},
+        "cpu_baseline": None,
+        "parity_check": check,
+        "source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def run_selected(args, w) -> int:
+    """The selected-query read ("Fast Attention Residuals" page, Multi-query AttnRes: per-token
+    query selection) with K ids per token, uniform over an [E, R] bank; one JSON line."""
+    import math
+    import torch
+    import attention_residuals_amd as A
+    import attnres_workloads as W
+
+    dev = "cuda:0"
+    E, K, S, N, D, R = args.bank, args.slots, w.S, w.N, w.D, w.R
+    x = W.generate(w, device=dev, with_dout=False)
+    values = x["values"]
+    del x
+    g = torch.Generator(device=dev).manual_seed(w.seed + 1000 * E + K)
+    bank = (torch.randn((E, R), generator=g, device=dev)
+            / math.sqrt(R if w.query_over_rank else D)).to(w.torch_dtype)
+    ids = torch.randint(0, E, (N, K), generator=g, device=dev, dtype=torch.int64)
+    dout = torch.randn((N, K, D), generator=g, device=dev).to(w.torch_dtype)
+    desc = A.make_selected_desc(S, N, D, R, E, K, w.torch_dtype, eps=w.eps, scale=w.scale,
+                                accumulate_dvalues=args.accumulate)
+    y = torch.empty((N, K, D), dtype=w.torch_dtype, device=dev)
+    lse = torch.empty((N, K), dtype=torch.float32, device=dev)
+    dv = (torch.zeros if args.accumulate else torch.empty)((S, N, D), dtype=w.torch_dtype,
+                                                           device=dev)
+    dbank = torch.empty((E, R), dtype=w.torch_dtype, device=dev)
+    ws = torch.empty((max(A.selected_workspace_bytes(desc), 256),), dtype=torch.uint8, device=dev)
+    fws = torch.empty((A.selected_fwd_workspace_bytes(desc),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        A.attnres_selected_fwd(values, bank, ids, eps=w.eps, scale=w.scale, out=y, lse=lse,
+                               workspace=fws, stream=stream)
+
+    def bwd():
+        A.attnres_selected_bwd(values, bank, ids, lse, dout, eps=w.eps, scale=w.scale,
+                               accumulate=args.accumulate, dvalues=dv, dbank=dbank, workspace=ws,
+                               stream=stream)
+
+    ms, fwd_ms, bwd_ms = _timed(args, fwd, bwd, stream)
+    b = w.elem_bytes
+    acc = S * N * D * b if args.accumulate else 0
+    # sources, outputs / output gradients, lse and ids per token; the bank (and its gradient) once
+    fwd_bytes = (S + K) * N * D * b + 12 * K * N + E * R * b
+    bwd_bytes = (2 * S + K) * N * D * b + 12 * K * N + 2 * E * R * b + acc
+    algo = fwd_bytes + bwd_bytes
+    value = algo / (ms * 1e-3) / 1e9
+
+    check = None
+    if args.check:
+        if args.accumulate:
+            dv.zero_()
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
+        import oracle
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from parity import compare_rows, compare_stat, sample_tokens
+        toks = sample_tokens(N, 6, seed=7)
+        sel = torch.tensor(toks, device=dev)
+        ref = oracle.run_selected(values.index_select(1, sel).cpu(), bank.cpu(),
+                                  ids.index_select(0, sel).cpu(),
+                                  dout.index_select(0, sel).cpu(), eps=w.eps, scale=w.scale,
+                                  reduce=False)
+        f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
+        res = {"y": compare_rows(f64(y.index_select(0, sel)).reshape(-1, D),
+                                 ref["y"].reshape(-1, D), w.dtype),
+               "lse": compare_stat(f64(lse.index_select(0, sel)), ref["lse"]),
+               "dvalues": compare_rows(f64(dv.index_select(1, sel)), ref["dvalues"], w.dtype,
+                                       roundings=-(-K // 2))}
+        check = {k: {"metric": v["metric"], "ok": bool(v["ok"])} for k, v in res.items()}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}_selected_e{E}_k{K}", "S": S, "N": N, "D": D, "R": R,
+                   "E": E, "K": K, "accumulate_dvalues": args.accumulate,
+                   "algorithmic_bytes": algo,
+                   "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 1),
+                   "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4)},
+        "roofline": {"bound": "hbm", "kernel": "attnres_selected_bwd (backward kernels + finaliser)",
                      "achieved": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),

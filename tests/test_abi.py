@@ -226,6 +226,7 @@ def _selected_status(**kw):
     (dict(), OK), (dict(K=16), OK), (dict(K=0), INVALID), (dict(K=17), INVALID),
     (dict(E=0), INVALID), (dict(R=300), INVALID), (dict(R=5), OK),
     (dict(S=24, D=4096, R=4096), OK), (dict(S=12, D=8192, R=8192), OK),
+    (dict(S=4, D=8192, R=8192), OK),
     (dict(S=13, D=8192, R=8192), UNSUPPORTED), (dict(D=16384, R=16384), UNSUPPORTED),
     (dict(E=1 << 18, D=4096, R=4096), UNSUPPORTED),
 ])

@@ -77,15 +77,16 @@ def _check(V, bank, ids, G, label, dtype, init=None, ref_bank=None, ref_ids=None
 
 
 @pytest.mark.parametrize("S,N,D,R,E,K,dtype", [
-    (10, 701, 4096, 4096, 8, 2, "bf16"),    # partial bank in global blocks
+    (10, 701, 4096, 4096, 8, 2, "bf16"),    # partial bank in LDS where a workgroup may hold 160 KiB
+    (10, 301, 4096, 4096, 16, 2, "bf16"),   # partial bank in global blocks
     (8, 513, 2048, 512, 16, 3, "bf16"),     # LDS bank, two groups
     (6, 257, 1024, 1024, 4, 1, "f32"),      # LDS bank, a padded slot
-    (4, 300, 8192, 8192, 3, 2, "bf16"),     # two chunks per thread, global blocks
+    (4, 300, 8192, 8192, 3, 2, "bf16"),     # two chunks per thread
     (5, 129, 256, 5, 3, 5, "f32"),          # slice start not a multiple of four, three groups
     (3, 97, 2048, 6, 3, 2, "bf16"),
     (24, 199, 2048, 640, 5, 2, "bf16"),
     (4, 200, 512, 512, 1, 3, "bf16"),       # every slot names the same row
-    (12, 333, 1024, 1024, 40, 2, "bf16"),   # many rows, global blocks
+    (12, 333, 1024, 1024, 40, 2, "bf16"),   # many rows (global blocks)
 ])
 def test_selected_parity(S, N, D, R, E, K, dtype):
     print(f"[case] selected S={S} N={N} D={D} R={R} E={E} K={K} {dtype}", flush=True)
