@@ -7,20 +7,24 @@
 namespace attnres {
 
 // Source-block sizes instantiated per chunks-per-thread CH. A token's rows are kept on chip when
-// S <= the largest bucket of its CH (the register budget: SB * CH 16-byte chunks per thread).
-#define ATTNRES_SB_CH1(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 4) \
-  M(__VA_ARGS__, 8) M(__VA_ARGS__, 10) M(__VA_ARGS__, 12) M(__VA_ARGS__, 16)       \
-  M(__VA_ARGS__, 24)
-#define ATTNRES_SB_CH2(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 4) \
-  M(__VA_ARGS__, 8) M(__VA_ARGS__, 10) M(__VA_ARGS__, 12)
-#define ATTNRES_SB_CH4(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 4)
+// S <= the largest bucket of its CH (the register budget: SB * CH 16-byte chunks per thread). A
+// source count between buckets runs the next bucket up with empty slots; exact blocks of 3 and 5
+// measured faster than padding to 4 and 8 (S = 6, 7, 9, 11 ran as fast or faster padded).
+#define ATTNRES_SB_CH1(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 3) \
+  M(__VA_ARGS__, 4) M(__VA_ARGS__, 5) M(__VA_ARGS__, 8) M(__VA_ARGS__, 10)          \
+  M(__VA_ARGS__, 12) M(__VA_ARGS__, 16) M(__VA_ARGS__, 24)
+#define ATTNRES_SB_CH2(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 3) \
+  M(__VA_ARGS__, 4) M(__VA_ARGS__, 5) M(__VA_ARGS__, 8) M(__VA_ARGS__, 10)          \
+  M(__VA_ARGS__, 12)
+#define ATTNRES_SB_CH4(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 3) \
+  M(__VA_ARGS__, 4)
 // Streaming backward source blocks.
 #define ATTNRES_SB_STREAM(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 4) \
   M(__VA_ARGS__, 8)
 
-inline constexpr int kSbCh1[] = {1, 2, 4, 8, 10, 12, 16, 24};
-inline constexpr int kSbCh2[] = {1, 2, 4, 8, 10, 12};
-inline constexpr int kSbCh4[] = {1, 2, 4};
+inline constexpr int kSbCh1[] = {1, 2, 3, 4, 5, 8, 10, 12, 16, 24};
+inline constexpr int kSbCh2[] = {1, 2, 3, 4, 5, 8, 10, 12};
+inline constexpr int kSbCh4[] = {1, 2, 3, 4};
 inline constexpr int kSbStream[] = {1, 2, 4, 8};
 
 // Largest workgroup any kernel is launched with (matches the kernels' launch bounds).

@@ -34,10 +34,19 @@ def _check(w, xc, label, **kw):
     return got
 
 
-@pytest.mark.parametrize("S", [1, 3, 7, 10, 15, 29])
+@pytest.mark.parametrize("S", [1, 3, 5, 7, 10, 15, 29])
 def test_source_counts(S):
     w = _wl(S, 333, 1024, 1024, seed=100 + S)
     _check(w, W.generate(w), f"S={S}")
+
+
+@pytest.mark.parametrize("S,D,dtype", [(3, 4096, "bf16"), (5, 4096, "bf16"), (3, 8192, "f32"),
+                                       (5, 8192, "f32"), (6, 4096, "bf16")])
+def test_exact_and_padded_source_blocks(S, D, dtype):
+    # blocks of exactly 3 and 5 sources at two and four chunks per thread, S = 5 with four chunks
+    # (no such block: the streaming backward), and S = 6 padded to a block of 8
+    w = _wl(S, 389, D, D, seed=150 + S + D, dtype=dtype)
+    _check(w, W.generate(w), f"S={S} D={D} {dtype}")
 
 
 @pytest.mark.parametrize("R", [1, 3, 16, 384, 512, 640, 2048])
