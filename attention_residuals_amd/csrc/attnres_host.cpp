@@ -273,7 +273,9 @@ attnres_status plan_bwd(const attnres_desc* d, const Shape& sh, BwdPlan* pl) {
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
   int per_cu = 0;
-  st = blocks_per_cu(fn, sh.threads, bwd_lds(sh), &per_cu, sh.resident ? 8 : 0);
+  static const int env_waves = env_int("ATTNRES_BWD_WAVES_PER_CU");
+  st = blocks_per_cu(fn, sh.threads, bwd_lds(sh), &per_cu,
+                     sh.resident ? (env_waves > 0 ? env_waves : 8) : 0);
   if (st != ATTNRES_OK) return st;
   static const int mult = std::max(1, env_int("ATTNRES_BWD_GRID_MULT"));
   const int64_t cap = (int64_t)f.cus * per_cu * mult;
