@@ -713,7 +713,7 @@ std::vector<Group> plan_groups(const attnres_multi_desc* m, const MultiShape& ms
   std::vector<Group> g;
   for (int m0 = 0; m0 < m->M;) {
     const int cnt = std::min(m->M - m0, ms.mq_max);
-    g.push_back(Group{m0, cnt, cnt <= 2 ? 2 : 4});
+    g.push_back(Group{m0, cnt, cnt <= 2 ? 2 : cnt});
     m0 += cnt;
   }
   return g;

@@ -29,6 +29,7 @@ static const void* bwd_ptr(int ch, int sb, bool full) {
 
 const void* multi_bwd_kernel_ptr_bf16(int ch, int sb, bool full, int mq) {
   if (mq == 2) return bwd_ptr<2>(ch, sb, full);
+  if (mq == 3) return bwd_ptr<3>(ch, sb, full);
   if (mq == 4) return bwd_ptr<4>(ch, sb, full);
   return nullptr;
 }

@@ -1,5 +1,5 @@
-// Instantiations of multi_fwd_kernel (bf16 and f32 storage). Groups of four queries are built for
-// one chunk per thread only (wider rows would spill registers).
+// Instantiations of multi_fwd_kernel (bf16 and f32 storage). Groups of three and four queries are
+// built for one chunk per thread only (wider rows would spill registers).
 #include "attnres_internal.hpp"
 #include "attnres_multi_kernels.hpp"
 
@@ -30,6 +30,7 @@ static const void* fwd_ptr(int ch, int sb, bool full) {
 
 const void* multi_fwd_kernel_ptr(bool bf16, int ch, int sb, bool full, int mq) {
   if (mq == 2) return bf16 ? fwd_ptr<true, 2>(ch, sb, full) : fwd_ptr<false, 2>(ch, sb, full);
+  if (mq == 3) return bf16 ? fwd_ptr<true, 3>(ch, sb, full) : fwd_ptr<false, 3>(ch, sb, full);
   if (mq == 4) return bf16 ? fwd_ptr<true, 4>(ch, sb, full) : fwd_ptr<false, 4>(ch, sb, full);
   return nullptr;
 }
