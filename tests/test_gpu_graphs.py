@@ -1,0 +1,135 @@
+"""HIP graph capture and replay of the multi-query and selected-query reads (several launch groups:
+ticket resets, accumulating later groups, the finaliser). Each read is captured once into a
+torch.cuda.CUDAGraph with preallocated outputs and workspaces, then replayed four times on inputs
+copied into the captured buffers (alternating two input sets), with eager work and synchronisation
+between replays; every replay is compared with an eager call on the same inputs: bitwise for y,
+lse and dvalues (per-token results), and bitwise for dq / dbank in deterministic mode (else to the
+reduction-order tolerance of the schedules test)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from parity import gpu_available, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+
+def _sources(S, N, D, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    V = torch.empty((S, N, D), dtype=torch.bfloat16, device="cuda")
+    for s in range(S):
+        V[s].copy_(torch.randn((N, D), generator=g, device="cuda") * math.sqrt(1.0 + s))
+    return V, g
+
+
+def _close(a, b, deterministic):
+    if deterministic:
+        assert torch.equal(a, b)
+    else:
+        x, y = to_f64(a), to_f64(b)
+        assert np.linalg.norm(x - y) <= 4e-3 * np.linalg.norm(y)
+
+
+def _replay_and_compare(capture_step, eager_step, bufs, inputs, outs, reduced, deterministic):
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        capture_step(s)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        capture_step(s)
+    torch.cuda.synchronize()
+    for xin in inputs + inputs:
+        for k in bufs:
+            bufs[k].copy_(xin[k])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = eager_step(xin)
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k], ref[k]), k
+        for k in reduced:
+            _close(reduced[k], ref[k], deterministic)
+
+
+@pytest.mark.parametrize("deterministic", [True, False])
+def test_multi_query_graph_replay(deterministic):
+    import attention_residuals_amd as A
+    S, N, D, M = 6, 1531, 2048, 5
+    inputs = []
+    for seed in (21, 22):
+        V, g = _sources(S, N, D, seed)
+        Q = (torch.randn((M, D), generator=g, device="cuda") / math.sqrt(D)).to(torch.bfloat16)
+        G = torch.randn((N, M, D), generator=g, device="cuda").to(torch.bfloat16)
+        inputs.append({"V": V, "Q": Q, "G": G})
+    bufs = {k: v.clone() for k, v in inputs[0].items()}
+    desc = A.make_multi_desc(S, N, D, D, M, torch.bfloat16, layout="token_major",
+                             deterministic=deterministic)
+    y = torch.empty((N, M, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((N, M), dtype=torch.float32, device="cuda")
+    dv = torch.empty((S, N, D), dtype=torch.bfloat16, device="cuda")
+    dq = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((A.multi_workspace_bytes(desc),), dtype=torch.uint8, device="cuda")
+    fws = torch.empty((A.multi_fwd_workspace_bytes(desc),), dtype=torch.uint8, device="cuda")
+
+    def step(s):
+        A.attnres_multi_fwd(bufs["V"], bufs["Q"], layout="token_major", out=y, lse=lse,
+                            workspace=None if deterministic else fws,
+                            dynamic=not deterministic, stream=s)
+        A.attnres_multi_bwd(bufs["V"], bufs["Q"], lse, bufs["G"], layout="token_major",
+                            deterministic=deterministic, dvalues=dv, dq=dq, workspace=ws,
+                            stream=s)
+
+    def eager(x):
+        ye, le = A.attnres_multi_fwd(x["V"], x["Q"], layout="token_major",
+                                     dynamic=not deterministic)
+        dve, dqe = A.attnres_multi_bwd(x["V"], x["Q"], le, x["G"], layout="token_major",
+                                       deterministic=deterministic)
+        return {"y": ye, "lse": le, "dv": dve, "dq": dqe}
+
+    print(f"[case] multi graph M={M} deterministic={deterministic}", flush=True)
+    _replay_and_compare(step, eager, bufs, inputs, {"y": y, "lse": lse, "dv": dv}, {"dq": dq},
+                        deterministic)
+
+
+@pytest.mark.parametrize("E,deterministic", [(6, True), (6, False), (48, False)])
+def test_selected_query_graph_replay(E, deterministic):
+    import attention_residuals_amd as A
+    S, N, D, K = 6, 1531, 2048, 3
+    inputs = []
+    for seed in (31, 32):
+        V, g = _sources(S, N, D, seed)
+        bank = (torch.randn((E, D), generator=g, device="cuda") / math.sqrt(D)).to(torch.bfloat16)
+        ids = torch.randint(0, E, (N, K), generator=g, device="cuda", dtype=torch.int64)
+        G = torch.randn((N, K, D), generator=g, device="cuda").to(torch.bfloat16)
+        inputs.append({"V": V, "bank": bank, "ids": ids, "G": G})
+    bufs = {k: v.clone() for k, v in inputs[0].items()}
+    desc = A.make_selected_desc(S, N, D, D, E, K, torch.bfloat16, deterministic=deterministic)
+    y = torch.empty((N, K, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    dv = torch.empty((S, N, D), dtype=torch.bfloat16, device="cuda")
+    db = torch.empty((E, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((A.selected_workspace_bytes(desc),), dtype=torch.uint8, device="cuda")
+    fws = torch.empty((A.selected_fwd_workspace_bytes(desc),), dtype=torch.uint8, device="cuda")
+
+    def step(s):
+        A.attnres_selected_fwd(bufs["V"], bufs["bank"], bufs["ids"], out=y, lse=lse,
+                               workspace=None if deterministic else fws,
+                               dynamic=not deterministic, stream=s)
+        A.attnres_selected_bwd(bufs["V"], bufs["bank"], bufs["ids"], lse, bufs["G"],
+                               deterministic=deterministic, dvalues=dv, dbank=db, workspace=ws,
+                               stream=s)
+
+    def eager(x):
+        ye, le = A.attnres_selected_fwd(x["V"], x["bank"], x["ids"], dynamic=not deterministic)
+        dve, dbe = A.attnres_selected_bwd(x["V"], x["bank"], x["ids"], le, x["G"],
+                                          deterministic=deterministic)
+        return {"y": ye, "lse": le, "dv": dve, "db": dbe}
+
+    print(f"[case] selected graph E={E} deterministic={deterministic}", flush=True)
+    _replay_and_compare(step, eager, bufs, inputs, {"y": y, "lse": lse, "dv": dv}, {"db": db},
+                        deterministic)
