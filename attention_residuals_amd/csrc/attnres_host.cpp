@@ -1037,9 +1037,10 @@ attnres_multi_desc multi_of(const attnres_selected_desc* d) {
 attnres_status make_sel_shape(const attnres_selected_desc* d, MultiShape* ms, bool backward) {
   if (!d) return fail(ATTNRES_ERR_INVALID_ARG, "desc is NULL");
   if (d->E < 1) return fail(ATTNRES_ERR_INVALID_ARG, "E=%d: the bank needs a row", d->E);
-  if (d->R >= 1 && (int64_t)d->E * d->R * 4 > (int64_t(1) << 31))
-    return fail(ATTNRES_ERR_UNSUPPORTED, "bank of %d x %d: over 2 GiB of FP32 partial rows", d->E,
-                d->R);
+  // the kernels address a workgroup's partial bank rows with 32-bit signed byte offsets
+  if (d->R >= 1 && (int64_t)d->E * d->R * 4 >= (int64_t(1) << 31))
+    return fail(ATTNRES_ERR_UNSUPPORTED, "bank of %d x %d: 2 GiB or more of FP32 partial rows",
+                d->E, d->R);
   const attnres_multi_desc m = multi_of(d);
   attnres_status st = make_multi_shape(&m, ms, backward);
   if (st == ATTNRES_OK && ms->ch > 2) {  // four-chunk rows: the eight-wave shape
@@ -1090,10 +1091,9 @@ attnres_status plan_sel_bwd(const attnres_selected_desc* d, const MultiShape& ms
   return ATTNRES_OK;
 }
 
-attnres_status check_ids(const int64_t* ids, int64_t N, int K) {
+attnres_status check_ids(const int64_t* ids, int64_t N) {
   if (N > 0 && (!ids || !aligned(ids, 8)))
     return fail(ids ? ATTNRES_ERR_ALIGNMENT : ATTNRES_ERR_INVALID_ARG, "ids NULL or misaligned");
-  (void)K;
   return ATTNRES_OK;
 }
 
@@ -1140,7 +1140,7 @@ attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnre
   const attnres_multi_desc m = multi_of(d);
   const attnres_desc d1 = single_desc(&m);
   if ((st = check_param(bank, true, ms.base.esz, "bank")) != ATTNRES_OK) return st;
-  if ((st = check_ids(ids, d->N, d->K)) != ATTNRES_OK) return st;
+  if ((st = check_ids(ids, d->N)) != ATTNRES_OK) return st;
   if (d->N == 0) return ATTNRES_OK;
   MultiFwdArgs a;
   std::memset(&a, 0, sizeof a);
@@ -1222,7 +1222,7 @@ attnres_status attnres_selected_bwd(const attnres_selected_desc* d, const attnre
   const void* dptr[kMaxSources] = {nullptr};
   if ((st = check_param(bank, true, ms.base.esz, "bank")) != ATTNRES_OK) return st;
   if ((st = check_param(dbank, true, ms.base.esz, "dbank")) != ATTNRES_OK) return st;
-  if ((st = check_ids(ids, N, (int)K)) != ATTNRES_OK) return st;
+  if ((st = check_ids(ids, N)) != ATTNRES_OK) return st;
   if (N > 0) {
     if ((st = check_sources(&d1, ms.base, values, "values", a.src)) != ATTNRES_OK) return st;
     if ((st = check_sources(&d1, ms.base, dvalues, "dvalues", dptr)) != ATTNRES_OK) return st;

@@ -16,6 +16,12 @@
 //   a_{m,s} = scale dz_{m,s} / r_s,   B_s = -sum_m a_{m,s} c_{m,s} / (R r_s^2)   (c = <t_s, q_m>)
 //   dV_s = sum_m p_{m,s} dY_m + sum_m a_{m,s} q_m + B_s t_s   (q, t zero outside the slice)
 //   du_m += sum_s a_{m,s} t_s   ->  dq_m (summed over tokens by the finaliser).
+//
+// Selected-query variant (SEL; same page and section, per-token query selection): token n's slot m
+// reads with the bank row ids[n, m0 + m] of an [E, R] bank, so the query slices are reloaded per
+// token (the next token's right after the exchange barrier), and the backward adds each token's
+// du_m into the FP32 partial row of the bank row it selected (a per-workgroup copy of the whole
+// bank's partial rows, in LDS or in a global block) instead of keeping du across tokens.
 #pragma once
 
 #include "attnres_kernels.hpp"

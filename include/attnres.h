@@ -192,7 +192,7 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* desc, const attnres_s
  * with one or two chunks per thread (D <= 8192 bf16 / 4096 f32); queries run in groups of two.
  * The bank gradient goes through per-workgroup FP32 partial rows of the whole bank (the workspace
  * is 256 + P * E * R * 4 bytes, P = backward workgroups), so a large bank costs workspace and
- * traffic. */
+ * traffic; E * R * 4 must stay below 2 GiB (else ATTNRES_ERR_UNSUPPORTED). */
 typedef struct {
   int32_t S, D, R;
   int32_t E;               /* bank rows, >= 1 */

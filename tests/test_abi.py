@@ -228,7 +228,8 @@ def _selected_status(**kw):
     (dict(S=24, D=4096, R=4096), OK), (dict(S=12, D=8192, R=8192), OK),
     (dict(S=4, D=8192, R=8192), OK),
     (dict(S=13, D=8192, R=8192), UNSUPPORTED), (dict(D=16384, R=16384), UNSUPPORTED),
-    (dict(E=1 << 18, D=4096, R=4096), UNSUPPORTED),
+    (dict(E=1 << 18, D=4096, R=4096), UNSUPPORTED), (dict(E=1 << 17, D=4096, R=4096), UNSUPPORTED),
+    (dict(E=(1 << 17) - 1, D=4096, R=4096), OK),
 ])
 def test_selected_descriptor_validation(kw, expect):
     st = _selected_status(**kw)
