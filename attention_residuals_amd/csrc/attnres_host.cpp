@@ -709,10 +709,14 @@ attnres_status make_multi_shape(const attnres_multi_desc* m, MultiShape* ms,
   return ATTNRES_OK;
 }
 
+// The fewest launch groups of at most mq_max queries, sized as evenly as possible (larger ones
+// first): the kernels are VALU-bound beyond two queries, so a padded slot costs time (M = 5 runs
+// as 3 + 2, not 4 + 1 padded to 2).
 std::vector<Group> plan_groups(const attnres_multi_desc* m, const MultiShape& ms) {
   std::vector<Group> g;
-  for (int m0 = 0; m0 < m->M;) {
-    const int cnt = std::min(m->M - m0, ms.mq_max);
+  const int n = (m->M + ms.mq_max - 1) / ms.mq_max;
+  for (int i = 0, m0 = 0; i < n; ++i) {
+    const int cnt = m->M / n + (i < m->M % n ? 1 : 0);
     g.push_back(Group{m0, cnt, cnt <= 2 ? 2 : cnt});
     m0 += cnt;
   }
