@@ -82,6 +82,35 @@ def test_compiled_multi_query_read_matches_eager():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("as_list", [False, True])
+def test_compiled_selected_query_read_matches_eager(as_list):
+    import attention_residuals_amd as A
+    torch._dynamo.reset()
+    x = _inputs(3250, S=5, D=2048, R=2048)
+    N = x["values"].shape[1]
+    g = torch.Generator(device="cuda").manual_seed(3251)
+    bank = torch.randn((7, 2048), generator=g, device="cuda").to(torch.bfloat16)
+    ids = torch.randint(0, 7, (2, N // 2, 3), generator=g, device="cuda", dtype=torch.int64)
+    dy = torch.randn((2, N // 2, 3, 2048), generator=g, device="cuda").to(torch.bfloat16)
+
+    def step(values, b):
+        y = A.attnres_selected(values, b, ids, deterministic=True)
+        return (y.float() * dy.float()).sum()
+
+    def grads(fn):
+        v = x["values"].view(5, 2, N // 2, 2048).clone().requires_grad_(True)
+        b = bank.clone().requires_grad_(True)
+        loss = fn(list(v.unbind(0)) if as_list else v, b)
+        loss.backward()
+        return loss.detach(), v.grad, b.grad
+
+    eager = grads(step)
+    compiled = grads(torch.compile(step, fullgraph=True, dynamic=False, backend="aot_eager"))
+    torch.testing.assert_close(eager[0], compiled[0], rtol=1e-5, atol=0)
+    for a, b in zip(eager[1:], compiled[1:]):
+        assert torch.equal(a, b)
+
+
 def test_opcheck_registrations():
     from attention_residuals_amd import ops
     x = _inputs(3300, S=4, N=67, D=256, R=256)
@@ -93,3 +122,7 @@ def test_opcheck_registrations():
     torch.library.opcheck(ops.fwd_list, (srcs, q, None, None, 2.0 ** -23, 1.0, False, True))
     qs = torch.randn((3, 256), device="cuda").to(torch.bfloat16).requires_grad_(True)
     torch.library.opcheck(ops.multi_fwd_packed, (v, qs, 2.0 ** -23, 1.0, "token_major", True))
+    bank = torch.randn((5, 256), device="cuda").to(torch.bfloat16).requires_grad_(True)
+    ids = torch.randint(0, 5, (67, 3), device="cuda", dtype=torch.int64)
+    torch.library.opcheck(ops.selected_fwd_packed, (v, bank, ids, 2.0 ** -23, 1.0, True))
+    torch.library.opcheck(ops.selected_fwd_list, (srcs, bank, ids, 2.0 ** -23, 1.0, True))
