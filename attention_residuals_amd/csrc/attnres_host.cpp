@@ -1054,7 +1054,13 @@ attnres_status make_sel_shape(const attnres_selected_desc* d, MultiShape* ms, bo
   if (st != ATTNRES_OK) return st;
   if (ms->ch > 2)
     return fail(ATTNRES_ERR_UNSUPPORTED, "selected-query read: D=%d is too wide", d->D);
-  ms->mq_max = 2;
+  // the forward runs up to four slots per launch with one chunk per thread (as the multi-query
+  // read); the backward three with one chunk per thread and at most 10 sources, else two (its
+  // per-token bank update needs the registers)
+  if (!backward)
+    ms->mq_max = (ms->ch == 1 && ms->sb <= 12) ? kMaxGroupQueries : 2;
+  else
+    ms->mq_max = (ms->ch == 1 && ms->sb <= 10) ? 3 : 2;
   return ATTNRES_OK;
 }
 
@@ -1068,25 +1074,31 @@ constexpr size_t kSelLdsCap = 160 * 1024;
 struct SelBwdPlan {
   int P = 0;
   bool lds_bank = false;
-  size_t lds = 0;
+  size_t bank_lds = 0;  // LDS bytes of the partial bank rows (0 with global blocks)
   size_t off_part = 256, bytes = 256;
 };
 
+const void* sel_bwd_ptr(const MultiShape& ms, bool acc, int mq) {
+  return ms.base.bf16 ? sel_bwd_kernel_ptr_bf16(ms.ch, ms.sb, ms.full, acc, mq)
+                      : sel_bwd_kernel_ptr_f32(ms.ch, ms.sb, ms.full, acc, mq);
+}
+
 attnres_status plan_sel_bwd(const attnres_selected_desc* d, const MultiShape& ms,
                             SelBwdPlan* pl) {
-  const bool acc = d->accumulate_dvalues != 0;
-  const void* fn = ms.base.bf16 ? sel_bwd_kernel_ptr_bf16(ms.ch, ms.sb, ms.full, acc)
-                                : sel_bwd_kernel_ptr_f32(ms.ch, ms.sb, ms.full, acc);
+  // the first (largest) group's kernel and exchange size the bank placement and the grid
+  const attnres_multi_desc m = multi_of(d);
+  const int mq = plan_groups(&m, ms)[0].mq;
+  const void* fn = sel_bwd_ptr(ms, d->accumulate_dvalues != 0, mq);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query backward kernel for this shape");
   DevFacts f;
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
   const size_t row = (size_t)d->E * d->R * sizeof(float);
-  const size_t base = multi_bwd_lds(ms, 2);
+  const size_t base = multi_bwd_lds(ms, mq);
   pl->lds_bank = base + row <= std::min<size_t>(kSelLdsCap, (size_t)f.lds_per_block);
-  pl->lds = pl->lds_bank ? base + row : base;
+  pl->bank_lds = pl->lds_bank ? row : 0;
   int per_cu = 0;
-  st = blocks_per_cu(fn, ms.threads, pl->lds, &per_cu, 8);
+  st = blocks_per_cu(fn, ms.threads, base + pl->bank_lds, &per_cu, 8);
   if (st != ATTNRES_OK) return st;
   const int64_t cap = std::max<int64_t>(1, (int64_t)(kMaxSelPartialBytes / row));
   pl->P = (int)std::min<int64_t>(std::min<int64_t>(d->N, (int64_t)f.cus * per_cu), cap);
@@ -1165,11 +1177,14 @@ attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnre
 
   DevFacts f;
   if ((st = device_facts(&f)) != ATTNRES_OK) return st;
-  const void* fn = sel_fwd_kernel_ptr(ms.base.bf16, ms.ch, ms.sb, ms.full);
-  if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query forward kernel for this shape");
-  const size_t lds = multi_fwd_lds(ms, 2);
+  const std::vector<Group> groups = plan_groups(&m, ms);
+  // occupancy of the largest group's kernel (the first) sizes the grid of every group
+  const void* fn0 = sel_fwd_kernel_ptr(ms.base.bf16, ms.ch, ms.sb, ms.full, groups[0].mq);
+  if (!fn0) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query forward kernel for this shape");
   int per_cu = 0;
-  if ((st = blocks_per_cu(fn, ms.threads, lds, &per_cu, 8)) != ATTNRES_OK) return st;
+  if ((st = blocks_per_cu(fn0, ms.threads, multi_fwd_lds(ms, groups[0].mq), &per_cu, 8)) !=
+      ATTNRES_OK)
+    return st;
   const int64_t resident = (int64_t)f.cus * per_cu;
   const bool dyn = workspace != nullptr && N >= 2 * resident && N < kMaxTicketTokens;
   const int64_t slots = resident * (dyn ? 1 : 8);
@@ -1190,8 +1205,12 @@ attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnre
   a.sel.ids = ids;
   a.sel.E = d->E;
   a.sel.K = (int)K;
-  for (const Group& g : plan_groups(&m, ms)) {
-    a.tpt = dyn ? tokens_per_ticket(N, slots, (double)(d->S + 2) * d->D * ms.base.esz, 55.0, 1) : 1;
+  for (const Group& g : groups) {
+    const void* fn = sel_fwd_kernel_ptr(ms.base.bf16, ms.ch, ms.sb, ms.full, g.mq);
+    if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query forward kernel for this shape");
+    const size_t lds = multi_fwd_lds(ms, g.mq);
+    a.tpt = dyn ? tokens_per_ticket(N, slots, (double)(d->S + g.cnt) * d->D * ms.base.esz, 55.0, 1)
+                : 1;
     a.ticket = nullptr;
     if (dyn) {
       a.ticket = static_cast<uint32_t*>(workspace);
@@ -1283,8 +1302,7 @@ attnres_status attnres_selected_bwd(const attnres_selected_desc* d, const attnre
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       const Group& g = groups[gi];
       const bool acc = d->accumulate_dvalues != 0 || gi > 0;
-      const void* fn = ms.base.bf16 ? sel_bwd_kernel_ptr_bf16(ms.ch, ms.sb, ms.full, acc)
-                                    : sel_bwd_kernel_ptr_f32(ms.ch, ms.sb, ms.full, acc);
+      const void* fn = sel_bwd_ptr(ms, acc, g.mq);
       if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query backward kernel");
       a.tpt = 1;
       a.ticket = nullptr;
@@ -1302,7 +1320,8 @@ attnres_status attnres_selected_bwd(const attnres_selected_desc* d, const attnre
       a.sel.lds_bank = pl.lds_bank ? 1 : 0;
       a.lse = lse + g.m0;
       a.dout = static_cast<const char*>(dout) + (int64_t)g.m0 * d->D * ms.base.esz;
-      st = launch(fn, pl.P, 1, ms.threads, pl.lds, &a, stream, "selected-query backward launch");
+      st = launch(fn, pl.P, 1, ms.threads, multi_bwd_lds(ms, g.mq) + pl.bank_lds, &a, stream,
+                  "selected-query backward launch");
       if (st != ATTNRES_OK) return st;
     }
   }

@@ -52,9 +52,9 @@ const void* multi_bwd_kernel_ptr_bf16(int ch, int sb, bool full, int mq);
 const void* multi_bwd_kernel_ptr_f32(int ch, int sb, bool full, int mq);
 const void* multi_bwd_kernel_ptr_acc_bf16(int ch, int sb, bool full, int mq);
 const void* multi_bwd_kernel_ptr_acc_f32(int ch, int sb, bool full, int mq);
-const void* sel_fwd_kernel_ptr(bool bf16, int ch, int sb, bool full);
-const void* sel_bwd_kernel_ptr_bf16(int ch, int sb, bool full, bool acc);
-const void* sel_bwd_kernel_ptr_f32(int ch, int sb, bool full, bool acc);
+const void* sel_fwd_kernel_ptr(bool bf16, int ch, int sb, bool full, int mq);
+const void* sel_bwd_kernel_ptr_bf16(int ch, int sb, bool full, bool acc, int mq);
+const void* sel_bwd_kernel_ptr_f32(int ch, int sb, bool full, bool acc, int mq);
 const void* ticket_reset_kernel_ptr();
 
 }  // namespace attnres

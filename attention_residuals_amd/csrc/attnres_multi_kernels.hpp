@@ -473,9 +473,11 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
     const bool take = dyn && n + 1 >= batch_end;
     uint32_t tk = 0;
     if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
-    // SEL: this token's query gradients start from zero; with global partial blocks the rows they
-    // add into are read now (the thread's own stores of earlier tokens precede these loads)
-    float pold[SEL ? MQ : 1][CH][SEL ? VEC : 1];
+    // SEL: this token's query gradients start from zero; with global partial blocks and up to two
+    // slots the rows they add into are read now (the thread's own stores of earlier tokens precede
+    // these loads); with three slots there are no registers for them and they are read at the end
+    constexpr bool kPrefetchPart = SEL && MQ <= 2;
+    float pold[kPrefetchPart ? MQ : 1][CH][kPrefetchPart ? VEC : 1];
     if constexpr (SEL) {
 #pragma unroll
       for (int m = 0; m < MQ; ++m)
@@ -483,9 +485,11 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
         for (int j = 0; j < CH; ++j) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) du[m][j][e] = 0.f;
-          if (!a.sel.lds_bank && bid[m] >= 0)
-            part_load<VEC>(rpart, static_cast<uint32_t>(bid[m] * a.R * 4), cs.col0[j], a.lo, a.D,
-                           pend, al4, pold[m][j]);
+          if constexpr (kPrefetchPart) {
+            if (!a.sel.lds_bank && bid[m] >= 0)
+              part_load<VEC>(rpart, static_cast<uint32_t>(bid[m] * a.R * 4), cs.col0[j], a.lo,
+                             a.D, pend, al4, pold[m][j]);
+          }
         }
     }
     float* xb = lds + buf * xfl;
@@ -629,7 +633,7 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) v[e] += du[m][j][e];
             lds_part_store<VEC>(blk, cs.col0[j], a.lo, a.D, al4, v);
-          } else {
+          } else if constexpr (kPrefetchPart) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) v[e] = pold[m][j][e] + du[m][j][e];
             part_store<VEC>(rpart, static_cast<uint32_t>(bid[m] * a.R * 4), cs.col0[j], a.lo, a.D,
@@ -639,6 +643,12 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
               if (bid[m2] == bid[m])
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) pold[m2][j][e] = v[e];
+          } else {
+            const uint32_t row = static_cast<uint32_t>(bid[m] * a.R * 4);
+            part_load<VEC>(rpart, row, cs.col0[j], a.lo, a.D, pend, al4, v);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] += du[m][j][e];
+            part_store<VEC>(rpart, row, cs.col0[j], a.lo, a.D, pend, al4, v);
           }
         }
       }
