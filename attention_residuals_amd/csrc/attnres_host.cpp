@@ -723,8 +723,11 @@ std::vector<Group> plan_groups(const attnres_multi_desc* m, const MultiShape& ms
   return g;
 }
 
-size_t multi_fwd_lds(const MultiShape& ms, int mq) {
-  return 2u * (size_t)(1 + mq) * ms.sb * (4u * ms.W) * sizeof(float) + 4 * sizeof(float);
+// Exchange buffers and ticket slots; with fixed queries (not the selected read) and two or more
+// chunks per thread also the group's query slices, 16 bytes per thread, query and chunk.
+size_t multi_fwd_lds(const MultiShape& ms, int mq, bool fixed_queries) {
+  return 2u * (size_t)(1 + mq) * ms.sb * (4u * ms.W) * sizeof(float) + 4 * sizeof(float) +
+         (fixed_queries && ms.ch >= 2 ? (size_t)mq * ms.ch * ms.threads * 16u : 0u);
 }
 size_t multi_bwd_lds(const MultiShape& ms, int mq) {
   return 2u * (size_t)(1 + 2 * mq) * ms.sb * (4u * ms.W) * sizeof(float) + 4 * sizeof(float);
@@ -871,7 +874,7 @@ attnres_status attnres_multi_fwd(const attnres_multi_desc* m, const attnres_sour
   for (const Group& g : plan_groups(m, ms)) {
     const void* fn = multi_fwd_kernel_ptr(ms.base.bf16, ms.ch, ms.sb, ms.full, g.mq);
     if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no multi-query forward kernel for this shape");
-    const size_t lds = multi_fwd_lds(ms, g.mq);
+    const size_t lds = multi_fwd_lds(ms, g.mq, true);
     int per_cu = 0;
     if ((st = blocks_per_cu(fn, ms.threads, lds, &per_cu, 8)) != ATTNRES_OK) return st;
     const int64_t resident = (int64_t)f.cus * per_cu;
@@ -1182,9 +1185,8 @@ attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnre
   const void* fn0 = sel_fwd_kernel_ptr(ms.base.bf16, ms.ch, ms.sb, ms.full, groups[0].mq);
   if (!fn0) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query forward kernel for this shape");
   int per_cu = 0;
-  if ((st = blocks_per_cu(fn0, ms.threads, multi_fwd_lds(ms, groups[0].mq), &per_cu, 8)) !=
-      ATTNRES_OK)
-    return st;
+  st = blocks_per_cu(fn0, ms.threads, multi_fwd_lds(ms, groups[0].mq, false), &per_cu, 8);
+  if (st != ATTNRES_OK) return st;
   const int64_t resident = (int64_t)f.cus * per_cu;
   const bool dyn = workspace != nullptr && N >= 2 * resident && N < kMaxTicketTokens;
   const int64_t slots = resident * (dyn ? 1 : 8);
@@ -1208,7 +1210,7 @@ attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnre
   for (const Group& g : groups) {
     const void* fn = sel_fwd_kernel_ptr(ms.base.bf16, ms.ch, ms.sb, ms.full, g.mq);
     if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query forward kernel for this shape");
-    const size_t lds = multi_fwd_lds(ms, g.mq);
+    const size_t lds = multi_fwd_lds(ms, g.mq, false);
     a.tpt = dyn ? tokens_per_ticket(N, slots, (double)(d->S + g.cnt) * d->D * ms.base.esz, 55.0, 1)
                 : 1;
     a.ticket = nullptr;

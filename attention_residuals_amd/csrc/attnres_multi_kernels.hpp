@@ -240,6 +240,19 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
 
   MultiCols<BF16, CH, FULL, MQ> cs;
   cs.init(tid, nthr, a.D, a.lo, SEL ? 0 : a.M, a.query, a.R);
+  // with two or more chunks per thread the group's fixed query slices (not SEL) wait in LDS after
+  // the exchange buffers and the ticket slots (each thread its own chunks; only the exchange reads
+  // them), so their registers go to the row slab (measured: the two-query forward at D = 4096 went
+  // from 0.592 to 0.521 ms); the compiler cannot hoist the per-token reloads past the exchange's
+  // LDS stores. With one chunk per thread registers are not short and the reloads cost time.
+  constexpr bool kQLds = !SEL && CH >= 2;
+  Chunk* qlds = reinterpret_cast<Chunk*>(lds + 2 * xfl + 4);
+  if constexpr (kQLds) {
+#pragma unroll
+    for (int m = 0; m < MQ; ++m)
+#pragma unroll
+      for (int j = 0; j < CH; ++j) qlds[(m * CH + j) * nthr + tid] = cs.q[m][j];
+  }
   int buf = 0;
   Chunk rows[SB][CH];
 
@@ -291,7 +304,16 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
         if (i0 + g < SB) {
           part[0][g] = slice_sumsq<BF16, CH, FULL, MQ>(rows[i0 + g], cs, a.lo);
 #pragma unroll
-          for (int m = 0; m < MQ; ++m) part[1 + m][g] = dot_rows<BF16, CH>(rows[i0 + g], cs.q[m]);
+          for (int m = 0; m < MQ; ++m) {
+            if constexpr (!kQLds) {
+              part[1 + m][g] = dot_rows<BF16, CH>(rows[i0 + g], cs.q[m]);
+            } else {
+              Chunk qv[CH];
+#pragma unroll
+              for (int j = 0; j < CH; ++j) qv[j] = qlds[(m * CH + j) * nthr + tid];
+              part[1 + m][g] = dot_rows<BF16, CH>(rows[i0 + g], qv);
+            }
+          }
         }
       }
       xchg_group<NV, SB>(part, i0, xb, R4, tid);
