@@ -460,8 +460,12 @@ attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
   DevFacts f;
   if ((st = device_facts(&f)) != ATTNRES_OK) return st;
   int per_cu = 0;
+  // waves per CU of the single-block forward's grid: 12 with one chunk per thread and at most 8
+  // sources (short rows: more tokens in flight per CU; 4-6% faster at D = 2048, S = 8), else 8
+  // (12 measured slower with two chunks per thread and with 24-source blocks)
   static const int env_waves = env_int("ATTNRES_FWD_WAVES_PER_CU");
-  const int wave_cap = sh.fwd_one ? (env_waves > 0 ? env_waves : 8) : 0;
+  const int def_waves = (sh.ch == 1 && sh.sb_fwd <= 8) ? 12 : 8;
+  const int wave_cap = sh.fwd_one ? (env_waves > 0 ? env_waves : def_waves) : 0;
   if ((st = blocks_per_cu(fn, sh.threads, fwd_lds(sh), &per_cu, wave_cap)) != ATTNRES_OK)
     return st;
   // With the token counter (single-block path and a workspace) the grid is one resident pass and
