@@ -359,6 +359,12 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
       for (int j = 0; j < CH; ++j)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[m][j][e] = 0.f;
+    // SEL: raised wave priority while the mixture is folded in and the rows and outputs go out
+    // (the fixed-query forward ran 1.5% slower with it and keeps the default). Placed here, ahead
+    // of the next token's row offsets, the two-chunk kernel allocates without spilling (0.583 ->
+    // 0.532 ms for two slots at D = 4096); placed right before the loop below it spilled 68
+    // registers (0.877 ms).
+    if constexpr (SEL) __builtin_amdgcn_s_setprio(1);
     const int64_t next_byte = next * a.row_stride * ESZ;
     const int live_next = next < a.N ? a.S : 0;
 #pragma unroll
@@ -392,6 +398,7 @@ __global__ __launch_bounds__(512) void multi_fwd_kernel(const MultiFwdArgs a) {
       for (int m = 1; m < MQ; ++m) v = (tid == m) ? lse[m] : v;
       a.lse[tid * a.l_sm + n * a.l_sn] = v;
     }
+    if constexpr (SEL) __builtin_amdgcn_s_setprio(0);
     n = next;
   }
 }
@@ -593,6 +600,10 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
     const int64_t drow_byte = n * a.drow_stride * ESZ;
     const int64_t next_byte = next * a.row_stride * ESZ;
     const int64_t next_dbyte = next * a.drow_stride * ESZ;
+    // not SEL: raised wave priority while the gradient rows are stored and the next rows loaded
+    // (measured: the two- and four-query backwards 2.7% faster; the selected backward ran 1.2%
+    // slower with it, so it keeps the default priority)
+    if constexpr (!SEL) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
       float pi[MQ], ai[MQ];
@@ -640,6 +651,7 @@ __global__ __launch_bounds__(512) void multi_bwd_kernel(const MultiBwdArgs a) {
         for (int j = 0; j < CH; ++j) odv[i][j] = ld_row(rn, cs.voff[j]);
       }
     }
+    if constexpr (!SEL) __builtin_amdgcn_s_setprio(0);
     if constexpr (SEL) {
       // this token's query gradients into the partial bank rows it selected, slot by slot (a row
       // named by two slots adds both: the later slot starts from the earlier one's result)
