@@ -195,16 +195,13 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def attnres_fwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor] = None,
+def _prep_fwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor] = None,
                 out_w: Optional[torch.Tensor] = None, *, eps: float = EPS_DEFAULT,
                 scale: float = 1.0, out_norm: bool = False,
                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                 out_rstd: Optional[torch.Tensor] = None, o32: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None, dynamic: bool = True, stream=None):
-    """Forward read. values: packed [S, N, D] or a list of [N, D] device tensors.
-    Returns (out [N, D], lse [N] f32, out_rstd [N] f32 or None, o32 [N, D] f32 or None);
-    output buffers are allocated with torch when not given. dynamic: hand tokens out through a
-    counter in `workspace` (allocated when not given); False: static token split, no workspace."""
+    """Marshals a forward call: (C function, its arguments, outputs, objects to keep alive)."""
     sv = _SourceView(values)
     desc = make_desc(sv.S, sv.N, sv.D, query.numel(), sv.dtype, eps=eps, scale=scale,
                      has_norm_weight=norm_w is not None, out_norm=out_norm,
@@ -222,14 +219,26 @@ def attnres_fwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor] = No
         workspace = None
     elif workspace is None:
         workspace = torch.empty((fwd_workspace_bytes(desc),), dtype=torch.uint8, device=dev)
-    _check(load().attnres_fwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query),
-                              _ptr(norm_w), _ptr(out_w), _ptr(out), _ptr(lse), _ptr(out_rstd),
-                              _ptr(o32), _ptr(workspace),
-                              0 if workspace is None else workspace.numel(), _stream(stream)))
-    return out, lse, out_rstd, o32
+    cargs = (ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query), _ptr(norm_w), _ptr(out_w),
+             _ptr(out), _ptr(lse), _ptr(out_rstd), _ptr(o32), _ptr(workspace),
+             0 if workspace is None else workspace.numel(), _stream(stream))
+    keep = (desc, sv, query, norm_w, out_w, workspace)
+    return load().attnres_fwd, cargs, (out, lse, out_rstd, o32), keep
 
 
-def attnres_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
+def attnres_fwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor] = None,
+                out_w: Optional[torch.Tensor] = None, **kw):
+    """Forward read. values: packed [S, N, D] or a list of [N, D] device tensors.
+    Keywords: eps, scale, out_norm, out, lse, out_rstd, o32, workspace, dynamic, stream.
+    Returns (out [N, D], lse [N] f32, out_rstd [N] f32 or None, o32 [N, D] f32 or None);
+    output buffers are allocated with torch when not given. dynamic: hand tokens out through a
+    counter in `workspace` (allocated when not given); False: static token split, no workspace."""
+    fn, cargs, outs, _ = _prep_fwd(values, query, norm_w, out_w, **kw)
+    _check(fn(*cargs))
+    return outs
+
+
+def _prep_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
                 out_w: Optional[torch.Tensor], lse: torch.Tensor,
                 out_rstd: Optional[torch.Tensor], o32: Optional[torch.Tensor],
                 dout: torch.Tensor, *, eps: float = EPS_DEFAULT, scale: float = 1.0,
@@ -238,10 +247,7 @@ def attnres_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
                 dq: Optional[torch.Tensor] = None,
                 dw: Optional[torch.Tensor] = None, dow: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None, stream=None):
-    """Backward read. dvalues: packed [S, N, D] or list of [N, D] tensors to write (allocated
-    packed when None). deterministic: fixed token split (bitwise-reproducible dq/dw/dow).
-    accumulate: add this read's gradient to the existing dvalues (which must then be given).
-    Returns (dvalues, dq, dw or None, dow or None)."""
+    """Marshals a backward call: (C function, its arguments, outputs, objects to keep alive)."""
     sv = _SourceView(values)
     desc = make_desc(sv.S, sv.N, sv.D, query.numel(), sv.dtype, eps=eps, scale=scale,
                      has_norm_weight=norm_w is not None, out_norm=out_norm,
@@ -265,11 +271,56 @@ def attnres_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
     dstride = dout.stride(0) if sv.N > 1 else sv.D
-    _check(load().attnres_bwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query),
-                              _ptr(norm_w), _ptr(out_w), _ptr(lse), _ptr(out_rstd), _ptr(o32),
-                              _ptr(dout), dstride, ctypes.byref(dv.struct), _ptr(dq), _ptr(dw),
-                              _ptr(dow), _ptr(workspace), workspace.numel(), _stream(stream)))
-    return dvalues, dq, dw, dow
+    cargs = (ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query), _ptr(norm_w), _ptr(out_w),
+             _ptr(lse), _ptr(out_rstd), _ptr(o32), _ptr(dout), dstride, ctypes.byref(dv.struct),
+             _ptr(dq), _ptr(dw), _ptr(dow), _ptr(workspace), workspace.numel(), _stream(stream))
+    keep = (desc, sv, dv, query, norm_w, out_w, lse, out_rstd, o32, dout, workspace)
+    return load().attnres_bwd, cargs, (dvalues, dq, dw, dow), keep
+
+
+def attnres_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
+                out_w: Optional[torch.Tensor], lse: torch.Tensor,
+                out_rstd: Optional[torch.Tensor], o32: Optional[torch.Tensor],
+                dout: torch.Tensor, **kw):
+    """Backward read. Keywords: eps, scale, out_norm, deterministic, accumulate, dvalues, dq, dw,
+    dow, workspace, stream. dvalues: packed [S, N, D] or list of [N, D] tensors to write
+    (allocated packed when None). deterministic: fixed token split (bitwise-reproducible
+    dq/dw/dow). accumulate: add this read's gradient to the existing dvalues (which must then be
+    given). Returns (dvalues, dq, dw or None, dow or None)."""
+    fn, cargs, outs, _ = _prep_bwd(values, query, norm_w, out_w, lse, out_rstd, o32, dout, **kw)
+    _check(fn(*cargs))
+    return outs
+
+
+class BoundCall:
+    """One library call with every argument marshalled in advance: calling it runs the C entry
+    point on the same buffers and stream (a few microseconds of host time, for loops in which the
+    per-call marshalling would otherwise leave the GPU waiting). `outputs` are the call's output
+    tensors; the inputs and outputs are kept alive by the object and must not be reallocated."""
+
+    def __init__(self, fn, cargs, outputs, keep):
+        self._fn, self._cargs, self.outputs, self._keep = fn, cargs, outputs, keep
+
+    def __call__(self):
+        status = self._fn(*self._cargs)
+        if status != 0:
+            _check(status)
+        return self.outputs
+
+
+def bind_fwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor] = None,
+             out_w: Optional[torch.Tensor] = None, **kw) -> BoundCall:
+    """attnres_fwd's arguments marshalled once; see BoundCall."""
+    return BoundCall(*_prep_fwd(values, query, norm_w, out_w, **kw))
+
+
+def bind_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
+             out_w: Optional[torch.Tensor], lse: torch.Tensor, out_rstd: Optional[torch.Tensor],
+             o32: Optional[torch.Tensor], dout: torch.Tensor, **kw) -> BoundCall:
+    """attnres_bwd's arguments marshalled once; see BoundCall."""
+    return BoundCall(*_prep_bwd(values, query, norm_w, out_w, lse, out_rstd, o32, dout, **kw))
+
+
 
 
 # ---------------------------------------------------------------- multi-query read

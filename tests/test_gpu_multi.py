@@ -6,8 +6,8 @@ to dvalues (summed over the queries), and per query to dq_m (relative L2 for bf1
 Covered: M = 1 (served by the single-query kernels), 2, 3 (a padded group of four), 4, 5 and 16
 (several groups: later groups accumulate into dvalues), both output layouts, sliced keys, bf16 and
 FP32, accumulation into existing dvalues, the widest rows (two query groups per launch), list
-sources, ragged token counts, determinism and the static schedule, the autograd wrapper, N = 0,
-and the unsupported (non-resident) shapes.
+sources, ragged token counts, several tokens per workgroup in both schedules, determinism and the
+static schedule, the autograd wrapper, N = 0, and the unsupported (non-resident) shapes.
 """
 import math
 
@@ -108,6 +108,19 @@ def test_multi_query_parity(S, N, D, R, M, dtype, layout):
     print(f"[case] S={S} N={N} D={D} R={R} M={M} {dtype} {layout}", flush=True)
     _check(V, Q, G, f"multi S={S} N={N} D={D} R={R} M={M} {dtype} {layout}", dtype,
            layout=layout)
+
+
+@pytest.mark.parametrize("M,dynamic", [(2, False), (2, True), (4, False), (4, True)])
+def test_multi_query_several_tokens_per_workgroup(M, dynamic):
+    # enough tokens that every workgroup of the forward's grid (static: 8x the resident count;
+    # dynamic: one resident pass taking tickets) and of the backward's reads several, so the
+    # one-token-ahead prefetch and the token loop are checked against the oracle, not only the
+    # first token of each workgroup
+    S, N, D, R = 6, 9001, 2048, 2048
+    V, Q, G = _inputs(S, N, D, R, M, "bf16", seed=2050 + M)
+    print(f"[case] multi several tokens per workgroup M={M} dynamic={dynamic}", flush=True)
+    _check(V, Q, G, f"multi N={N} M={M} dynamic={dynamic}", "bf16", dynamic=dynamic,
+           deterministic=not dynamic)
 
 
 @pytest.mark.parametrize("M,packed", [(2, True), (6, False)])

@@ -7,8 +7,8 @@ row to dbank (relative L2; rows no token selected must be exactly zero).
 Covered: banks whose FP32 partial rows fit in LDS and banks that take the global partial blocks,
 K = 1 (a padded slot), 2, 3 and 5 (several groups), repeated ids within a token (E = 1), key slices
 whose start is not a multiple of four, the two-chunk rows of D = 8192, bf16 and FP32, ids outside
-the bank, accumulation into existing dvalues, list sources, determinism and the static schedule, the
-autograd wrapper and N = 0.
+the bank, accumulation into existing dvalues, list sources, several tokens per workgroup in both
+schedules, determinism and the static schedule, the autograd wrapper and N = 0.
 """
 import math
 
@@ -92,6 +92,17 @@ def test_selected_parity(S, N, D, R, E, K, dtype):
     print(f"[case] selected S={S} N={N} D={D} R={R} E={E} K={K} {dtype}", flush=True)
     V, bank, ids, G = _inputs(S, N, D, R, E, K, dtype, seed=3000 + S * K + D + E)
     _check(V, bank, ids, G, f"selected S={S} N={N} D={D} R={R} E={E} K={K} {dtype}", dtype)
+
+
+@pytest.mark.parametrize("K,dynamic", [(2, False), (2, True), (3, True)])
+def test_selected_several_tokens_per_workgroup(K, dynamic):
+    # every workgroup reads several tokens (static grid of 8x the resident count, or tickets), so
+    # the next token's ids, bank rows and source rows loaded one token ahead are checked
+    S, N, D, R, E = 6, 9001, 2048, 2048, 8
+    print(f"[case] selected several tokens per workgroup K={K} dynamic={dynamic}", flush=True)
+    V, bank, ids, G = _inputs(S, N, D, R, E, K, "bf16", seed=3050 + K)
+    _check(V, bank, ids, G, f"selected N={N} K={K} dynamic={dynamic}", "bf16", dynamic=dynamic,
+           deterministic=not dynamic)
 
 
 def test_selected_ids_outside_the_bank_read_a_zero_query():
