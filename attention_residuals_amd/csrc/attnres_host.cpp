@@ -1062,12 +1062,12 @@ attnres_status make_sel_shape(const attnres_selected_desc* d, MultiShape* ms, bo
   if (ms->ch > 2)
     return fail(ATTNRES_ERR_UNSUPPORTED, "selected-query read: D=%d is too wide", d->D);
   // the forward runs up to four slots per launch with one chunk per thread (as the multi-query
-  // read); the backward three with one chunk per thread and at most 10 sources, else two (its
-  // per-token bank update needs the registers)
+  // read); the backward also four with one chunk per thread and at most 10 sources, else two (its
+  // per-token bank update needs the registers of two-chunk rows)
   if (!backward)
     ms->mq_max = (ms->ch == 1 && ms->sb <= 12) ? kMaxGroupQueries : 2;
   else
-    ms->mq_max = (ms->ch == 1 && ms->sb <= 10) ? 3 : 2;
+    ms->mq_max = (ms->ch == 1 && ms->sb <= 10) ? kMaxGroupQueries : 2;
   return ATTNRES_OK;
 }
 

@@ -13,6 +13,9 @@ namespace attnres {
 #define ATTNRES_SB_CH1(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 3) \
   M(__VA_ARGS__, 4) M(__VA_ARGS__, 5) M(__VA_ARGS__, 8) M(__VA_ARGS__, 10)          \
   M(__VA_ARGS__, 12) M(__VA_ARGS__, 16) M(__VA_ARGS__, 24)
+// Blocks of at most 10 sources with one chunk per thread (the four-slot selected backward).
+#define ATTNRES_SB_CH1_LE10(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 3) \
+  M(__VA_ARGS__, 4) M(__VA_ARGS__, 5) M(__VA_ARGS__, 8) M(__VA_ARGS__, 10)
 #define ATTNRES_SB_CH2(M, ...) M(__VA_ARGS__, 1) M(__VA_ARGS__, 2) M(__VA_ARGS__, 3) \
   M(__VA_ARGS__, 4) M(__VA_ARGS__, 5) M(__VA_ARGS__, 8) M(__VA_ARGS__, 10)          \
   M(__VA_ARGS__, 12)
