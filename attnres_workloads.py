@@ -132,6 +132,30 @@ def generate(w: Workload, device: str = "cpu", with_dout: bool = True) -> dict:
     return {"values": values, "query": query, "norm_w": norm_w, "out_w": out_w, "dout": dout}
 
 
+def multi_inputs(w: Workload, M: int, layout: str = "query_major", device: str = "cpu") -> dict:
+    """Inputs of the multi-query read over the workload's sources: ``queries`` [M, R] (standard
+    normals over sqrt(R) or sqrt(D), like the single query) and ``dout`` ([M, N, D] query-major or
+    [N, M, D] token-major standard normals), from their own generator seeded seed + 100 * M."""
+    g = torch.Generator(device=device).manual_seed(w.seed + 100 * M)
+    qd = w.R if w.query_over_rank else w.D
+    queries = torch.randn((M, w.R), generator=g, device=device) / math.sqrt(qd)
+    shape = (M, w.N, w.D) if layout == "query_major" else (w.N, M, w.D)
+    dout = torch.randn(shape, generator=g, device=device)
+    return {"queries": queries.to(w.torch_dtype), "dout": dout.to(w.torch_dtype)}
+
+
+def selected_inputs(w: Workload, E: int, K: int, device: str = "cpu") -> dict:
+    """Inputs of the selected-query read over the workload's sources: ``bank`` [E, R] (scaled like
+    the single query), ``ids`` [N, K] int64 uniform over the bank, ``dout`` [N, K, D] standard
+    normals, from their own generator seeded seed + 1000 * E + K."""
+    g = torch.Generator(device=device).manual_seed(w.seed + 1000 * E + K)
+    qd = w.R if w.query_over_rank else w.D
+    bank = (torch.randn((E, w.R), generator=g, device=device) / math.sqrt(qd)).to(w.torch_dtype)
+    ids = torch.randint(0, E, (w.N, K), generator=g, device=device, dtype=torch.int64)
+    dout = torch.randn((w.N, K, w.D), generator=g, device=device).to(w.torch_dtype)
+    return {"bank": bank, "ids": ids, "dout": dout}
+
+
 def small(w: Workload, N: int, seed: Optional[int] = None, **kw) -> Workload:
     """The same workload at a reduced token count (and optionally another seed)."""
     return w.with_(N=N, seed=w.seed if seed is None else seed, **kw)

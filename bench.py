@@ -319,7 +319,6 @@ def _timed(args, fwd, bwd, stream):
 def run_multi(args, w) -> int:
     """The multi-query read ("Fast Attention Residuals" page, Multi-query AttnRes) with M queries
     over the workload's sources; one JSON line like the default mode."""
-    import math
     import numpy as np
     import torch
     import attention_residuals_amd as A
@@ -330,11 +329,9 @@ def run_multi(args, w) -> int:
     x = W.generate(w, device=dev, with_dout=False)
     values = x["values"]
     del x
-    g = torch.Generator(device=dev).manual_seed(w.seed + 100 * M)
-    qs = (torch.randn((M, R), generator=g, device=dev) / math.sqrt(R if w.query_over_rank else D))
-    queries = qs.to(w.torch_dtype)
-    shape = (M, N, D) if args.layout == "query_major" else (N, M, D)
-    dout = torch.randn(shape, generator=g, device=dev).to(w.torch_dtype)
+    mi = W.multi_inputs(w, M, args.layout, device=dev)
+    queries, dout = mi["queries"], mi["dout"]
+    shape = tuple(dout.shape)
     desc = A.make_multi_desc(S, N, D, R, M, w.torch_dtype, eps=w.eps, scale=w.scale,
                              layout=args.layout, accumulate_dvalues=args.accumulate)
     y = torch.empty(shape, dtype=w.torch_dtype, device=dev)
@@ -413,7 +410,6 @@ def run_multi(args, w) -> int:
 def run_selected(args, w) -> int:
     """The selected-query read ("Fast Attention Residuals" page, Multi-query AttnRes: per-token
     query selection) with K ids per token, uniform over an [E, R] bank; one JSON line."""
-    import math
     import torch
     import attention_residuals_amd as A
     import attnres_workloads as W
@@ -423,11 +419,8 @@ def run_selected(args, w) -> int:
     x = W.generate(w, device=dev, with_dout=False)
     values = x["values"]
     del x
-    g = torch.Generator(device=dev).manual_seed(w.seed + 1000 * E + K)
-    bank = (torch.randn((E, R), generator=g, device=dev)
-            / math.sqrt(R if w.query_over_rank else D)).to(w.torch_dtype)
-    ids = torch.randint(0, E, (N, K), generator=g, device=dev, dtype=torch.int64)
-    dout = torch.randn((N, K, D), generator=g, device=dev).to(w.torch_dtype)
+    si = W.selected_inputs(w, E, K, device=dev)
+    bank, ids, dout = si["bank"], si["ids"], si["dout"]
     desc = A.make_selected_desc(S, N, D, R, E, K, w.torch_dtype, eps=w.eps, scale=w.scale,
                                 accumulate_dvalues=args.accumulate)
     y = torch.empty((N, K, D), dtype=w.torch_dtype, device=dev)
