@@ -92,9 +92,14 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if _stale():
-            build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        # ATTNRES_ORACLE_LIB: a copy of the oracle built elsewhere (the mutation tests build copies
+        # with one planted mistake each and check that the pins reject them)
+        path = os.environ.get("ATTNRES_ORACLE_LIB")
+        if not path:
+            if _stale():
+                build(force=True)
+            path = _LIB
+        lib = ctypes.CDLL(path)
         lib.attnres_oracle_run.restype = ctypes.c_int
         lib.attnres_oracle_run.argtypes = [
             ctypes.POINTER(_Problem), ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
