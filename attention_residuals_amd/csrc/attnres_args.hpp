@@ -90,6 +90,20 @@ struct MultiFwdArgs {
   SelArgs sel;                   // selected-query kernels only
 };
 
+// Multi-query forward through matrix cores (all M <= 16 queries of a call in one pass; bf16).
+struct MfmaFwdArgs {
+  const void* src[kMaxSources];
+  int64_t row_stride;
+  int64_t N;
+  int S, D, R, lo, M;
+  float eps, scale, inv_R;
+  const void* query;             // [M, R]
+  void* y;                       // output of query 0, token 0
+  int64_t y_sm, y_sn;            // element strides between queries / tokens
+  float* lse;
+  int64_t l_sm, l_sn;
+};
+
 struct MultiBwdArgs {
   const void* src[kMaxSources];
   void* dsrc[kMaxSources];

@@ -862,6 +862,47 @@ attnres_status attnres_multi_fwd(const attnres_multi_desc* m, const attnres_sour
   if ((st = device_facts(&f)) != ATTNRES_OK) return st;
   int64_t y_sm, y_sn, l_sm, l_sn;
   multi_strides(m, &y_sm, &y_sn, &l_sm, &l_sn);
+
+  // Three to sixteen bf16 queries over 2 to 16 sources of width <= 4096: one pass through the
+  // matrix-core forward (the vector-ALU kernels below are bound by VALU issue beyond two queries).
+  // ATTNRES_MULTI_MFMA=0 turns it off.
+  {
+    const char* e = std::getenv("ATTNRES_MULTI_MFMA");
+    const bool off = e && e[0] == '0';
+    const int cgw = (m->D + 1023) / 1024;
+    const int mq = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
+    const size_t lds = multi_fwd_mfma_lds(cgw, mq);
+    if (!off && ms.base.bf16 && m->S >= 2 && m->S <= 16 && M >= 3 && M <= 16 && cgw <= 4 &&
+        lds <= (size_t)f.lds_per_block) {
+      const void* fn = multi_fwd_mfma_kernel_ptr(cgw, mq, m->R == m->D);
+      if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query forward kernel");
+      int per_cu = 0;
+      if ((st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu)) != ATTNRES_OK) return st;
+      MfmaFwdArgs ma;
+      std::memset(&ma, 0, sizeof ma);
+      for (int s = 0; s < m->S; ++s) ma.src[s] = a.src[s];
+      ma.row_stride = values->row_stride;
+      ma.N = N;
+      ma.S = m->S;
+      ma.D = m->D;
+      ma.R = m->R;
+      ma.lo = m->D - m->R;
+      ma.M = (int)M;
+      ma.eps = m->eps;
+      ma.scale = m->scale;
+      ma.inv_R = 1.0f / (float)m->R;
+      ma.query = queries;
+      ma.y = y;
+      ma.y_sm = y_sm;
+      ma.y_sn = y_sn;
+      ma.lse = lse;
+      ma.l_sm = l_sm;
+      ma.l_sn = l_sn;
+      const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
+      return launch(fn, grid, 1, 64 * kMfmaWaves, lds, &ma, stream,
+                    "matrix-core multi-query forward launch");
+    }
+  }
   a.row_stride = values->row_stride;
   a.N = N;
   a.S = m->S;
