@@ -102,6 +102,8 @@ struct MfmaFwdArgs {
   int64_t y_sm, y_sn;            // element strides between queries / tokens
   float* lse;
   int64_t l_sm, l_sn;
+  const int64_t* ids;            // selected-query read: [N, M] bank rows per token (query = bank)
+  int E;                         //   bank rows; ids outside [0, E) read a zero query
 };
 
 struct MultiBwdArgs {

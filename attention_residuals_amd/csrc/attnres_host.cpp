@@ -871,10 +871,10 @@ attnres_status attnres_multi_fwd(const attnres_multi_desc* m, const attnres_sour
     const bool off = e && e[0] == '0';
     const int cgw = (m->D + 1023) / 1024;
     const int mq = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
-    const size_t lds = multi_fwd_mfma_lds(cgw, mq);
+    const size_t lds = multi_fwd_mfma_lds(cgw, mq, mq);
     if (!off && ms.base.bf16 && m->S >= 2 && m->S <= 16 && M >= 3 && M <= 16 && cgw <= 4 &&
         lds <= (size_t)f.lds_per_block) {
-      const void* fn = multi_fwd_mfma_kernel_ptr(cgw, mq, m->R == m->D);
+      const void* fn = multi_fwd_mfma_kernel_ptr(cgw, mq, m->R == m->D, false);
       if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query forward kernel");
       int per_cu = 0;
       if ((st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu)) != ATTNRES_OK) return st;
@@ -1225,6 +1225,49 @@ attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnre
 
   DevFacts f;
   if ((st = device_facts(&f)) != ATTNRES_OK) return st;
+
+  // Three to sixteen bf16 slots over 2 to 16 sources of width <= 4096, with the bank staged in
+  // LDS: one pass through the matrix-core forward (ATTNRES_MULTI_MFMA=0 turns it off).
+  {
+    const char* e = std::getenv("ATTNRES_MULTI_MFMA");
+    const bool off = e && e[0] == '0';
+    const int cgw = (d->D + 1023) / 1024;
+    const int mq = K <= 4 ? 4 : (K <= 8 ? 8 : 16);
+    const size_t lds = multi_fwd_mfma_lds(cgw, mq, d->E + 1);
+    if (!off && ms.base.bf16 && d->S >= 2 && d->S <= 16 && K >= 3 && K <= 16 && cgw <= 4 &&
+        lds <= (size_t)f.lds_per_block) {
+      const void* fn = multi_fwd_mfma_kernel_ptr(cgw, mq, d->R == d->D, true);
+      if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core selected-query forward kernel");
+      int per_cu = 0;
+      if ((st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu)) != ATTNRES_OK) return st;
+      MfmaFwdArgs ma;
+      std::memset(&ma, 0, sizeof ma);
+      for (int s = 0; s < d->S; ++s) ma.src[s] = a.src[s];
+      ma.row_stride = values->row_stride;
+      ma.N = N;
+      ma.S = d->S;
+      ma.D = d->D;
+      ma.R = d->R;
+      ma.lo = d->D - d->R;
+      ma.M = (int)K;
+      ma.eps = d->eps;
+      ma.scale = d->scale;
+      ma.inv_R = 1.0f / (float)d->R;
+      ma.query = bank;
+      ma.y = y;
+      ma.y_sm = d->D;
+      ma.y_sn = K * d->D;
+      ma.lse = lse;
+      ma.l_sm = 1;
+      ma.l_sn = K;
+      ma.ids = ids;
+      ma.E = d->E;
+      const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
+      return launch(fn, grid, 1, 64 * kMfmaWaves, lds, &ma, stream,
+                    "matrix-core selected-query forward launch");
+    }
+  }
+
   const std::vector<Group> groups = plan_groups(&m, ms);
   // occupancy of the largest group's kernel (the first) sizes the grid of every group
   const void* fn0 = sel_fwd_kernel_ptr(ms.base.bf16, ms.ch, ms.sb, ms.full, groups[0].mq);

@@ -57,10 +57,11 @@ const void* multi_bwd_kernel_ptr_acc_bf16(int ch, int sb, bool full, int mq);
 const void* multi_bwd_kernel_ptr_acc_f32(int ch, int sb, bool full, int mq);
 const void* sel_fwd_kernel_ptr(bool bf16, int ch, int sb, bool full, int mq);
 // Multi-query forward through matrix cores: cgw = 128-column chunk groups per wave (8 waves),
-// mq = queries the kernel is built for (4, 8 or 16); kMfmaWaves waves per workgroup.
+// mq = queries the kernel is built for (4, 8 or 16), sel = the selected-query read (queries from a
+// bank by per-token ids); LDS for qrows staged query rows (M, or E + 1 for the selected read).
 inline constexpr int kMfmaWaves = 8;
-const void* multi_fwd_mfma_kernel_ptr(int cgw, int mq, bool full);
-size_t multi_fwd_mfma_lds(int cgw, int mq);
+const void* multi_fwd_mfma_kernel_ptr(int cgw, int mq, bool full, bool sel);
+size_t multi_fwd_mfma_lds(int cgw, int mq, int qrows);
 const void* sel_bwd_kernel_ptr_bf16(int ch, int sb, bool full, bool acc, int mq);
 const void* sel_bwd_kernel_ptr_f32(int ch, int sb, bool full, bool acc, int mq);
 const void* ticket_reset_kernel_ptr();

@@ -69,21 +69,25 @@ __device__ __forceinline__ float sum8(const float* p) {
 
 }  // namespace
 
-template <int CGW, int MQ, bool FULL, bool PF>
+// SEL: the selected-query read: token n's query m is bank row ids[n, m] (M = slots per token); the
+// whole bank plus one zero row (for ids outside [0, E)) is staged instead of M fixed queries.
+template <int CGW, int MQ, bool FULL, bool PF, bool SEL>
 __global__ __launch_bounds__(512) void multi_fwd_mfma_kernel(const MfmaFwdArgs a) {
   constexpr int W = kMfmaWaves;
   constexpr int NQ = W * CGW * 16;           // 16-byte chunks of a row the workgroup covers
   constexpr int XF = 16 * (MQ + 1) * W;      // one exchange buffer: [16 sources][MQ + 1][W]
   extern __shared__ float lds[];
-  Chunk* qlds = reinterpret_cast<Chunk*>(lds);  // [MQ][NQ] query chunks
-  float* xch = lds + MQ * NQ * 4;               // two exchange buffers
+  const int QROWS = SEL ? a.E + 1 : MQ;         // staged query rows
+  Chunk* qlds = reinterpret_cast<Chunk*>(lds);  // [QROWS][NQ] query chunks
+  float* xch = lds + (size_t)QROWS * NQ * 4;    // two exchange buffers
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
 
-  // the queries as bf16 chunks of full-width rows: zero outside the key slice [lo, D) and for
-  // query slots past M, so <row, query> needs no mask
+  // the queries (SEL: the bank rows) as bf16 chunks of full-width rows: zero outside the key slice
+  // [lo, D) and for rows past M (SEL: the extra row E), so <row, query> needs no mask
   const uint16_t* qsrc = static_cast<const uint16_t*>(a.query);
-  for (int idx = tid; idx < MQ * NQ; idx += W * 64) {
+  const int qlive_rows = SEL ? a.E : a.M;
+  for (int idx = tid; idx < QROWS * NQ; idx += W * 64) {
     const int m = idx / NQ, q = idx - m * NQ;
     Chunk v;
 #pragma unroll
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(512) void multi_fwd_mfma_kernel(const MfmaFwdArgs a
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int col = q * 8 + 2 * i + k;
-        h[k] = (m < a.M && col >= a.lo && col < a.D)
+        h[k] = (m < qlive_rows && col >= a.lo && col < a.D)
                    ? static_cast<uint32_t>(qsrc[(int64_t)m * a.R + (col - a.lo)])
                    : 0u;
       }
@@ -163,6 +167,18 @@ __global__ __launch_bounds__(512) void multi_fwd_mfma_kernel(const MfmaFwdArgs a
       load_rows(rows, n);
     }
 
+    // SEL: the staged row of each slot's query (uniform: the ids are read through the scalar cache)
+    int qrow[MQ];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      if constexpr (SEL) {
+        const int64_t id = m < a.M ? a.ids[n * a.M + m] : -1;
+        qrow[m] = (id >= 0 && id < a.E) ? (int)id : a.E;
+      } else {
+        qrow[m] = m;
+      }
+    }
+
     // per source: sum t^2 over the key slice and <row, query_m> (queries zero off the slice)
     float ss[4], acc[4][MQ];
 #pragma unroll
@@ -182,7 +198,7 @@ __global__ __launch_bounds__(512) void multi_fwd_mfma_kernel(const MfmaFwdArgs a
         }
 #pragma unroll
       for (int m = 0; m < MQ; ++m) {
-        const Chunk qv = qlds[m * NQ + qidx[cg]];
+        const Chunk qv = qlds[qrow[m] * NQ + qidx[cg]];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -285,10 +301,10 @@ __global__ __launch_bounds__(512) void multi_fwd_mfma_kernel(const MfmaFwdArgs a
 
 // the one-token-ahead row prefetch where the registers allow it (up to eight queries)
 #define ATTNRES_MFMA_CASE(CGW) \
-  case CGW: return full ? (const void*)&multi_fwd_mfma_kernel<CGW, MQ, true, (MQ <= 8)> \
-                        : (const void*)&multi_fwd_mfma_kernel<CGW, MQ, false, (MQ <= 8)>;
+  case CGW: return full ? (const void*)&multi_fwd_mfma_kernel<CGW, MQ, true, (MQ <= 8), SEL> \
+                        : (const void*)&multi_fwd_mfma_kernel<CGW, MQ, false, (MQ <= 8), SEL>;
 
-template <int MQ>
+template <int MQ, bool SEL>
 static const void* mfma_ptr(int cgw, bool full) {
   switch (cgw) {
     ATTNRES_MFMA_CASE(1) ATTNRES_MFMA_CASE(2) ATTNRES_MFMA_CASE(3) ATTNRES_MFMA_CASE(4)
@@ -297,15 +313,22 @@ static const void* mfma_ptr(int cgw, bool full) {
   return nullptr;
 }
 
-const void* multi_fwd_mfma_kernel_ptr(int cgw, int mq, bool full) {
-  if (mq == 4) return mfma_ptr<4>(cgw, full);
-  if (mq == 8) return mfma_ptr<8>(cgw, full);
-  if (mq == 16) return mfma_ptr<16>(cgw, full);
+const void* multi_fwd_mfma_kernel_ptr(int cgw, int mq, bool full, bool sel) {
+  if (sel) {
+    if (mq == 4) return mfma_ptr<4, true>(cgw, full);
+    if (mq == 8) return mfma_ptr<8, true>(cgw, full);
+    if (mq == 16) return mfma_ptr<16, true>(cgw, full);
+    return nullptr;
+  }
+  if (mq == 4) return mfma_ptr<4, false>(cgw, full);
+  if (mq == 8) return mfma_ptr<8, false>(cgw, full);
+  if (mq == 16) return mfma_ptr<16, false>(cgw, full);
   return nullptr;
 }
 
-size_t multi_fwd_mfma_lds(int cgw, int mq) {
-  return (size_t)mq * kMfmaWaves * cgw * 16 * 16 + 2 * sizeof(float) * 16 * (mq + 1) * kMfmaWaves;
+size_t multi_fwd_mfma_lds(int cgw, int mq, int qrows) {
+  return (size_t)qrows * kMfmaWaves * cgw * 16 * 16 +
+         2 * sizeof(float) * 16 * (mq + 1) * kMfmaWaves;
 }
 
 }  // namespace attnres
