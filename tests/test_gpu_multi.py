@@ -185,6 +185,39 @@ def test_matrix_core_forward_matches_the_vector_kernels(S, N, D, R, M, monkeypat
     assert np.max(np.abs(to_f64(l0) - to_f64(l1))) <= 1e-5 * (1 + np.max(np.abs(to_f64(l0))))
 
 
+@pytest.mark.parametrize("case", ["one_token", "three_tokens", "list_sources", "strided_rows"])
+def test_matrix_core_forward_edges(case):
+    # the matrix-core forward (bf16, 3 <= M <= 16) with fewer tokens than workgroups, sources as a
+    # list of separate allocations, and rows further apart than D (a view into wider rows)
+    import attention_residuals_amd as A
+    S, D, R, M = 7, 1544, 1544, 6
+    N = {"one_token": 1, "three_tokens": 3}.get(case, 301)
+    V, Q, G = _inputs(S, N, D, R, M, "bf16", seed=2400 + N)
+    print(f"[case] matrix-core forward {case}", flush=True)
+    if case == "list_sources":
+        vals = [V[s].clone().cuda() for s in range(S)]
+    elif case == "strided_rows":
+        wide = torch.zeros((S, N, D + 72), dtype=V.dtype, device="cuda")
+        wide[:, :, :D] = V.cuda()
+        vals = wide[:, :, :D]
+        assert vals.stride(1) == D + 72
+    else:
+        vals = V.cuda()
+    y, lse = A.attnres_multi_fwd(vals, Q.cuda())
+    dv, dq = A.attnres_multi_bwd(vals, Q.cuda(), lse, G.cuda())
+    torch.cuda.synchronize()
+    dv = torch.stack(dv) if isinstance(dv, list) else dv
+    ref = oracle.run_multi(V, Q, G)
+    res = {"y": compare_rows(to_f64(y).reshape(-1, D), ref["y"].reshape(-1, D), "bf16"),
+           "lse": compare_stat(to_f64(lse), ref["lse"]),
+           "dvalues": compare_rows(to_f64(dv), ref["dvalues"], "bf16",
+                                   slack=_dvalues_slack(V, Q, G, None,
+                                                        _bwd_groups(S, D, M, "bf16")))}
+    for m in range(M):
+        res[f"dq{m}"] = compare_vec(to_f64(dq[m]), ref["dq"][m], "bf16")
+    assert_ok(res, f"matrix-core forward {case}")
+
+
 def test_multi_query_schedules_and_determinism():
     S, N, D, R, M = 10, 3001, 4096, 4096, 2
     V, Q, G = (t.cuda() for t in _inputs(S, N, D, R, M, "bf16", seed=2200))
