@@ -727,6 +727,56 @@ std::vector<Group> plan_groups(const attnres_multi_desc* m, const MultiShape& ms
   return g;
 }
 
+// The one-pass matrix-core forward of the multi-query read (ids == nullptr: M fixed queries) or
+// of the selected-query read (M slots per token, queries = the [E, R] bank): bf16, 3 <= M <= 16,
+// 2 <= S <= 16, D <= 4096, and the staged queries (M rows, or E + 1 with a zero row) within the
+// workgroup's LDS; ATTNRES_MULTI_MFMA=0 turns it off. *used tells whether it was launched.
+attnres_status try_mfma_fwd(int S, int D, int R, int M, float eps, float scale, bool bf16,
+                            const void* const* src, int64_t row_stride, int64_t N,
+                            const void* queries, const int64_t* ids, int E, void* y, int64_t y_sm,
+                            int64_t y_sn, float* lse, int64_t l_sm, int64_t l_sn, const DevFacts& f,
+                            void* stream, bool* used) {
+  *used = false;
+  const char* e = std::getenv("ATTNRES_MULTI_MFMA");
+  if (e && e[0] == '0') return ATTNRES_OK;
+  const int cgw = (D + 1023) / 1024;
+  const int mq = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
+  const bool sel = ids != nullptr;
+  const size_t lds = multi_fwd_mfma_lds(cgw, mq, sel ? E + 1 : mq);
+  if (!bf16 || S < 2 || S > 16 || M < 3 || M > 16 || cgw > 4 || lds > (size_t)f.lds_per_block)
+    return ATTNRES_OK;
+  const void* fn = multi_fwd_mfma_kernel_ptr(cgw, mq, R == D, sel);
+  if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query forward kernel");
+  int per_cu = 0;
+  attnres_status st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu);
+  if (st != ATTNRES_OK) return st;
+  MfmaFwdArgs ma;
+  std::memset(&ma, 0, sizeof ma);
+  for (int s = 0; s < S; ++s) ma.src[s] = src[s];
+  ma.row_stride = row_stride;
+  ma.N = N;
+  ma.S = S;
+  ma.D = D;
+  ma.R = R;
+  ma.lo = D - R;
+  ma.M = M;
+  ma.eps = eps;
+  ma.scale = scale;
+  ma.inv_R = 1.0f / (float)R;
+  ma.query = queries;
+  ma.y = y;
+  ma.y_sm = y_sm;
+  ma.y_sn = y_sn;
+  ma.lse = lse;
+  ma.l_sm = l_sm;
+  ma.l_sn = l_sn;
+  ma.ids = ids;
+  ma.E = E;
+  *used = true;
+  const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
+  return launch(fn, grid, 1, 64 * kMfmaWaves, lds, &ma, stream, "matrix-core forward launch");
+}
+
 // Exchange buffers and ticket slots; with fixed queries (not the selected read) and two or more
 // chunks per thread also the group's query slices, 16 bytes per thread, query and chunk.
 size_t multi_fwd_lds(const MultiShape& ms, int mq, bool fixed_queries) {
@@ -863,45 +913,13 @@ attnres_status attnres_multi_fwd(const attnres_multi_desc* m, const attnres_sour
   int64_t y_sm, y_sn, l_sm, l_sn;
   multi_strides(m, &y_sm, &y_sn, &l_sm, &l_sn);
 
-  // Three to sixteen bf16 queries over 2 to 16 sources of width <= 4096: one pass through the
-  // matrix-core forward (the vector-ALU kernels below are bound by VALU issue beyond two queries).
-  // ATTNRES_MULTI_MFMA=0 turns it off.
+  // Three to sixteen bf16 queries: one pass through the matrix-core forward when it applies.
   {
-    const char* e = std::getenv("ATTNRES_MULTI_MFMA");
-    const bool off = e && e[0] == '0';
-    const int cgw = (m->D + 1023) / 1024;
-    const int mq = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
-    const size_t lds = multi_fwd_mfma_lds(cgw, mq, mq);
-    if (!off && ms.base.bf16 && m->S >= 2 && m->S <= 16 && M >= 3 && M <= 16 && cgw <= 4 &&
-        lds <= (size_t)f.lds_per_block) {
-      const void* fn = multi_fwd_mfma_kernel_ptr(cgw, mq, m->R == m->D, false);
-      if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query forward kernel");
-      int per_cu = 0;
-      if ((st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu)) != ATTNRES_OK) return st;
-      MfmaFwdArgs ma;
-      std::memset(&ma, 0, sizeof ma);
-      for (int s = 0; s < m->S; ++s) ma.src[s] = a.src[s];
-      ma.row_stride = values->row_stride;
-      ma.N = N;
-      ma.S = m->S;
-      ma.D = m->D;
-      ma.R = m->R;
-      ma.lo = m->D - m->R;
-      ma.M = (int)M;
-      ma.eps = m->eps;
-      ma.scale = m->scale;
-      ma.inv_R = 1.0f / (float)m->R;
-      ma.query = queries;
-      ma.y = y;
-      ma.y_sm = y_sm;
-      ma.y_sn = y_sn;
-      ma.lse = lse;
-      ma.l_sm = l_sm;
-      ma.l_sn = l_sn;
-      const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
-      return launch(fn, grid, 1, 64 * kMfmaWaves, lds, &ma, stream,
-                    "matrix-core multi-query forward launch");
-    }
+    bool used = false;
+    st = try_mfma_fwd(m->S, m->D, m->R, (int)M, m->eps, m->scale, ms.base.bf16, a.src,
+                      values->row_stride, N, queries, nullptr, 0, y, y_sm, y_sn, lse, l_sm, l_sn, f,
+                      stream, &used);
+    if (st != ATTNRES_OK || used) return st;
   }
   a.row_stride = values->row_stride;
   a.N = N;
@@ -1226,46 +1244,14 @@ attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnre
   DevFacts f;
   if ((st = device_facts(&f)) != ATTNRES_OK) return st;
 
-  // Three to sixteen bf16 slots over 2 to 16 sources of width <= 4096, with the bank staged in
-  // LDS: one pass through the matrix-core forward (ATTNRES_MULTI_MFMA=0 turns it off).
+  // Three to sixteen bf16 slots, the bank staged in LDS: one pass through the matrix-core forward
+  // when it applies.
   {
-    const char* e = std::getenv("ATTNRES_MULTI_MFMA");
-    const bool off = e && e[0] == '0';
-    const int cgw = (d->D + 1023) / 1024;
-    const int mq = K <= 4 ? 4 : (K <= 8 ? 8 : 16);
-    const size_t lds = multi_fwd_mfma_lds(cgw, mq, d->E + 1);
-    if (!off && ms.base.bf16 && d->S >= 2 && d->S <= 16 && K >= 3 && K <= 16 && cgw <= 4 &&
-        lds <= (size_t)f.lds_per_block) {
-      const void* fn = multi_fwd_mfma_kernel_ptr(cgw, mq, d->R == d->D, true);
-      if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core selected-query forward kernel");
-      int per_cu = 0;
-      if ((st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu)) != ATTNRES_OK) return st;
-      MfmaFwdArgs ma;
-      std::memset(&ma, 0, sizeof ma);
-      for (int s = 0; s < d->S; ++s) ma.src[s] = a.src[s];
-      ma.row_stride = values->row_stride;
-      ma.N = N;
-      ma.S = d->S;
-      ma.D = d->D;
-      ma.R = d->R;
-      ma.lo = d->D - d->R;
-      ma.M = (int)K;
-      ma.eps = d->eps;
-      ma.scale = d->scale;
-      ma.inv_R = 1.0f / (float)d->R;
-      ma.query = bank;
-      ma.y = y;
-      ma.y_sm = d->D;
-      ma.y_sn = K * d->D;
-      ma.lse = lse;
-      ma.l_sm = 1;
-      ma.l_sn = K;
-      ma.ids = ids;
-      ma.E = d->E;
-      const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
-      return launch(fn, grid, 1, 64 * kMfmaWaves, lds, &ma, stream,
-                    "matrix-core selected-query forward launch");
-    }
+    bool used = false;
+    st = try_mfma_fwd(d->S, d->D, d->R, (int)K, d->eps, d->scale, ms.base.bf16, a.src,
+                      values->row_stride, N, bank, ids, d->E, y, d->D, K * d->D, lse, 1, K, f,
+                      stream, &used);
+    if (st != ATTNRES_OK || used) return st;
   }
 
   const std::vector<Group> groups = plan_groups(&m, ms);
