@@ -71,7 +71,7 @@ __device__ __forceinline__ float sum8(const float* p) {
 
 // SEL: the selected-query read: token n's query m is bank row ids[n, m] (M = slots per token); the
 // whole bank plus one zero row (for ids outside [0, E)) is staged instead of M fixed queries.
-template <int CGW, int MQ, bool FULL, bool PF, bool SEL>
+template <int CGW, int MQ, bool FULL, bool SEL>
 __global__ __launch_bounds__(512) void multi_fwd_mfma_kernel(const MfmaFwdArgs a) {
   constexpr int W = kMfmaWaves;
   constexpr int NQ = W * CGW * 16;           // 16-byte chunks of a row the workgroup covers
@@ -135,37 +135,23 @@ __global__ __launch_bounds__(512) void multi_fwd_mfma_kernel(const MfmaFwdArgs a
   char* ybase = static_cast<char*>(a.y);
   __syncthreads();
 
-  // a token's rows; with PF the next token's are loaded as soon as this token's have arrived, so
-  // their transfer overlaps this token's math and stores
-  auto load_rows = [&](Chunk (&r)[CGW][4], int64_t tok) {
-    const int64_t roff = tok * a.row_stride * 2;
-    const bool tok_ok = tok < a.N;
+  // Tokens are strided over the grid, each loading its rows at its start: a one-token-ahead
+  // prefetch into a second register set measured 2-3% slower (its per-token register copies cost
+  // more than it hid, with two workgroups per CU where the registers allow).
+  int buf = 0;
+  for (int64_t n = blockIdx.x; n < a.N; n += gridDim.x) {
+    const int64_t roff = n * a.row_stride * 2;
+    Chunk rows[CGW][4];
 #pragma unroll
     for (int cg = 0; cg < CGW; ++cg)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (tok_ok && live[j] && qok[cg]) {
-          r[cg][j] = nt_load16(base[j] + roff + (int64_t)qidx[cg] * 16);
+        if (live[j] && qok[cg]) {
+          rows[cg][j] = nt_load16(base[j] + roff + (int64_t)qidx[cg] * 16);
         } else {
-          r[cg][j] = Chunk{};
+          rows[cg][j] = Chunk{};
         }
       }
-  };
-  Chunk rows[CGW][4];
-  Chunk nrows[PF ? CGW : 1][4];
-  if constexpr (PF) load_rows(nrows, blockIdx.x);
-
-  int buf = 0;
-  for (int64_t n = blockIdx.x; n < a.N; n += gridDim.x) {
-    if constexpr (PF) {
-#pragma unroll
-      for (int cg = 0; cg < CGW; ++cg)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) rows[cg][j] = nrows[cg][j];
-      load_rows(nrows, n + gridDim.x);
-    } else {
-      load_rows(rows, n);
-    }
 
     // SEL: the staged row of each slot's query (uniform: the ids are read through the scalar cache)
     int qrow[MQ];
@@ -299,10 +285,10 @@ __global__ __launch_bounds__(512) void multi_fwd_mfma_kernel(const MfmaFwdArgs a
   }
 }
 
-// the one-token-ahead row prefetch where the registers allow it (up to eight queries)
+// instantiations: 1 to 4 column groups per wave, with or without a key slice
 #define ATTNRES_MFMA_CASE(CGW) \
-  case CGW: return full ? (const void*)&multi_fwd_mfma_kernel<CGW, MQ, true, (MQ <= 8), SEL> \
-                        : (const void*)&multi_fwd_mfma_kernel<CGW, MQ, false, (MQ <= 8), SEL>;
+  case CGW: return full ? (const void*)&multi_fwd_mfma_kernel<CGW, MQ, true, SEL> \
+                        : (const void*)&multi_fwd_mfma_kernel<CGW, MQ, false, SEL>;
 
 template <int MQ, bool SEL>
 static const void* mfma_ptr(int cgw, bool full) {
