@@ -146,8 +146,11 @@ attnres_status attnres_bwd(const attnres_desc* desc, const attnres_sources* valu
  * written: no key-norm weight and no output norm. The backward returns dvalues summed over the
  * queries and dq [M, R], each row summed over all tokens.
  * Token-resident only: a token's S rows must fit on chip (attnres_multi_*_workspace_bytes and the
- * entry points return ATTNRES_ERR_UNSUPPORTED otherwise; at D = 4096, bf16, S <= 24). M > 4 runs as
- * groups of at most four queries, each reading the sources again.
+ * entry points return ATTNRES_ERR_UNSUPPORTED otherwise; at D = 4096, bf16, S <= 24). The forward of
+ * 3 <= M <= 16 bf16 queries over 2 <= S <= 16 sources with D <= 4096 runs in one pass on matrix cores
+ * (tokens strided over the grid: the optional forward workspace is then not used); otherwise, and
+ * always in the backward, queries run in groups of at most four, each group reading the sources
+ * again (later backward groups add into dvalues).
  * Layout of y, dout [.., D] and lse: ATTNRES_QUERY_MAJOR = [M, N] rows (the page's default),
  * ATTNRES_TOKEN_MAJOR = [N, M] rows (the page's output_layout="token_major"). */
 typedef enum { ATTNRES_QUERY_MAJOR = 0, ATTNRES_TOKEN_MAJOR = 1 } attnres_layout;
@@ -189,7 +192,10 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* desc, const attnres_s
  * [N, K]. The backward returns dvalues (summed over the K reads) and dbank [E, R]: for every bank
  * row e, the sum of the query gradients of all (n, k) with ids[n, k] = e. ids are int64 on the
  * device; an id outside [0, E) reads a zero query and its bank gradient is dropped. Token-resident
- * with one or two chunks per thread (D <= 8192 bf16 / 4096 f32); queries run in groups of two.
+ * with one or two chunks per thread (D <= 8192 bf16 / 4096 f32). The forward of 3 <= K <= 16 bf16
+ * slots over 2 <= S <= 16 sources with D <= 4096 runs in one pass on matrix cores when the bank
+ * (E + 1 rows of D bf16) fits in a workgroup's LDS (the optional forward workspace is then not
+ * used); otherwise, and in the backward, slots run in groups of at most four.
  * The bank gradient goes through per-workgroup FP32 partial rows of the whole bank (the workspace
  * is 256 + P * E * R * 4 bytes, P = backward workgroups), so a large bank costs workspace and
  * traffic; E * R * 4 must stay below 2 GiB (else ATTNRES_ERR_UNSUPPORTED). */
