@@ -139,6 +139,7 @@ def _check(V, Q, G, label, dtype, init=None, **kw):
     (6, 211, 1032, 1032, 3, "bf16", "query_major"),    # ragged last column group
     (12, 157, 3072, 768, 5, "bf16", "token_major"),    # sliced key, three column groups
     (2, 300, 2048, 7, 4, "bf16", "query_major"),        # slice start inside a chunk
+    (10, 257, 4096, 4096, 16, "bf16", "token_major"),  # the largest staged-query LDS (~145 KiB)
 ])
 def test_multi_query_parity(S, N, D, R, M, dtype, layout):
     V, Q, G = _inputs(S, N, D, R, M, dtype, seed=2000 + S * M + D)

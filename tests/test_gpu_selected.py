@@ -100,6 +100,7 @@ def _check(V, bank, ids, G, label, dtype, init=None, ref_bank=None, ref_ids=None
     (10, 301, 4096, 4096, 8, 4, "bf16"),    # four slots in one backward launch, LDS bank
     (8, 257, 1024, 1024, 4, 4, "f32"),      # four slots, FP32
     (10, 211, 2048, 2048, 24, 7, "bf16"),   # seven slots: groups of four and three, global blocks
+    (6, 149, 2048, 2048, 40, 4, "bf16"),    # a bank too large to stage: the slot-group forward
 ])
 def test_selected_parity(S, N, D, R, E, K, dtype):
     print(f"[case] selected S={S} N={N} D={D} R={R} E={E} K={K} {dtype}", flush=True)
