@@ -135,7 +135,7 @@ def main() -> int:
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the read "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the read "
               "shards over tokens, so N GPUs run N independent copies of this step plus one "
               "small all-reduce of the q/w gradients.", file=sys.stderr)
         return 2
