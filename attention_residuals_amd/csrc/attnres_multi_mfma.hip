@@ -138,23 +138,37 @@ void multi_fwd_mfma_kernel(const MfmaFwdArgs a) {
   char* ybase = static_cast<char*>(a.y);
   __syncthreads();
 
-  // Tokens are strided over the grid, each loading its rows at its start: a one-token-ahead
-  // prefetch into a second register set measured 2-3% slower (its per-token register copies cost
-  // more than it hid, with two workgroups per CU where the registers allow).
+  // Tokens are strided over the grid. With 16 query slots (one workgroup per CU, no other latency
+  // hiding) a column group's rows for the next token are loaded as soon as this token's mixture has
+  // read them, into the same registers, so loads stay in flight through the rest of the token
+  // (forward at M = 16: 1.89 -> 1.72 ms); with up to 8 slots (two workgroups per CU up to four) each
+  // token loads its rows at its start, which measured faster there (M = 3: 0.74 ms against 1.06;
+  // M = 8: 1.04 against 1.14). A one-token-ahead prefetch into a second register set measured 2-3%
+  // slower than loading at the start: its per-token register copies cost more than it hid.
+  constexpr bool kInPlace = MQ == 16;
+  auto load_group = [&](Chunk (&r)[4], int cg, int64_t tok) {
+    const int64_t roff = tok * a.row_stride * 2;
+    const bool tok_ok = tok < a.N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (tok_ok && live[j] && qok[cg]) {
+        r[j] = nt_load16(base[j] + roff + (int64_t)qidx[cg] * 16);
+      } else {
+        r[j] = Chunk{};
+      }
+    }
+  };
+  Chunk rows[CGW][4];
+  if constexpr (kInPlace) {
+#pragma unroll
+    for (int cg = 0; cg < CGW; ++cg) load_group(rows[cg], cg, blockIdx.x);
+  }
   int buf = 0;
   for (int64_t n = blockIdx.x; n < a.N; n += gridDim.x) {
-    const int64_t roff = n * a.row_stride * 2;
-    Chunk rows[CGW][4];
+    if constexpr (!kInPlace) {
 #pragma unroll
-    for (int cg = 0; cg < CGW; ++cg)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (live[j] && qok[cg]) {
-          rows[cg][j] = nt_load16(base[j] + roff + (int64_t)qidx[cg] * 16);
-        } else {
-          rows[cg][j] = Chunk{};
-        }
-      }
+      for (int cg = 0; cg < CGW; ++cg) load_group(rows[cg], cg, n);
+    }
 
     // SEL: the staged row of each slot's query (uniform: the ids are read through the scalar cache)
     int qrow[MQ];
@@ -270,6 +284,8 @@ void multi_fwd_mfma_kernel(const MfmaFwdArgs a) {
         o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, bv, o, 0, 0, 0);
         acc_o[e] = o;
       }
+      // the mixture has read this column group: its registers take the next token's rows
+      if constexpr (kInPlace) load_group(rows[cg], cg, n + gridDim.x);
       // lane (g, c) holds query 4g + r at chunk qidx[cg], element e, in acc_o[e][r]
       if (qok[cg]) {
 #pragma unroll
