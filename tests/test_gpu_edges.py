@@ -13,8 +13,8 @@ import pytest
 import torch
 
 import attnres_workloads as W
-from parity import (assert_ok, check_all, compare_rows, compare_vec, gpu_available, inputs_on,
-                    run_gpu, run_oracle, to_f64)
+from parity import (assert_ok, check_all, compare_rows, compare_vec, gpu_available, half_ulp_bf16,
+                    inputs_on, run_gpu, run_oracle, to_f64)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
@@ -228,6 +228,43 @@ def test_accumulate_into_existing_dvalues(S, N, D, R, dtype, out_norm, packed):
     ref = run_oracle(w, xc)
     ref["dvalues"] = ref["dvalues"] + init.double().numpy()
     assert_ok(check_all(w, got, ref), f"accumulate S={S} N={N} D={D} R={R} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_schedule_reads_share_completed_sources(dtype):
+    # fast-attnres page, "Full and Block schedules": a Block read takes the embedding and the
+    # completed block sums and, inside a block, the caller's partial sum as one more ordinary
+    # source. Two reads in one block: the first without a partial sum (three sources in one
+    # allocation), the second with one (its own allocation). The completed sources' gradients sum
+    # over both reads: the first backward writes them, the second adds into them.
+    N, D = 401, 2048
+    wa = _wl(3, N, D, D, dtype=dtype, seed=2101)
+    wb = _wl(4, N, D, D, dtype=dtype, seed=2102)
+    xa, xb = W.generate(wa), W.generate(wb)
+    xb["values"][:3].copy_(xa["values"])
+    completed = xa["values"].to("cuda")
+    partial = xb["values"][3].to("cuda").clone()
+    dcompleted = torch.empty_like(completed)
+    dpartial = torch.zeros_like(partial)
+    srcs = [completed[s] for s in range(3)]
+    dsrcs = [dcompleted[s] for s in range(3)]
+    print(f"[case] block schedule {dtype}: read without, then with a partial sum", flush=True)
+    ga = run_gpu(wa, inputs_on(xa, "cuda"), values=srcs, dvalues=dsrcs)
+    gb = run_gpu(wb, inputs_on(xb, "cuda"), values=srcs + [partial], dvalues=dsrcs + [dpartial],
+                 accumulate=True)
+    ra, rb = run_oracle(wa, xa), run_oracle(wb, xb)
+    assert_ok(check_all(wa, ga, ra), f"block read without a partial sum {dtype}")
+    want = rb["dvalues"].copy()
+    want[:3] += ra["dvalues"]
+    res = check_all(wb, gb, dict(rb, dvalues=want))
+    if dtype == "bf16":
+        # the completed sources are rounded to bf16 after each read: half an ulp of each running
+        # sum, taken at the larger of the stored and the exact magnitude as for one rounding
+        got, first = to_f64(gb["dvalues"]), to_f64(ga["dvalues"])
+        slack = half_ulp_bf16(np.maximum(np.abs(got), np.abs(want)))
+        slack[:3] += half_ulp_bf16(np.maximum(np.abs(first), np.abs(ra["dvalues"])))
+        res["dvalues"] = compare_rows(got, want, dtype, slack=slack)
+    assert_ok(res, f"block read with a partial sum, gradients summed over both reads {dtype}")
 
 
 @pytest.mark.parametrize("S,N,D", [(8, 32768 + 5, 2048), (10, 32768 + 3, 4096)])
