@@ -104,6 +104,8 @@ struct MfmaFwdArgs {
   int64_t l_sm, l_sn;
   const int64_t* ids;            // selected-query read: [N, M] bank rows per token (query = bank)
   int E;                         //   bank rows; ids outside [0, E) read a zero query
+  uint32_t* ticket;              // token batch counter (zeroed before the launch), or null: static
+  int64_t tpt;                   //   tokens per ticket
 };
 
 struct MultiBwdArgs {

@@ -734,8 +734,8 @@ std::vector<Group> plan_groups(const attnres_multi_desc* m, const MultiShape& ms
 attnres_status try_mfma_fwd(int S, int D, int R, int M, float eps, float scale, bool bf16,
                             const void* const* src, int64_t row_stride, int64_t N,
                             const void* queries, const int64_t* ids, int E, void* y, int64_t y_sm,
-                            int64_t y_sn, float* lse, int64_t l_sm, int64_t l_sn, const DevFacts& f,
-                            void* stream, bool* used) {
+                            int64_t y_sn, float* lse, int64_t l_sm, int64_t l_sn, void* workspace,
+                            const DevFacts& f, void* stream, bool* used) {
   *used = false;
   const char* e = std::getenv("ATTNRES_MULTI_MFMA");
   if (e && e[0] == '0') return ATTNRES_OK;
@@ -772,8 +772,22 @@ attnres_status try_mfma_fwd(int S, int D, int R, int M, float eps, float scale, 
   ma.l_sn = l_sn;
   ma.ids = ids;
   ma.E = E;
+  // sixteen slots, a workspace and at least two tokens per resident workgroup: tokens come in
+  // batches from a counter in the workspace (reset by a kernel: no memset, so the call stays
+  // capturable); the kernels of fewer slots keep the static stride
+  const int64_t resident = (int64_t)f.cus * per_cu;
+  const bool dyn = mq == 16 && workspace != nullptr && N >= 2 * resident && N < kMaxTicketTokens;
+  ma.tpt = dyn ? tokens_per_ticket(N, resident, (double)(S + M) * D * 2, 55.0, 1) : 1;
+  ma.ticket = nullptr;
   *used = true;
-  const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
+  if (dyn) {
+    ma.ticket = static_cast<uint32_t*>(workspace);
+    void* targ = ma.ticket;
+    attnres_status rs = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream,
+                               "ticket reset launch");
+    if (rs != ATTNRES_OK) return rs;
+  }
+  const int grid = (int)std::min<int64_t>((N + ma.tpt - 1) / ma.tpt, resident);
   return launch(fn, grid, 1, 64 * kMfmaWaves, lds, &ma, stream, "matrix-core forward launch");
 }
 
@@ -917,8 +931,8 @@ attnres_status attnres_multi_fwd(const attnres_multi_desc* m, const attnres_sour
   {
     bool used = false;
     st = try_mfma_fwd(m->S, m->D, m->R, (int)M, m->eps, m->scale, ms.base.bf16, a.src,
-                      values->row_stride, N, queries, nullptr, 0, y, y_sm, y_sn, lse, l_sm, l_sn, f,
-                      stream, &used);
+                      values->row_stride, N, queries, nullptr, 0, y, y_sm, y_sn, lse, l_sm, l_sn,
+                      workspace, f, stream, &used);
     if (st != ATTNRES_OK || used) return st;
   }
   a.row_stride = values->row_stride;
@@ -1249,8 +1263,8 @@ attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnre
   {
     bool used = false;
     st = try_mfma_fwd(d->S, d->D, d->R, (int)K, d->eps, d->scale, ms.base.bf16, a.src,
-                      values->row_stride, N, bank, ids, d->E, y, d->D, K * d->D, lse, 1, K, f,
-                      stream, &used);
+                      values->row_stride, N, bank, ids, d->E, y, d->D, K * d->D, lse, 1, K,
+                      workspace, f, stream, &used);
     if (st != ATTNRES_OK || used) return st;
   }
 

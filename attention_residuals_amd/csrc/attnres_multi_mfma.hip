@@ -83,6 +83,7 @@ void multi_fwd_mfma_kernel(const MfmaFwdArgs a) {
   const int QROWS = SEL ? a.E + 1 : MQ;         // staged query rows
   Chunk* qlds = reinterpret_cast<Chunk*>(lds);  // [QROWS][NQ] query chunks
   float* xch = lds + (size_t)QROWS * NQ * 4;    // two exchange buffers
+  uint32_t* tslot = reinterpret_cast<uint32_t*>(xch + 2 * XF);  // two ticket slots
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
 
@@ -158,13 +159,26 @@ void multi_fwd_mfma_kernel(const MfmaFwdArgs a) {
       }
     }
   };
+  // Tokens: with a counter, batches of tpt consecutive tokens, the first batch by workgroup index
+  // and each later one by a ticket taken during the batch's last token (read after that token's
+  // exchange barrier, before the next token's rows are loaded); without one, a static stride.
+  // Only the sixteen-slot kernels (one workgroup per CU) take tickets: M = 16, 1.86 -> 1.79 ms.
+  // With up to eight slots the counter's registers cost more than it balances (two or more
+  // workgroups per CU; M = 4 0.78 -> 0.97 ms, M = 8 1.03 -> 1.15, even on the static stride).
+  constexpr bool kTickets = MQ == 16;
+  const bool dyn = kTickets && a.ticket != nullptr;
+  const int64_t B = dyn ? a.tpt : 1;
+  int64_t n = (int64_t)blockIdx.x * B, batch_end = n + B;
   Chunk rows[CGW][4];
   if constexpr (kInPlace) {
 #pragma unroll
-    for (int cg = 0; cg < CGW; ++cg) load_group(rows[cg], cg, blockIdx.x);
+    for (int cg = 0; cg < CGW; ++cg) load_group(rows[cg], cg, n);
   }
   int buf = 0;
-  for (int64_t n = blockIdx.x; n < a.N; n += gridDim.x) {
+  while (n < a.N) {
+    const bool take = dyn && n + 1 >= batch_end;
+    uint32_t tk = 0;
+    if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
     if constexpr (!kInPlace) {
 #pragma unroll
       for (int cg = 0; cg < CGW; ++cg) load_group(rows[cg], cg, n);
@@ -224,7 +238,13 @@ void multi_fwd_mfma_kernel(const MfmaFwdArgs a) {
         for (int m = 0; m < MQ; ++m) xb[(s * (MQ + 1) + 1 + m) * W + wave] = acc[j][m];
       }
     }
+    if (take && tid == 0) tslot[buf] = tk;
     __syncthreads();
+    int64_t next = dyn ? n + 1 : n + gridDim.x;
+    if (take) {
+      next = ((int64_t)gridDim.x + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf])) * B;
+      batch_end = next + B;
+    }
     buf ^= 1;
 
     // lane (g, c) finishes query c on its sources 4g .. 4g+3; the softmax's maximum and sum
@@ -285,7 +305,7 @@ void multi_fwd_mfma_kernel(const MfmaFwdArgs a) {
         acc_o[e] = o;
       }
       // the mixture has read this column group: its registers take the next token's rows
-      if constexpr (kInPlace) load_group(rows[cg], cg, n + gridDim.x);
+      if constexpr (kInPlace) load_group(rows[cg], cg, next);
       // lane (g, c) holds query 4g + r at chunk qidx[cg], element e, in acc_o[e][r]
       if (qok[cg]) {
 #pragma unroll
@@ -301,6 +321,7 @@ void multi_fwd_mfma_kernel(const MfmaFwdArgs a) {
         }
       }
     }
+    n = next;
   }
 }
 
@@ -333,7 +354,7 @@ const void* multi_fwd_mfma_kernel_ptr(int cgw, int mq, bool full, bool sel) {
 
 size_t multi_fwd_mfma_lds(int cgw, int mq, int qrows) {
   return (size_t)qrows * kMfmaWaves * cgw * 16 * 16 +
-         2 * sizeof(float) * 16 * (mq + 1) * kMfmaWaves;
+         2 * sizeof(float) * 16 * (mq + 1) * kMfmaWaves + 2 * sizeof(uint32_t);
 }
 
 }  // namespace attnres

@@ -148,7 +148,8 @@ attnres_status attnres_bwd(const attnres_desc* desc, const attnres_sources* valu
  * Token-resident only: a token's S rows must fit on chip (attnres_multi_*_workspace_bytes and the
  * entry points return ATTNRES_ERR_UNSUPPORTED otherwise; at D = 4096, bf16, S <= 24). The forward of
  * 3 <= M <= 16 bf16 queries over 2 <= S <= 16 sources with D <= 4096 runs in one pass on matrix cores
- * (tokens strided over the grid: the optional forward workspace is then not used); otherwise, and
+ * (tokens strided over the grid; with 9 to 16 queries and the optional forward workspace they come
+ * from its counter instead; outputs are the same either way, bit for bit); otherwise, and
  * always in the backward, queries run in groups of at most four, each group reading the sources
  * again (later backward groups add into dvalues).
  * Layout of y, dout [.., D] and lse: ATTNRES_QUERY_MAJOR = [M, N] rows (the page's default),
@@ -194,8 +195,9 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* desc, const attnres_s
  * device; an id outside [0, E) reads a zero query and its bank gradient is dropped. Token-resident
  * with one or two chunks per thread (D <= 8192 bf16 / 4096 f32). The forward of 3 <= K <= 16 bf16
  * slots over 2 <= S <= 16 sources with D <= 4096 runs in one pass on matrix cores when the bank
- * (E + 1 rows of D bf16) fits in a workgroup's LDS (the optional forward workspace is then not
- * used); otherwise, and in the backward, slots run in groups of at most four.
+ * (E + 1 rows of D bf16) fits in a workgroup's LDS (the optional forward workspace holds the token
+ * counter of 9 to 16 slots, as in the multi-query read); otherwise, and in the backward, slots run
+ * in groups of at most four.
  * The bank gradient goes through per-workgroup FP32 partial rows of the whole bank (the workspace
  * is 256 + P * E * R * 4 bytes, P = backward workgroups), so a large bank costs workspace and
  * traffic; E * R * 4 must stay below 2 GiB (else ATTNRES_ERR_UNSUPPORTED). */

@@ -263,3 +263,63 @@ def test_multi_query_zero_tokens_and_unsupported_shape():
     with pytest.raises(A.AttnResError) as e:
         A.attnres_multi_fwd(big, torch.zeros((2, 8192), dtype=torch.bfloat16, device="cuda"))
     assert e.value.status == 2
+
+
+
+def _fwd_counter_case(fwd, ref, N, label, uses_counter):
+    """Runs the forward `fwd(dynamic, workspace)` with a workspace (poisoned) and without one
+    (static stride): outputs must agree bit for bit (per-token results do not depend on which
+    workgroup ran the token) and match the oracle. Sixteen-slot kernels take their tokens from the
+    workspace's counter (reset, then one ticket per batch: at most N); the others leave it alone."""
+    ws = torch.full((256,), 0xFF, dtype=torch.uint8, device="cuda")
+    y_d, lse_d = fwd(True, ws)
+    y_s, lse_s = fwd(False, None)
+    torch.cuda.synchronize()
+    tickets = int(ws[:4].cpu().view(torch.int32).item())
+    if uses_counter:
+        assert 0 < tickets <= N, f"{label}: token counter not used ({tickets})"
+    else:
+        assert tickets == -1, f"{label}: token counter touched ({tickets})"
+    assert torch.equal(y_d, y_s) and torch.equal(lse_d, lse_s), label
+    D = y_d.shape[-1]
+    res = {"y": compare_rows(to_f64(y_d).reshape(-1, D), ref["y"].reshape(-1, D), "bf16"),
+           "lse": compare_stat(to_f64(lse_d).reshape(-1), ref["lse"].reshape(-1))}
+    assert_ok(res, label)
+
+
+@pytest.mark.parametrize("M,S,D,R,layout", [
+    (16, 10, 1024, 1024, "query_major"),  # sixteen slots: the next token's rows loaded in place
+    (12, 7, 3072, 768, "token_major"),    # padded to sixteen slots, sliced key, three groups
+    (4, 10, 1024, 1024, "token_major"),   # four slots: static stride with or without workspace
+])
+def test_matrix_core_forward_token_counter(M, S, D, R, layout):
+    # enough tokens for at least two per resident workgroup, so the counter schedule runs
+    import attention_residuals_amd as A
+    N = 2 * 4 * 256 + 37
+    print(f"[case] matrix-core forward counter M={M} S={S} D={D} R={R} {layout} N={N}", flush=True)
+    V, Q, _ = _inputs(S, N, D, R, M, "bf16", seed=4100 + M)
+    Vg, Qg = V.cuda(), Q.cuda()
+
+    def fwd(dynamic, ws):
+        y, lse = A.attnres_multi_fwd(Vg, Qg, layout=layout, dynamic=dynamic, workspace=ws)
+        return _from_layout(y, layout), _from_layout(lse, layout)
+
+    ref = oracle.run_multi(V, Q, want=("y", "lse"))
+    _fwd_counter_case(fwd, ref, N, f"matrix-core forward counter M={M} {layout}", M > 8)
+
+
+def test_matrix_core_selected_forward_token_counter():
+    import attention_residuals_amd as A
+    S, N, D, E, K = 10, 2 * 4 * 256 + 37, 1024, 8, 12
+    print(f"[case] matrix-core selected forward counter E={E} K={K} N={N}", flush=True)
+    g = torch.Generator().manual_seed(4200)
+    V = torch.randn((S, N, D), generator=g).to(torch.bfloat16)
+    bank = (torch.randn((E, D), generator=g) / math.sqrt(D)).to(torch.bfloat16)
+    ids = torch.randint(0, E, (N, K), generator=g, dtype=torch.int64)
+    Vg, bg, ig = V.cuda(), bank.cuda(), ids.cuda()
+
+    def fwd(dynamic, ws):
+        return A.attnres_selected_fwd(Vg, bg, ig, dynamic=dynamic, workspace=ws)
+
+    ref = oracle.run_selected(V, bank, ids, want=("y", "lse"))
+    _fwd_counter_case(fwd, ref, N, "matrix-core selected forward counter", True)
