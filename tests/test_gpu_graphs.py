@@ -56,10 +56,12 @@ def _replay_and_compare(capture_step, eager_step, bufs, inputs, outs, reduced, d
             _close(reduced[k], ref[k], deterministic)
 
 
-@pytest.mark.parametrize("deterministic", [True, False])
-def test_multi_query_graph_replay(deterministic):
+# M = 5: the matrix-core forward's eight-slot kernel (static stride); M = 12: its sixteen-slot
+# kernel, which takes tokens from the forward workspace's counter unless deterministic
+@pytest.mark.parametrize("M,deterministic", [(5, True), (5, False), (12, True), (12, False)])
+def test_multi_query_graph_replay(M, deterministic):
     import attention_residuals_amd as A
-    S, N, D, M = 6, 1531, 2048, 5
+    S, N, D = 6, 1531, 2048
     inputs = []
     for seed in (21, 22):
         V, g = _sources(S, N, D, seed)
@@ -96,10 +98,11 @@ def test_multi_query_graph_replay(deterministic):
                         deterministic)
 
 
-@pytest.mark.parametrize("E,deterministic", [(6, True), (6, False), (48, False)])
-def test_selected_query_graph_replay(E, deterministic):
+@pytest.mark.parametrize("E,K,deterministic", [(6, 3, True), (6, 3, False), (48, 3, False),
+                                               (6, 12, False)])
+def test_selected_query_graph_replay(E, K, deterministic):
     import attention_residuals_amd as A
-    S, N, D, K = 6, 1531, 2048, 3
+    S, N, D = 6, 1531, 2048
     inputs = []
     for seed in (31, 32):
         V, g = _sources(S, N, D, seed)
@@ -130,6 +133,6 @@ def test_selected_query_graph_replay(E, deterministic):
                                           deterministic=deterministic)
         return {"y": ye, "lse": le, "dv": dve, "db": dbe}
 
-    print(f"[case] selected graph E={E} deterministic={deterministic}", flush=True)
+    print(f"[case] selected graph E={E} K={K} deterministic={deterministic}", flush=True)
     _replay_and_compare(step, eager, bufs, inputs, {"y": y, "lse": lse, "dv": dv}, {"db": db},
                         deterministic)
