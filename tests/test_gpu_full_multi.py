@@ -58,6 +58,28 @@ def test_multi_query_full_size(M, layout):
     torch.cuda.empty_cache()
 
 
+def test_multi_query_full_size_forward_sixteen_slots():
+    # the sixteen-slot matrix-core forward with its token counter, as `bench.py --queries 16`
+    # runs it (outputs and lse of sampled tokens)
+    import attention_residuals_amd as A
+    w, M, layout = HEADLINE, 16, "query_major"
+    print(f"[case] full multi forward M={M} {layout}", flush=True)
+    values = W.generate(w, device="cuda", with_dout=False)["values"]
+    q = W.multi_inputs(w, M, layout, device="cuda")["queries"]
+    y, lse = A.attnres_multi_fwd(values, q, eps=w.eps, scale=w.scale, layout=layout)
+    torch.cuda.synchronize()
+    toks = sample_tokens(w.N, 24, seed=w.seed + M)
+    sel = torch.tensor(toks, device="cuda")
+    ref = oracle.run_multi(values.cpu(), q.cpu(), eps=w.eps, scale=w.scale, tokens=toks,
+                           want=("y", "lse"), reduce=False)
+    res = {"y": compare_rows(to_f64(y.index_select(1, sel)).reshape(-1, w.D),
+                             ref["y"].reshape(-1, w.D), w.dtype),
+           "lse": compare_stat(to_f64(lse.index_select(1, sel)), ref["lse"])}
+    assert_ok(res, f"full multi forward M={M} {layout}")
+    del values, y, lse
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("E,K", [(8, 2), (8, 4)])
 def test_selected_query_full_size(E, K):
     import attention_residuals_amd as A
