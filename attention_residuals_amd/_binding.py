@@ -195,6 +195,21 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _scratch(nbytes: int, device, stream, zero: bool = False) -> torch.Tensor:
+    """A workspace the binding allocates itself (the caller gave none). It is freed when the
+    binding drops it, which torch's caching allocator orders after the work queued so far on the
+    CURRENT stream only; when the call runs on another stream, the tensor is recorded on that
+    stream too, so its memory is not handed out again before the call's kernels finish. `zero`:
+    counters that must be zero at launch (the single-query read's workspaces)."""
+    t = (torch.zeros if zero else torch.empty)((nbytes,), dtype=torch.uint8, device=device)
+    if stream is not None:
+        ts = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(
+            stream, device=t.device)
+        if ts != torch.cuda.current_stream(t.device):
+            t.record_stream(ts)
+    return t
+
+
 def _prep_fwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor] = None,
                 out_w: Optional[torch.Tensor] = None, *, eps: float = EPS_DEFAULT,
                 scale: float = 1.0, out_norm: bool = False,
@@ -218,7 +233,7 @@ def _prep_fwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor] = None
     if not dynamic:
         workspace = None
     elif workspace is None:
-        workspace = torch.empty((fwd_workspace_bytes(desc),), dtype=torch.uint8, device=dev)
+        workspace = _scratch(fwd_workspace_bytes(desc), dev, stream, zero=True)
     cargs = (ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query), _ptr(norm_w), _ptr(out_w),
              _ptr(out), _ptr(lse), _ptr(out_rstd), _ptr(o32), _ptr(workspace),
              0 if workspace is None else workspace.numel(), _stream(stream))
@@ -269,7 +284,7 @@ def _prep_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
         dow = torch.empty((sv.D,), dtype=sv.dtype, device=dev)
     need = workspace_bytes(desc)
     if workspace is None:
-        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+        workspace = _scratch(max(need, 256), dev, stream, zero=True)
     dstride = dout.stride(0) if sv.N > 1 else sv.D
     cargs = (ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query), _ptr(norm_w), _ptr(out_w),
              _ptr(lse), _ptr(out_rstd), _ptr(o32), _ptr(dout), dstride, ctypes.byref(dv.struct),
@@ -284,8 +299,10 @@ def attnres_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
                 dout: torch.Tensor, **kw):
     """Backward read. Keywords: eps, scale, out_norm, deterministic, accumulate, dvalues, dq, dw,
     dow, workspace, stream. dvalues: packed [S, N, D] or list of [N, D] tensors to write
-    (allocated packed when None). deterministic: fixed token split (bitwise-reproducible
-    dq/dw/dow). accumulate: add this read's gradient to the existing dvalues (which must then be
+    (allocated packed when None). deterministic: a static token split (both schedules give
+    bitwise-reproducible results; the default also hands the last batches out by counter).
+    workspace: at least workspace_bytes(desc) bytes whose first 256 are zero before its first use
+    (allocated zero-filled when None). accumulate: add this read's gradient to the existing dvalues (which must then be
     given). Returns (dvalues, dq, dw or None, dow or None)."""
     fn, cargs, outs, _ = _prep_bwd(values, query, norm_w, out_w, lse, out_rstd, o32, dout, **kw)
     _check(fn(*cargs))
@@ -373,7 +390,7 @@ def attnres_multi_fwd(values, queries: torch.Tensor, *, eps: float = EPS_DEFAULT
     if not dynamic:
         workspace = None
     elif workspace is None:
-        workspace = torch.empty((multi_fwd_workspace_bytes(desc),), dtype=torch.uint8, device=dev)
+        workspace = _scratch(multi_fwd_workspace_bytes(desc), dev, stream)
     _check(load().attnres_multi_fwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(queries),
                                     _ptr(out), _ptr(lse), _ptr(workspace),
                                     0 if workspace is None else workspace.numel(),
@@ -403,8 +420,7 @@ def attnres_multi_bwd(values, queries: torch.Tensor, lse: torch.Tensor, dout: to
     if dq is None:
         dq = torch.empty((M, R), dtype=sv.dtype, device=dev)
     if workspace is None:
-        workspace = torch.empty((max(multi_workspace_bytes(desc), 256),), dtype=torch.uint8,
-                                device=dev)
+        workspace = _scratch(max(multi_workspace_bytes(desc), 256), dev, stream)
     _check(load().attnres_multi_bwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(queries),
                                     _ptr(lse), _ptr(dout), ctypes.byref(dv.struct), _ptr(dq),
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -460,8 +476,7 @@ def attnres_selected_fwd(values, bank: torch.Tensor, ids: torch.Tensor, *,
     if not dynamic:
         workspace = None
     elif workspace is None:
-        workspace = torch.empty((selected_fwd_workspace_bytes(desc),), dtype=torch.uint8,
-                                device=dev)
+        workspace = _scratch(selected_fwd_workspace_bytes(desc), dev, stream)
     _check(load().attnres_selected_fwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(bank),
                                        _ptr(ids), _ptr(out), _ptr(lse), _ptr(workspace),
                                        0 if workspace is None else workspace.numel(),
@@ -491,8 +506,7 @@ def attnres_selected_bwd(values, bank: torch.Tensor, ids: torch.Tensor, lse: tor
     if dbank is None:
         dbank = torch.empty((E, R), dtype=sv.dtype, device=dev)
     if workspace is None:
-        workspace = torch.empty((max(selected_workspace_bytes(desc), 256),), dtype=torch.uint8,
-                                device=dev)
+        workspace = _scratch(max(selected_workspace_bytes(desc), 256), dev, stream)
     _check(load().attnres_selected_bwd(ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(bank),
                                        _ptr(ids), _ptr(lse), _ptr(dout), ctypes.byref(dv.struct),
                                        _ptr(dbank), _ptr(workspace), workspace.numel(),

@@ -7,9 +7,29 @@ namespace attnres {
 
 constexpr int kMaxSources = 64;
 
-// Finaliser workgroup: 64 columns x 16 row phases.
+// Finaliser workgroups: 64 columns x 16 row phases (multi- and selected-query reads); 16 columns x
+// 64 row phases (single-query read: more workgroups over its wider binned rows).
 constexpr int kFinCols = 64;
 constexpr int kFinPhases = 16;
+constexpr int kFinRowsCols = 16;
+constexpr int kFinRowsPhases = 64;
+
+// Counter words of a forward or backward workspace (uint32 indices, each in its own 128-byte
+// line). They are zero when a kernel starts and are returned to zero by the same call (the
+// forward's last workgroup, the backward's finaliser), so a workspace is zeroed once when it is
+// allocated and then serves any number of calls.
+constexpr int kCtrTicket = 0;    // next batch handed out by ticket
+constexpr int kCtrArrive = 32;   // forward: workgroups that have taken their last ticket
+constexpr int kCtrWords = 64;    // 256 bytes
+
+// Exact accumulation of the backward's per-token gradient contributions (token-resident kernel):
+// each FP32 contribution c is split into a multiple of 2^-20 (bin A) and a multiple of 2^-53
+// (bin B, the remainder rounded, |.| <= 2^-21), and each bin is summed in FP64. Every partial sum
+// of bin A stays a multiple of 2^-20 below 2^33 in magnitude and every partial sum of bin B a
+// multiple of 2^-53 below 1 (for fewer than 2^21 tokens), so both sums are exact and their values
+// do not depend on which workgroup summed which tokens, or in which order.
+constexpr double kBinMagicA = 6442450944.0;  // 1.5 * 2^32: (c + M) - M rounds c to 2^-20
+constexpr double kBinMagicB = 0.75;          // 1.5 * 2^-1: rounds to 2^-53
 
 struct FwdArgs {
   const void* src[kMaxSources];  // base of source s ([N, D] rows, row_stride elements apart)
@@ -24,11 +44,18 @@ struct FwdArgs {
   float* lse;                    // [N]
   float* o_rstd;                 // [N] or nullptr
   float* o32;                    // [N, D] or nullptr
-  uint32_t* ticket;              // dynamic token counter, zero at launch (nullptr: static split)
+  uint32_t* ticket;              // counter words (kCtr*; nullptr: static split)
   int64_t tpt;                   // tokens per ticket (batch size of the dynamic schedule)
   int out_norm;
 };
 
+// Backward token schedule: batches of tpt consecutive tokens, nbatch = ceil(N / tpt). Head
+// batches [0, hb_end): workgroup g takes g, g + P, g + 2P, ... (P = gridDim.x). Tail batches
+// [hb_end, nbatch): handed out by the ticket counter as workgroups finish. The token-resident
+// kernel sums every token's q/w gradient into exact bins (kBinMagic*), so it writes one partial
+// row per workgroup whatever tokens it ran (hb_end = P: only each workgroup's first batch is
+// fixed). The streaming kernel sums in FP32 and writes one row per fixed token set: row g for its
+// head batches and row P + (b - hb_end) for tail batch b.
 struct BwdArgs {
   const void* src[kMaxSources];
   void* dsrc[kMaxSources];
@@ -43,11 +70,31 @@ struct BwdArgs {
   const float* o_rstd;
   const float* o32;
   const void* dout;
-  float* part_du;                // [gridDim.x, R]
-  float* part_dow;               // [gridDim.x, D] or nullptr
-  uint32_t* ticket;              // dynamic token counter, zero at launch (nullptr: static split)
-  int64_t tpt;                   // tokens per ticket (batch size of the dynamic schedule)
+  void* part;                    // partial rows: token-resident [P][2][wc] FP64 (bins A, B),
+                                 //   streaming [rows][wc] FP32; du at absolute columns
+                                 //   [lo, D), dow at [D, 2D)
+  int64_t wc;                    // columns of a partial row (D, or 2D with dow)
+  int64_t tpt;                   // tokens per batch
+  int64_t nbatch;                // ceil(N / tpt)
+  int64_t hb_end;                // first tail batch
+  uint32_t* ctr;                 // counter words (kCtr*)
   int out_norm;
+};
+
+// Finaliser of the single-query backward: sums every column's partial rows in a fixed order in
+// FP64 and writes dq = du * w (du without w), dw = du * q and dow; zeroes the ticket counter.
+struct FinRowsArgs {
+  const void* part;              // as BwdArgs::part
+  int64_t wc;
+  int rows, binned;              // binned: [rows][2][wc] FP64, else [rows][wc] FP32
+  int lo, D, R, cols;            // cols = R (+ D with dow): column c < R is du at lo + c, else
+                                 //   dow at c - R
+  const void* query;
+  const void* norm_w;            // nullptr: dq = du and no dw
+  void* dq;
+  void* dw;
+  void* dow;
+  uint32_t* ctr;
 };
 
 struct FinArgs {

@@ -1,4 +1,4 @@
-// Instantiations of bwd_stream_kernel and finalize_kernel, and the ticket reset kernel.
+// Instantiations of bwd_stream_kernel and finalize_kernel, and the counter reset kernels.
 #include "attnres_kernels.hpp"
 #include "attnres_internal.hpp"
 
@@ -24,16 +24,21 @@ const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full, bool acc
   return bf16 ? stream_ptr<true, false>(ch, sb, full) : stream_ptr<false, false>(ch, sb, full);
 }
 
-// Zeroes the backward's token counter on the launch stream (a kernel store: no memset node, so
-// the call stays capturable into a HIP graph).
-__global__ __launch_bounds__(64) void ticket_reset_kernel(uint32_t* ticket) {
-  if (threadIdx.x == 0) *ticket = 0u;
+// Zeroes the 64 counter words (256 bytes) of a workspace on the launch stream (kernel stores: no
+// memset node, so the call stays capturable into a HIP graph). Every word a kernel counts with
+// is among them.
+__global__ __launch_bounds__(64) void ticket_reset_kernel(uint32_t* ctr) {
+  if (threadIdx.x < kCtrWords) ctr[threadIdx.x] = 0u;
 }
 
 const void* ticket_reset_kernel_ptr() { return (const void*)&ticket_reset_kernel; }
 
 const void* finalize_kernel_ptr(bool bf16) {
   return bf16 ? (const void*)&finalize_kernel<true> : (const void*)&finalize_kernel<false>;
+}
+
+const void* finalize_rows_kernel_ptr(bool bf16) {
+  return bf16 ? (const void*)&finalize_rows_kernel<true> : (const void*)&finalize_rows_kernel<false>;
 }
 
 }  // namespace attnres

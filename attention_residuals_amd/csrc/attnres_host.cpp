@@ -8,8 +8,12 @@
 //     and no output norm is applied; otherwise it streams the sources and needs the forward's
 //     FP32 mixture o (attnres_o32_elems);
 //   * persistent grids: min(N, CUs x resident workgroups per CU from the occupancy calculator);
-//   * the backward writes one FP32 partial row per workgroup; the finaliser sums each column's
-//     rows in a fixed order (64 columns per workgroup, 16 row phases merged through LDS).
+//   * the single-query backward's token-resident kernel sums every token's q/w gradient into
+//     exact FP64 bins (one partial row per workgroup, tokens by ticket); the streaming kernel
+//     writes FP32 rows of fixed token sets (a static head per workgroup, each ticketed tail batch
+//     its own row); a finaliser sums each column's rows in a fixed order and zeroes the counter.
+//     The multi- and selected-query backwards write one FP32 row per workgroup (tokens by ticket
+//     unless deterministic) and the same kind of finaliser merges them.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -259,14 +263,21 @@ int64_t tokens_per_ticket(int64_t N, int64_t grid, double bytes_per_token, doubl
 // ------------------------------------------------------------------ backward plan
 
 struct BwdPlan {
-  int P = 0;     // backward workgroups = partial rows
-  int cols = 0;  // R (+ D with the output-norm weight)
-  size_t off_ticket = 0, off_du = 0, off_dow = 0, bytes = 0;
+  int P = 0;               // backward workgroups (0: nothing to read, N == 0)
+  int64_t tpt = 1;         // tokens per batch
+  int64_t nbatch = 0;      // ceil(N / tpt)
+  int64_t hb_end = 0;      // first tail batch (== nbatch: static split, no ticket)
+  int rows = 0;            // partial rows
+  bool binned = false;     // rows of exact FP64 bins (token-resident kernel) or FP32 sums
+  int64_t wc = 0;          // columns per partial row
+  int cols = 0;            // finaliser columns: R (+ D with dow)
+  size_t off_part = 0, bytes = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-attnres_status plan_bwd(const attnres_desc* d, const Shape& sh, BwdPlan* pl) {
+// Workgroups per CU from the occupancy calculator, capped like the resident grids.
+attnres_status bwd_grid(const attnres_desc* d, const Shape& sh, int64_t* cap) {
   const void* fn = bwd_ptr(sh, d->accumulate_dvalues != 0);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no backward kernel for this shape");
   DevFacts f;
@@ -278,15 +289,59 @@ attnres_status plan_bwd(const attnres_desc* d, const Shape& sh, BwdPlan* pl) {
                      sh.resident ? (env_waves > 0 ? env_waves : 8) : 0);
   if (st != ATTNRES_OK) return st;
   static const int mult = std::max(1, env_int("ATTNRES_BWD_GRID_MULT"));
-  const int64_t cap = (int64_t)f.cus * per_cu * mult;
-  pl->P = (int)std::min<int64_t>(d->N, cap);
+  *cap = (int64_t)f.cus * per_cu * mult;
+  return ATTNRES_OK;
+}
+
+// The backward's schedule (see BwdArgs) and its partial rows. `budget` > 0 caps the workspace
+// bytes: the streaming kernel's ticketed tail shrinks (down to a static split) until its rows
+// fit, and ATTNRES_ERR_WORKSPACE is returned when even one row per workgroup does not.
+attnres_status plan_bwd(const attnres_desc* d, const Shape& sh, BwdPlan* pl, size_t budget = 0) {
+  int64_t cap = 0;
+  attnres_status st = bwd_grid(d, sh, &cap);
+  if (st != ATTNRES_OK) return st;
+  const int64_t N = d->N;
+  const int64_t P0 = std::max<int64_t>(1, std::min<int64_t>(N, cap));
+  const bool dyn = !d->deterministic && N >= 2 * P0 && N < kMaxTicketTokens;
+  pl->tpt = 1;
+  if (dyn) {
+    const double row_bytes = (double)d->D * sh.esz;
+    const double per_token =
+        ((d->accumulate_dvalues ? 3 : 2) * d->S + 1) * row_bytes + (sh.resident ? 0 : 4.0 * d->D);
+    pl->tpt = tokens_per_ticket(N, P0, per_token, 30.0, 16);
+  }
+  pl->nbatch = (N + pl->tpt - 1) / pl->tpt;
+  pl->P = (int)std::min<int64_t>(pl->nbatch, P0);
+  pl->binned = sh.resident;
+  pl->hb_end = pl->nbatch;
+  if (dyn && sh.resident) {
+    pl->hb_end = pl->P;  // exact bins: every batch after a workgroup's first goes by ticket
+  } else if (dyn) {
+    // FP32 rows of fixed token sets: a static head, then about a quarter of the batches (at
+    // least two per workgroup) by ticket, each into its own row (ATTNRES_BWD_TAIL: batches per
+    // workgroup); a row costs D or 2D floats against a batch's (2S+1) rows of sources
+    // and gradients plus the FP32 mixture
+    static const int env_tail = env_int("ATTNRES_BWD_TAIL");
+    const int64_t tail = env_tail > 0 ? env_tail : std::max<int64_t>(2, pl->nbatch / pl->P / 4);
+    const int64_t h = std::max<int64_t>(1, pl->nbatch / pl->P - tail);
+    pl->hb_end = std::min<int64_t>(pl->nbatch, h * pl->P);
+  }
+  pl->wc = (int64_t)d->D * (d->has_out_weight ? 2 : 1);
   pl->cols = d->R + (d->has_out_weight ? d->D : 0);
-  pl->off_ticket = 0;
-  pl->off_du = 256;
-  pl->off_dow = align256(pl->off_du + (size_t)pl->P * d->R * sizeof(float));
-  pl->bytes = align256(pl->off_dow +
-                       (d->has_out_weight ? (size_t)pl->P * d->D * sizeof(float) : 0));
-  if (pl->bytes == 0) pl->bytes = 256;
+  const size_t row_bytes = (size_t)pl->wc * (pl->binned ? 2 * sizeof(double) : sizeof(float));
+  pl->off_part = kCtrWords * sizeof(uint32_t);
+  auto bytes_for = [&](int64_t rows) { return align256(pl->off_part + (size_t)rows * row_bytes); };
+  int64_t rows = pl->binned ? pl->P : pl->P + (pl->nbatch - pl->hb_end);
+  if (budget > 0 && bytes_for(rows) > budget) {
+    const int64_t fit = budget > pl->off_part ? (int64_t)((budget - pl->off_part) / row_bytes) : 0;
+    if (fit < pl->P)
+      return fail(ATTNRES_ERR_WORKSPACE, "the backward needs %zu bytes of scratch, %zu available",
+                  bytes_for(pl->P), budget);
+    pl->hb_end = pl->nbatch - (fit - pl->P);  // (streaming rows only: binned rows are P)
+    rows = fit;
+  }
+  pl->rows = (int)rows;
+  pl->bytes = bytes_for(rows);
   return ATTNRES_OK;
 }
 
@@ -479,12 +534,7 @@ attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
   const int64_t slots = resident * mult;
   a.tpt = dyn ? tokens_per_ticket(N, slots, (double)(d->S + 1) * d->D * sh.esz, 55.0, 1) : 1;
   const int grid = (int)std::min<int64_t>((N + a.tpt - 1) / a.tpt, slots);
-  if (dyn) {
-    a.ticket = static_cast<uint32_t*>(workspace);
-    void* targ = a.ticket;
-    st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");
-    if (st != ATTNRES_OK) return st;
-  }
+  if (dyn) a.ticket = static_cast<uint32_t*>(workspace);  // counters zero at launch (contract)
 
   a.row_stride = values->row_stride;
   a.N = N;
@@ -507,12 +557,16 @@ attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
   return launch(fn, grid, 1, sh.threads, fwd_lds(sh), &a, stream, "forward launch");
 }
 
-attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
-                           const void* query, const void* norm_w, const void* out_w,
-                           const float* lse, const float* out_rstd, const float* o32,
-                           const void* dout, int64_t dout_row_stride,
-                           const attnres_sources* dvalues, void* dq, void* dw, void* dow,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace attnres {
+
+attnres_status bwd_call(const attnres_desc* d, const attnres_sources* values, const void* query,
+                        const void* norm_w, const void* out_w, const float* lse,
+                        const float* out_rstd, const float* o32, const void* dout,
+                        int64_t dout_row_stride, const attnres_sources* dvalues, void* dq, void* dw,
+                        void* dow, void* workspace, size_t workspace_bytes, size_t budget,
+                        bool clear_counters, void* stream) {
   g_err.clear();
   Shape sh;
   attnres_status st = make_shape(d, &sh);
@@ -561,13 +615,18 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
   if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
 
   BwdPlan pl;
-  if ((st = plan_bwd(d, sh, &pl)) != ATTNRES_OK) return st;
+  if ((st = plan_bwd(d, sh, &pl, budget)) != ATTNRES_OK) return st;
   if (workspace_bytes < pl.bytes)
     return fail(ATTNRES_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
                 pl.bytes);
   const void* fn = bwd_ptr(sh, d->accumulate_dvalues != 0);
-  const void* fin = finalize_kernel_ptr(sh.bf16);
   char* ws = static_cast<char*>(workspace);
+  uint32_t* ctr = reinterpret_cast<uint32_t*>(ws);
+  if (clear_counters) {
+    void* carg = ctr;
+    st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &carg, stream, "counter clear launch");
+    if (st != ATTNRES_OK) return st;
+  }
 
   if (pl.P > 0) {
     for (int s = 0; s < d->S; ++s) a.dsrc[s] = const_cast<void*>(dptr[s]);
@@ -590,39 +649,50 @@ attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
     a.o_rstd = out_rstd;
     a.o32 = o32;
     a.dout = dout;
-    a.part_du = reinterpret_cast<float*>(ws + pl.off_du);
-    a.part_dow = d->has_out_weight ? reinterpret_cast<float*>(ws + pl.off_dow) : nullptr;
     a.out_norm = d->out_norm ? 1 : 0;
-    a.tpt = 1;
-    if (!d->deterministic && N >= 2 * (int64_t)pl.P && N < kMaxTicketTokens) {
-      const double row_bytes = (double)d->D * sh.esz;
-      const double per_token =
-          ((d->accumulate_dvalues ? 3 : 2) * d->S + 1) * row_bytes + (sh.resident ? 0 : 4.0 * d->D);
-      a.tpt = tokens_per_ticket(N, pl.P, per_token, 30.0, 16);
-      a.ticket = reinterpret_cast<uint32_t*>(ws + pl.off_ticket);
-      void* targ = a.ticket;
-      st = launch(ticket_reset_kernel_ptr(), 1, 1, 64, 0, &targ, stream, "ticket reset launch");
-      if (st != ATTNRES_OK) return st;
-    }
+    a.part = ws + pl.off_part;
+    a.wc = pl.wc;
+    a.tpt = pl.tpt;
+    a.nbatch = pl.nbatch;
+    a.hb_end = pl.hb_end;
+    a.ctr = ctr;
     st = launch(fn, pl.P, 1, sh.threads, bwd_lds(sh), &a, stream, "backward launch");
     if (st != ATTNRES_OK) return st;
   }
 
-  FinArgs fa;
+  FinRowsArgs fa;
   std::memset(&fa, 0, sizeof fa);
-  fa.part_du = reinterpret_cast<const float*>(ws + pl.off_du);
-  fa.part_dow = d->has_out_weight ? reinterpret_cast<const float*>(ws + pl.off_dow) : nullptr;
-  fa.P = pl.P;
-  fa.R = d->R;
+  fa.part = ws + pl.off_part;
+  fa.wc = pl.wc;
+  fa.rows = pl.rows;
+  fa.binned = pl.binned ? 1 : 0;
+  fa.lo = d->D - d->R;
   fa.D = d->D;
+  fa.R = d->R;
   fa.cols = pl.cols;
   fa.query = query;
   fa.norm_w = norm_w;
   fa.dq = dq;
   fa.dw = dw;
   fa.dow = dow;
-  return launch(fin, (pl.cols + kFinCols - 1) / kFinCols, 1, kFinCols * kFinPhases, 0, &fa, stream,
-                "finalize launch");
+  fa.ctr = ctr;
+  return launch(finalize_rows_kernel_ptr(sh.bf16), (pl.cols + kFinRowsCols - 1) / kFinRowsCols, 1,
+                kFinRowsCols * kFinRowsPhases, 0, &fa, stream, "finalize launch");
+}
+
+}  // namespace attnres
+
+extern "C" {
+
+attnres_status attnres_bwd(const attnres_desc* d, const attnres_sources* values,
+                           const void* query, const void* norm_w, const void* out_w,
+                           const float* lse, const float* out_rstd, const float* o32,
+                           const void* dout, int64_t dout_row_stride,
+                           const attnres_sources* dvalues, void* dq, void* dw, void* dow,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return attnres::bwd_call(d, values, query, norm_w, out_w, lse, out_rstd, o32, dout,
+                           dout_row_stride, dvalues, dq, dw, dow, workspace, workspace_bytes, 0,
+                           false, stream);
 }
 
 }  // extern "C"

@@ -50,6 +50,7 @@ const void* bwd_resident_acc_kernel_ptr_bf16(int ch, int sb, bool full);
 const void* bwd_resident_acc_kernel_ptr_f32(int ch, int sb, bool full);
 const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full, bool acc);
 const void* finalize_kernel_ptr(bool bf16);
+const void* finalize_rows_kernel_ptr(bool bf16);
 const void* multi_fwd_kernel_ptr(bool bf16, int ch, int sb, bool full, int mq);
 const void* multi_bwd_kernel_ptr_bf16(int ch, int sb, bool full, int mq);
 const void* multi_bwd_kernel_ptr_f32(int ch, int sb, bool full, int mq);

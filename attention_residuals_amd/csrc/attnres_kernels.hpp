@@ -522,6 +522,18 @@ constexpr int occupancy_hint(int ch, int sb, bool full) {
   return ch * sb <= (full ? 20 : 12) ? 3 : 1;
 }
 
+// The forward's counters return to zero once every workgroup has taken its last ticket.
+__device__ __forceinline__ void fwd_release_counters(uint32_t* ctr, int tid) {
+  if (tid == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(ctr + kCtrArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == gridDim.x) {
+      __hip_atomic_store(ctr + kCtrTicket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctr + kCtrArrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ forward
 
 // Output row: o (= acc / l already applied) to y, with the optional output RMSNorm, plus lse,
@@ -653,7 +665,7 @@ void fwd_kernel(const FwdArgs a) {
   while (n < a.N) {
     const bool take = dyn && n + 1 >= batch_end;  // last token of its batch
     uint32_t tk = 0;
-    if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
+    if (take && tid == 0) tk = atomicAdd(a.ticket + kCtrTicket, 1u);
     int64_t next = dyn ? n + 1 : n + gridDim.x;
     float acc[CH][VEC];
 #pragma unroll
@@ -766,33 +778,78 @@ void fwd_kernel(const FwdArgs a) {
     __builtin_amdgcn_s_setprio(0);
     n = next;
   }
+  if (dyn) fwd_release_counters(a.ticket, tid);
 }
 
 // ------------------------------------------------------------------ backward, shared tail
 
-// Writes this workgroup's partial sums of du (slice columns) and dow (all columns).
+// Writes this thread's columns of one FP32 partial row (du at absolute columns [lo, D), dow at
+// [D, 2D) when `with_dow`) with 16-byte stores, then clears the sums. Chunks that start below the
+// key slice carry zeros there (du only accumulates slice columns), so whole chunks are written.
 template <bool BF16, int CH, bool FULL>
-__device__ __forceinline__ void write_partials(const BwdArgs& a, const Cols<BF16, CH, FULL>& cs,
-                                               const float (&du)[CH][Fmt<BF16>::VEC],
-                                               const float (&dow)[CH][Fmt<BF16>::VEC]) {
+__device__ __forceinline__ void store_row(const BwdArgs& a, const Cols<BF16, CH, FULL>& cs,
+                                          float (&du)[CH][Fmt<BF16>::VEC],
+                                          float (&dow)[CH][Fmt<BF16>::VEC], int64_t row,
+                                          bool with_dow) {
   constexpr int VEC = Fmt<BF16>::VEC;
-  float* pdu = a.part_du + (int64_t)blockIdx.x * a.R;
+  float* pr = static_cast<float*>(a.part) + row * a.wc;
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
     if (!cs.valid[j]) continue;
+    if (FULL || cs.col0[j] + VEC > a.lo)
+#pragma unroll
+      for (int h = 0; h < VEC; h += 4)
+        st_f32x4(pr + cs.col0[j] + h, du[j][h], du[j][h + 1], du[j][h + 2], du[j][h + 3]);
+    if (with_dow)
+#pragma unroll
+      for (int h = 0; h < VEC; h += 4)
+        st_f32x4(pr + a.D + cs.col0[j] + h, dow[j][h], dow[j][h + 1], dow[j][h + 2],
+                 dow[j][h + 3]);
+  }
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) du[j][e] = dow[j][e] = 0.f;
+}
+
+// Adds one batch's FP32 contribution of every column to the exact bins (kBinMagicA/B) and clears
+// it. With contraction off no step is fused: each rounding below is the one the bins rely on.
+template <int CH, int VEC>
+__device__ __forceinline__ void bin_token(float (&c)[CH][VEC], double (&ba)[CH][VEC],
+                                          double (&bb)[CH][VEC]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      const int idx = cs.col0[j] + e - a.lo;
-      if (idx >= 0) pdu[idx] = du[j][e];
+      const double x = static_cast<double>(c[j][e]);
+      const double xa = (x + kBinMagicA) - kBinMagicA;  // multiple of 2^-20 (|x| < 2^31)
+      const double xb = ((x - xa) + kBinMagicB) - kBinMagicB;  // remainder to 2^-53
+      ba[j][e] += xa;
+      bb[j][e] += xb;
+      c[j][e] = 0.f;
     }
-  }
-  if (a.part_dow) {
-    float* pdw = a.part_dow + (int64_t)blockIdx.x * a.D;
+}
+
+// Writes this thread's columns of the workgroup's binned partial row (bin A at [row][0][col], bin
+// B at [row][1][col]) with 16-byte stores.
+template <bool BF16, int CH, bool FULL>
+__device__ __forceinline__ void store_bins(const BwdArgs& a, const Cols<BF16, CH, FULL>& cs,
+                                           const double (&ba)[CH][Fmt<BF16>::VEC],
+                                           const double (&bb)[CH][Fmt<BF16>::VEC], int64_t row) {
+  constexpr int VEC = Fmt<BF16>::VEC;
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+  double* pa = static_cast<double*>(a.part) + row * 2 * a.wc;
+  double* pb = pa + a.wc;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      if (!cs.valid[j]) continue;
+  for (int j = 0; j < CH; ++j) {
+    if (!cs.valid[j] || !(FULL || cs.col0[j] + VEC > a.lo)) continue;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) pdw[cs.col0[j] + e] = dow[j][e];
+    for (int h = 0; h < VEC; h += 2) {
+      const f64x2 va = {ba[j][h], ba[j][h + 1]};
+      const f64x2 vb = {bb[j][h], bb[j][h + 1]};
+      *reinterpret_cast<f64x2*>(pa + cs.col0[j] + h) = va;
+      *reinterpret_cast<f64x2*>(pb + cs.col0[j] + h) = vb;
     }
   }
 }
@@ -802,8 +859,10 @@ __device__ __forceinline__ void write_partials(const BwdArgs& a, const Cols<BF16
 // All S <= SB rows of a token stay in VGPRs: delta = sum_s p_s <dY, v_s> is exact in FP32.
 // No output norm on this path (dL/do = dY). ACC: dvalues accumulate (the existing gradient rows
 // are prefetched one token ahead like the source rows and added before the store).
+// Two waves per SIMD: the grid holds two 4-wave workgroups per CU (more measured slower), and the
+// row slab, the exact FP64 bins and the pipelined loads need the registers of that occupancy.
 template <bool BF16, int CH, int SB, bool FULL, bool ACC>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(occupancy_hint(CH, ACC ? 2 * SB : SB, FULL), 8)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void bwd_resident_kernel(const BwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
   constexpr int ESZ = Fmt<BF16>::ESZ;
@@ -834,19 +893,26 @@ void bwd_resident_kernel(const BwdArgs a) {
   Chunk rows[SB][CH];
   Chunk odv[ACC ? SB : 1][CH];  // ACC: the existing dvalues rows of the current token
   Chunk gy[CH];
-  // Token schedule: tokens go out in batches of B = a.tpt consecutive tokens. Workgroup g starts
-  // with batch g; each later batch is grid + a ticket from the device-wide counter, so workgroups
-  // that run faster take more batches and all finish together (B > 1 divides the counter's
-  // traffic, which is served one atomic at a time). Thread 0 takes the ticket at the top of a
+  // Token schedule (BwdArgs): head batches g, g + P, ... below hb_end, then batches from the
+  // ticket counter as this workgroup finishes, so faster workgroups take more of them and all
+  // finish together (the two workgroups that share a CU run at unequal speeds, so a static split
+  // leaves one of them working alone at the end). Thread 0 takes the ticket at the top of a
   // batch's last token; its latency hides behind pass 1, and it is published through LDS at the
-  // barrier pass 1 ends with. Without a counter (deterministic mode) tokens are strided by the
-  // grid, so each workgroup's partial sums cover a fixed token set.
-  const bool dyn = a.ticket != nullptr;
-  const int64_t B = dyn ? a.tpt : 1;
-  const int64_t n0 = (int64_t)blockIdx.x * B;
+  // barrier pass 1 ends with.
+  const int64_t P = gridDim.x;
+  const bool dyn = a.hb_end < a.nbatch;
+  int64_t b = blockIdx.x;
+  const int64_t n0 = b < a.nbatch ? b * a.tpt : a.N;
+  // exact bins of this workgroup's q/w gradient sums (kBinMagicA/B): whatever tokens the counter
+  // hands this workgroup, the merged sums are the same
+  double ba[CH][VEC], bb[CH][VEC];
+#pragma unroll
+  for (int j = 0; j < CH; ++j)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ba[j][e] = bb[j][e] = 0.0;
   // lse of the current token; the next one is loaded with the next token's rows (a vector load
   // waited for at its use would otherwise also drain every store issued before it)
-  float lse = a.lse[min(n0, a.N - 1)];
+  float lse = n0 < a.N ? a.lse[n0] : 0.f;
   {
     // issued in the order the loop body issues the next token's loads (dY, then rows 0..SB-1):
     // the wait counts at the loop head are the minimum over both entry paths
@@ -870,11 +936,14 @@ void bwd_resident_kernel(const BwdArgs a) {
   }
 
   uint32_t* tslot = reinterpret_cast<uint32_t*>(lds + 2 * xfl);
-  int64_t n = n0, batch_end = n0 + B;
+  int64_t n = n0, batch_end = min(n0 + a.tpt, a.N);
   while (n < a.N) {
-    const bool take = dyn && n + 1 >= batch_end;  // last token of its batch
+    const bool last_tok = n + 1 >= batch_end;
+    const bool in_tail = b >= a.hb_end;
+    const bool head_more = !in_tail && b + P < a.hb_end;  // another head batch follows
+    const bool take = dyn && last_tok && !head_more;
     uint32_t tk = 0;
-    if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
+    if (take && tid == 0) tk = atomicAdd(a.ctr + kCtrTicket, 1u);
     float* xb = lds + buf * xfl;
     uint32_t us[3][CH][4];
     float u[CH][VEC];
@@ -895,10 +964,12 @@ void bwd_resident_kernel(const BwdArgs a) {
     }
     if (take && tid == 0) tslot[buf] = tk;
     __syncthreads();
-    int64_t next = dyn ? n + 1 : n + gridDim.x;
-    if (take) {
-      next = ((int64_t)gridDim.x + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf])) * B;
-      batch_end = next + B;
+    int64_t next = n + 1, b_next = b;
+    if (last_tok) {
+      if (head_more) b_next = b + P;
+      else if (take) b_next = a.hb_end + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf]);
+      else b_next = a.nbatch;
+      next = b_next < a.nbatch ? b_next * a.tpt : a.N;
     }
     const bool has_next = next < a.N;
     buf ^= 1;
@@ -959,10 +1030,16 @@ void bwd_resident_kernel(const BwdArgs a) {
       }
     }
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+    // a batch is a fixed token set summed in token order, so its FP32 sum is binned once
+    if (last_tok) bin_token<CH, VEC>(du, ba, bb);
+    if (last_tok) {
+      b = b_next;
+      batch_end = min(next + a.tpt, a.N);
+    }
     lse = lse_next;
     n = next;
   }
-  write_partials<BF16, CH, FULL>(a, cs, du, dow);
+  store_bins<BF16, CH, FULL>(a, cs, ba, bb, blockIdx.x);
 }
 
 // ------------------------------------------------------------------ backward, streaming
@@ -1002,9 +1079,12 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
   int buf = 0;
   const int nblk = (a.S + SB - 1) / SB;
 
-  const bool dyn = a.ticket != nullptr;
-  const int64_t B = dyn ? a.tpt : 1;
-  const int64_t n0 = (int64_t)blockIdx.x * B;
+  // token schedule (BwdArgs): head batches summed into row g, each tail batch into its own row
+  const int64_t P = gridDim.x;
+  const bool dyn = a.hb_end < a.nbatch;
+  int64_t b = blockIdx.x;
+  const int64_t n0 = b < a.nbatch ? b * a.tpt : a.N;
+  bool head_open = true;
 
   // a token's head (dY row and FP32 mixture row) and one source block's rows (+ existing grads)
   Chunk g[CH], oc[CH][OC];
@@ -1042,12 +1122,15 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
   load_block(cur, odc, n0, 0, n0 < a.N);
 
   uint32_t* tslot = reinterpret_cast<uint32_t*>(lds + 2 * xfl);
-  int64_t n = n0, batch_end = n0 + B;
+  int64_t n = n0, batch_end = min(n0 + a.tpt, a.N);
   while (n < a.N) {
-    const bool take = dyn && n + 1 >= batch_end;
+    const bool last_tok = n + 1 >= batch_end;
+    const bool in_tail = b >= a.hb_end;
+    const bool head_more = !in_tail && b + P < a.hb_end;
+    const bool take = dyn && last_tok && !head_more;
     uint32_t tk = 0;
-    if (take && tid == 0) tk = atomicAdd(a.ticket, 1u);
-    int64_t next = dyn ? n + 1 : n + gridDim.x;
+    if (take && tid == 0) tk = atomicAdd(a.ctr + kCtrTicket, 1u);
+    int64_t next = n + 1, b_next = b;
 
     float dov[CH][VEC], o[CH][VEC];
 #pragma unroll
@@ -1081,9 +1164,11 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
       xchg_group<2, 1>(part, 0, xb, R4, tid);
       if (take && tid == 0) tslot[buf] = tk;
       __syncthreads();
-      if (take) {
-        next = ((int64_t)gridDim.x + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf])) * B;
-        batch_end = next + B;
+      if (last_tok) {
+        if (head_more) b_next = b + P;
+        else if (take) b_next = a.hb_end + (int64_t)__builtin_amdgcn_readfirstlane(tslot[buf]);
+        else b_next = a.nbatch;
+        next = b_next < a.nbatch ? b_next * a.tpt : a.N;
       }
       buf ^= 1;
       const float t0 = xchg_total(xb, 0, R4);
@@ -1171,9 +1256,18 @@ __global__ __launch_bounds__(512) void bwd_stream_kernel(const BwdArgs a) {
           if constexpr (ACC) odc[i][j] = odn[i][j];
         }
     }
+    if (last_tok && !head_more) {
+      store_row<BF16, CH, FULL>(a, cs, du, dow, in_tail ? P + (b - a.hb_end) : (int64_t)blockIdx.x,
+                                a.out_w != nullptr);
+      head_open = head_open && in_tail;
+    }
+    if (last_tok) {
+      b = b_next;
+      batch_end = min(next + a.tpt, a.N);
+    }
     n = next;
   }
-  write_partials<BF16, CH, FULL>(a, cs, du, dow);
+  if (head_open) store_row<BF16, CH, FULL>(a, cs, du, dow, blockIdx.x, a.out_w != nullptr);
 }
 
 // ------------------------------------------------------------------ finaliser
@@ -1202,6 +1296,60 @@ __global__ __launch_bounds__(kFinCols * kFinPhases) void finalize_kernel(const F
 #pragma unroll
   for (int r = 0; r < kFinPhases; ++r) total += red[r][cl];
   if (is_du) {
+    const float wv = a.norm_w ? load_param<BF16>(a.norm_w, c) : 1.f;
+    store_param<BF16>(a.dq, c, total * wv);
+    if (a.norm_w) store_param<BF16>(a.dw, c, total * load_param<BF16>(a.query, c));
+  } else {
+    store_param<BF16>(a.dow, c - a.R, total);
+  }
+}
+
+// Single-query finaliser: a workgroup owns kFinRowsCols columns; thread (phase r, column c) adds
+// rows r, r + kFinRowsPhases, ... in FP64 (for binned rows bins A and B separately), the phase sums
+// are added in phase order through LDS, then dq = du * w (du without w), dw = du * q and dow are
+// written. Binned sums are exact, so the result does not depend on the order; FP32 rows are summed
+// in the same fixed order every call. Block 0 returns the backward's ticket counter to zero (this
+// kernel runs after the backward).
+template <bool BF16>
+__global__ __launch_bounds__(kFinRowsCols * kFinRowsPhases) void finalize_rows_kernel(
+    const FinRowsArgs a) {
+  __shared__ double red[2][kFinRowsPhases][kFinRowsCols];
+  const int cl = threadIdx.x % kFinRowsCols, ph = threadIdx.x / kFinRowsCols;
+  const int c = blockIdx.x * kFinRowsCols + cl;
+  const bool has = c < a.cols;
+  const int col = c < a.R ? a.lo + c : a.D + (c - a.R);  // partial-row column
+  double sa = 0.0, sb = 0.0;
+  if (has) {
+    if (a.binned) {
+      const double* pa = static_cast<const double*>(a.part) + col;
+#pragma unroll 4
+      for (int r = ph; r < a.rows; r += kFinRowsPhases) {
+        sa += pa[(int64_t)r * 2 * a.wc];
+        sb += pa[(int64_t)r * 2 * a.wc + a.wc];
+      }
+    } else {
+      const float* pf = static_cast<const float*>(a.part) + col;
+#pragma unroll 4
+      for (int r = ph; r < a.rows; r += kFinRowsPhases)
+        sa += static_cast<double>(pf[(int64_t)r * a.wc]);
+    }
+  }
+  red[0][ph][cl] = sa;
+  red[1][ph][cl] = sb;
+  __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.ctr[kCtrTicket] = 0u;
+    a.ctr[kCtrArrive] = 0u;
+  }
+  if (ph != 0 || !has) return;
+  double ta = 0.0, tb = 0.0;
+#pragma unroll
+  for (int r = 0; r < kFinRowsPhases; ++r) {
+    ta += red[0][r][cl];
+    tb += red[1][r][cl];
+  }
+  const float total = static_cast<float>(ta + tb);
+  if (c < a.R) {
     const float wv = a.norm_w ? load_param<BF16>(a.norm_w, c) : 1.f;
     store_param<BF16>(a.dq, c, total * wv);
     if (a.norm_w) store_param<BF16>(a.dw, c, total * load_param<BF16>(a.query, c));

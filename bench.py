@@ -176,8 +176,9 @@ def main() -> int:
     dq = torch.empty((R,), dtype=w.torch_dtype, device=dev)
     dw = torch.empty((R,), dtype=w.torch_dtype, device=dev) if x["norm_w"] is not None else None
     dow = torch.empty((D,), dtype=w.torch_dtype, device=dev) if x["out_w"] is not None else None
-    ws = torch.empty((max(A.workspace_bytes(desc), 256),), dtype=torch.uint8, device=dev)
-    fws = torch.empty((A.fwd_workspace_bytes(desc),), dtype=torch.uint8, device=dev)
+    # counters zero before first use (the library leaves them zero after every call)
+    ws = torch.zeros((max(A.workspace_bytes(desc), 256),), dtype=torch.uint8, device=dev)
+    fws = torch.zeros((A.fwd_workspace_bytes(desc),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     # both calls marshalled once (the C entry points then run with a few microseconds of host

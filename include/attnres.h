@@ -9,10 +9,10 @@
  * ("[Perf] Parallelize AttnRes long-sequence reduction", FLA PR page, Summary) an output RMSNorm
  * follows: y = o * rho_o * ow with rho_o = (mean_D(o^2) + eps)^(-1/2) saved per row (o_rstd) for
  * the backward, ow optional. Without it y = o.
- * The backward (same PR page: dq/dw/dow reduced over the flattened token dimension in FP32
- * partials and finalised by a separate kernel) returns dvalues for every source row and the
- * gradients of q, w and ow summed over all N tokens. It recomputes the routing weights from the
- * saved per-row log-sum-exp.
+ * The backward (same PR page: dq/dw/dow reduced over the flattened token dimension through FP32
+ * partial sums, merged in a fixed order) returns dvalues for every source row and the gradients
+ * of q, w and ow summed over all N tokens. It recomputes the routing weights from the saved
+ * per-row log-sum-exp.
  *
  * Conventions shared by every entry point:
  *   - All array arguments are DEVICE pointers of the current HIP device unless stated otherwise.
@@ -62,10 +62,21 @@ typedef struct {
   int32_t has_norm_weight; /* key-norm weight w[R] present */
   int32_t out_norm;        /* output RMSNorm after the mixture */
   int32_t has_out_weight;  /* output-norm weight ow[D] present (requires out_norm) */
-  int32_t deterministic;   /* 1: fixed token split, dq/dw/dow bitwise reproducible across calls;
-                              0: tokens handed out by a device-wide counter (faster: workgroups
-                              finish together), dq/dw/dow reproducible to FP32 rounding only.
-                              y, lse and dvalues are bitwise reproducible in both modes. */
+  int32_t deterministic;   /* Backward token schedule. Single-query read: every output is
+                              bitwise reproducible across calls in both modes.
+                              0: tokens go out in batches through a device-wide counter as
+                              workgroups finish (faster). The token-resident backward adds each
+                              batch's q/w gradient into exact FP64 bins (a multiple of 2^-20 and
+                              a remainder rounded to 2^-53, each summed exactly while per-batch
+                              contributions stay below 2^31 in magnitude and a call has fewer than
+                              2^21 tokens per workgroup), so the sums do not depend on which
+                              workgroup took which batch; the streaming backward gives each
+                              workgroup a fixed share and each counter batch of the last quarter
+                              its own partial row.
+                              1: a static token split (no counter).
+                              The two modes may differ from each other in the last bits of
+                              dq/dw/dow. Multi- and selected-query reads: 0 reproduces dq/dbank
+                              to FP32 rounding only; 1 is a static split, bitwise reproducible. */
   int32_t accumulate_dvalues; /* backward only. 0: dvalues are overwritten with this read's
                               gradient. 1: the gradient is added to the existing dvalues (read,
                               summed in FP32, rounded once to storage), so a source shared by
@@ -93,9 +104,13 @@ typedef struct {
  * keep a token's rows on chip), else 0. */
 attnres_status attnres_o32_elems(const attnres_desc* desc, size_t* elems);
 
-/* Bytes of device workspace attnres_bwd needs on the CURRENT device (a token counter and FP32
- * partial sums of the q/w/ow gradients, one row per workgroup of the backward). The contents need
- * no initialisation. */
+/* Bytes of device workspace attnres_bwd needs on the CURRENT device: 256 bytes of counters, then
+ * partial sums of the q/w/ow gradients, one row of D (2D with ow) columns per workgroup (exact
+ * FP64 bins, 16 bytes a column, for the token-resident backward; FP32 per fixed token set for the
+ * streaming one). The first 256 bytes must be ZERO before the first call that uses the buffer
+ * (allocate it zero-filled); every call leaves them zero again when its finaliser completes, so
+ * one buffer serves any number of later calls and graph replays. The rest needs no
+ * initialisation. */
 attnres_status attnres_workspace_bytes(const attnres_desc* desc, size_t* bytes);
 
 /* Bytes of the optional forward workspace (a device-wide token counter); currently 256. */
@@ -109,10 +124,10 @@ attnres_status attnres_fwd_workspace_bytes(const attnres_desc* desc, size_t* byt
  *   out_rstd [N] FP32 rho_o (written iff out_norm, else must be NULL).
  *   o32      [N, D] FP32 mixture o (written iff attnres_o32_elems > 0, else must be NULL).
  *   workspace, workspace_bytes: optional. With a 256-byte aligned buffer of at least
- *            attnres_fwd_workspace_bytes bytes (contents need no initialisation; not shared with a
- *            concurrent call), workgroups take tokens from a counter kept there as they finish
- *            (a one-thread kernel zeroes it first). NULL with 0 bytes: a static token split. The
- *            outputs are bitwise identical either way.
+ *            attnres_fwd_workspace_bytes bytes (zero before its first use, like the backward's
+ *            counters, and left zero by every call; not shared with a concurrent call),
+ *            workgroups take tokens from a counter kept there as they finish. NULL with 0 bytes:
+ *            a static token split. The outputs are bitwise identical either way.
  * All device pointers 16-byte aligned; row strides multiples of 16 bytes. */
 attnres_status attnres_fwd(const attnres_desc* desc, const attnres_sources* values,
                            const void* query, const void* norm_w, const void* out_w,
@@ -126,10 +141,12 @@ attnres_status attnres_fwd(const attnres_desc* desc, const attnres_sources* valu
  *   dq [R]          gradient of the query, summed over tokens (written).
  *   dw [R]          gradient of the key-norm weight (iff has_norm_weight, else NULL).
  *   dow [D]         gradient of the output-norm weight (iff has_out_weight, else NULL).
- *   workspace       at least attnres_workspace_bytes(desc) bytes, 256-byte aligned; not shared
+ *   workspace       at least attnres_workspace_bytes(desc) bytes, 256-byte aligned, first 256
+ *                   bytes zero before its first use (see attnres_workspace_bytes); not shared
  *                   with any concurrent call.
- * With desc->deterministic, the reductions over tokens use a fixed order and repeated calls give
- * bitwise-identical results; otherwise only dq/dw/dow may differ in the last bits. */
+ * Two kernel launches: the backward, then a finaliser that sums each column's partial rows in a
+ * fixed order, writes dq, dw and dow and returns the workspace's counters to zero, so repeated
+ * calls give bitwise-identical results in both schedules (desc->deterministic). */
 attnres_status attnres_bwd(const attnres_desc* desc, const attnres_sources* values,
                            const void* query, const void* norm_w, const void* out_w,
                            const float* lse, const float* out_rstd, const float* o32,

@@ -143,14 +143,14 @@ def run_gpu(w: W.Workload, xg: dict, *, packed: bool = True, poison: bool = True
     dq = torch.empty((w.R,), dtype=w.torch_dtype, device=dev)
     dw = torch.empty((w.R,), dtype=w.torch_dtype, device=dev) if xg["norm_w"] is not None else None
     dow = torch.empty((D,), dtype=w.torch_dtype, device=dev) if xg["out_w"] is not None else None
-    ws = torch.empty((max(A.workspace_bytes(desc), 256),), dtype=torch.uint8, device=dev)
+    ws = torch.zeros((max(A.workspace_bytes(desc), 256),), dtype=torch.uint8, device=dev)
     if poison:
         for t in (y, lse, rstd, o32, dq, dw, dow):
             poison_(t)
         if not accumulate:
             for t in (dvalues if isinstance(dvalues, list) else [dvalues]):
                 poison_(t)
-        ws.fill_(0xFF)
+        ws[256:].fill_(0xFF)  # partial rows; the counter words must start at zero
     A.attnres_fwd(v, xg["query"], xg["norm_w"], xg["out_w"], eps=w.eps, scale=w.scale,
                   out_norm=w.out_norm, out=y, lse=lse, out_rstd=rstd, o32=o32, stream=stream)
     g = xg["dout"] if dout is None else dout

@@ -194,11 +194,13 @@ def test_bound_calls_match_the_plain_calls():
 
 
 def test_ticket_schedule_matches_deterministic_mode():
-    # per-token outputs do not depend on which workgroup ran the token; the token reductions only
-    # differ by FP32 reassociation (bf16 storage: at most a few bf16 ulps of dq/dw)
+    # per-token outputs do not depend on which workgroup ran the token; the token reductions of
+    # the two schedules differ by FP32 reassociation only (bf16 storage: a few bf16 ulps of dq/dw),
+    # and repeated calls of the default schedule (ticketed tail) are bitwise identical
     w = _wl(10, 3001, 4096, 4096, seed=1202)
     xg = inputs_on(W.generate(w), "cuda")
     det = run_gpu(w, xg, deterministic=True)
+    first = None
     for _ in range(3):
         dyn = run_gpu(w, xg, deterministic=False)
         for k in ("y", "lse", "dvalues"):
@@ -206,6 +208,57 @@ def test_ticket_schedule_matches_deterministic_mode():
         for k in ("dq", "dw"):
             a, b = to_f64(det[k]), to_f64(dyn[k])
             assert np.linalg.norm(a - b) <= 4e-3 * np.linalg.norm(a), k
+        if first is None:
+            first = dyn
+        for k in ("dq", "dw"):
+            assert torch.equal(first[k], dyn[k]), k
+
+
+@pytest.mark.parametrize("S,N,D,R,out_norm,out_weight", [
+    (10, 4096 + 7, 4096, 4096, False, False),    # resident, two tail batches per workgroup
+    (24, 8195, 2048, 512, False, False),         # resident, sliced key
+    (5, 4099, 1024, 1024, True, True),           # streaming with the output weight (dow rows)
+    (29, 3001, 4096, 4096, False, False),        # streaming without the output norm
+])
+def test_default_schedule_repeats_bitwise_and_matches_oracle(S, N, D, R, out_norm, out_weight):
+    # the default backward hands its tail batches out by ticket, each batch into its own partial
+    # row: which workgroup ran a batch changes between calls, the merged sums must not
+    w = _wl(S, N, D, R, out_norm=out_norm, out_weight=out_weight, seed=1270 + S)
+    xc = W.generate(w)
+    xg = inputs_on(xc, "cuda")
+    print(f"[case] default schedule S={S} N={N} D={D} R={R} out_norm={out_norm}", flush=True)
+    runs = [run_gpu(w, xg, deterministic=False, poison=False) for _ in range(3)]
+    for r in runs[1:]:
+        for k in ("y", "lse", "dvalues", "dq", "dw", "dow"):
+            if runs[0].get(k) is not None:
+                assert torch.equal(runs[0][k], r[k]), k
+    ref = run_oracle(w, xc)
+    assert_ok(check_all(w, runs[0], ref, tokens=None), f"default schedule S={S} N={N}")
+
+
+def test_workspace_serves_calls_of_different_sizes():
+    # the counters return to zero after every call: one workspace (sized for the largest call)
+    # serves a long call, a short one (static split) and the long one again, each bitwise equal
+    # to a call on a fresh workspace
+    import attention_residuals_amd as A
+    wl = _wl(10, 9001, 4096, 4096, seed=1281)
+    ws_ = _wl(10, 33, 4096, 4096, seed=1282)
+    xl = inputs_on(W.generate(wl), "cuda")
+    xs = inputs_on(W.generate(ws_), "cuda")
+    need = max(A.workspace_bytes(A.make_desc(w.S, w.N, w.D, w.R, w.torch_dtype,
+                                             has_norm_weight=True)) for w in (wl, ws_))
+    shared = torch.zeros((need,), dtype=torch.uint8, device="cuda")
+    fresh = {id(w): run_gpu(w, x, poison=False) for w, x in ((wl, xl), (ws_, xs))}
+    for w, x in ((wl, xl), (ws_, xs), (wl, xl)):
+        y, lse, _, _ = A.attnres_fwd(x["values"], x["query"], x["norm_w"], None,
+                                     workspace=shared[:256])
+        dv, dq, dw, _ = A.attnres_bwd(x["values"], x["query"], x["norm_w"], None, lse, None, None,
+                                      x["dout"], workspace=shared)
+        torch.cuda.synchronize()
+        ref = fresh[id(w)]
+        for k, t in (("y", y), ("lse", lse), ("dvalues", dv), ("dq", dq), ("dw", dw)):
+            assert torch.equal(ref[k], t), (k, w.N)
+        assert int(shared[:256].count_nonzero()) == 0  # counters back at zero
 
 
 @pytest.mark.parametrize("S,N,D,R,dtype,out_norm,packed", [
@@ -345,8 +398,8 @@ def test_graph_capture_and_replay_with_changed_inputs(deterministic):
     dv = torch.empty_like(buf["values"])
     dq = torch.empty((w.R,), dtype=w.torch_dtype, device="cuda")
     dw = torch.empty_like(dq)
-    ws = torch.empty((A.workspace_bytes(d),), dtype=torch.uint8, device="cuda")
-    fws = torch.empty((A.fwd_workspace_bytes(d),), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((A.workspace_bytes(d),), dtype=torch.uint8, device="cuda")
+    fws = torch.zeros((A.fwd_workspace_bytes(d),), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
 
     def step():
