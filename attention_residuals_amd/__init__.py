@@ -5,7 +5,8 @@ The compute lives in ``libattnres.so`` (hand-written HIP kernels behind the C AB
 ``python -m attention_residuals_amd.build``. Nothing here falls back to a CPU implementation.
 """
 from ._binding import (ATTNRES_BF16, ATTNRES_F32, EPS_DEFAULT, EXPORTS, AttnResError, BoundCall,
-                       Desc, MultiDesc, SelectedDesc, Sources, attnres_bwd, attnres_fwd,
+                       Desc, MultiDesc, SelectedDesc, Sources, attnres_bwd, attnres_bwd_noalloc,
+                       attnres_fwd,
                        bind_bwd, bind_fwd,
                        attnres_multi_bwd, attnres_multi_fwd, attnres_selected_bwd,
                        attnres_selected_fwd, fwd_workspace_bytes, load, make_desc,
@@ -15,6 +16,7 @@ from ._binding import (ATTNRES_BF16, ATTNRES_F32, EPS_DEFAULT, EXPORTS, AttnResE
 from .ops import attnres, attnres_multi, attnres_selected
 
 __all__ = ["attnres", "attnres_multi", "attnres_selected", "attnres_fwd", "attnres_bwd",
+           "attnres_bwd_noalloc",
            "bind_fwd", "bind_bwd", "BoundCall",
            "attnres_multi_fwd", "attnres_multi_bwd", "attnres_selected_fwd",
            "attnres_selected_bwd", "o32_elems", "workspace_bytes", "fwd_workspace_bytes",

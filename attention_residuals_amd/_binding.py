@@ -20,7 +20,8 @@ EPS_DEFAULT = 2.0 ** -23
 
 # Every function the header declares, with its ctypes signature.
 EXPORTS = ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd_workspace_bytes",
-           "attnres_fwd", "attnres_bwd", "attnres_multi_fwd_workspace_bytes",
+           "attnres_fwd", "attnres_bwd", "attnres_bwd_noalloc",
+           "attnres_multi_fwd_workspace_bytes",
            "attnres_multi_workspace_bytes", "attnres_multi_fwd", "attnres_multi_bwd",
            "attnres_selected_fwd_workspace_bytes", "attnres_selected_workspace_bytes",
            "attnres_selected_fwd", "attnres_selected_bwd",
@@ -84,6 +85,7 @@ def load() -> ctypes.CDLL:
     lib.attnres_fwd_workspace_bytes.argtypes = [pd, ctypes.POINTER(sz)]
     lib.attnres_fwd.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.attnres_bwd.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, i64, ps, vp, vp, vp, vp, sz, vp]
+    lib.attnres_bwd_noalloc.argtypes = [pd, ps, vp, vp, vp, vp, vp, vp, vp, i64, ps, vp, vp, vp, vp]
     pm = ctypes.POINTER(MultiDesc)
     lib.attnres_multi_fwd_workspace_bytes.argtypes = [pm, ctypes.POINTER(sz)]
     lib.attnres_multi_workspace_bytes.argtypes = [pm, ctypes.POINTER(sz)]
@@ -261,8 +263,9 @@ def _prep_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
                 accumulate: bool = False, dvalues=None,
                 dq: Optional[torch.Tensor] = None,
                 dw: Optional[torch.Tensor] = None, dow: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None, stream=None):
-    """Marshals a backward call: (C function, its arguments, outputs, objects to keep alive)."""
+                workspace: Optional[torch.Tensor] = None, noalloc: bool = False, stream=None):
+    """Marshals a backward call: (C function, its arguments, outputs, objects to keep alive).
+    noalloc: attnres_bwd_noalloc (no workspace; the library's own device array)."""
     sv = _SourceView(values)
     desc = make_desc(sv.S, sv.N, sv.D, query.numel(), sv.dtype, eps=eps, scale=scale,
                      has_norm_weight=norm_w is not None, out_norm=out_norm,
@@ -282,15 +285,34 @@ def _prep_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
         dw = torch.empty((query.numel(),), dtype=sv.dtype, device=dev)
     if out_w is not None and dow is None:
         dow = torch.empty((sv.D,), dtype=sv.dtype, device=dev)
+    dstride = dout.stride(0) if sv.N > 1 else sv.D
+    head = (ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query), _ptr(norm_w), _ptr(out_w),
+            _ptr(lse), _ptr(out_rstd), _ptr(o32), _ptr(dout), dstride, ctypes.byref(dv.struct),
+            _ptr(dq), _ptr(dw), _ptr(dow))
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        keep = (desc, sv, dv, query, norm_w, out_w, lse, out_rstd, o32, dout)
+        return load().attnres_bwd_noalloc, head + (_stream(stream),), (dvalues, dq, dw, dow), keep
     need = workspace_bytes(desc)
     if workspace is None:
         workspace = _scratch(max(need, 256), dev, stream, zero=True)
-    dstride = dout.stride(0) if sv.N > 1 else sv.D
-    cargs = (ctypes.byref(desc), ctypes.byref(sv.struct), _ptr(query), _ptr(norm_w), _ptr(out_w),
-             _ptr(lse), _ptr(out_rstd), _ptr(o32), _ptr(dout), dstride, ctypes.byref(dv.struct),
-             _ptr(dq), _ptr(dw), _ptr(dow), _ptr(workspace), workspace.numel(), _stream(stream))
+    cargs = head + (_ptr(workspace), workspace.numel(), _stream(stream))
     keep = (desc, sv, dv, query, norm_w, out_w, lse, out_rstd, o32, dout, workspace)
     return load().attnres_bwd, cargs, (dvalues, dq, dw, dow), keep
+
+
+def attnres_bwd_noalloc(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],
+                        out_w: Optional[torch.Tensor], lse: torch.Tensor,
+                        out_rstd: Optional[torch.Tensor], o32: Optional[torch.Tensor],
+                        dout: torch.Tensor, **kw):
+    """attnres_bwd through the allocation-free entry point (no workspace: the library's device
+    array; calls on one device must not overlap). Keywords as attnres_bwd except workspace; give
+    dvalues, dq (and dw, dow) to keep the binding itself from allocating outputs."""
+    fn, cargs, outs, _ = _prep_bwd(values, query, norm_w, out_w, lse, out_rstd, o32, dout,
+                                   noalloc=True, **kw)
+    _check(fn(*cargs))
+    return outs
 
 
 def attnres_bwd(values, query: torch.Tensor, norm_w: Optional[torch.Tensor],

@@ -561,6 +561,16 @@ attnres_status attnres_fwd(const attnres_desc* d, const attnres_sources* values,
 
 namespace attnres {
 
+attnres_status report(attnres_status st, const char* what) {
+  g_err.clear();
+  return fail(st, "%s", what);
+}
+
+attnres_status report_hip(hipError_t e, const char* what) {
+  g_err.clear();
+  return hip_fail(e, what);
+}
+
 attnres_status bwd_call(const attnres_desc* d, const attnres_sources* values, const void* query,
                         const void* norm_w, const void* out_w, const float* lse,
                         const float* out_rstd, const float* o32, const void* dout,

@@ -1,8 +1,11 @@
 // attnres_internal.hpp -- host-side tables shared by the dispatcher and the instantiation files.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include "../../include/attnres.h"
 
 namespace attnres {
 
@@ -66,5 +69,22 @@ size_t multi_fwd_mfma_lds(int cgw, int mq, int qrows);
 const void* sel_bwd_kernel_ptr_bf16(int ch, int sb, bool full, bool acc, int mq);
 const void* sel_bwd_kernel_ptr_f32(int ch, int sb, bool full, bool acc, int mq);
 const void* ticket_reset_kernel_ptr();
+
+// Bytes of the allocation-free backward's device array (attnres_bwd_noalloc).
+inline constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+
+// attnres_bwd with its workspace given explicitly: `budget` > 0 caps the planned workspace
+// (ATTNRES_ERR_WORKSPACE when even a static split's partial rows do not fit), `clear_counters`
+// first launches a kernel that zeroes the workspace's counter words on the stream.
+attnres_status bwd_call(const attnres_desc* d, const attnres_sources* values, const void* query,
+                        const void* norm_w, const void* out_w, const float* lse,
+                        const float* out_rstd, const float* o32, const void* dout,
+                        int64_t dout_row_stride, const attnres_sources* dvalues, void* dq, void* dw,
+                        void* dow, void* workspace, size_t workspace_bytes, size_t budget,
+                        bool clear_counters, void* stream);
+
+// Record a failure for attnres_last_error (from other translation units of the library).
+attnres_status report(attnres_status st, const char* what);
+attnres_status report_hip(hipError_t e, const char* what);
 
 }  // namespace attnres

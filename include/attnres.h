@@ -155,6 +155,21 @@ attnres_status attnres_bwd(const attnres_desc* desc, const attnres_sources* valu
                            void* dq, void* dw, void* dow,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free backward, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. Arguments, results and
+ * errors as attnres_bwd, without the workspace: it lives in a 64 MiB device array that the library
+ * holds on every device it runs on until the process ends. Every call first zeroes the array's
+ * counter words with a kernel on `stream`. ATTNRES_ERR_WORKSPACE: the call's partial rows do not
+ * fit the array (the streaming backward first shrinks its counter-scheduled tail, down to a static
+ * split). All calls on one device share the one array, so calls that overlap on a device (other
+ * streams, other threads) race: the caller must order them. */
+attnres_status attnres_bwd_noalloc(const attnres_desc* desc, const attnres_sources* values,
+                                   const void* query, const void* norm_w, const void* out_w,
+                                   const float* lse, const float* out_rstd, const float* o32,
+                                   const void* dout, int64_t dout_row_stride,
+                                   const attnres_sources* dvalues,
+                                   void* dq, void* dw, void* dow, void* stream);
+
 /* ---------------------------------------------------------------- multi-query read
  * "Fast Attention Residuals" PyPI page, section "Multi-query AttnRes": M queries q_m (1 <= M <= 16)
  * read the same S sources; each has its own routing weights
