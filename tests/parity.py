@@ -202,6 +202,15 @@ def assert_ok(res: dict, label: str) -> None:
     assert not bad, f"{label}: out of tolerance: {bad}"
 
 
+def multi_bwd_passes(S: int, D: int, M: int, dtype: str) -> int:
+    """Backward launches (query groups) of the multi- and selected-query reads as the library plans
+    them: up to four queries per launch with one 16-byte chunk per thread (D <= 512 chunks at
+    eight waves) and S <= 12, else two. Each launch after the first adds into dvalues, rounding
+    the running sum to storage again."""
+    per = 4 if (D // (8 if dtype == "bf16" else 4) <= 512 and S <= 12) else 2
+    return -(-M // per)
+
+
 def sample_tokens(N: int, k: int, seed: int) -> list:
     rng = np.random.default_rng(seed)
     picks = set([0, N - 1, N // 2]) | set(rng.integers(0, N, size=k).tolist())

@@ -1,12 +1,17 @@
 """torch.compile(fullgraph=True) over the AttnRes reads (the "Fast Attention Residuals" page's
-Quickstart uses the read this way): the custom operators trace as single nodes, and compiled
-forward + backward equal eager bit for bit. torch.library.opcheck validates the registrations
-(schema, fake implementations, autograd) on small inputs."""
+Quickstart uses the read this way, and its "Validation scope" checks compiled use against an
+independent reference): the custom operators trace as single nodes, compiled forward + backward
+equal eager bit for bit, and the compiled outputs and gradients match the FP64 oracle on the same
+inputs. torch.library.opcheck validates the registrations (schema, fake implementations, autograd)
+on small inputs."""
+import numpy as np
 import pytest
 import torch
 
 import attnres_workloads as W
-from parity import gpu_available
+import oracle
+from parity import (assert_ok, compare_rows, compare_stat, compare_vec, gpu_available,
+                    multi_bwd_passes, to_f64)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
@@ -56,6 +61,18 @@ def test_compiled_read_matches_eager(backend, as_list):
     torch.testing.assert_close(eager[0], compiled[0], rtol=1e-5, atol=0)
     for a, b in zip(eager[1:], compiled[1:]):
         assert torch.equal(a, b)
+    # and against the oracle: the compiled forward's output, and the compiled gradients of
+    # sum(y * dy) (dL/dy = dy)
+    y = torch.compile(read, fullgraph=True, dynamic=False, backend=backend)(
+        list(x["values"].unbind(0)) if as_list else x["values"], x["query"], x["norm_w"])
+    xc = {k: v.cpu() for k, v in x.items() if v is not None}
+    ref = oracle.run(xc["values"], xc["query"], xc["norm_w"], None, xc["dout"])
+    D = x["values"].shape[2]
+    res = {"y": compare_rows(to_f64(y), ref["y"], "bf16"),
+           "dvalues": compare_rows(to_f64(compiled[1]), ref["dvalues"], "bf16"),
+           "dq": compare_vec(to_f64(compiled[2]), ref["dq"], "bf16"),
+           "dw": compare_vec(to_f64(compiled[3]), ref["dw"], "bf16")}
+    assert_ok(res, f"compiled read {backend} list={as_list} D={D}")
 
 
 def test_compiled_multi_query_read_matches_eager():
@@ -80,6 +97,17 @@ def test_compiled_multi_query_read_matches_eager():
     torch.testing.assert_close(eager[0], compiled[0], rtol=1e-5, atol=0)
     for a, b in zip(eager[1:], compiled[1:]):
         assert torch.equal(a, b)
+    y = torch.compile(lambda v, q: A.attnres_multi(v, q, deterministic=True), fullgraph=True,
+                      dynamic=False, backend="aot_eager")(x["values"], qs)
+    V = x["values"].cpu()
+    ref = oracle.run_multi(V, qs.cpu(), dy.cpu())
+    S, D = V.shape[0], V.shape[2]
+    res = {"y": compare_rows(to_f64(y).reshape(-1, D), ref["y"].reshape(-1, D), "bf16"),
+           "dvalues": compare_rows(to_f64(compiled[1]), ref["dvalues"], "bf16",
+                                   roundings=multi_bwd_passes(S, D, qs.shape[0], "bf16"))}
+    for m in range(qs.shape[0]):
+        res[f"dq{m}"] = compare_vec(to_f64(compiled[2][m]), ref["dq"][m], "bf16")
+    assert_ok(res, "compiled multi-query read")
 
 
 @pytest.mark.parametrize("as_list", [False, True])
@@ -109,6 +137,18 @@ def test_compiled_selected_query_read_matches_eager(as_list):
     torch.testing.assert_close(eager[0], compiled[0], rtol=1e-5, atol=0)
     for a, b in zip(eager[1:], compiled[1:]):
         assert torch.equal(a, b)
+    vals = x["values"].view(5, 2, N // 2, 2048)
+    y = torch.compile(lambda v, b: A.attnres_selected(v, b, ids, deterministic=True),
+                      fullgraph=True, dynamic=False, backend="aot_eager")(
+        list(vals.unbind(0)) if as_list else vals, bank)
+    K = ids.shape[-1]
+    ref = oracle.run_selected(x["values"].cpu(), bank.cpu(), ids.reshape(N, K).cpu(),
+                              dy.reshape(N, K, 2048).cpu())
+    res = {"y": compare_rows(to_f64(y).reshape(-1, 2048), ref["y"].reshape(-1, 2048), "bf16"),
+           "dvalues": compare_rows(to_f64(compiled[1]).reshape(5, N, 2048), ref["dvalues"],
+                                   "bf16", roundings=multi_bwd_passes(5, 2048, K, "bf16")),
+           "dbank": compare_vec(to_f64(compiled[2]), ref["dbank"], "bf16")}
+    assert_ok(res, f"compiled selected-query read list={as_list}")
 
 
 def test_opcheck_registrations():

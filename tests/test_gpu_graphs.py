@@ -4,14 +4,18 @@ torch.cuda.CUDAGraph with preallocated outputs and workspaces, then replayed fou
 copied into the captured buffers (alternating two input sets), with eager work and synchronisation
 between replays; every replay is compared with an eager call on the same inputs: bitwise for y,
 lse and dvalues (per-token results), and bitwise for dq / dbank in deterministic mode (else to the
-reduction-order tolerance of the schedules test)."""
+reduction-order tolerance of the schedules test). Every replay is also compared with the FP64
+oracle on the inputs copied in for it (the "Fast Attention Residuals" page, "Validation scope":
+replayed use checked against an independent reference)."""
 import math
 
 import numpy as np
 import pytest
 import torch
 
-from parity import gpu_available, to_f64
+import oracle
+from parity import (assert_ok, compare_rows, compare_stat, compare_vec, gpu_available,
+                    multi_bwd_passes, to_f64)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
@@ -33,7 +37,8 @@ def _close(a, b, deterministic):
         assert np.linalg.norm(x - y) <= 4e-3 * np.linalg.norm(y)
 
 
-def _replay_and_compare(capture_step, eager_step, bufs, inputs, outs, reduced, deterministic):
+def _replay_and_compare(capture_step, eager_step, bufs, inputs, outs, reduced, deterministic,
+                        check_oracle):
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         capture_step(s)  # warm-up outside capture
@@ -54,6 +59,7 @@ def _replay_and_compare(capture_step, eager_step, bufs, inputs, outs, reduced, d
             assert torch.equal(outs[k], ref[k]), k
         for k in reduced:
             _close(reduced[k], ref[k], deterministic)
+        check_oracle(xin)
 
 
 # M = 5: the matrix-core forward's eight-slot kernel (static stride); M = 12: its sixteen-slot
@@ -93,9 +99,26 @@ def test_multi_query_graph_replay(M, deterministic):
                                        deterministic=deterministic)
         return {"y": ye, "lse": le, "dv": dve, "dq": dqe}
 
+    refs = {}
+
+    def check(x):
+        key = id(x)
+        if key not in refs:  # the oracle of each input set, computed once
+            refs[key] = oracle.run_multi(x["V"].cpu(), x["Q"].cpu(),
+                                         x["G"].transpose(0, 1).contiguous().cpu())
+        ref = refs[key]
+        res = {"y": compare_rows(to_f64(y.transpose(0, 1)).reshape(-1, D),
+                                 ref["y"].reshape(-1, D), "bf16"),
+               "lse": compare_stat(to_f64(lse.transpose(0, 1)), ref["lse"]),
+               "dvalues": compare_rows(to_f64(dv), ref["dvalues"], "bf16",
+                                       roundings=multi_bwd_passes(S, D, M, "bf16"))}
+        for m in range(M):
+            res[f"dq{m}"] = compare_vec(to_f64(dq[m]), ref["dq"][m], "bf16")
+        assert_ok(res, f"multi graph replay M={M} deterministic={deterministic}")
+
     print(f"[case] multi graph M={M} deterministic={deterministic}", flush=True)
     _replay_and_compare(step, eager, bufs, inputs, {"y": y, "lse": lse, "dv": dv}, {"dq": dq},
-                        deterministic)
+                        deterministic, check)
 
 
 @pytest.mark.parametrize("E,K,deterministic", [(6, 3, True), (6, 3, False), (48, 3, False),
@@ -133,6 +156,21 @@ def test_selected_query_graph_replay(E, K, deterministic):
                                           deterministic=deterministic)
         return {"y": ye, "lse": le, "dv": dve, "db": dbe}
 
+    refs = {}
+
+    def check(x):
+        key = id(x)
+        if key not in refs:
+            refs[key] = oracle.run_selected(x["V"].cpu(), x["bank"].cpu(), x["ids"].cpu(),
+                                            x["G"].cpu())
+        ref = refs[key]
+        res = {"y": compare_rows(to_f64(y).reshape(-1, D), ref["y"].reshape(-1, D), "bf16"),
+               "lse": compare_stat(to_f64(lse), ref["lse"]),
+               "dvalues": compare_rows(to_f64(dv), ref["dvalues"], "bf16",
+                                       roundings=multi_bwd_passes(S, D, K, "bf16")),
+               "dbank": compare_vec(to_f64(db), ref["dbank"], "bf16")}
+        assert_ok(res, f"selected graph replay E={E} K={K} deterministic={deterministic}")
+
     print(f"[case] selected graph E={E} K={K} deterministic={deterministic}", flush=True)
     _replay_and_compare(step, eager, bufs, inputs, {"y": y, "lse": lse, "dv": dv}, {"db": db},
-                        deterministic)
+                        deterministic, check)
