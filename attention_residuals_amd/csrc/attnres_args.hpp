@@ -155,6 +155,34 @@ struct MfmaFwdArgs {
   int64_t tpt;                   //   tokens per ticket
 };
 
+// Multi-query backward through matrix cores (all M <= 16 queries in one pass; bf16).
+struct MfmaBwdArgs {
+  const void* src[kMaxSources];
+  void* dsrc[kMaxSources];
+  int64_t row_stride, drow_stride;
+  int64_t N;
+  int S, D, R, lo, M;
+  float eps, scale, inv_R;
+  const void* query;             // [M, R]
+  const float* lse;              // query m, token n at m * l_sm + n * l_sn
+  int64_t l_sm, l_sn;
+  const void* dout;              // dY rows: query m, token n at (m * g_sm + n * g_sn) elements
+  int64_t g_sm, g_sn;
+  float* coef;                   // [N][16][16] a_{m,s} per token (written; zero past M and S)
+};
+
+// Its dq kernel: partial rows [ranges][M * R] over static token ranges of tpr tokens.
+struct MfmaDqArgs {
+  const void* src[kMaxSources];
+  int64_t row_stride;
+  int64_t N;
+  int S, D, R, lo, M;
+  int chunk0;                    // first 16-byte chunk of the key slice (lo / 8)
+  int64_t tpr;                   // tokens per range
+  const float* coef;             // [N][16][16]
+  float* part;                   // [ranges][M * R]
+};
+
 struct MultiBwdArgs {
   const void* src[kMaxSources];
   void* dsrc[kMaxSources];

@@ -918,10 +918,57 @@ bool single_query_fast_path(const attnres_multi_desc* m, attnres_desc* d) {
 struct MultiBwdPlan {
   int P = 0;
   size_t off_part = 256, bytes = 256;
+  // one-pass matrix-core backward (bf16, 3 <= M <= 16, 2 <= S <= 16, D <= 4096)
+  bool mfma = false;
+  int cgw = 0, grid = 0, tiles = 0, ranges = 0, chunk0 = 0;
+  int64_t tpr = 0;
+  size_t lds = 0, off_coef = 0;
 };
+
+// The one-pass matrix-core backward: every query's gradient in one pass over the sources, so
+// dvalues are written (and rounded) once. Its per-token coefficients a_{m,s} go to the workspace
+// ([N][16][16] FP32) for the dq kernel, which reads the key slice of the sources again over static
+// token ranges (about two workgroups per CU) into [ranges][M * R] partial rows.
+// ATTNRES_MULTI_MFMA=0 turns it off.
+attnres_status plan_multi_bwd_mfma(const attnres_multi_desc* m, const MultiShape& ms,
+                                   MultiBwdPlan* pl) {
+  pl->mfma = false;
+  const char* e = std::getenv("ATTNRES_MULTI_MFMA");
+  if (e && e[0] == '0') return ATTNRES_OK;
+  const int cgw = (m->D + 1023) / 1024;
+  if (!ms.base.bf16 || m->S < 2 || m->S > 16 || m->M < 3 || m->M > 16 || cgw > 4)
+    return ATTNRES_OK;
+  DevFacts f;
+  attnres_status st = device_facts(&f);
+  if (st != ATTNRES_OK) return st;
+  const size_t lds = multi_bwd_mfma_lds(cgw, m->M);
+  if (lds > (size_t)f.lds_per_block) return ATTNRES_OK;
+  const void* fn = multi_bwd_mfma_kernel_ptr(cgw, m->R == m->D, m->accumulate_dvalues != 0);
+  if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query backward kernel");
+  int per_cu = 0;
+  if ((st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu)) != ATTNRES_OK) return st;
+  const int64_t N = m->N;
+  pl->mfma = true;
+  pl->cgw = cgw;
+  pl->lds = lds;
+  pl->grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
+  pl->chunk0 = (m->D - m->R) / 8;
+  const int key_chunks = m->D / 8 - pl->chunk0;
+  pl->tiles = (key_chunks + 16 * kMfmaWaves - 1) / (16 * kMfmaWaves);
+  const int64_t want = std::max<int64_t>(1, (2 * (int64_t)f.cus + pl->tiles - 1) / pl->tiles);
+  pl->tpr = N > 0 ? (N + std::min<int64_t>(N, want) - 1) / std::min<int64_t>(N, want) : 1;
+  pl->ranges = N > 0 ? (int)((N + pl->tpr - 1) / pl->tpr) : 0;
+  pl->P = pl->ranges;
+  pl->off_coef = 256;
+  pl->off_part = align256(pl->off_coef + (size_t)N * 256 * sizeof(float));
+  pl->bytes = align256(pl->off_part + (size_t)pl->ranges * m->M * m->R * sizeof(float));
+  return ATTNRES_OK;
+}
 
 attnres_status plan_multi_bwd(const attnres_multi_desc* m, const MultiShape& ms,
                               MultiBwdPlan* pl) {
+  attnres_status st0 = plan_multi_bwd_mfma(m, ms, pl);
+  if (st0 != ATTNRES_OK || pl->mfma) return st0;
   const std::vector<Group> groups = plan_groups(m, ms);
   const void* fn = multi_bwd_ptr(ms, groups[0].mq, m->accumulate_dvalues != 0);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no multi-query backward kernel for this shape");
@@ -1106,7 +1153,56 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* m, const attnres_sour
     return fail(ATTNRES_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
                 pl.bytes);
   char* ws = static_cast<char*>(workspace);
-  if (pl.P > 0) {
+  if (pl.mfma && N > 0) {
+    int64_t g_sm, g_sn, l_sm, l_sn;
+    multi_strides(m, &g_sm, &g_sn, &l_sm, &l_sn);
+    MfmaBwdArgs b;
+    std::memset(&b, 0, sizeof b);
+    for (int s = 0; s < m->S; ++s) {
+      b.src[s] = a.src[s];
+      b.dsrc[s] = const_cast<void*>(dptr[s]);
+    }
+    b.row_stride = values->row_stride;
+    b.drow_stride = dvalues->row_stride;
+    b.N = N;
+    b.S = m->S;
+    b.D = m->D;
+    b.R = m->R;
+    b.lo = m->D - m->R;
+    b.M = m->M;
+    b.eps = m->eps;
+    b.scale = m->scale;
+    b.inv_R = 1.0f / (float)m->R;
+    b.query = queries;
+    b.lse = lse;
+    b.l_sm = l_sm;
+    b.l_sn = l_sn;
+    b.dout = dout;
+    b.g_sm = g_sm;
+    b.g_sn = g_sn;
+    b.coef = reinterpret_cast<float*>(ws + pl.off_coef);
+    const void* fn = multi_bwd_mfma_kernel_ptr(pl.cgw, m->R == m->D, m->accumulate_dvalues != 0);
+    st = launch(fn, pl.grid, 1, 64 * kMfmaWaves, pl.lds, &b, stream,
+                "matrix-core multi-query backward launch");
+    if (st != ATTNRES_OK) return st;
+    MfmaDqArgs q;
+    std::memset(&q, 0, sizeof q);
+    for (int s = 0; s < m->S; ++s) q.src[s] = a.src[s];
+    q.row_stride = values->row_stride;
+    q.N = N;
+    q.S = m->S;
+    q.D = m->D;
+    q.R = m->R;
+    q.lo = m->D - m->R;
+    q.M = m->M;
+    q.chunk0 = pl.chunk0;
+    q.tpr = pl.tpr;
+    q.coef = b.coef;
+    q.part = reinterpret_cast<float*>(ws + pl.off_part);
+    st = launch(multi_dq_mfma_kernel_ptr(), pl.tiles, pl.ranges, 64 * kMfmaWaves, 0, &q, stream,
+                "matrix-core multi-query dq launch");
+    if (st != ATTNRES_OK) return st;
+  } else if (pl.P > 0 && !pl.mfma) {
     int64_t g_sm, g_sn, l_sm, l_sn;
     multi_strides(m, &g_sm, &g_sn, &l_sm, &l_sn);
     for (int s = 0; s < m->S; ++s) a.dsrc[s] = const_cast<void*>(dptr[s]);

@@ -370,7 +370,7 @@ def run_multi(args, w) -> int:
         torch.cuda.synchronize()
         import oracle
         sys.path.insert(0, os.path.join(ROOT, "tests"))
-        from parity import compare_rows, compare_stat, sample_tokens
+        from parity import compare_rows, compare_stat, multi_bwd_passes, sample_tokens
         toks = sample_tokens(N, 6, seed=7)
         sel = torch.tensor(toks, device=dev)
         gq = dout if args.layout == "query_major" else dout.transpose(0, 1)
@@ -380,7 +380,7 @@ def run_multi(args, w) -> int:
                                gq.index_select(1, sel).cpu(), eps=w.eps, scale=w.scale,
                                reduce=False)
         f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
-        groups = -(-M // (4 if (D // (8 if w.dtype == "bf16" else 4) <= 512 and S <= 12) else 2))
+        groups = multi_bwd_passes(S, D, M, w.dtype)
         res = {"y": compare_rows(f64(yq.index_select(1, sel)).reshape(-1, D),
                                  ref["y"].reshape(-1, D), w.dtype),
                "lse": compare_stat(f64(lq.index_select(1, sel)), ref["lse"]),
@@ -460,7 +460,7 @@ def run_selected(args, w) -> int:
         torch.cuda.synchronize()
         import oracle
         sys.path.insert(0, os.path.join(ROOT, "tests"))
-        from parity import compare_rows, compare_stat, sample_tokens
+        from parity import compare_rows, compare_stat, multi_bwd_passes, sample_tokens
         toks = sample_tokens(N, 6, seed=7)
         sel = torch.tensor(toks, device=dev)
         ref = oracle.run_selected(values.index_select(1, sel).cpu(), bank.cpu(),
@@ -472,8 +472,8 @@ def run_selected(args, w) -> int:
                                  ref["y"].reshape(-1, D), w.dtype),
                "lse": compare_stat(f64(lse.index_select(0, sel)), ref["lse"]),
                "dvalues": compare_rows(f64(dv.index_select(1, sel)), ref["dvalues"], w.dtype,
-                                       roundings=-(-K // (4 if (D // (8 if w.dtype == "bf16" else 4)
-                                                                  <= 512 and S <= 10) else 2)))}
+                                       roundings=multi_bwd_passes(S, D, K, w.dtype,
+                                                                  selected=True))}
         check = {k: {"metric": v["metric"], "ok": bool(v["ok"])} for k, v in res.items()}
 
     out = {

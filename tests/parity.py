@@ -202,13 +202,32 @@ def assert_ok(res: dict, label: str) -> None:
     assert not bad, f"{label}: out of tolerance: {bad}"
 
 
-def multi_bwd_passes(S: int, D: int, M: int, dtype: str) -> int:
-    """Backward launches (query groups) of the multi- and selected-query reads as the library plans
-    them: up to four queries per launch with one 16-byte chunk per thread (D <= 512 chunks at
-    eight waves) and S <= 12, else two. Each launch after the first adds into dvalues, rounding
-    the running sum to storage again."""
+def multi_mfma_bwd(S: int, D: int, M: int, dtype: str) -> bool:
+    """True when the multi-query backward runs in one pass on matrix cores (bf16, 3 <= M <= 16,
+    2 <= S <= 16, D <= 4096)."""
+    return dtype == "bf16" and 3 <= M <= 16 and 2 <= S <= 16 and D <= 4096
+
+
+def multi_bwd_groups(S: int, D: int, M: int, dtype: str, selected: bool = False) -> list:
+    """Backward launch groups (first query, count) of the multi- and selected-query reads as the
+    library plans them: one pass on matrix cores where multi_mfma_bwd holds (multi-query read),
+    else up to four queries per launch with one 16-byte chunk per thread (D <= 512 chunks at
+    eight waves) and S <= 12, else two, sized as evenly as possible (larger groups first). Each
+    launch after the first adds into dvalues, rounding the running sum to storage again."""
+    if not selected and multi_mfma_bwd(S, D, M, dtype):
+        return [(0, M)]
     per = 4 if (D // (8 if dtype == "bf16" else 4) <= 512 and S <= 12) else 2
-    return -(-M // per)
+    n = -(-M // per)
+    out, m0 = [], 0
+    for i in range(n):
+        cnt = M // n + (1 if i < M % n else 0)
+        out.append((m0, cnt))
+        m0 += cnt
+    return out
+
+
+def multi_bwd_passes(S: int, D: int, M: int, dtype: str, selected: bool = False) -> int:
+    return len(multi_bwd_groups(S, D, M, dtype, selected))
 
 
 def sample_tokens(N: int, k: int, seed: int) -> list:

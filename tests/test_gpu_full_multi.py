@@ -14,7 +14,7 @@ import torch
 import attnres_workloads as W
 import oracle
 from parity import (assert_ok, compare_rows, compare_stat, compare_vec, gpu_available,
-                    sample_tokens, to_f64)
+                    multi_bwd_passes, sample_tokens, to_f64)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
@@ -22,9 +22,8 @@ pytestmark = [pytest.mark.gpu,
 HEADLINE = W.ALL[W.HEADLINE]
 
 
-def _groups(w, M, backward_max):
-    chunks = w.D // (8 if w.dtype == "bf16" else 4)
-    return -(-M // (backward_max if chunks <= 512 else 2))
+def _groups(w, M, selected):
+    return multi_bwd_passes(w.S, w.D, M, w.dtype, selected)
 
 
 @pytest.mark.parametrize("M,layout", [(2, "query_major"), (4, "token_major")])
@@ -50,7 +49,7 @@ def test_multi_query_full_size(M, layout):
                              ref["y"].reshape(-1, w.D), w.dtype),
            "lse": compare_stat(to_f64(lq.index_select(1, sel)), ref["lse"]),
            "dvalues": compare_rows(to_f64(dv.index_select(1, sel)), ref["dvalues"], w.dtype,
-                                   roundings=_groups(w, M, 4))}
+                                   roundings=_groups(w, M, False))}
     for m in range(M):
         res[f"dq{m}"] = compare_vec(to_f64(dq[m]), red["dq"][m], w.dtype)
     assert_ok(res, f"full multi M={M} {layout}")
@@ -100,7 +99,7 @@ def test_selected_query_full_size(E, K):
                              ref["y"].reshape(-1, w.D), w.dtype),
            "lse": compare_stat(to_f64(lse.index_select(0, sel)), ref["lse"]),
            "dvalues": compare_rows(to_f64(dv.index_select(1, sel)), ref["dvalues"], w.dtype,
-                                   roundings=_groups(w, K, 4))}
+                                   roundings=_groups(w, K, True))}
     got_b = to_f64(db)
     for e in range(E):
         if not np.any(red["dbank"][e]):

@@ -17,7 +17,8 @@ import pytest
 import torch
 
 import oracle
-from parity import assert_ok, compare_rows, compare_stat, compare_vec, gpu_available, to_f64
+from parity import (assert_ok, compare_rows, compare_stat, compare_vec, gpu_available,
+                    multi_bwd_passes, to_f64)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
@@ -48,12 +49,8 @@ def _run(V, bank, ids, G, dvalues=None, accumulate=False, deterministic=False, d
 
 
 def _bwd_groups(S, D, K, dtype):
-    """Backward launch groups the library runs; each after the first adds into dvalues, which then
-    carry one bf16 rounding per group. Four slots share a launch with one 16-byte chunk per thread
-    (D <= 512 chunks at eight waves) and S <= 10, else two."""
-    chunks = D // (8 if dtype == "bf16" else 4)
-    per_launch = 4 if (chunks <= 512 and S <= 10) else 2
-    return -(-K // per_launch)
+    """Backward launch groups of the selected-query read (each rounds dvalues to storage)."""
+    return multi_bwd_passes(S, D, K, dtype, selected=True)
 
 
 def _compare_bank(got, ref, dtype, res):
