@@ -168,7 +168,8 @@ struct MfmaBwdArgs {
   int64_t l_sm, l_sn;
   const void* dout;              // dY rows: query m, token n at (m * g_sm + n * g_sn) elements
   int64_t g_sm, g_sn;
-  float* coef;                   // [N][16][16] a_{m,s} per token (written; zero past M and S)
+  float* coef;                   // [N][16][16] a_{m,s} per token when the dq kernel forms dq
+  float* part;                   // [grid][M * R] dq partial rows when the kernel sums dq itself
 };
 
 // Its dq kernel: partial rows [ranges][M * R] over static token ranges of tpr tokens.

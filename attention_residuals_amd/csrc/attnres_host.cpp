@@ -920,38 +920,55 @@ struct MultiBwdPlan {
   size_t off_part = 256, bytes = 256;
   // one-pass matrix-core backward (bf16, 3 <= M <= 16, 2 <= S <= 16, D <= 4096)
   bool mfma = false;
-  int cgw = 0, grid = 0, tiles = 0, ranges = 0, chunk0 = 0;
+  int nt = 0, dqm = 0, grid = 0, tiles = 0, ranges = 0, chunk0 = 0;
   int64_t tpr = 0;
   size_t lds = 0, off_coef = 0;
 };
 
 // The one-pass matrix-core backward: every query's gradient in one pass over the sources, so
-// dvalues are written (and rounded) once. Its per-token coefficients a_{m,s} go to the workspace
-// ([N][16][16] FP32) for the dq kernel, which reads the key slice of the sources again over static
-// token ranges (about two workgroups per CU) into [ranges][M * R] partial rows.
-// ATTNRES_MULTI_MFMA=0 turns it off.
+// dvalues are written (and rounded) once. One workgroup per CU over a static token stride, the
+// queries staged in its LDS. With M <= 4 each workgroup also sums dq for its tokens in LDS and
+// writes one [M * R] partial row; otherwise the per-token coefficients a_{m,s} go to the workspace
+// ([N][16][16] FP32) and the dq kernel reads the key slice of the sources again over static token
+// ranges (about two workgroups per CU). The finaliser adds the partial rows in a fixed order.
+// Rows of D = 256 nt columns (nt = 4, 8, 12 or 16 tiles of 32 columns per wave), R and the row
+// strides multiples of 8 elements. ATTNRES_MULTI_MFMA=0 turns it off.
 attnres_status plan_multi_bwd_mfma(const attnres_multi_desc* m, const MultiShape& ms,
-                                   MultiBwdPlan* pl) {
+                                   int64_t row_stride, int64_t drow_stride, MultiBwdPlan* pl) {
   pl->mfma = false;
   const char* e = std::getenv("ATTNRES_MULTI_MFMA");
   if (e && e[0] == '0') return ATTNRES_OK;
-  const int cgw = (m->D + 1023) / 1024;
-  if (!ms.base.bf16 || m->S < 2 || m->S > 16 || m->M < 3 || m->M > 16 || cgw > 4)
+  const int nt = m->D / 256;
+  // up to four queries with S <= 12 (and D <= 4096) are one launch of the query-group kernel,
+  // which measured faster there (M = 3, 4 at S = 10, N = 32768, D = 4096: 1.42 / 1.69 ms against
+  // 1.85 / 1.90 ms); it rounds dvalues once as well
+  if (m->M <= 4 && m->S <= 12) return ATTNRES_OK;
+  if (!ms.base.bf16 || m->S < 2 || m->S > 16 || m->M < 3 || m->M > 16 || m->D % 256 != 0 ||
+      (nt != 4 && nt != 8 && nt != 12 && nt != 16) || m->R % 8 != 0 || row_stride % 8 != 0 ||
+      drow_stride % 8 != 0)
     return ATTNRES_OK;
+  const int dqm = m->M <= 4 ? 1 : 0;
   DevFacts f;
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
-  const size_t lds = multi_bwd_mfma_lds(cgw, m->M);
+  const size_t lds = multi_bwd_mfma_lds(nt, dqm, m->M);
   if (lds > (size_t)f.lds_per_block) return ATTNRES_OK;
-  const void* fn = multi_bwd_mfma_kernel_ptr(cgw, m->R == m->D, m->accumulate_dvalues != 0);
+  const void* fn = multi_bwd_mfma_kernel_ptr(nt, dqm, m->R == m->D, m->accumulate_dvalues != 0);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query backward kernel");
   int per_cu = 0;
   if ((st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu)) != ATTNRES_OK) return st;
   const int64_t N = m->N;
   pl->mfma = true;
-  pl->cgw = cgw;
+  pl->nt = nt;
+  pl->dqm = dqm;
   pl->lds = lds;
   pl->grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
+  if (dqm != 0) {
+    pl->P = pl->grid;
+    pl->off_part = 256;
+    pl->bytes = align256(pl->off_part + (size_t)pl->P * m->M * m->R * sizeof(float));
+    return ATTNRES_OK;
+  }
   pl->chunk0 = (m->D - m->R) / 8;
   const int key_chunks = m->D / 8 - pl->chunk0;
   pl->tiles = (key_chunks + 16 * kMfmaWaves - 1) / (16 * kMfmaWaves);
@@ -965,10 +982,16 @@ attnres_status plan_multi_bwd_mfma(const attnres_multi_desc* m, const MultiShape
   return ATTNRES_OK;
 }
 
+// The backward's plan for rows with the given strides (in elements); mfma_ok = false (or rows
+// the matrix-core kernel cannot take) plans the query-group kernels.
 attnres_status plan_multi_bwd(const attnres_multi_desc* m, const MultiShape& ms,
+                              int64_t row_stride, int64_t drow_stride, bool mfma_ok,
                               MultiBwdPlan* pl) {
-  attnres_status st0 = plan_multi_bwd_mfma(m, ms, pl);
-  if (st0 != ATTNRES_OK || pl->mfma) return st0;
+  *pl = MultiBwdPlan();
+  if (mfma_ok) {
+    attnres_status st0 = plan_multi_bwd_mfma(m, ms, row_stride, drow_stride, pl);
+    if (st0 != ATTNRES_OK || pl->mfma) return st0;
+  }
   const std::vector<Group> groups = plan_groups(m, ms);
   const void* fn = multi_bwd_ptr(ms, groups[0].mq, m->accumulate_dvalues != 0);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no multi-query backward kernel for this shape");
@@ -1006,9 +1029,16 @@ attnres_status attnres_multi_workspace_bytes(const attnres_multi_desc* m, size_t
   if (st != ATTNRES_OK) return st;
   attnres_desc d;
   if (single_query_fast_path(m, &d)) return attnres_workspace_bytes(&d, bytes);
-  MultiBwdPlan pl;
-  if ((st = plan_multi_bwd(m, ms, &pl)) != ATTNRES_OK) return st;
-  *bytes = pl.bytes;
+  // enough for either backward: the matrix-core one (when the rows are dense and aligned) and the
+  // query-group one that serves other strides
+  MultiBwdPlan pm, pv;
+  if ((st = plan_multi_bwd(m, ms, m->D, m->D, true, &pm)) != ATTNRES_OK) return st;
+  *bytes = pm.bytes;
+  if (pm.mfma) {
+    if (plan_multi_bwd(m, ms, m->D, m->D, false, &pv) == ATTNRES_OK)
+      *bytes = std::max(pm.bytes, pv.bytes);
+    g_err.clear();
+  }
   return ATTNRES_OK;
 }
 
@@ -1148,7 +1178,9 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* m, const attnres_sour
                        dvalues, dq, nullptr, nullptr, workspace, workspace_bytes, stream);
 
   MultiBwdPlan pl;
-  if ((st = plan_multi_bwd(m, ms, &pl)) != ATTNRES_OK) return st;
+  if ((st = plan_multi_bwd(m, ms, values->row_stride, dvalues->row_stride, aligned(queries, 16),
+                           &pl)) != ATTNRES_OK)
+    return st;
   if (workspace_bytes < pl.bytes)
     return fail(ATTNRES_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
                 pl.bytes);
@@ -1180,28 +1212,32 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* m, const attnres_sour
     b.dout = dout;
     b.g_sm = g_sm;
     b.g_sn = g_sn;
-    b.coef = reinterpret_cast<float*>(ws + pl.off_coef);
-    const void* fn = multi_bwd_mfma_kernel_ptr(pl.cgw, m->R == m->D, m->accumulate_dvalues != 0);
+    if (pl.dqm == 0) b.coef = reinterpret_cast<float*>(ws + pl.off_coef);
+    else b.part = reinterpret_cast<float*>(ws + pl.off_part);
+    const void* fn =
+        multi_bwd_mfma_kernel_ptr(pl.nt, pl.dqm, m->R == m->D, m->accumulate_dvalues != 0);
     st = launch(fn, pl.grid, 1, 64 * kMfmaWaves, pl.lds, &b, stream,
                 "matrix-core multi-query backward launch");
     if (st != ATTNRES_OK) return st;
-    MfmaDqArgs q;
-    std::memset(&q, 0, sizeof q);
-    for (int s = 0; s < m->S; ++s) q.src[s] = a.src[s];
-    q.row_stride = values->row_stride;
-    q.N = N;
-    q.S = m->S;
-    q.D = m->D;
-    q.R = m->R;
-    q.lo = m->D - m->R;
-    q.M = m->M;
-    q.chunk0 = pl.chunk0;
-    q.tpr = pl.tpr;
-    q.coef = b.coef;
-    q.part = reinterpret_cast<float*>(ws + pl.off_part);
-    st = launch(multi_dq_mfma_kernel_ptr(), pl.tiles, pl.ranges, 64 * kMfmaWaves, 0, &q, stream,
-                "matrix-core multi-query dq launch");
-    if (st != ATTNRES_OK) return st;
+    if (pl.dqm == 0) {
+      MfmaDqArgs q;
+      std::memset(&q, 0, sizeof q);
+      for (int s = 0; s < m->S; ++s) q.src[s] = a.src[s];
+      q.row_stride = values->row_stride;
+      q.N = N;
+      q.S = m->S;
+      q.D = m->D;
+      q.R = m->R;
+      q.lo = m->D - m->R;
+      q.M = m->M;
+      q.chunk0 = pl.chunk0;
+      q.tpr = pl.tpr;
+      q.coef = b.coef;
+      q.part = reinterpret_cast<float*>(ws + pl.off_part);
+      st = launch(multi_dq_mfma_kernel_ptr(), pl.tiles, pl.ranges, 64 * kMfmaWaves, 0, &q, stream,
+                  "matrix-core multi-query dq launch");
+      if (st != ATTNRES_OK) return st;
+    }
   } else if (pl.P > 0 && !pl.mfma) {
     int64_t g_sm, g_sn, l_sm, l_sn;
     multi_strides(m, &g_sm, &g_sn, &l_sm, &l_sn);

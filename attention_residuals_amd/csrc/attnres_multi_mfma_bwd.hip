@@ -8,23 +8,30 @@
 //   B_s = -rho_s^2 / R * sum_m a_{m,s} c_{m,s};   dq_m = sum_{n,s} a_{m,s} t_s.
 // All M <= 16 queries in one pass over the sources: dvalues are written (and rounded) once.
 //
-// Kernel 1 (multi_bwd_mfma_kernel): one 8-wave workgroup per CU owns one token at a time. Rows sit
-// in the matrix-core forward's layout: lane (g, c) of a wave holds, per 128-column group, the
-// 16-byte chunk c of sources 4g .. 4g+3 and of the dY rows of queries 4g .. 4g+3.
-//   * The contractions over columns (c, dp and the key sums of squares) run on matrix cores too:
-//     each wave copies one 32-column block of its source and dY rows to a small LDS staging area
-//     and reads it back with row = lane % 16, columns 4 * (lane / 16) .. + 3, which is the operand
-//     layout of a 16x16x16 MFMA whose contraction index is the column; the staged queries come
-//     from LDS in the same way. Per block: scores = Q V^T, dp = dY V^T, sum t^2 = diag(V V^T).
-//   * One LDS exchange sums the 8 waves' 16 x 16 tiles; 256 threads then finish one (m, s) pair
-//     each (routing weight from the saved lse, delta by a 16-lane row sum, a, and the B terms),
-//     write a_{m,s} to the coefficient array and p, a to LDS.
-//   * dv = P^T dY + A^T Q (two MFMA contractions over the queries, weights as two bf16 terms) plus
-//     B_s t_s on the vector ALU, rounded once to bf16 (with accumulate: added to the existing row
-//     first); the next token's rows of a column group load as soon as its dv is done.
+// Kernel 1 (multi_bwd_mfma_kernel): one 8-wave workgroup per CU owns one token at a time; wave w
+// owns the 32-column tiles (t * 8 + w), t < NT, of every row. Rows are held in the layout of a
+// matrix-core operand whose contraction index is the column: lane (g, c) keeps, per tile, the 16
+// bytes at columns 8g .. 8g+7 of source c and of query c's dY row. So the column contractions run
+// on 16x16x32 MFMAs straight from the loaded registers: scores = Q V^T, dp = dY V^T and the key
+// sums of squares diag(V V^T). The contractions over queries and sources (dv, dq) need the other
+// index in the operand's k slots: a 16x16x16 MFMA against the identity transposes a 16 x 16 block
+// (lane (g, c) then holds rows 4g .. 4g+3 of one column), exact for bf16 data.
+//   * Per token: the score tiles of the 8 waves meet in LDS; 256 threads finish one (m, s) pair
+//     each (routing weight from the saved lse, delta by a 16-lane row sum, a, and the B terms).
+//   * dv^T = dY^T P + Q^T A per 16-column half-tile: one K = 32 operand carries four queries' dY
+//     and q values, the other the matching p and a values, as two bf16 terms (hi, then lo, in two
+//     MFMAs); B_s t_s is added on the vector ALU and each dv row chunk is rounded once to bf16
+//     (with accumulate: added to the existing row first).
+//   * As soon as a tile's dv is written, its registers take the next token's rows, and the next
+//     token's score contractions run a few tiles behind those loads, so the loads overlap the
+//     current token's work.
+//   * dq: with M <= 8 the partial sums over the workgroup's tokens sit in LDS ([8][columns] FP32,
+//     two half-tiles stacked into one 16x16x32 MFMA per term); with M <= 16 and rows of at most
+//     2048 columns, [16][columns]. Otherwise the per-token a_{m,s} go to the workspace and kernel 2
+//     forms dq. Either way one FP32 partial row per workgroup or range, summed by the finaliser in
+//     a fixed order.
 // Kernel 2 (multi_dq_mfma_kernel): dq_m[j] = sum_n sum_s a_{m,s,n} t_{s,n}[j] over a static token
-// range per workgroup (16x16x16 MFMAs with the sources as the contraction index), one FP32 partial
-// row per range; the finaliser sums the ranges in a fixed order.
+// range per workgroup (16x16x16 MFMAs with the sources as the contraction index).
 #include "attnres_internal.hpp"
 #include "attnres_kernels.hpp"
 
@@ -35,13 +42,17 @@ typedef short mb_short4 __attribute__((ext_vector_type(4)));
 typedef float mb_float4 __attribute__((ext_vector_type(4)));
 typedef uint32_t mb_u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t mb_u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 mb_bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ Chunk bnt_load16(const char* p) {
   return __builtin_bit_cast(Chunk,
                             __builtin_nontemporal_load(reinterpret_cast<const mb_u32x4*>(p)));
 }
-__device__ __forceinline__ void bnt_store16(char* p, const Chunk& v) {
-  __builtin_nontemporal_store(__builtin_bit_cast(mb_u32x4, v), reinterpret_cast<mb_u32x4*>(p));
+__device__ __forceinline__ mb_u32x4 nt_ld(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const mb_u32x4*>(p));
+}
+__device__ __forceinline__ void nt_st(char* p, const mb_u32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<mb_u32x4*>(p));
 }
 
 // {a.low, b.low} / {a.high, b.high} of two words (v_perm_b32)
@@ -60,20 +71,47 @@ __device__ __forceinline__ mb_short4 gather_e(const Chunk (&r)[4], int e) {
   return __builtin_bit_cast(mb_short4, mb_u32x2{b0, b1});
 }
 
-// Four FP32 weights as an A operand in two bf16 terms (w = hi + lo, ~16 bits kept)
-__device__ __forceinline__ void split_a(const float (&w)[4], mb_short4& hi, mb_short4& lo) {
-  uint32_t h[2], l[2];
+// Four FP32 weights as two bf16 terms (w = hi + lo, ~16 bits kept), each packed as 4 bf16
+__device__ __forceinline__ void split4(const float (&w)[4], mb_u32x2& hi, mb_u32x2& lo) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    h[i] = pack_bf16x2(w[2 * i], w[2 * i + 1]);
-    l[i] = pack_bf16x2(w[2 * i] - lo_f(h[i]), w[2 * i + 1] - hi_f(h[i]));
+    hi[i] = pack_bf16x2(w[2 * i], w[2 * i + 1]);
+    lo[i] = pack_bf16x2(w[2 * i] - lo_f(hi[i]), w[2 * i + 1] - hi_f(hi[i]));
   }
-  hi = __builtin_bit_cast(mb_short4, mb_u32x2{h[0], h[1]});
-  lo = __builtin_bit_cast(mb_short4, mb_u32x2{l[0], l[1]});
+}
+__device__ __forceinline__ void split_a(const float (&w)[4], mb_short4& hi, mb_short4& lo) {
+  mb_u32x2 h, l;
+  split4(w, h, l);
+  hi = __builtin_bit_cast(mb_short4, h);
+  lo = __builtin_bit_cast(mb_short4, l);
 }
 
-__device__ __forceinline__ mb_short4 ld8(const char* p) {
-  return __builtin_bit_cast(mb_short4, *reinterpret_cast<const mb_u32x2*>(p));
+__device__ __forceinline__ mb_float4 mfma_k32(const mb_u32x4& a, const mb_u32x4& b,
+                                              const mb_float4& acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mb_bf16x8, a),
+                                                 __builtin_bit_cast(mb_bf16x8, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ mb_float4 mfma_k16(const mb_u32x2& a, const mb_u32x2& b,
+                                              const mb_float4& acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mb_short4, a),
+                                                   __builtin_bit_cast(mb_short4, b), acc, 0, 0, 0);
+}
+
+// Transpose of half h of a tile held in operand layout (lane (g, c): row c, columns 8g .. 8g+7 in
+// x's eight bf16 slots). The 16x16x16 A operand takes slots 4h .. 4h+3 (columns 8g + 4h + i as
+// k = 4g + i); against the identity the product is that block itself in the output layout, so
+// lane (g, c) receives rows 4g .. 4g+3 at column 8(c/4) + 4h + c%4 of the tile, exact in FP32,
+// and the high halves of the FP32 words are those bf16 values again.
+__device__ __forceinline__ mb_u32x2 tr_half(const mb_u32x4& x, int h, const mb_u32x2& ident) {
+  const mb_u32x2 a = h ? mb_u32x2{x[2], x[3]} : mb_u32x2{x[0], x[1]};
+  const mb_float4 t = mfma_k16(a, ident, mb_float4{0.f, 0.f, 0.f, 0.f});
+  return mb_u32x2{bpair_hi(f_bits(t[0]), f_bits(t[1])), bpair_hi(f_bits(t[2]), f_bits(t[3]))};
+}
+
+// The same transpose of a block already in the 16x16x16 A layout (four bf16 per lane).
+__device__ __forceinline__ mb_u32x2 tr2(const mb_u32x2& a, const mb_u32x2& ident) {
+  const mb_float4 t = mfma_k16(a, ident, mb_float4{0.f, 0.f, 0.f, 0.f});
+  return mb_u32x2{bpair_hi(f_bits(t[0]), f_bits(t[1])), bpair_hi(f_bits(t[2]), f_bits(t[3]))};
 }
 
 // Sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the same lane of the wave's four DPP rows).
@@ -84,187 +122,142 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return bits_f(b[0]) + bits_f(b[1]);
 }
 
-// Lanes of one wave pass data through LDS here with no workgroup barrier between the write and
-// the read. The hardware completes a wave's LDS operations in issue order, but the compiler sees
-// only one lane: without a fence it may reuse a value it loaded earlier from the same address (a
-// lane that did not store assumes the memory unchanged) or move a store above another lane's read.
-// A wavefront-scope fence orders them for the compiler and emits no instruction.
-__device__ __forceinline__ void wave_lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-}
+constexpr int kXchFloats = 2 * 256 + 16;  // a wave's score and dp tiles and its 16 sums of squares
 
-constexpr int kStageRow = 80;                    // bytes per staged row (64 + pad: no conflicts)
-constexpr int kWaveRegion = 32 * kStageRow;      // 16 source + 16 dY rows of one 32-column block
-constexpr int kXchFloats = 2 * 256 + 16;         // scores, dp tiles and the 16 sums of squares
+constexpr int dq_rows(int dqm) { return dqm == 1 ? 4 : 0; }
+// LDS row stride of the dq sums: the row's columns plus a pad that puts the two halves' lane groups
+// of one access on different banks
+constexpr int dq_stride(int nt, int dqm) { return dqm ? kMfmaWaves * nt * 32 + 8 : 0; }
 
 }  // namespace
 
-size_t multi_bwd_mfma_lds(int cgw, int M) {
-  return (size_t)M * kMfmaWaves * cgw * 16 * 16 + (size_t)kMfmaWaves * kWaveRegion +
-         (2 * 256 + 4 * 16) * sizeof(float);
+size_t multi_bwd_mfma_lds(int nt, int dqm, int M) {
+  const size_t D = (size_t)nt * kMfmaWaves * 32;
+  return ((size_t)dq_rows(dqm) * dq_stride(nt, dqm) + (size_t)kMfmaWaves * kXchFloats + 512 + 64) *
+             sizeof(float) +
+         D * ((M + 3) / 4) * 8;
 }
 
-template <int CGW, bool FULL, bool ACC>
+template <int NT, bool FULL, bool ACC, int DQM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 8)))
 void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   constexpr int W = kMfmaWaves;
-  constexpr int NQ = W * CGW * 16;  // 16-byte chunks of a row the workgroup covers
+  constexpr int D = NT * W * 32;          // the row width this kernel is built for
+  constexpr int LAG = NT >= 8 ? 4 : 2;    // the next token's contractions trail its loads
+  constexpr int DQR = dq_rows(DQM);
+  constexpr int DQS = dq_stride(NT, DQM);
   extern __shared__ float lds[];
-  Chunk* qlds = reinterpret_cast<Chunk*>(lds);  // [M][NQ] staged queries
-  char* regions = reinterpret_cast<char*>(lds) + (size_t)a.M * NQ * 16;
-  float* pa = reinterpret_cast<float*>(regions + W * kWaveRegion);  // p[16][16], a[16][16]
-  float* bpart = pa + 512;                                           // [4][16] partial B sums
+  float* dql = lds;                                          // [DQR][DQS] dq partial sums
+  const int QG = (a.M + 3) >> 2;                             // query groups of four
+  char* qtl = reinterpret_cast<char*>(lds + DQR * DQS);      // [D][QG][4] bf16 queries
+  float* xch = lds + DQR * DQS + D * QG * 2;                 // [W][kXchFloats]
+  float* pa = xch + W * kXchFloats;                          // p[16][16], a[16][16]
+  float* bpart = pa + 512;                                   // [4][16] partial B sums
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
-  char* stage = regions + wave * kWaveRegion;
-  float* xw = reinterpret_cast<float*>(stage);  // the wave's exchange (after its blocks)
+  const mb_u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  // queries as bf16 chunks of full-width rows, zero outside the key slice [lo, D)
-  const uint16_t* qsrc = static_cast<const uint16_t*>(a.query);
-  for (int idx = tid; idx < a.M * NQ; idx += W * 64) {
-    const int m = idx / NQ, q = idx - m * NQ;
-    Chunk v;
+  // Wave w owns columns [w * NT * 32, (w + 1) * NT * 32): tile t of lane (g, c) is the 16 bytes
+  // at column ccol(t) = (w * NT + t) * 32 + 8g of source c and of query c's dY row, so a tile's
+  // addresses are the lane's base plus the immediate 64 t.
+  const int col_w = wave * NT * 32 + 8 * g;
+  auto keyok = [&](int t) { return FULL || col_w + 32 * t >= a.lo; };
+
+  // lane (g, c) streams source c and query c's dY row; dead lanes read the first row's chunk (the
+  // same addresses as lane c = 0, so the loads coalesce) and discard it
+  const bool vlive = c < a.S, qlive = c < a.M;
+  const char* vsrc = static_cast<const char*>(a.src[0]);
+  char* vdst = static_cast<char*>(a.dsrc[0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int s = 1; s < 16; ++s)
+    if (s == c && vlive) {
+      vsrc = static_cast<const char*>(a.src[s]);
+      vdst = static_cast<char*>(a.dsrc[s]);
+    }
+  vsrc += col_w * 2;
+  vdst += col_w * 2;
+  const char* gsrc = static_cast<const char*>(a.dout) + ((qlive ? c * a.g_sm : 0) + col_w) * 2;
+
+  auto ld_v = [&](int t, int64_t n) {
+    const mb_u32x4 x = nt_ld(vsrc + n * a.row_stride * 2 + 64 * t);
+    return vlive ? x : zero4;
+  };
+  auto ld_y = [&](int t, int64_t n) {
+    const mb_u32x4 x = nt_ld(gsrc + n * a.g_sn * 2 + 64 * t);
+    return qlive ? x : zero4;
+  };
+  auto ld_old = [&](int t, int64_t n) {
+    const mb_u32x4 x = nt_ld(vdst + n * a.drow_stride * 2 + 64 * t);
+    return vlive ? x : zero4;
+  };
+
+  // The queries live in LDS as qtl[column][group][4]: the four queries of a group at one column.
+  // The dv contraction reads them as they are (queries 4g .. 4g+3 at the lane's column), and the
+  // score contraction takes their transpose (query c at eight consecutive columns). Global loads
+  // would wait behind the row loads in flight: the vector-memory counter completes in order.
+  for (int idx = tid; idx < D * QG; idx += W * 64) {
+    const int j = idx / QG, grp = idx - j * QG;
+    uint32_t w2[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
       uint32_t h[2];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int col = q * 8 + 2 * i + k;
-        h[k] = (col >= a.lo && col < a.D) ? static_cast<uint32_t>(qsrc[(int64_t)m * a.R + (col - a.lo)])
-                                          : 0u;
+      for (int e = 0; e < 2; ++e) {
+        const int m = 4 * grp + 2 * k + e;
+        h[e] = (m < a.M && j >= a.lo)
+                   ? static_cast<const uint16_t*>(a.query)[(int64_t)m * a.R + (j - a.lo)]
+                   : 0u;
       }
-      v.w[i] = h[0] | (h[1] << 16);
+      w2[k] = h[0] | (h[1] << 16);
     }
-    qlds[idx] = v;
+    *reinterpret_cast<mb_u32x2*>(qtl + (size_t)idx * 8) = mb_u32x2{w2[0], w2[1]};
   }
+  // lane (g, c), half h of tile t: queries 4g .. 4g+3 at column (w NT + t) 32 + 8(c/4) + 4h + c%4
+  const bool qgl = g < QG;
+  const char* qtp = qtl + ((size_t)(wave * NT * 32 + 8 * (c >> 2) + (c & 3)) * QG + (qgl ? g : 0)) * 8;
+  auto ld_qt = [&](int t, int h) {
+    const mb_u32x2 x = *reinterpret_cast<const mb_u32x2*>(qtp + (32 * t + 4 * h) * QG * 8);
+    return qgl ? x : mb_u32x2{0u, 0u};
+  };
 
-  // this lane's sources 4g + j and dY rows of queries 4g + j
-  const char* vbase[4];
-  bool vlive[4], glive[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    vlive[j] = 4 * g + j < a.S;
-    glive[j] = 4 * g + j < a.M;
-    vbase[j] = static_cast<const char*>(vlive[j] ? a.src[4 * g + j] : nullptr);
-  }
-  const char* gbase = static_cast<const char*>(a.dout);
-  int qidx[CGW];
-  bool qok[CGW];
-#pragma unroll
-  for (int cg = 0; cg < CGW; ++cg) {
-    qidx[cg] = (wave * CGW + cg) * 16 + c;
-    qok[cg] = qidx[cg] * 8 < a.D;
-  }
-  // key-slice masks of the chunks' bf16 halves (columns >= lo) for the B t terms
-  uint32_t gm[FULL ? 1 : CGW][4];
-  if constexpr (!FULL) {
-#pragma unroll
-    for (int cg = 0; cg < CGW; ++cg)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col0 = qidx[cg] * 8 + 2 * i;
-        gm[cg][i] = (col0 >= a.lo ? 0x0000ffffu : 0u) | (col0 + 1 >= a.lo ? 0xffff0000u : 0u);
-      }
+  // identity B operand of the transposes: lane (g, c) holds I[4g + i][c]
+  mb_u32x2 ident = {0u, 0u};
+  if ((c >> 2) == g) ident[(c >> 1) & 1] = (c & 1) ? 0x3F800000u : 0x00003F80u;
+
+  if constexpr (DQM != 0) {
+    for (int i = tid; i < DQR * DQS; i += W * 64) dql[i] = 0.f;
   }
   __syncthreads();
 
-  auto load_v = [&](Chunk (&r)[4], int cg, int64_t tok) {
-    const int64_t off = tok * a.row_stride * 2 + (int64_t)qidx[cg] * 16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      r[j] = (tok < a.N && vlive[j] && qok[cg]) ? bnt_load16(vbase[j] + off) : Chunk{};
+  mb_u32x4 V[NT], Y[NT];
+  mb_float4 tsc, tdp, tss;
+  // scores, dp and sums of squares of tile t (lane (g, c) ends with rows 4g + i, column c); the
+  // score operand is query c at the tile's eight columns 8g .. 8g+7, the transpose of its groups
+  auto contract = [&](int t) {
+    const mb_u32x2 q0 = tr2(ld_qt(t, 0), ident);
+    const mb_u32x2 q1 = tr2(ld_qt(t, 1), ident);
+    tsc = mfma_k32(mb_u32x4{q0[0], q0[1], q1[0], q1[1]}, V[t], tsc);
+    tdp = mfma_k32(Y[t], V[t], tdp);
+    const mb_u32x4 vm = keyok(t) ? V[t] : zero4;
+    tss = mfma_k32(vm, vm, tss);
   };
-  auto load_g = [&](Chunk (&r)[4], int cg, int64_t tok) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      r[j] = (tok < a.N && glive[j] && qok[cg])
-                 ? bnt_load16(gbase + ((4 * g + j) * a.g_sm + tok * a.g_sn + (int64_t)qidx[cg] * 8) * 2)
-                 : Chunk{};
-  };
-  auto load_old = [&](Chunk (&r)[4], int cg, int64_t tok) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      r[j] = (vlive[j] && qok[cg])
-                 ? bnt_load16(static_cast<const char*>(a.dsrc[4 * g + j]) + tok * a.drow_stride * 2 +
-                              (int64_t)qidx[cg] * 16)
-                 : Chunk{};
-  };
-
-  Chunk rows[CGW][4], gy[CGW][4];
-  int64_t n = blockIdx.x;
-#pragma unroll
-  for (int cg = 0; cg < CGW; ++cg) {
-    load_v(rows[cg], cg, n);
-    load_g(gy[cg], cg, n);
-  }
-  const int pm = tid >> 4, ps = tid & 15;  // (query, source) finished by thread tid < 256
-  while (n < a.N) {
-    const int64_t next = n + gridDim.x;
-    float lse_t = 0.f;
-    if (tid < 256 && pm < a.M) lse_t = a.lse[pm * a.l_sm + n * a.l_sn];
-
-    // ---- contractions over the columns: 32-column blocks through the staging area
-    mb_float4 tsc = {0.f, 0.f, 0.f, 0.f}, tdp = tsc, tss = tsc;
-#pragma unroll
-    for (int cg = 0; cg < CGW; ++cg) {
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        wave_lds_order();  // the previous block's reads precede these writes
-        if ((c >> 2) == blk) {
-          char* dst = stage + (c & 3) * 16;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<Chunk*>(dst + (4 * g + j) * kStageRow) = rows[cg][j];
-            *reinterpret_cast<Chunk*>(dst + (16 + 4 * g + j) * kStageRow) = gy[cg][j];
-          }
-        }
-        wave_lds_order();  // the reads below see the other lanes' writes above
-        const int chunk0 = (wave * CGW + cg) * 16 + 4 * blk;  // first chunk of the block
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int off = 32 * kb + 8 * g;  // byte offset of this lane's 4 columns in a row
-          const mb_short4 vop = ld8(stage + c * kStageRow + off);
-          const mb_short4 gop = ld8(stage + (16 + c) * kStageRow + off);
-          const mb_short4 qop = (c < a.M)
-              ? ld8(reinterpret_cast<const char*>(qlds + c * NQ + chunk0 + 2 * kb + (g >> 1)) +
-                    (g & 1) * 8)
-              : mb_short4{0, 0, 0, 0};
-          mb_short4 vm = vop;
-          if constexpr (!FULL) {
-            const int col0 = chunk0 * 8 + 16 * kb + 4 * g;
-            uint32_t w2[2];
-            const mb_u32x2 raw = __builtin_bit_cast(mb_u32x2, vop);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-              const uint32_t mk = (col0 + 2 * i >= a.lo ? 0x0000ffffu : 0u) |
-                                  (col0 + 2 * i + 1 >= a.lo ? 0xffff0000u : 0u);
-              w2[i] = raw[i] & mk;
-            }
-            vm = __builtin_bit_cast(mb_short4, mb_u32x2{w2[0], w2[1]});
-          }
-          tsc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qop, vop, tsc, 0, 0, 0);
-          tdp = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(gop, vop, tdp, 0, 0, 0);
-          tss = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vm, vm, tss, 0, 0, 0);
-        }
-      }
-    }
-    // the wave's tiles into its exchange (over its staging area): lane (g, c) holds rows 4g + i,
-    // column c
-    wave_lds_order();
+  auto exchange = [&]() {
+    float* xw = xch + wave * kXchFloats;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       xw[(4 * g + i) * 16 + c] = tsc[i];
       xw[256 + (4 * g + i) * 16 + c] = tdp[i];
       if (4 * g + i == c) xw[512 + c] = tss[i];
     }
-    __syncthreads();
-
-    // ---- (query, source) pairs: routing weight, delta, a and the B terms
+  };
+  const int pm = tid >> 4, ps = tid & 15;  // (query, source) finished by thread tid < 256
+  // the pairs of token n: routing weight, delta, a and the B terms into LDS
+  auto pairs = [&](int64_t n, float lse_t) {
     if (tid < 256) {
       float sc = 0.f, dpv = 0.f, ss = 0.f;
 #pragma unroll
       for (int w = 0; w < W; ++w) {  // wave order: a fixed summation order
-        const float* x = reinterpret_cast<const float*>(regions + w * kWaveRegion);
+        const float* x = xch + w * kXchFloats;
         sc += x[pm * 16 + ps];
         dpv += x[256 + pm * 16 + ps];
         ss += x[512 + ps];
@@ -273,72 +266,158 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
       const Score scv = source_score(ss, sc, a.inv_R, a.eps, a.scale);
       const float p = valid ? routing_weight(scv.z, lse_t) : 0.f;
       const float delta = row_sum(p * dpv);
-      const float av = a.scale * p * (dpv - delta) * scv.rho;
+      const float av = valid ? a.scale * p * (dpv - delta) * scv.rho : 0.f;
       const float bt = valid ? -av * scv.rho * scv.rho * sc * a.inv_R : 0.f;
       pa[pm * 16 + ps] = p;
       pa[256 + pm * 16 + ps] = av;
-      a.coef[n * 256 + tid] = av;
+      if constexpr (DQM == 0) a.coef[n * 256 + tid] = av;
       const float bs = rows4_sum(bt);  // over this wave's four queries
       if (lane < 16) bpart[wave * 16 + ps] = bs;
     }
-    __syncthreads();
+  };
+  auto load_lse = [&](int64_t n) {
+    return (tid < 256 && pm < a.M) ? a.lse[pm * a.l_sm + n * a.l_sn] : 0.f;
+  };
 
-    // ---- dv = P^T dY + A^T Q + B t (one rounding to bf16)
-    float pt[4], at[4], bsrc[4];
+  // first token: rows, contractions, pairs
+  int64_t n = blockIdx.x;
+  {
+    const float lse_t = load_lse(n);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pt[i] = pa[(4 * g + i) * 16 + c];
-      at[i] = pa[256 + (4 * g + i) * 16 + c];
-      bsrc[i] = ((bpart[4 * g + i] + bpart[16 + 4 * g + i]) + bpart[32 + 4 * g + i]) +
-                bpart[48 + 4 * g + i];
+    for (int t = 0; t < NT; ++t) {
+      V[t] = ld_v(t, n);
+      Y[t] = ld_y(t, n);
     }
-    mb_short4 p_hi, p_lo, a_hi, a_lo;
-    split_a(pt, p_hi, p_lo);
-    split_a(at, a_hi, a_lo);
-    Chunk old[ACC ? 2 : 1][4];
-    if constexpr (ACC) load_old(old[0], 0, n);
+    tsc = tdp = tss = mb_float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cg = 0; cg < CGW; ++cg) {
-      if constexpr (ACC) {
-        if (cg + 1 < CGW) load_old(old[(cg + 1) & 1], cg + 1, n);
+    for (int t = 0; t < NT; ++t) contract(t);
+    exchange();
+    __syncthreads();
+    pairs(n, lse_t);
+    __syncthreads();
+  }
+
+  while (n < a.N) {
+    const int64_t next = n + gridDim.x;
+    const bool more = next < a.N;
+    const int64_t ln = more ? next : n;  // rows loaded behind this token (unused after the last)
+    const float lse_next = more ? load_lse(next) : 0.f;
+
+    // this token's coefficient operands: lane (g, c) pairs p and a of queries 4g .. 4g+3 with
+    // source c (hi and lo terms), and B_c
+    mb_u32x4 bop_hi, bop_lo;
+    {
+      float pv[4], av[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = pa[(4 * g + i) * 16 + c];
+        av[i] = pa[256 + (4 * g + i) * 16 + c];
       }
-      Chunk qv[4];
+      mb_u32x2 ph, pl, ah, al;
+      split4(pv, ph, pl);
+      split4(av, ah, al);
+      bop_hi = mb_u32x4{ph[0], ph[1], ah[0], ah[1]};
+      bop_lo = mb_u32x4{pl[0], pl[1], al[0], al[1]};
+    }
+    const float bsrc = ((bpart[c] + bpart[16 + c]) + bpart[32 + c]) + bpart[48 + c];
+    // dq A operands (M <= 4): output row r = m + 8h (m = r % 8) takes a[m][4g + i] in slots
+    // 4h .. 4h+3 and zero in the other four
+    mb_u32x4 dqa_hi = zero4, dqa_lo = zero4;
+    if constexpr (DQM != 0) {
+      const int m = c & 7;
+      float av[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        qv[i] = (4 * g + i < a.M) ? qlds[(4 * g + i) * NQ + qidx[cg]] : Chunk{};
-      mb_float4 acc[8];
+      for (int i = 0; i < 4; ++i) av[i] = pa[256 + m * 16 + 4 * g + i];
+      mb_u32x2 ah, al;
+      split4(av, ah, al);
+      if (c >> 3) {
+        dqa_hi = mb_u32x4{0u, 0u, ah[0], ah[1]};
+        dqa_lo = mb_u32x4{0u, 0u, al[0], al[1]};
+      } else {
+        dqa_hi = mb_u32x4{ah[0], ah[1], 0u, 0u};
+        dqa_lo = mb_u32x4{al[0], al[1], 0u, 0u};
+      }
+    }
+
+    tsc = tdp = tss = mb_float4{0.f, 0.f, 0.f, 0.f};
+    mb_u32x4 old[NT];
+    if constexpr (ACC) {
+      old[0] = ld_old(0, n);
+      if (NT > 1) old[1] = ld_old(1, n);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (ACC) {
+        if (t + 2 < NT) old[t + 2] = ld_old(t + 2, n);
+      }
+      // dv^T of tile t, two 16-column halves: k slots 0-3 carry dY of queries 4g .. 4g+3 against
+      // p, slots 4-7 their q values against a
+      float f[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const mb_u32x2 yt = tr_half(Y[t], h, ident);
+        const mb_u32x2 qt = ld_qt(t, h);
+        const mb_u32x4 op = {yt[0], yt[1], qt[0], qt[1]};
+        mb_float4 d = mfma_k32(op, bop_hi, mb_float4{0.f, 0.f, 0.f, 0.f});
+        d = mfma_k32(op, bop_lo, d);
+        // lane (g, c): dv of source c at columns ccol(t) + 4h + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[4 * h + i] = d[i];
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const mb_short4 bdy = gather_e(gy[cg], e);
-        const mb_short4 bq = gather_e(qv, e);
-        mb_float4 o = {0.f, 0.f, 0.f, 0.f};
-        o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_hi, bdy, o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(p_lo, bdy, o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, bq, o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, bq, o, 0, 0, 0);
-        acc[e] = o;
+        const uint32_t w = V[t][e >> 1];
+        const float tv = keyok(t) ? ((e & 1) ? hi_f(w) : lo_f(w)) : 0.f;
+        float d = fmaf(bsrc, tv, f[e]);
+        if constexpr (ACC) d += (e & 1) ? hi_f(old[t][e >> 1]) : lo_f(old[t][e >> 1]);
+        f[e] = d;
       }
-      load_g(gy[cg], cg, next);  // the MFMAs have read this column group's dY rows
-      // lane (g, c) holds dv of source 4g + j at chunk qidx[cg], element e, in acc[e][j]
+      // dq (M <= 4): the sources in the k slots (their transposed half-tiles); output row 4g + i
+      // is query 4(g % 2) + i of half g / 2 (rows of queries 4 .. 7 are zero)
+      if constexpr (DQM != 0) {
+        const mb_u32x2 v0 = tr_half(V[t], 0, ident);
+        const mb_u32x2 v1 = tr_half(V[t], 1, ident);
+        const mb_u32x4 b = {v0[0], v0[1], v1[0], v1[1]};
+        mb_float4 acc = {0.f, 0.f, 0.f, 0.f};
+        float* acc_p = dql + (wave * NT + t) * 32 + 8 * (c >> 2) + (c & 3) + 4 * (g >> 1);
+        if (!(g & 1)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float f[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t w = FULL ? rows[cg][j].w[e >> 1] : (rows[cg][j].w[e >> 1] & gm[FULL ? 0 : cg][e >> 1]);
-          const float t = (e & 1) ? hi_f(w) : lo_f(w);
-          float d = fmaf(bsrc[j], t, acc[e][j]);
-          if constexpr (ACC) d += elem<true>(old[cg & 1][j], e);
-          f[e] = d;
+          for (int i = 0; i < 4; ++i) acc[i] = acc_p[i * DQS];
         }
-        if (vlive[j] && qok[cg])
-          bnt_store16(static_cast<char*>(a.dsrc[4 * g + j]) + n * a.drow_stride * 2 +
-                          (int64_t)qidx[cg] * 16,
-                      pack<true>(f));
+        acc = mfma_k32(dqa_hi, b, acc);
+        acc = mfma_k32(dqa_lo, b, acc);
+        if (!(g & 1)) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc_p[i * DQS] = acc[i];
+        }
       }
-      load_v(rows[cg], cg, next);
+      // the tile's registers take the next token's rows
+      V[t] = ld_v(t, ln);
+      Y[t] = ld_y(t, ln);
+      if (vlive)
+        nt_st(vdst + n * a.drow_stride * 2 + 64 * t,
+              mb_u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])});
+      if (t >= LAG) contract(t - LAG);
     }
+#pragma unroll
+    for (int t = NT - LAG; t < NT; ++t) contract(t);
+    if (!more) break;
+    exchange();
+    __syncthreads();
+    pairs(next, lse_next);
+    __syncthreads();
     n = next;
+  }
+
+  // this workgroup's dq partial row [M][R] (key columns)
+  if constexpr (DQM != 0) {
+    __syncthreads();
+    float* prow = a.part + (int64_t)blockIdx.x * a.M * a.R;
+    for (int idx = tid; idx < a.M * a.R; idx += W * 64) {
+      const int m = idx / a.R, j = idx - m * a.R;
+      prow[idx] = dql[m * DQS + a.lo + j];
+    }
   }
 }
 
@@ -403,17 +482,24 @@ __global__ __launch_bounds__(512) void multi_dq_mfma_kernel(const MfmaDqArgs a) 
   }
 }
 
-#define ATTNRES_MFMA_BWD_CASE(CGW)                                                    \
-  case CGW:                                                                           \
-    return acc ? (full ? (const void*)&multi_bwd_mfma_kernel<CGW, true, true>         \
-                       : (const void*)&multi_bwd_mfma_kernel<CGW, false, true>)       \
-               : (full ? (const void*)&multi_bwd_mfma_kernel<CGW, true, false>        \
-                       : (const void*)&multi_bwd_mfma_kernel<CGW, false, false>);
+#define ATTNRES_MFMA_BWD_K(NT, DQM)                                                    \
+  (acc ? (full ? (const void*)&multi_bwd_mfma_kernel<NT, true, true, DQM>                     \
+               : (const void*)&multi_bwd_mfma_kernel<NT, false, true, DQM>)                   \
+       : (full ? (const void*)&multi_bwd_mfma_kernel<NT, true, false, DQM>                    \
+               : (const void*)&multi_bwd_mfma_kernel<NT, false, false, DQM>))
 
-const void* multi_bwd_mfma_kernel_ptr(int cgw, bool full, bool acc) {
-  switch (cgw) {
-    ATTNRES_MFMA_BWD_CASE(1) ATTNRES_MFMA_BWD_CASE(2) ATTNRES_MFMA_BWD_CASE(3)
-    ATTNRES_MFMA_BWD_CASE(4)
+// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); dqm = 1: dq summed in LDS (M <= 4),
+// 0: coefficients to the workspace for the dq kernel
+const void* multi_bwd_mfma_kernel_ptr(int nt, int dqm, bool full, bool acc) {
+  switch (nt * 4 + dqm) {
+    case 4 * 4 + 1: return ATTNRES_MFMA_BWD_K(4, 1);
+    case 4 * 4 + 0: return ATTNRES_MFMA_BWD_K(4, 0);
+    case 8 * 4 + 1: return ATTNRES_MFMA_BWD_K(8, 1);
+    case 8 * 4 + 0: return ATTNRES_MFMA_BWD_K(8, 0);
+    case 12 * 4 + 1: return ATTNRES_MFMA_BWD_K(12, 1);
+    case 12 * 4 + 0: return ATTNRES_MFMA_BWD_K(12, 0);
+    case 16 * 4 + 1: return ATTNRES_MFMA_BWD_K(16, 1);
+    case 16 * 4 + 0: return ATTNRES_MFMA_BWD_K(16, 0);
     default: break;
   }
   return nullptr;

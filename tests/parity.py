@@ -202,19 +202,26 @@ def assert_ok(res: dict, label: str) -> None:
     assert not bad, f"{label}: out of tolerance: {bad}"
 
 
-def multi_mfma_bwd(S: int, D: int, M: int, dtype: str) -> bool:
-    """True when the multi-query backward runs in one pass on matrix cores (bf16, 3 <= M <= 16,
-    2 <= S <= 16, D <= 4096)."""
-    return dtype == "bf16" and 3 <= M <= 16 and 2 <= S <= 16 and D <= 4096
+def multi_mfma_bwd(S: int, D: int, M: int, dtype: str, R=None, row_stride=None) -> bool:
+    """True when the multi-query backward runs in one pass on matrix cores: bf16, 3 <= M <= 16,
+    2 <= S <= 16, D in (1024, 2048, 3072, 4096), R and the row stride multiples of 8 elements,
+    and not M <= 4 with S <= 12 (one launch of the query-group kernel there)."""
+    R = D if R is None else R
+    row_stride = D if row_stride is None else row_stride
+    if M <= 4 and S <= 12:
+        return False
+    return (dtype == "bf16" and 3 <= M <= 16 and 2 <= S <= 16 and D in (1024, 2048, 3072, 4096)
+            and R % 8 == 0 and row_stride % 8 == 0)
 
 
-def multi_bwd_groups(S: int, D: int, M: int, dtype: str, selected: bool = False) -> list:
+def multi_bwd_groups(S: int, D: int, M: int, dtype: str, selected: bool = False, R=None,
+                     row_stride=None) -> list:
     """Backward launch groups (first query, count) of the multi- and selected-query reads as the
     library plans them: one pass on matrix cores where multi_mfma_bwd holds (multi-query read),
     else up to four queries per launch with one 16-byte chunk per thread (D <= 512 chunks at
     eight waves) and S <= 12, else two, sized as evenly as possible (larger groups first). Each
     launch after the first adds into dvalues, rounding the running sum to storage again."""
-    if not selected and multi_mfma_bwd(S, D, M, dtype):
+    if not selected and multi_mfma_bwd(S, D, M, dtype, R, row_stride):
         return [(0, M)]
     per = 4 if (D // (8 if dtype == "bf16" else 4) <= 512 and S <= 12) else 2
     n = -(-M // per)
@@ -226,8 +233,9 @@ def multi_bwd_groups(S: int, D: int, M: int, dtype: str, selected: bool = False)
     return out
 
 
-def multi_bwd_passes(S: int, D: int, M: int, dtype: str, selected: bool = False) -> int:
-    return len(multi_bwd_groups(S, D, M, dtype, selected))
+def multi_bwd_passes(S: int, D: int, M: int, dtype: str, selected: bool = False, R=None,
+                     row_stride=None) -> int:
+    return len(multi_bwd_groups(S, D, M, dtype, selected, R, row_stride))
 
 
 def sample_tokens(N: int, k: int, seed: int) -> list:

@@ -56,9 +56,9 @@ def _run(V, Q, G, layout="query_major", dvalues=None, accumulate=False, determin
     return _from_layout(y, layout), _from_layout(lse, layout), dv, dq
 
 
-def _bwd_groups(S, D, M, dtype):
+def _bwd_groups(S, D, M, dtype, R=None):
     """The backward's launch groups (first query, count), as the library plans them."""
-    return multi_bwd_groups(S, D, M, dtype)
+    return multi_bwd_groups(S, D, M, dtype, R=R)
 
 
 def _dvalues_slack(V, Q, G, init, groups):
@@ -91,7 +91,7 @@ def _check(V, Q, G, label, dtype, init=None, **kw):
                             dtype)
     res["lse"] = compare_stat(to_f64(lse), ref["lse"])
     S, D = V.shape[0], V.shape[2]
-    groups = _bwd_groups(S, D, M, dtype)
+    groups = _bwd_groups(S, D, M, dtype, Q.shape[1])
     slack = (_dvalues_slack(V, Q, G, init, groups)
              if dtype == "bf16" and (len(groups) > 1 or init is not None) else None)
     res["dvalues"] = compare_rows(to_f64(dv), ref["dvalues"], dtype, slack=slack)
@@ -121,6 +121,11 @@ def _check(V, Q, G, label, dtype, init=None, **kw):
     (12, 157, 3072, 768, 5, "bf16", "token_major"),    # sliced key, three column groups
     (2, 300, 2048, 7, 4, "bf16", "query_major"),        # slice start inside a chunk
     (10, 257, 4096, 4096, 16, "bf16", "token_major"),  # the largest staged-query LDS (~145 KiB)
+    # more than twelve sources with up to four queries: the matrix-core backward that sums dq in
+    # its own LDS (no second pass over the sources)
+    (14, 300, 2048, 2048, 4, "bf16", "token_major"),
+    (16, 201, 1024, 512, 3, "bf16", "query_major"),
+    (13, 150, 3072, 3072, 3, "bf16", "query_major"),
 ])
 def test_multi_query_parity(S, N, D, R, M, dtype, layout):
     V, Q, G = _inputs(S, N, D, R, M, dtype, seed=2000 + S * M + D)
@@ -129,7 +134,8 @@ def test_multi_query_parity(S, N, D, R, M, dtype, layout):
            layout=layout)
 
 
-@pytest.mark.parametrize("M,dynamic", [(2, False), (2, True), (4, False), (4, True)])
+@pytest.mark.parametrize("M,dynamic", [(2, False), (2, True), (4, False), (4, True), (6, False),
+                                       (6, True)])
 def test_multi_query_several_tokens_per_workgroup(M, dynamic):
     # enough tokens that every workgroup of the forward's grid (static: 8x the resident count;
     # dynamic: one resident pass taking tickets) and of the backward's reads several, so the
@@ -142,9 +148,9 @@ def test_multi_query_several_tokens_per_workgroup(M, dynamic):
            deterministic=not dynamic)
 
 
-@pytest.mark.parametrize("M,packed", [(2, True), (6, False)])
-def test_multi_query_accumulate_into_dvalues(M, packed):
-    S, N, D, R = 6, 301, 2048, 2048
+@pytest.mark.parametrize("S,M,packed", [(6, 2, True), (6, 6, False), (14, 3, True)])
+def test_multi_query_accumulate_into_dvalues(S, M, packed):
+    N, D, R = 301, 2048, 2048
     V, Q, G = _inputs(S, N, D, R, M, "bf16", seed=2100 + M)
     init = (2.0 * torch.randn((S, N, D), generator=torch.Generator().manual_seed(5))).to(V.dtype)
     _check(V, Q, G, f"multi accumulate M={M}", "bf16", init=init, accumulate=True, packed=packed)
@@ -167,15 +173,17 @@ def test_matrix_core_forward_matches_the_vector_kernels(S, N, D, R, M, monkeypat
     assert np.max(np.abs(to_f64(l0) - to_f64(l1))) <= 1e-5 * (1 + np.max(np.abs(to_f64(l0))))
 
 
+@pytest.mark.parametrize("D", [1544, 2048])
 @pytest.mark.parametrize("case", ["one_token", "three_tokens", "list_sources", "strided_rows"])
-def test_matrix_core_forward_edges(case):
+def test_matrix_core_forward_edges(case, D):
     # the matrix-core forward (bf16, 3 <= M <= 16) with fewer tokens than workgroups, sources as a
-    # list of separate allocations, and rows further apart than D (a view into wider rows)
+    # list of separate allocations, and rows further apart than D (a view into wider rows); at
+    # D = 2048 the backward runs on matrix cores too
     import attention_residuals_amd as A
-    S, D, R, M = 7, 1544, 1544, 6
+    S, R, M = 7, D, 6
     N = {"one_token": 1, "three_tokens": 3}.get(case, 301)
     V, Q, G = _inputs(S, N, D, R, M, "bf16", seed=2400 + N)
-    print(f"[case] matrix-core forward {case}", flush=True)
+    print(f"[case] matrix-core forward {case} D={D}", flush=True)
     if case == "list_sources":
         vals = [V[s].clone().cuda() for s in range(S)]
     elif case == "strided_rows":
@@ -194,7 +202,7 @@ def test_matrix_core_forward_edges(case):
            "lse": compare_stat(to_f64(lse), ref["lse"]),
            "dvalues": compare_rows(to_f64(dv), ref["dvalues"], "bf16",
                                    slack=_dvalues_slack(V, Q, G, None,
-                                                        _bwd_groups(S, D, M, "bf16")))}
+                                                        _bwd_groups(S, D, M, "bf16", Q.shape[1])))}
     for m in range(M):
         res[f"dq{m}"] = compare_vec(to_f64(dq[m]), ref["dq"][m], "bf16")
     assert_ok(res, f"matrix-core forward {case}")
