@@ -9,7 +9,8 @@ from ._binding import (ATTNRES_BF16, ATTNRES_F32, EPS_DEFAULT, EXPORTS, AttnResE
                        attnres_fwd,
                        bind_bwd, bind_fwd,
                        attnres_multi_bwd, attnres_multi_fwd, attnres_selected_bwd,
-                       attnres_selected_fwd, fwd_workspace_bytes, load, make_desc,
+                       attnres_selected_fwd, attnres_selected_ids_flag, fwd_workspace_bytes, load,
+                       make_desc,
                        make_multi_desc, make_selected_desc, multi_fwd_workspace_bytes,
                        multi_workspace_bytes, o32_elems, selected_fwd_workspace_bytes,
                        selected_workspace_bytes, workspace_bytes)
@@ -19,7 +20,7 @@ __all__ = ["attnres", "attnres_multi", "attnres_selected", "attnres_fwd", "attnr
            "attnres_bwd_noalloc",
            "bind_fwd", "bind_bwd", "BoundCall",
            "attnres_multi_fwd", "attnres_multi_bwd", "attnres_selected_fwd",
-           "attnres_selected_bwd", "o32_elems", "workspace_bytes", "fwd_workspace_bytes",
+           "attnres_selected_bwd", "attnres_selected_ids_flag", "o32_elems", "workspace_bytes", "fwd_workspace_bytes",
            "multi_workspace_bytes", "multi_fwd_workspace_bytes", "selected_workspace_bytes",
            "selected_fwd_workspace_bytes", "make_desc", "make_multi_desc", "make_selected_desc",
            "MultiDesc", "SelectedDesc",

@@ -13,7 +13,9 @@ from typing import Optional, Sequence, Union
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libattnres.so")
+# ATTNRES_LIB names another build of the same library (the host-side AddressSanitizer build of the
+# argument checks, attention_residuals_amd/build_asan.py); by default the in-tree libattnres.so.
+LIB_PATH = os.environ.get("ATTNRES_LIB") or os.path.join(_PKG, "libattnres.so")
 
 ATTNRES_F32, ATTNRES_BF16 = 0, 1
 EPS_DEFAULT = 2.0 ** -23
@@ -24,8 +26,8 @@ EXPORTS = ("attnres_o32_elems", "attnres_workspace_bytes", "attnres_fwd_workspac
            "attnres_multi_fwd_workspace_bytes",
            "attnres_multi_workspace_bytes", "attnres_multi_fwd", "attnres_multi_bwd",
            "attnres_selected_fwd_workspace_bytes", "attnres_selected_workspace_bytes",
-           "attnres_selected_fwd", "attnres_selected_bwd",
-           "attnres_status_str", "attnres_last_error")
+           "attnres_selected_fwd", "attnres_selected_bwd", "attnres_selected_ids_flag",
+           "attnres_stream_probe", "attnres_status_str", "attnres_last_error")
 
 QUERY_MAJOR, TOKEN_MAJOR = 0, 1
 LAYOUTS = {"query_major": QUERY_MAJOR, "token_major": TOKEN_MAJOR}
@@ -96,6 +98,11 @@ def load() -> ctypes.CDLL:
     lib.attnres_selected_workspace_bytes.argtypes = [pe, ctypes.POINTER(sz)]
     lib.attnres_selected_fwd.argtypes = [pe, ps, vp, vp, vp, vp, vp, sz, vp]
     lib.attnres_selected_bwd.argtypes = [pe, ps, vp, vp, vp, vp, ps, vp, vp, sz, vp]
+    lib.attnres_selected_ids_flag.argtypes = [vp, sz, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                              vp]
+    lib.attnres_stream_probe.argtypes = [ctypes.POINTER(vp), ctypes.c_int32, ctypes.POINTER(vp),
+                                         ctypes.c_int32, i64, i64, ctypes.c_int32, ctypes.c_int32,
+                                         vp]
     for f in EXPORTS:
         if f not in ("attnres_status_str", "attnres_last_error"):
             getattr(lib, f).restype = ctypes.c_int
@@ -504,6 +511,36 @@ def attnres_selected_fwd(values, bank: torch.Tensor, ids: torch.Tensor, *,
                                        0 if workspace is None else workspace.numel(),
                                        _stream(stream)))
     return out, lse
+
+
+def attnres_selected_ids_flag(workspace: torch.Tensor, clear: bool = False, stream=None) -> bool:
+    """True if a selected-query forward that was given this workspace has read an id outside
+    [0, E) since the flag was last cleared (clear=True clears it after reading). Waits for the
+    work queued on the stream."""
+    flag = ctypes.c_int32(0)
+    _check(load().attnres_selected_ids_flag(_ptr(workspace), workspace.numel(), int(bool(clear)),
+                                            ctypes.byref(flag), _stream(stream)))
+    return bool(flag.value)
+
+
+def stream_probe(inputs, outputs, chunks_per_thread: int = 1, blocks_per_cu: int = 8,
+                 stream=None) -> None:
+    """Measurement aid (not the AttnRes computation): streams the rows of every input tensor to
+    the outputs (output j = input j for 1 <= j < len(inputs); output 0 and the outputs beyond the
+    inputs = XOR of the inputs). At most 128 of each; all tensors contiguous, same shape
+    [rows, ...] with rows of a multiple of 16 bytes, on one device."""
+    if not inputs or not outputs:
+        raise ValueError("stream_probe needs at least one input and one output")
+    t0 = inputs[0]
+    nbytes = t0.numel() * t0.element_size()
+    rows = t0.shape[0] if t0.dim() > 0 else 1
+    for t in list(inputs) + list(outputs):
+        if not t.is_contiguous() or t.numel() * t.element_size() != nbytes or t.shape[0] != rows:
+            raise ValueError("stream_probe tensors must be contiguous and alike")
+    ins = (ctypes.c_void_p * len(inputs))(*[_ptr(t) for t in inputs])
+    outs = (ctypes.c_void_p * len(outputs))(*[_ptr(t) for t in outputs])
+    _check(load().attnres_stream_probe(ins, len(inputs), outs, len(outputs), rows, nbytes // rows,
+                                       chunks_per_thread, blocks_per_cu, _stream(stream)))
 
 
 def attnres_selected_bwd(values, bank: torch.Tensor, ids: torch.Tensor, lse: torch.Tensor,

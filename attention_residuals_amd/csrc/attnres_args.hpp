@@ -20,6 +20,8 @@ constexpr int kFinRowsPhases = 64;
 // allocated and then serves any number of calls.
 constexpr int kCtrTicket = 0;    // next batch handed out by ticket
 constexpr int kCtrArrive = 32;   // forward: workgroups that have taken their last ticket
+constexpr int kCtrIdFlag = 48;   // selected-query forward: set to 1 when an id outside [0, E)
+                                 // was read (sticky: never cleared by a kernel)
 constexpr int kCtrWords = 64;    // 256 bytes
 
 // Exact accumulation of the backward's per-token gradient contributions (token-resident kernel):
@@ -119,6 +121,7 @@ struct SelArgs {
   int E, K, m0;
   int first;                     // backward: the first query group (its partial rows start at 0)
   int lds_bank;                  // backward: the partial bank rows live in LDS
+  uint32_t* id_flag;             // forward: word set to 1 on an id outside [0, E), or null
 };
 
 struct MultiFwdArgs {
@@ -151,6 +154,7 @@ struct MfmaFwdArgs {
   int64_t l_sm, l_sn;
   const int64_t* ids;            // selected-query read: [N, M] bank rows per token (query = bank)
   int E;                         //   bank rows; ids outside [0, E) read a zero query
+  uint32_t* id_flag;             //   word set to 1 when such an id is read, or null
   uint32_t* ticket;              // token batch counter (zeroed before the launch), or null: static
   int64_t tpt;                   //   tokens per ticket
 };
@@ -182,6 +186,16 @@ struct MfmaDqArgs {
   int64_t tpr;                   // tokens per range
   const float* coef;             // [N][16][16]
   float* part;                   // [ranges][M * R]
+};
+
+// Streaming probe (measurement aid): n_in input and n_out output streams of n_rows rows of
+// row_chunks 16-byte chunks each.
+constexpr int kProbeMaxStreams = 128;
+struct ProbeArgs {
+  const void* in[kProbeMaxStreams];
+  void* out[kProbeMaxStreams];
+  int n_in, n_out;
+  int64_t n_rows, row_chunks;
 };
 
 struct MultiBwdArgs {

@@ -24,11 +24,11 @@ const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full, bool acc
   return bf16 ? stream_ptr<true, false>(ch, sb, full) : stream_ptr<false, false>(ch, sb, full);
 }
 
-// Zeroes the 64 counter words (256 bytes) of a workspace on the launch stream (kernel stores: no
-// memset node, so the call stays capturable into a HIP graph). Every word a kernel counts with
-// is among them.
+// Zeroes the counter words of a workspace's first 256 bytes on the launch stream (kernel stores:
+// no memset node, so the call stays capturable into a HIP graph). Every word a kernel counts with
+// is among them; the selected-query forward's id flag (word kCtrIdFlag) is left as it is.
 __global__ __launch_bounds__(64) void ticket_reset_kernel(uint32_t* ctr) {
-  if (threadIdx.x < kCtrWords) ctr[threadIdx.x] = 0u;
+  if (threadIdx.x < kCtrIdFlag) ctr[threadIdx.x] = 0u;  // not the sticky id flag
 }
 
 const void* ticket_reset_kernel_ptr() { return (const void*)&ticket_reset_kernel; }

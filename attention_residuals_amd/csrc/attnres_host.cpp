@@ -852,6 +852,7 @@ attnres_status try_mfma_fwd(int S, int D, int R, int M, float eps, float scale, 
   ma.l_sn = l_sn;
   ma.ids = ids;
   ma.E = E;
+  ma.id_flag = (sel && workspace) ? static_cast<uint32_t*>(workspace) + kCtrIdFlag : nullptr;
   // sixteen slots, a workspace and at least two tokens per resident workgroup: tokens come in
   // batches from a counter in the workspace (reset by a kernel: no memset, so the call stays
   // capturable); the kernels of fewer slots keep the static stride
@@ -1432,6 +1433,71 @@ attnres_status attnres_selected_workspace_bytes(const attnres_selected_desc* d, 
   return ATTNRES_OK;
 }
 
+attnres_status attnres_stream_probe(const void* const* in_rows, int32_t n_in,
+                                    void* const* out_rows, int32_t n_out, int64_t n_rows,
+                                    int64_t row_bytes, int32_t chunks_per_thread,
+                                    int32_t blocks_per_cu, void* stream) {
+  g_err.clear();
+  if (!in_rows || !out_rows) return fail(ATTNRES_ERR_INVALID_ARG, "stream arrays are NULL");
+  if (n_in < 1 || n_in > kProbeMaxStreams || n_out < 1 || n_out > kProbeMaxStreams)
+    return fail(ATTNRES_ERR_INVALID_ARG, "n_in=%d, n_out=%d: 1 .. %d streams each", n_in, n_out,
+                kProbeMaxStreams);
+  const void* fn = stream_probe_kernel_ptr(chunks_per_thread);
+  if (!fn || blocks_per_cu < 1 || blocks_per_cu > 64)
+    return fail(ATTNRES_ERR_INVALID_ARG, "chunks_per_thread=%d (1, 2 or 4), blocks_per_cu=%d "
+                "(1 .. 64)", chunks_per_thread, blocks_per_cu);
+  if (n_rows < 0 || row_bytes < 16 || row_bytes % 16 != 0)
+    return fail(ATTNRES_ERR_INVALID_ARG, "n_rows=%lld, row_bytes=%lld: rows of whole 16-byte "
+                "chunks", (long long)n_rows, (long long)row_bytes);
+  ProbeArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int j = 0; j < n_in; ++j) {
+    if (!in_rows[j] || !aligned(in_rows[j], 16))
+      return fail(ATTNRES_ERR_ALIGNMENT, "input stream %d NULL or not 16-byte aligned", j);
+    a.in[j] = in_rows[j];
+  }
+  for (int j = 0; j < n_out; ++j) {
+    if (!out_rows[j] || !aligned(out_rows[j], 16))
+      return fail(ATTNRES_ERR_ALIGNMENT, "output stream %d NULL or not 16-byte aligned", j);
+    a.out[j] = out_rows[j];
+  }
+  std::vector<Range> ins, outs;
+  for (int j = 0; j < n_in; ++j)
+    ins.push_back(rows_range(a.in[j], n_rows, row_bytes, (int)row_bytes, 1, "in"));
+  for (int j = 0; j < n_out; ++j)
+    outs.push_back(rows_range(a.out[j], n_rows, row_bytes, (int)row_bytes, 1, "out"));
+  attnres_status st = check_disjoint(outs, ins);
+  if (st != ATTNRES_OK) return st;
+  if (n_rows == 0) return ATTNRES_OK;
+  a.n_in = n_in;
+  a.n_out = n_out;
+  a.n_rows = n_rows;
+  a.row_chunks = row_bytes / 16;
+  DevFacts f;
+  if ((st = device_facts(&f)) != ATTNRES_OK) return st;
+  const int64_t chunks = n_rows * a.row_chunks;
+  const int grid = (int)std::min<int64_t>((chunks + 255) / 256, (int64_t)f.cus * blocks_per_cu);
+  return launch(fn, grid, 1, 256, 0, &a, stream, "stream probe launch");
+}
+
+attnres_status attnres_selected_ids_flag(const void* workspace, size_t workspace_bytes,
+                                         int32_t clear, int32_t* flag, void* stream) {
+  g_err.clear();
+  if (!flag) return fail(ATTNRES_ERR_INVALID_ARG, "flag is NULL");
+  if (!workspace || workspace_bytes < kFwdWorkspaceBytes || !aligned(workspace, 256))
+    return fail(ATTNRES_ERR_WORKSPACE, "forward workspace NULL, smaller than %zu bytes or not "
+                "256-byte aligned", kFwdWorkspaceBytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* word = static_cast<uint32_t*>(const_cast<void*>(workspace)) + kCtrIdFlag;
+  uint32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, word, sizeof host, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess && clear) e = hipMemsetAsync(word, 0, sizeof host, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return report_hip(e, "reading the id flag");
+  *flag = host != 0u;
+  return ATTNRES_OK;
+}
+
 attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnres_sources* values,
                                     const void* bank, const int64_t* ids, void* y, float* lse,
                                     void* workspace, size_t workspace_bytes, void* stream) {
@@ -1507,6 +1573,7 @@ attnres_status attnres_selected_fwd(const attnres_selected_desc* d, const attnre
   a.sel.ids = ids;
   a.sel.E = d->E;
   a.sel.K = (int)K;
+  a.sel.id_flag = workspace ? static_cast<uint32_t*>(workspace) + kCtrIdFlag : nullptr;
   for (const Group& g : groups) {
     const void* fn = sel_fwd_kernel_ptr(ms.base.bf16, ms.ch, ms.sb, ms.full, g.mq);
     if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no selected-query forward kernel for this shape");

@@ -70,6 +70,7 @@ size_t multi_fwd_mfma_lds(int cgw, int mq, int qrows);
 // dqm = where dq is summed (1: in the kernel's LDS, M <= 4; 0: by the separate dq kernel).
 const void* multi_bwd_mfma_kernel_ptr(int nt, int dqm, bool full, bool acc);
 const void* multi_dq_mfma_kernel_ptr();
+const void* stream_probe_kernel_ptr(int cpt);
 size_t multi_bwd_mfma_lds(int nt, int dqm, int M);
 const void* sel_bwd_kernel_ptr_bf16(int ch, int sb, bool full, bool acc, int mq);
 const void* sel_bwd_kernel_ptr_f32(int ch, int sb, bool full, bool acc, int mq);

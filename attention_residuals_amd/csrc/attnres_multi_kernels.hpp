@@ -72,15 +72,20 @@ struct MultiCols {
 };
 
 // Selected-query read: the bank rows a token's slots select (ids[tok, m0 + m]); -1 for padded slots,
-// dead tokens and ids outside [0, E).
+// dead tokens and ids outside [0, E). An id outside [0, E) read from memory sets the flag word when
+// there is one (an ordinary vector store from the lanes that met it).
 template <int MQ>
 __device__ __forceinline__ void load_sel_ids(const SelArgs& sa, int M, int64_t tok, bool live,
                                              int (&id)[MQ]) {
+  bool bad = false;
 #pragma unroll
   for (int m = 0; m < MQ; ++m) {
-    const int64_t v = (live && m < M) ? sa.ids[tok * sa.K + sa.m0 + m] : -1;
+    const bool read = live && m < M;
+    const int64_t v = read ? sa.ids[tok * sa.K + sa.m0 + m] : -1;
     id[m] = (v >= 0 && v < sa.E) ? static_cast<int>(v) : -1;
+    bad |= read && id[m] < 0;
   }
+  if (bad && sa.id_flag) *sa.id_flag = 1u;
 }
 
 // The query slices of bank rows `id` (zero for id < 0). With R % VEC == 0 a chunk lies wholly

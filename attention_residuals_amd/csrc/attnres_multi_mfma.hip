@@ -186,15 +186,19 @@ void multi_fwd_mfma_kernel(const MfmaFwdArgs a) {
 
     // SEL: the staged row of each slot's query (uniform: the ids are read through the scalar cache)
     int qrow[MQ];
+    bool bad_id = false;
 #pragma unroll
     for (int m = 0; m < MQ; ++m) {
       if constexpr (SEL) {
         const int64_t id = m < a.M ? a.ids[n * a.M + m] : -1;
         qrow[m] = (id >= 0 && id < a.E) ? (int)id : a.E;
+        bad_id |= m < a.M && qrow[m] == a.E;
       } else {
         qrow[m] = m;
       }
     }
+    // an id outside [0, E): one lane sets the flag word (an ordinary vector store)
+    if (SEL && bad_id && tid == 0 && a.id_flag) *a.id_flag = 1u;
 
     // per source: sum t^2 over the key slice and <row, query_m> (queries zero off the slice)
     float ss[4], acc[4][MQ];

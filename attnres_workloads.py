@@ -144,6 +144,21 @@ def multi_inputs(w: Workload, M: int, layout: str = "query_major", device: str =
     return {"queries": queries.to(w.torch_dtype), "dout": dout.to(w.torch_dtype)}
 
 
+def multi_case(S: int, N: int, D: int, R: int, M: int, dtype: str, seed: int,
+               device: str = "cpu"):
+    """A small multi-query case (parity tests): values [S, N, D] with source s ~ N(0,1) sqrt(1+s),
+    queries [M, R] ~ N(0,1) / sqrt(R), query-major dY [M, N, D] ~ N(0,1), drawn in that order from
+    one generator and rounded once to the storage dtype."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    V = torch.empty((S, N, D), dtype=dt, device=device)
+    for s in range(S):
+        V[s].copy_(torch.randn((N, D), generator=g, device=device) * math.sqrt(1.0 + s))
+    Q = (torch.randn((M, R), generator=g, device=device) / math.sqrt(R)).to(dt)
+    G = torch.randn((M, N, D), generator=g, device=device).to(dt)
+    return V, Q, G
+
+
 def selected_inputs(w: Workload, E: int, K: int, device: str = "cpu") -> dict:
     """Inputs of the selected-query read over the workload's sources: ``bank`` [E, R] (scaled like
     the single query), ``ids`` [N, K] int64 uniform over the bank, ``dout`` [N, K, D] standard

@@ -59,6 +59,76 @@ def kernel_source_hash(scope: str = "single") -> str:
 PEAK_VALU_GINSTR = 256 * 4 * 2.4e9 / 4 / 1e9
 
 
+def cpu_info() -> dict:
+    """The host CPU as /proc/cpuinfo names it: model, physical cores (distinct (package, core)
+    pairs) and logical CPUs, plus the CPUs this process may run on."""
+    model, pairs, logical = None, set(), 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            phys = core = None
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "processor":
+                    logical += 1
+                elif k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None:
+                    pairs.add((phys, core))
+                    phys = core = None
+            if phys is not None:
+                pairs.add((phys, core))
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count()
+    return {"cpu_model": model, "physical_cores": len(pairs) or None, "logical_cpus": logical or None,
+            "cpus_available": allowed}
+
+
+def stream_ceiling(streams_fwd, streams_bwd, fwd_bytes, bwd_bytes, reps=10):
+    """The practical ceiling of the step's traffic: attnres_stream_probe moving the forward's and
+    the backward's streams (lists of (inputs, outputs) tensors, rows as the kernels read them)
+    with no arithmetic, timed with HIP events on the current stream (median of `reps` runs of
+    each launch shape; the fastest shape counts). Returns GB/s of the forward, the backward and
+    the whole step at the algorithmic bytes."""
+    import numpy as np
+    import torch
+    from attention_residuals_amd._binding import stream_probe
+    stream = torch.cuda.current_stream()
+    res, shape = {}, {}
+    for name, (ins, outs) in (("fwd", streams_fwd), ("bwd", streams_bwd)):
+        best = None
+        for cpt in (1, 2):
+            for bpc in (1, 2, 4, 8, 16):
+                for _ in range(2):
+                    stream_probe(ins, outs, cpt, bpc)
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(reps)]
+                for a, b in ev:
+                    a.record(stream)
+                    stream_probe(ins, outs, cpt, bpc)
+                    b.record(stream)
+                torch.cuda.synchronize()
+                t = float(np.median([a.elapsed_time(b) for a, b in ev]))
+                if best is None or t < best[0]:
+                    best = (t, cpt, bpc)
+        res[name] = best[0]
+        shape[name] = {"chunks_per_thread": best[1], "blocks_per_cu": best[2]}
+    return {"kind": "attnres_stream_probe: the step's row streams, no arithmetic (fastest of 10 "
+                    "launch shapes)", "shapes": shape,
+            "fwd_ms": round(res["fwd"], 4), "bwd_ms": round(res["bwd"], 4),
+            "fwd_GBps": round(fwd_bytes / (res["fwd"] * 1e-3) / 1e9, 1),
+            "bwd_GBps": round(bwd_bytes / (res["bwd"] * 1e-3) / 1e9, 1),
+            "step_GBps": round((fwd_bytes + bwd_bytes) / ((res["fwd"] + res["bwd"]) * 1e-3) / 1e9, 1)}
+
+
 def load_valu(run_key: str):
     """Committed SQ_INSTS_VALU counts (wave instructions per call of each entry point) of the
     configuration `run_key`, if they were taken on the current sources (all files); else None."""
@@ -73,7 +143,7 @@ def load_valu(run_key: str):
 
 
 def roofline_for(kernel: str, bwd_bytes: int, fwd_bytes: int, bwd_ms: float, fwd_ms: float,
-                 run_key: str, traffic=None) -> dict:
+                 run_key: str, traffic=None, ceiling_gbps=None) -> dict:
     """Roofline object of the backward call (the dominant one). With committed VALU counts for
     this configuration the kernels' VALU busy fraction is known: when it exceeds the HBM fraction
     the call is bound by VALU issue and reported against PEAK_VALU_GINSTR, else against HBM."""
@@ -81,6 +151,10 @@ def roofline_for(kernel: str, bwd_bytes: int, fwd_bytes: int, bwd_ms: float, fwd
     out = {"bound": "hbm", "kernel": kernel, "achieved": round(hbm, 1), "peak": PEAK_HBM_GBPS,
            "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBPS, 4), "traffic": traffic,
            "fwd_achieved": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1)}
+    if ceiling_gbps:
+        # the same backward traffic moved by the stream probe: the practical ceiling
+        out["ceiling"] = ceiling_gbps
+        out["frac_of_ceiling"] = round(hbm / ceiling_gbps, 4)
     v = load_valu(run_key)
     if v is not None:
         valu = v["bwd_call_valu_instr"] / (bwd_ms * 1e-3) / 1e9
@@ -255,12 +329,22 @@ def main() -> int:
             tc += time.perf_counter() - t1
             reps += 1
         cpu = {"value": round(algo * reps / tc / 1e9, 3), "unit": "GB/s",
-               "cores": oracle.threads_used(), "kind": "oracle",
+               "cores": oracle.threads_used(), "kind": "oracle", **cpu_info(),
                "ms_per_step": round(tc * 1e3 / reps, 1),
                "sample": f"{reps} passes over the full workload ({S} sources x {N} tokens x "
                          f"{D}), forward and backward with the dq/dw reduction, FP64, OpenMP "
                          f"over tokens, {tc:.1f} s in total"}
 
+    # the practical ceiling: the same row streams moved with no arithmetic (after the check: the
+    # probe overwrites y and dvalues)
+    # probe overwrites y and dvalues). Not with accumulation: its backward reads and writes the
+    # same dvalues rows, which the probe's disjoint streams cannot express.
+    ceiling = None
+    if not args.accumulate:
+        vs = [x["values"][s] for s in range(S)]
+        ceiling = stream_ceiling((vs, [y]), (vs + [x["dout"]], [dv[s] for s in range(S)]),
+                                 fwd_bytes, bwd_bytes)
+        ceiling["value_frac"] = round(value / ceiling["step_GBps"], 4)
     traffic = None if args.accumulate else load_traffic(w.name, bwd_bytes)
     out = {
         "metric": METRIC,
@@ -284,7 +368,9 @@ def main() -> int:
                    "b200_ms_context": B200_MS.get(w.name)},
         "roofline": roofline_for("attnres_bwd (backward kernel + finaliser)", bwd_bytes, fwd_bytes,
                                  bwd_avg, fwd_avg,
-                                 w.name + ("_accumulate" if args.accumulate else ""), traffic),
+                                 w.name + ("_accumulate" if args.accumulate else ""), traffic,
+                                 ceiling["bwd_GBps"] if ceiling else None),
+        "practical_ceiling": ceiling,
         "cpu_baseline": cpu,
         "parity_check": check,
         "source_hash": kernel_source_hash(),

@@ -224,7 +224,9 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* desc, const attnres_s
  * bank[ids[n, k]] (1 <= K <= 16) of an [E, R] bank; outputs are token-major y [N, K, D] and lse
  * [N, K]. The backward returns dvalues (summed over the K reads) and dbank [E, R]: for every bank
  * row e, the sum of the query gradients of all (n, k) with ids[n, k] = e. ids are int64 on the
- * device; an id outside [0, E) reads a zero query and its bank gradient is dropped. Token-resident
+ * device; an id outside [0, E) reads a zero query and its bank gradient is dropped, and the
+ * forward, when given its workspace, then sets the workspace's id flag (see
+ * attnres_selected_ids_flag). Token-resident
  * with one or two chunks per thread (D <= 8192 bf16 / 4096 f32). The forward of 3 <= K <= 16 bf16
  * slots over 2 <= S <= 16 sources with D <= 4096 runs in one pass on matrix cores when the bank
  * (E + 1 rows of D bf16) fits in a workgroup's LDS (the optional forward workspace holds the token
@@ -249,11 +251,23 @@ attnres_status attnres_selected_fwd_workspace_bytes(const attnres_selected_desc*
 attnres_status attnres_selected_workspace_bytes(const attnres_selected_desc* desc, size_t* bytes);
 
 /* Forward. bank [E, R]; ids [N, K] int64 (device); y [N, K, D] and lse [N, K] FP32 (written);
- * workspace optional as for attnres_fwd. */
+ * workspace optional as for attnres_fwd. With a workspace, the 32-bit word at byte offset 192 is
+ * the id flag: any id outside [0, E) that the call reads sets it to 1 (an ordinary store from the
+ * kernel). No kernel clears it: it stays set over later calls until the caller clears it
+ * (attnres_selected_ids_flag with clear = 1, or a zeroed workspace). */
 attnres_status attnres_selected_fwd(const attnres_selected_desc* desc,
                                     const attnres_sources* values, const void* bank,
                                     const int64_t* ids, void* y, float* lse, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/* The id flag of a selected-query forward workspace (device memory, workspace_bytes as given to
+ * the forward): *flag = 1 if a forward that used this workspace met an id outside [0, E) since it
+ * was last cleared, else 0. clear = 1 zeroes the flag afterwards. Runs on `stream` after the work
+ * already queued there and waits for it (a device-to-host copy and a stream synchronisation), so
+ * it is not for use under graph capture. ATTNRES_ERR_WORKSPACE for a NULL, short or misaligned
+ * workspace; ATTNRES_ERR_HIP if the copy fails. */
+attnres_status attnres_selected_ids_flag(const void* workspace, size_t workspace_bytes,
+                                         int32_t clear, int32_t* flag, void* stream);
 
 /* Backward. dout [N, K, D] (contiguous); dbank [E, R] (written). */
 attnres_status attnres_selected_bwd(const attnres_selected_desc* desc,
@@ -261,6 +275,23 @@ attnres_status attnres_selected_bwd(const attnres_selected_desc* desc,
                                     const int64_t* ids, const float* lse, const void* dout,
                                     const attnres_sources* dvalues, void* dbank, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- measurement aid
+ * Not part of the AttnRes computation: streams n_rows rows of row_bytes bytes (a multiple of 16)
+ * from each of the n_in input streams to each of the n_out output streams (1 .. 128 each; host
+ * arrays of device pointers, rows contiguous, 16-byte aligned): output j (1 <= j < n_in) receives a
+ * copy of input j, output 0 and outputs j >= n_in the bitwise XOR of all inputs. Outputs must not
+ * overlap inputs
+ * (ATTNRES_ERR_INVALID_ARG). Timed beside a read's kernels with the same streams (for example
+ * S + 1 inputs and S outputs for the single-query backward), it gives the rate the device reaches
+ * on that traffic pattern with no arithmetic: the practical ceiling the kernels are measured
+ * against besides the 8 TB/s peak. Launch shape: chunks_per_thread (1, 2 or 4 16-byte chunks per
+ * thread and step, their loads in flight together) and blocks_per_cu (1 .. 64 blocks of 256
+ * threads per CU); callers try several and keep the fastest. Asynchronous on `stream`. */
+attnres_status attnres_stream_probe(const void* const* in_rows, int32_t n_in,
+                                    void* const* out_rows, int32_t n_out, int64_t n_rows,
+                                    int64_t row_bytes, int32_t chunks_per_thread,
+                                    int32_t blocks_per_cu, void* stream);
 
 /* Static text for a status code. */
 const char* attnres_status_str(attnres_status status);

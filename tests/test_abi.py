@@ -234,3 +234,42 @@ def _selected_status(**kw):
 def test_selected_descriptor_validation(kw, expect):
     st = _selected_status(**kw)
     assert st == expect, (kw, st, A.load().attnres_last_error())
+
+
+@host_only
+def test_device_errors_are_reported_as_hip_status():
+    # a call that passes every argument check and then fails in the HIP runtime (no device here)
+    # returns ATTNRES_ERR_HIP with the runtime's error in the thread's last-error text; the
+    # argument checks before it return their own codes
+    lib = A.load()
+    flag = ctypes.c_int32(7)
+    assert lib.attnres_selected_ids_flag(None, 256, 0, ctypes.byref(flag), None) == WORKSPACE
+    assert lib.attnres_selected_ids_flag(0x20000000, 128, 0, ctypes.byref(flag), None) == WORKSPACE
+    assert lib.attnres_selected_ids_flag(0x20000010, 256, 0, ctypes.byref(flag), None) == WORKSPACE
+    assert lib.attnres_selected_ids_flag(0x20000000, 256, 0, None, None) == INVALID
+    st = lib.attnres_selected_ids_flag(0x20000000, 256, 1, ctypes.byref(flag), None)
+    assert st == HIP, (st, lib.attnres_last_error())
+    msg = lib.attnres_last_error().decode()
+    assert "id flag" in msg and msg.strip(), msg
+    assert flag.value == 7                                # untouched on failure
+
+
+@host_only
+def test_stream_probe_argument_checks():
+    lib = A.load()
+
+    def arr(*p):
+        return (ctypes.c_void_p * len(p))(*p)
+    ins, outs = arr(0x100000, 0x200000), arr(0x300000)
+
+    def call(i=ins, ni=2, o=outs, no=1, rows=16, rb=256, cpt=1, bpc=8):
+        return lib.attnres_stream_probe(i, ni, o, no, rows, rb, cpt, bpc, None)
+    assert call(i=None) == INVALID
+    assert call(ni=0) == INVALID
+    assert call(no=129) == INVALID
+    assert call(rb=100) == INVALID                                   # not 16-byte rows
+    assert call(cpt=3) == INVALID
+    assert call(bpc=0) == INVALID
+    assert call(i=arr(0x100008, 0x200000)) == ALIGN
+    assert call(o=arr(0x100000 + 256)) == INVALID                    # output overlaps an input
+    assert call(rows=0) == OK                                        # no rows: nothing to do

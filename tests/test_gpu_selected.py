@@ -130,6 +130,30 @@ def test_selected_ids_outside_the_bank_read_a_zero_query():
     _check(V, bank, ids, G, "selected invalid ids", "bf16", ref_bank=ext, ref_ids=ref_ids)
 
 
+@pytest.mark.parametrize("K", [2, 3])  # the query-group forward and the matrix-core forward
+def test_selected_ids_outside_the_bank_set_the_workspace_flag(K):
+    # a forward given its workspace flags an id outside [0, E) in the workspace's flag word; the
+    # flag stays set over a later clean call and is cleared on request
+    import attention_residuals_amd as A
+    S, N, D, R, E = 6, 211, 1024, 1024, 5
+    print(f"[case] selected id flag K={K}", flush=True)
+    V, bank, ids, _ = (t.cuda() for t in _inputs(S, N, D, R, E, K, "bf16", seed=3150 + K))
+    desc = A.make_selected_desc(S, N, D, R, E, K, torch.bfloat16)
+    ws = torch.zeros((A.selected_fwd_workspace_bytes(desc),), dtype=torch.uint8, device="cuda")
+    A.attnres_selected_fwd(V, bank, ids, workspace=ws)
+    assert not A.attnres_selected_ids_flag(ws)
+    bad = ids.clone()
+    bad[N // 2, K - 1] = E
+    A.attnres_selected_fwd(V, bank, bad, workspace=ws)
+    assert A.attnres_selected_ids_flag(ws)
+    A.attnres_selected_fwd(V, bank, ids, workspace=ws)      # sticky over a clean call
+    assert A.attnres_selected_ids_flag(ws, clear=True)
+    assert not A.attnres_selected_ids_flag(ws)
+    bad[N // 2, K - 1] = -3
+    A.attnres_selected_fwd(V, bank, bad, workspace=ws)
+    assert A.attnres_selected_ids_flag(ws)
+
+
 @pytest.mark.parametrize("K,packed", [(2, True), (3, False), (4, True)])
 def test_selected_accumulate_into_dvalues(K, packed):
     S, N, D, R, E = 6, 301, 2048, 2048, 6
