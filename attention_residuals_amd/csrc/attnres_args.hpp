@@ -173,7 +173,10 @@ struct MfmaBwdArgs {
   const void* dout;              // dY rows: query m, token n at (m * g_sm + n * g_sn) elements
   int64_t g_sm, g_sn;
   float* coef;                   // [N][16][16] a_{m,s} per token when the dq kernel forms dq
+                                 //   (selected read: summed per bank row, rows e < E)
   float* part;                   // [grid][M * R] dq partial rows when the kernel sums dq itself
+  const int64_t* ids;            // selected read: [N, M] bank rows of the slots (query = bank)
+  int E;                         //   bank rows (<= 16); ids outside [0, E) read a zero query
 };
 
 // Its dq kernel: partial rows [ranges][M * R] over static token ranges of tpr tokens.

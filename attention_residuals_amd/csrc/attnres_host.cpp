@@ -934,31 +934,30 @@ struct MultiBwdPlan {
 // ranges (about two workgroups per CU). The finaliser adds the partial rows in a fixed order.
 // Rows of D = 256 nt columns (nt = 4, 8, 12 or 16 tiles of 32 columns per wave), R and the row
 // strides multiples of 8 elements. ATTNRES_MULTI_MFMA=0 turns it off.
-attnres_status plan_multi_bwd_mfma(const attnres_multi_desc* m, const MultiShape& ms,
-                                   int64_t row_stride, int64_t drow_stride, MultiBwdPlan* pl) {
+// The plan of the per-token matrix-core backward for M queries (or slots) of rows D = 256 nt, the
+// queries staged as M rows (sel: E bank rows, the dq kernel forming dbank). No plan (mfma false)
+// when the shape or the LDS does not fit.
+attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_t N, bool acc,
+                             int64_t row_stride, int64_t drow_stride, MultiBwdPlan* pl) {
   pl->mfma = false;
   const char* e = std::getenv("ATTNRES_MULTI_MFMA");
   if (e && e[0] == '0') return ATTNRES_OK;
-  const int nt = m->D / 256;
-  // up to four queries with S <= 12 (and D <= 4096) are one launch of the query-group kernel,
-  // which measured faster there (M = 3, 4 at S = 10, N = 32768, D = 4096: 1.42 / 1.69 ms against
-  // 1.85 / 1.90 ms); it rounds dvalues once as well
-  if (m->M <= 4 && m->S <= 12) return ATTNRES_OK;
-  if (!ms.base.bf16 || m->S < 2 || m->S > 16 || m->M < 3 || m->M > 16 || m->D % 256 != 0 ||
-      (nt != 4 && nt != 8 && nt != 12 && nt != 16) || m->R % 8 != 0 || row_stride % 8 != 0 ||
-      drow_stride % 8 != 0)
+  const int nt = D / 256;
+  if (S < 2 || S > 16 || M < 3 || M > 16 || D % 256 != 0 ||
+      (nt != 4 && nt != 8 && nt != 12 && nt != 16) || R % 8 != 0 || row_stride % 8 != 0 ||
+      drow_stride % 8 != 0 || (sel && (E < 1 || E > 16)))
     return ATTNRES_OK;
-  const int dqm = m->M <= 4 ? 1 : 0;
+  const int dqm = (!sel && M <= 4) ? 1 : 0;
   DevFacts f;
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
-  const size_t lds = multi_bwd_mfma_lds(nt, dqm, m->M);
+  const size_t lds = multi_bwd_mfma_lds(nt, dqm, M, sel, E);
   if (lds > (size_t)f.lds_per_block) return ATTNRES_OK;
-  const void* fn = multi_bwd_mfma_kernel_ptr(nt, dqm, m->R == m->D, m->accumulate_dvalues != 0);
+  const void* fn = multi_bwd_mfma_kernel_ptr(nt, dqm, R == D, acc, sel);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query backward kernel");
   int per_cu = 0;
   if ((st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu)) != ATTNRES_OK) return st;
-  const int64_t N = m->N;
+  const int rows = sel ? E : M;  // rows of the reduced gradient (dq or dbank)
   pl->mfma = true;
   pl->nt = nt;
   pl->dqm = dqm;
@@ -967,11 +966,11 @@ attnres_status plan_multi_bwd_mfma(const attnres_multi_desc* m, const MultiShape
   if (dqm != 0) {
     pl->P = pl->grid;
     pl->off_part = 256;
-    pl->bytes = align256(pl->off_part + (size_t)pl->P * m->M * m->R * sizeof(float));
+    pl->bytes = align256(pl->off_part + (size_t)pl->P * rows * R * sizeof(float));
     return ATTNRES_OK;
   }
-  pl->chunk0 = (m->D - m->R) / 8;
-  const int key_chunks = m->D / 8 - pl->chunk0;
+  pl->chunk0 = (D - R) / 8;
+  const int key_chunks = D / 8 - pl->chunk0;
   pl->tiles = (key_chunks + 16 * kMfmaWaves - 1) / (16 * kMfmaWaves);
   const int64_t want = std::max<int64_t>(1, (2 * (int64_t)f.cus + pl->tiles - 1) / pl->tiles);
   pl->tpr = N > 0 ? (N + std::min<int64_t>(N, want) - 1) / std::min<int64_t>(N, want) : 1;
@@ -979,8 +978,47 @@ attnres_status plan_multi_bwd_mfma(const attnres_multi_desc* m, const MultiShape
   pl->P = pl->ranges;
   pl->off_coef = 256;
   pl->off_part = align256(pl->off_coef + (size_t)N * 256 * sizeof(float));
-  pl->bytes = align256(pl->off_part + (size_t)pl->ranges * m->M * m->R * sizeof(float));
+  pl->bytes = align256(pl->off_part + (size_t)pl->ranges * rows * R * sizeof(float));
   return ATTNRES_OK;
+}
+
+attnres_status plan_multi_bwd_mfma(const attnres_multi_desc* m, const MultiShape& ms,
+                                   int64_t row_stride, int64_t drow_stride, MultiBwdPlan* pl) {
+  pl->mfma = false;
+  // up to four queries with S <= 12 (and D <= 4096) are one launch of the query-group kernel,
+  // which measured faster there (M = 3, 4 at S = 10, N = 32768, D = 4096: 1.42 / 1.69 ms against
+  // 1.85 / 1.90 ms); it rounds dvalues once as well
+  if (!ms.base.bf16 || (m->M <= 4 && m->S <= 12)) return ATTNRES_OK;
+  return plan_mfma_bwd(m->S, m->D, m->R, m->M, false, 0, m->N, m->accumulate_dvalues != 0,
+                       row_stride, drow_stride, pl);
+}
+
+// Launches the per-token matrix-core backward and, when it does not sum dq itself, the dq kernel;
+// `b` carries the call's rows, queries and gradients. The finaliser is the caller's.
+attnres_status launch_mfma_bwd(const MultiBwdPlan& pl, MfmaBwdArgs& b, bool sel, bool acc,
+                               char* ws, void* stream) {
+  if (pl.dqm == 0) b.coef = reinterpret_cast<float*>(ws + pl.off_coef);
+  else b.part = reinterpret_cast<float*>(ws + pl.off_part);
+  const void* fn = multi_bwd_mfma_kernel_ptr(pl.nt, pl.dqm, b.R == b.D, acc, sel);
+  attnres_status st = launch(fn, pl.grid, 1, 64 * kMfmaWaves, pl.lds, &b, stream,
+                             "matrix-core multi-query backward launch");
+  if (st != ATTNRES_OK || pl.dqm != 0) return st;
+  MfmaDqArgs q;
+  std::memset(&q, 0, sizeof q);
+  for (int s = 0; s < b.S; ++s) q.src[s] = b.src[s];
+  q.row_stride = b.row_stride;
+  q.N = b.N;
+  q.S = b.S;
+  q.D = b.D;
+  q.R = b.R;
+  q.lo = b.lo;
+  q.M = sel ? b.E : b.M;
+  q.chunk0 = pl.chunk0;
+  q.tpr = pl.tpr;
+  q.coef = b.coef;
+  q.part = reinterpret_cast<float*>(ws + pl.off_part);
+  return launch(multi_dq_mfma_kernel_ptr(), pl.tiles, pl.ranges, 64 * kMfmaWaves, 0, &q, stream,
+                "matrix-core multi-query dq launch");
 }
 
 // The backward's plan for rows with the given strides (in elements); mfma_ok = false (or rows
@@ -1213,32 +1251,8 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* m, const attnres_sour
     b.dout = dout;
     b.g_sm = g_sm;
     b.g_sn = g_sn;
-    if (pl.dqm == 0) b.coef = reinterpret_cast<float*>(ws + pl.off_coef);
-    else b.part = reinterpret_cast<float*>(ws + pl.off_part);
-    const void* fn =
-        multi_bwd_mfma_kernel_ptr(pl.nt, pl.dqm, m->R == m->D, m->accumulate_dvalues != 0);
-    st = launch(fn, pl.grid, 1, 64 * kMfmaWaves, pl.lds, &b, stream,
-                "matrix-core multi-query backward launch");
+    st = launch_mfma_bwd(pl, b, false, m->accumulate_dvalues != 0, ws, stream);
     if (st != ATTNRES_OK) return st;
-    if (pl.dqm == 0) {
-      MfmaDqArgs q;
-      std::memset(&q, 0, sizeof q);
-      for (int s = 0; s < m->S; ++s) q.src[s] = a.src[s];
-      q.row_stride = values->row_stride;
-      q.N = N;
-      q.S = m->S;
-      q.D = m->D;
-      q.R = m->R;
-      q.lo = m->D - m->R;
-      q.M = m->M;
-      q.chunk0 = pl.chunk0;
-      q.tpr = pl.tpr;
-      q.coef = b.coef;
-      q.part = reinterpret_cast<float*>(ws + pl.off_part);
-      st = launch(multi_dq_mfma_kernel_ptr(), pl.tiles, pl.ranges, 64 * kMfmaWaves, 0, &q, stream,
-                  "matrix-core multi-query dq launch");
-      if (st != ATTNRES_OK) return st;
-    }
   } else if (pl.P > 0 && !pl.mfma) {
     int64_t g_sm, g_sn, l_sm, l_sn;
     multi_strides(m, &g_sm, &g_sn, &l_sm, &l_sn);
@@ -1430,6 +1444,15 @@ attnres_status attnres_selected_workspace_bytes(const attnres_selected_desc* d, 
   SelBwdPlan pl;
   if ((st = plan_sel_bwd(d, ms, &pl)) != ATTNRES_OK) return st;
   *bytes = pl.bytes;
+  // or the matrix-core backward's, when it may serve the call (dense rows assumed here)
+  if (ms.base.bf16 && d->K >= 3 && d->N > 0) {
+    MultiBwdPlan mp;
+    if (plan_mfma_bwd(d->S, d->D, d->R, d->K, true, d->E, d->N, d->accumulate_dvalues != 0, d->D,
+                      d->D, &mp) == ATTNRES_OK &&
+        mp.mfma)
+      *bytes = std::max(*bytes, mp.bytes);
+    g_err.clear();
+  }
   return ATTNRES_OK;
 }
 
@@ -1639,12 +1662,65 @@ attnres_status attnres_selected_bwd(const attnres_selected_desc* d, const attnre
   outs.push_back(rows_range(dbank, d->E, d->R, d->R, ms.base.esz, "dbank"));
   if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
 
+  char* ws = static_cast<char*>(workspace);
+  // three or more bf16 slots: one pass on matrix cores when the shape and the bank fit (dvalues
+  // rounded once; the query-group kernels take slots in pairs)
+  MultiBwdPlan mp;
+  if (N > 0 && ms.base.bf16 && K >= 3 && aligned(bank, 16)) {
+    st = plan_mfma_bwd(d->S, d->D, d->R, (int)K, true, d->E, N, d->accumulate_dvalues != 0,
+                       values->row_stride, dvalues->row_stride, &mp);
+    if (st != ATTNRES_OK) return st;
+  }
+  if (mp.mfma) {
+    if (workspace_bytes < mp.bytes)
+      return fail(ATTNRES_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                  mp.bytes);
+    MfmaBwdArgs b;
+    std::memset(&b, 0, sizeof b);
+    for (int s = 0; s < d->S; ++s) {
+      b.src[s] = a.src[s];
+      b.dsrc[s] = const_cast<void*>(dptr[s]);
+    }
+    b.row_stride = values->row_stride;
+    b.drow_stride = dvalues->row_stride;
+    b.N = N;
+    b.S = d->S;
+    b.D = d->D;
+    b.R = d->R;
+    b.lo = d->D - d->R;
+    b.M = (int)K;
+    b.eps = d->eps;
+    b.scale = d->scale;
+    b.inv_R = 1.0f / (float)d->R;
+    b.query = bank;
+    b.lse = lse;
+    b.l_sm = 1;
+    b.l_sn = K;
+    b.dout = dout;
+    b.g_sm = d->D;
+    b.g_sn = K * d->D;
+    b.ids = ids;
+    b.E = d->E;
+    if ((st = launch_mfma_bwd(mp, b, true, d->accumulate_dvalues != 0, ws, stream)) != ATTNRES_OK)
+      return st;
+    FinArgs fm;
+    std::memset(&fm, 0, sizeof fm);
+    fm.part_du = reinterpret_cast<const float*>(ws + mp.off_part);
+    fm.P = mp.P;
+    fm.R = d->E * d->R;
+    fm.D = 0;
+    fm.cols = d->E * d->R;
+    fm.query = bank;
+    fm.dq = dbank;
+    return launch(finalize_kernel_ptr(true), (fm.cols + kFinCols - 1) / kFinCols, 1,
+                  kFinCols * kFinPhases, 0, &fm, stream, "finalize launch");
+  }
+
   SelBwdPlan pl;
   if ((st = plan_sel_bwd(d, ms, &pl)) != ATTNRES_OK) return st;
   if (workspace_bytes < pl.bytes)
     return fail(ATTNRES_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
                 pl.bytes);
-  char* ws = static_cast<char*>(workspace);
   if (pl.P > 0) {
     for (int s = 0; s < d->S; ++s) a.dsrc[s] = const_cast<void*>(dptr[s]);
     a.row_stride = values->row_stride;

@@ -131,16 +131,25 @@ constexpr int dq_stride(int nt, int dqm) { return dqm ? kMfmaWaves * nt * 32 + 8
 
 }  // namespace
 
-size_t multi_bwd_mfma_lds(int nt, int dqm, int M) {
+// LDS of the per-token kernel: the dq sums (dqm = 1), the staged queries as four-row groups per
+// column (M rows; selected read: the E bank rows, plus the bank as E + 1 row-major rows, the last
+// zero, and the token's slot ids), the waves' exchange, p and a, and the B partial sums.
+size_t multi_bwd_mfma_lds(int nt, int dqm, int M, bool sel, int E) {
   const size_t D = (size_t)nt * kMfmaWaves * 32;
-  return ((size_t)dq_rows(dqm) * dq_stride(nt, dqm) + (size_t)kMfmaWaves * kXchFloats + 512 + 64) *
-             sizeof(float) +
-         D * ((M + 3) / 4) * 8;
+  const int rows = sel ? E : M;
+  size_t b = ((size_t)dq_rows(dqm) * dq_stride(nt, dqm) + (size_t)kMfmaWaves * kXchFloats + 512 +
+              64) * sizeof(float) + D * ((rows + 3) / 4) * 8;
+  if (sel) b += (size_t)(E + 1) * D * 2 + 16 * sizeof(int);
+  return b;
 }
 
-template <int NT, bool FULL, bool ACC, int DQM>
+// SEL: the selected-query read. Token n's query m is bank row ids[n, m] (M = slots per token);
+// the score operands come from the bank's row-major copy in LDS, the q term of dv and dq (here
+// dbank) take the token's a_{m,s} summed per bank row. dq is always formed by the dq kernel.
+template <int NT, bool FULL, bool ACC, int DQM, bool SEL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 8)))
 void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
+  static_assert(!SEL || DQM == 0, "the selected read forms dbank in the dq kernel");
   constexpr int W = kMfmaWaves;
   constexpr int D = NT * W * 32;          // the row width this kernel is built for
   constexpr int LAG = NT >= 8 ? 4 : 2;    // the next token's contractions trail its loads
@@ -148,11 +157,14 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   constexpr int DQS = dq_stride(NT, DQM);
   extern __shared__ float lds[];
   float* dql = lds;                                          // [DQR][DQS] dq partial sums
-  const int QG = (a.M + 3) >> 2;                             // query groups of four
+  const int QR = SEL ? a.E : a.M;                            // staged query rows
+  const int QG = (QR + 3) >> 2;                              // in groups of four
   char* qtl = reinterpret_cast<char*>(lds + DQR * DQS);      // [D][QG][4] bf16 queries
   float* xch = lds + DQR * DQS + D * QG * 2;                 // [W][kXchFloats]
   float* pa = xch + W * kXchFloats;                          // p[16][16], a[16][16]
   float* bpart = pa + 512;                                   // [4][16] partial B sums
+  char* bankl = reinterpret_cast<char*>(bpart + 64);         // SEL: [E + 1][D] bf16 bank rows
+  int* sid = reinterpret_cast<int*>(bankl + (SEL ? (size_t)(a.E + 1) * D * 2 : 0));  // [16]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
   const mb_u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -204,7 +216,7 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int m = 4 * grp + 2 * k + e;
-        h[e] = (m < a.M && j >= a.lo)
+        h[e] = (m < QR && j >= a.lo)
                    ? static_cast<const uint16_t*>(a.query)[(int64_t)m * a.R + (j - a.lo)]
                    : 0u;
       }
@@ -212,6 +224,27 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
     }
     *reinterpret_cast<mb_u32x2*>(qtl + (size_t)idx * 8) = mb_u32x2{w2[0], w2[1]};
   }
+  if constexpr (SEL) {
+    // the bank as full-width rows (zero before the key slice), row E zero for ids out of range
+    for (int idx = tid; idx < (a.E + 1) * (D / 8); idx += W * 64) {
+      const int e = idx / (D / 8), j = 8 * (idx - e * (D / 8));
+      mb_u32x4 v = zero4;
+      if (e < a.E && j >= a.lo)
+        v = *reinterpret_cast<const mb_u32x4*>(static_cast<const char*>(a.query) +
+                                                ((int64_t)e * a.R + (j - a.lo)) * 2);
+      *reinterpret_cast<mb_u32x4*>(bankl + ((size_t)e * D + j) * 2) = v;
+    }
+  }
+  // SEL: the staged row of slot c's query for token n (row E, zero, for ids outside [0, E) and
+  // for the lanes of absent slots)
+  auto slot_row = [&](int64_t n) {
+    int r = a.E;
+    if (SEL && qlive) {
+      const int64_t id = a.ids[n * a.M + c];
+      r = (id >= 0 && id < a.E) ? (int)id : a.E;
+    }
+    return r;
+  };
   // lane (g, c), half h of tile t: queries 4g .. 4g+3 at column (w NT + t) 32 + 8(c/4) + 4h + c%4
   const bool qgl = g < QG;
   const char* qtp = qtl + ((size_t)(wave * NT * 32 + 8 * (c >> 2) + (c & 3)) * QG + (qgl ? g : 0)) * 8;
@@ -233,10 +266,17 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   mb_float4 tsc, tdp, tss;
   // scores, dp and sums of squares of tile t (lane (g, c) ends with rows 4g + i, column c); the
   // score operand is query c at the tile's eight columns 8g .. 8g+7, the transpose of its groups
+  int qrow = 0;  // SEL: the bank row slot c reads for the token being contracted
   auto contract = [&](int t) {
-    const mb_u32x2 q0 = tr2(ld_qt(t, 0), ident);
-    const mb_u32x2 q1 = tr2(ld_qt(t, 1), ident);
-    tsc = mfma_k32(mb_u32x4{q0[0], q0[1], q1[0], q1[1]}, V[t], tsc);
+    mb_u32x4 qop;
+    if constexpr (SEL) {
+      qop = *reinterpret_cast<const mb_u32x4*>(bankl + ((size_t)qrow * D + col_w + 32 * t) * 2);
+    } else {
+      const mb_u32x2 q0 = tr2(ld_qt(t, 0), ident);
+      const mb_u32x2 q1 = tr2(ld_qt(t, 1), ident);
+      qop = mb_u32x4{q0[0], q0[1], q1[0], q1[1]};
+    }
+    tsc = mfma_k32(qop, V[t], tsc);
     tdp = mfma_k32(Y[t], V[t], tdp);
     const mb_u32x4 vm = keyok(t) ? V[t] : zero4;
     tss = mfma_k32(vm, vm, tss);
@@ -253,6 +293,7 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   const int pm = tid >> 4, ps = tid & 15;  // (query, source) finished by thread tid < 256
   // the pairs of token n: routing weight, delta, a and the B terms into LDS
   auto pairs = [&](int64_t n, float lse_t) {
+    if (SEL && tid < 16) sid[tid] = qrow;  // lanes 0 .. 15 of wave 0 hold slots 0 .. 15
     if (tid < 256) {
       float sc = 0.f, dpv = 0.f, ss = 0.f;
 #pragma unroll
@@ -270,7 +311,7 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
       const float bt = valid ? -av * scv.rho * scv.rho * sc * a.inv_R : 0.f;
       pa[pm * 16 + ps] = p;
       pa[256 + pm * 16 + ps] = av;
-      if constexpr (DQM == 0) a.coef[n * 256 + tid] = av;
+      if constexpr (DQM == 0 && !SEL) a.coef[n * 256 + tid] = av;
       const float bs = rows4_sum(bt);  // over this wave's four queries
       if (lane < 16) bpart[wave * 16 + ps] = bs;
     }
@@ -283,6 +324,7 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   int64_t n = blockIdx.x;
   {
     const float lse_t = load_lse(n);
+    if constexpr (SEL) qrow = slot_row(n);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       V[t] = ld_v(t, n);
@@ -302,6 +344,7 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
     const bool more = next < a.N;
     const int64_t ln = more ? next : n;  // rows loaded behind this token (unused after the last)
     const float lse_next = more ? load_lse(next) : 0.f;
+    if constexpr (SEL) qrow = slot_row(ln);
 
     // this token's coefficient operands: lane (g, c) pairs p and a of queries 4g .. 4g+3 with
     // source c (hi and lo terms), and B_c
@@ -311,7 +354,22 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         pv[i] = pa[(4 * g + i) * 16 + c];
-        av[i] = pa[256 + (4 * g + i) * 16 + c];
+        av[i] = SEL ? 0.f : pa[256 + (4 * g + i) * 16 + c];
+      }
+      if constexpr (SEL) {
+        // a of bank rows 4g .. 4g+3 with source c: the token's slots summed per bank row, in slot
+        // order; slots reading no bank row (ids out of range) add to none
+        for (int k = 0; k < a.M; ++k) {
+          const int e = sid[k] - 4 * g;
+          const float ak = pa[256 + k * 16 + c];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (e == i && sid[k] < a.E) av[i] += ak;
+        }
+        if (wave == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a.coef[n * 256 + (4 * g + i) * 16 + c] = av[i];
+        }
       }
       mb_u32x2 ph, pl, ah, al;
       split4(pv, ph, pl);
@@ -482,24 +540,34 @@ __global__ __launch_bounds__(512) void multi_dq_mfma_kernel(const MfmaDqArgs a) 
   }
 }
 
-#define ATTNRES_MFMA_BWD_K(NT, DQM)                                                    \
-  (acc ? (full ? (const void*)&multi_bwd_mfma_kernel<NT, true, true, DQM>                     \
-               : (const void*)&multi_bwd_mfma_kernel<NT, false, true, DQM>)                   \
-       : (full ? (const void*)&multi_bwd_mfma_kernel<NT, true, false, DQM>                    \
-               : (const void*)&multi_bwd_mfma_kernel<NT, false, false, DQM>))
+#define ATTNRES_MFMA_BWD_K(NT, DQM, SEL)                                                     \
+  (acc ? (full ? (const void*)&multi_bwd_mfma_kernel<NT, true, true, DQM, SEL>                      \
+               : (const void*)&multi_bwd_mfma_kernel<NT, false, true, DQM, SEL>)                    \
+       : (full ? (const void*)&multi_bwd_mfma_kernel<NT, true, false, DQM, SEL>                     \
+               : (const void*)&multi_bwd_mfma_kernel<NT, false, false, DQM, SEL>))
 
 // nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); dqm = 1: dq summed in LDS (M <= 4),
-// 0: coefficients to the workspace for the dq kernel
-const void* multi_bwd_mfma_kernel_ptr(int nt, int dqm, bool full, bool acc) {
+// 0: coefficients to the workspace for the dq kernel; sel: the selected-query read (dqm = 0)
+const void* multi_bwd_mfma_kernel_ptr(int nt, int dqm, bool full, bool acc, bool sel) {
+  if (sel) {
+    if (dqm != 0) return nullptr;
+    switch (nt) {
+      case 4: return ATTNRES_MFMA_BWD_K(4, 0, true);
+      case 8: return ATTNRES_MFMA_BWD_K(8, 0, true);
+      case 12: return ATTNRES_MFMA_BWD_K(12, 0, true);
+      case 16: return ATTNRES_MFMA_BWD_K(16, 0, true);
+      default: return nullptr;
+    }
+  }
   switch (nt * 4 + dqm) {
-    case 4 * 4 + 1: return ATTNRES_MFMA_BWD_K(4, 1);
-    case 4 * 4 + 0: return ATTNRES_MFMA_BWD_K(4, 0);
-    case 8 * 4 + 1: return ATTNRES_MFMA_BWD_K(8, 1);
-    case 8 * 4 + 0: return ATTNRES_MFMA_BWD_K(8, 0);
-    case 12 * 4 + 1: return ATTNRES_MFMA_BWD_K(12, 1);
-    case 12 * 4 + 0: return ATTNRES_MFMA_BWD_K(12, 0);
-    case 16 * 4 + 1: return ATTNRES_MFMA_BWD_K(16, 1);
-    case 16 * 4 + 0: return ATTNRES_MFMA_BWD_K(16, 0);
+    case 4 * 4 + 1: return ATTNRES_MFMA_BWD_K(4, 1, false);
+    case 4 * 4 + 0: return ATTNRES_MFMA_BWD_K(4, 0, false);
+    case 8 * 4 + 1: return ATTNRES_MFMA_BWD_K(8, 1, false);
+    case 8 * 4 + 0: return ATTNRES_MFMA_BWD_K(8, 0, false);
+    case 12 * 4 + 1: return ATTNRES_MFMA_BWD_K(12, 1, false);
+    case 12 * 4 + 0: return ATTNRES_MFMA_BWD_K(12, 0, false);
+    case 16 * 4 + 1: return ATTNRES_MFMA_BWD_K(16, 1, false);
+    case 16 * 4 + 0: return ATTNRES_MFMA_BWD_K(16, 0, false);
     default: break;
   }
   return nullptr;

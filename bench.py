@@ -559,7 +559,7 @@ def run_selected(args, w) -> int:
                "lse": compare_stat(f64(lse.index_select(0, sel)), ref["lse"]),
                "dvalues": compare_rows(f64(dv.index_select(1, sel)), ref["dvalues"], w.dtype,
                                        roundings=multi_bwd_passes(S, D, K, w.dtype,
-                                                                  selected=True))}
+                                                                  selected=True, R=R, E=E))}
         check = {k: {"metric": v["metric"], "ok": bool(v["ok"])} for k, v in res.items()}
 
     out = {

@@ -216,14 +216,34 @@ def multi_mfma_bwd(S: int, D: int, M: int, dtype: str, R=None, row_stride=None) 
             and R % 8 == 0 and row_stride % 8 == 0)
 
 
+LDS_PER_BLOCK = 160 * 1024  # gfx950
+
+
+def sel_mfma_bwd(S: int, D: int, K: int, E: int, dtype: str, R=None, row_stride=None) -> bool:
+    """True when the selected-query backward runs in one pass on matrix cores: bf16, 3 <= K <= 16,
+    2 <= S <= 16, D in (1024, 2048, 3072, 4096), R and the row stride multiples of 8 elements,
+    E <= 16 and the staged bank (E + 1 row-major rows and the transposed four-row groups) within
+    the workgroup's LDS beside the exchange."""
+    R = D if R is None else R
+    row_stride = D if row_stride is None else row_stride
+    if not (dtype == "bf16" and 3 <= K <= 16 and 2 <= S <= 16 and D in (1024, 2048, 3072, 4096)
+            and R % 8 == 0 and row_stride % 8 == 0 and 1 <= E <= 16):
+        return False
+    lds = (E + 1) * D * 2 + 16 * 4 + -(-E // 4) * D * 8 + (8 * (2 * 256 + 16) + 512 + 64) * 4
+    return lds <= LDS_PER_BLOCK
+
+
 def multi_bwd_groups(S: int, D: int, M: int, dtype: str, selected: bool = False, R=None,
-                     row_stride=None) -> list:
+                     row_stride=None, E=None) -> list:
     """Backward launch groups (first query, count) of the multi- and selected-query reads as the
-    library plans them: one pass on matrix cores where multi_mfma_bwd holds (multi-query read),
-    else up to four queries per launch with one 16-byte chunk per thread (D <= 512 chunks at
-    eight waves) and S <= 12, else two, sized as evenly as possible (larger groups first). Each
-    launch after the first adds into dvalues, rounding the running sum to storage again."""
+    library plans them: one pass on matrix cores where multi_mfma_bwd (multi-query read) or
+    sel_mfma_bwd (selected read, E bank rows) holds, else up to four queries per launch with one
+    16-byte chunk per thread (D <= 512 chunks at eight waves) and S <= 12, else two, sized as evenly
+    as possible (larger groups first). Each launch after the first adds into dvalues, rounding the
+    running sum to storage again."""
     if not selected and multi_mfma_bwd(S, D, M, dtype, R, row_stride):
+        return [(0, M)]
+    if selected and E is not None and sel_mfma_bwd(S, D, M, E, dtype, R, row_stride):
         return [(0, M)]
     per = 4 if (D // (8 if dtype == "bf16" else 4) <= 512 and S <= 12) else 2
     n = -(-M // per)
@@ -236,8 +256,8 @@ def multi_bwd_groups(S: int, D: int, M: int, dtype: str, selected: bool = False,
 
 
 def multi_bwd_passes(S: int, D: int, M: int, dtype: str, selected: bool = False, R=None,
-                     row_stride=None) -> int:
-    return len(multi_bwd_groups(S, D, M, dtype, selected, R, row_stride))
+                     row_stride=None, E=None) -> int:
+    return len(multi_bwd_groups(S, D, M, dtype, selected, R, row_stride, E))
 
 
 def sample_tokens(N: int, k: int, seed: int) -> list:

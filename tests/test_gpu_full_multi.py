@@ -22,8 +22,8 @@ pytestmark = [pytest.mark.gpu,
 HEADLINE = W.ALL[W.HEADLINE]
 
 
-def _groups(w, M, selected):
-    return multi_bwd_passes(w.S, w.D, M, w.dtype, selected)
+def _groups(w, M, selected, E=None):
+    return multi_bwd_passes(w.S, w.D, M, w.dtype, selected, R=w.R, E=E)
 
 
 # M = 2, 4: the query-group kernels (one launch); M = 8: the matrix-core backward and its dq pass
@@ -100,7 +100,7 @@ def test_selected_query_full_size(E, K):
                              ref["y"].reshape(-1, w.D), w.dtype),
            "lse": compare_stat(to_f64(lse.index_select(0, sel)), ref["lse"]),
            "dvalues": compare_rows(to_f64(dv.index_select(1, sel)), ref["dvalues"], w.dtype,
-                                   roundings=_groups(w, K, True))}
+                                   roundings=_groups(w, K, True, E))}
     got_b = to_f64(db)
     for e in range(E):
         if not np.any(red["dbank"][e]):

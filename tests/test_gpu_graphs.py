@@ -167,7 +167,8 @@ def test_selected_query_graph_replay(E, K, deterministic):
         res = {"y": compare_rows(to_f64(y).reshape(-1, D), ref["y"].reshape(-1, D), "bf16"),
                "lse": compare_stat(to_f64(lse), ref["lse"]),
                "dvalues": compare_rows(to_f64(dv), ref["dvalues"], "bf16",
-                                       roundings=multi_bwd_passes(S, D, K, "bf16", selected=True)),
+                                       roundings=multi_bwd_passes(S, D, K, "bf16", selected=True,
+                                                                  E=E)),
                "dbank": compare_vec(to_f64(db), ref["dbank"], "bf16")}
         assert_ok(res, f"selected graph replay E={E} K={K} deterministic={deterministic}")
 

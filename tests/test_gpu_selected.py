@@ -48,9 +48,9 @@ def _run(V, bank, ids, G, dvalues=None, accumulate=False, deterministic=False, d
     return y, lse, dv, db
 
 
-def _bwd_groups(S, D, K, dtype):
+def _bwd_groups(S, D, K, dtype, E=None, R=None):
     """Backward launch groups of the selected-query read (each rounds dvalues to storage)."""
-    return multi_bwd_passes(S, D, K, dtype, selected=True)
+    return multi_bwd_passes(S, D, K, dtype, selected=True, R=R, E=E)
 
 
 def _compare_bank(got, ref, dtype, res):
@@ -77,7 +77,8 @@ def _check(V, bank, ids, G, label, dtype, init=None, ref_bank=None, ref_ids=None
     res = {"y": compare_rows(to_f64(y).reshape(-1, D), ref["y"].reshape(-1, D), dtype),
            "lse": compare_stat(to_f64(lse), ref["lse"]),
            "dvalues": compare_rows(to_f64(dv), ref["dvalues"], dtype,
-                                     roundings=_bwd_groups(S, D, K, dtype))}
+                                     roundings=_bwd_groups(S, D, K, dtype, bank.shape[0],
+                                                           bank.shape[1]))}
     _compare_bank(to_f64(db), ref["dbank"][:bank.shape[0]], dtype, res)
     assert_ok(res, label)
     return y, lse, dv, db
@@ -98,6 +99,10 @@ def _check(V, bank, ids, G, label, dtype, init=None, ref_bank=None, ref_ids=None
     (8, 257, 1024, 1024, 4, 4, "f32"),      # four slots, FP32
     (10, 211, 2048, 2048, 24, 7, "bf16"),   # seven slots: groups of four and three, global blocks
     (6, 149, 2048, 2048, 40, 4, "bf16"),    # a bank too large to stage: the slot-group forward
+    # the one-pass matrix-core backward (3 <= K <= 16 bf16 slots, E <= 16, D = 256 nt)
+    (16, 257, 4096, 4096, 6, 16, "bf16"),   # sixteen slots and sources
+    (5, 300, 3072, 1024, 3, 9, "bf16"),     # twelve column tiles per wave, sliced key
+    (12, 150, 1024, 1024, 16, 5, "bf16"),   # sixteen bank rows
 ])
 def test_selected_parity(S, N, D, R, E, K, dtype):
     print(f"[case] selected S={S} N={N} D={D} R={R} E={E} K={K} {dtype}", flush=True)
