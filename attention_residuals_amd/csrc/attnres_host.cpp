@@ -921,7 +921,7 @@ struct MultiBwdPlan {
   size_t off_part = 256, bytes = 256;
   // one-pass matrix-core backward (bf16, 3 <= M <= 16, 2 <= S <= 16, D <= 4096)
   bool mfma = false;
-  int nt = 0, dqm = 0, grid = 0, tiles = 0, ranges = 0, chunk0 = 0;
+  int nt = 0, dqm = 0, qm = 0, grid = 0, tiles = 0, ranges = 0, chunk0 = 0;
   int64_t tpr = 0;
   size_t lds = 0, off_coef = 0;
 };
@@ -951,9 +951,15 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
   DevFacts f;
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
-  const size_t lds = multi_bwd_mfma_lds(nt, dqm, M, sel, E);
+  // the queries also as full rows where they fit (M <= 8): the score operand without transposes
+  int qm = sel ? 2 : (M <= 8 ? 1 : 0);
+  size_t lds = multi_bwd_mfma_lds(nt, dqm, M, qm, E);
+  if (qm == 1 && lds > (size_t)f.lds_per_block && dqm == 0) {
+    qm = 0;
+    lds = multi_bwd_mfma_lds(nt, dqm, M, qm, E);
+  }
   if (lds > (size_t)f.lds_per_block) return ATTNRES_OK;
-  const void* fn = multi_bwd_mfma_kernel_ptr(nt, dqm, R == D, acc, sel);
+  const void* fn = multi_bwd_mfma_kernel_ptr(nt, dqm, R == D, acc, qm);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query backward kernel");
   int per_cu = 0;
   if ((st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu)) != ATTNRES_OK) return st;
@@ -961,6 +967,7 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
   pl->mfma = true;
   pl->nt = nt;
   pl->dqm = dqm;
+  pl->qm = qm;
   pl->lds = lds;
   pl->grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
   if (dqm != 0) {
@@ -999,7 +1006,7 @@ attnres_status launch_mfma_bwd(const MultiBwdPlan& pl, MfmaBwdArgs& b, bool sel,
                                char* ws, void* stream) {
   if (pl.dqm == 0) b.coef = reinterpret_cast<float*>(ws + pl.off_coef);
   else b.part = reinterpret_cast<float*>(ws + pl.off_part);
-  const void* fn = multi_bwd_mfma_kernel_ptr(pl.nt, pl.dqm, b.R == b.D, acc, sel);
+  const void* fn = multi_bwd_mfma_kernel_ptr(pl.nt, pl.dqm, b.R == b.D, acc, pl.qm);
   attnres_status st = launch(fn, pl.grid, 1, 64 * kMfmaWaves, pl.lds, &b, stream,
                              "matrix-core multi-query backward launch");
   if (st != ATTNRES_OK || pl.dqm != 0) return st;

@@ -67,12 +67,13 @@ inline constexpr int kMfmaWaves = 8;
 const void* multi_fwd_mfma_kernel_ptr(int cgw, int mq, bool full, bool sel);
 size_t multi_fwd_mfma_lds(int cgw, int mq, int qrows);
 // Multi-query backward through matrix cores (8 waves): nt = 32-column tiles per wave (D = 256 nt),
-// dqm = where dq is summed (1: in the kernel's LDS, M <= 4; 0: by the separate dq kernel); sel =
-// the selected-query read (M slots per token, E <= 16 bank rows).
-const void* multi_bwd_mfma_kernel_ptr(int nt, int dqm, bool full, bool acc, bool sel);
+// dqm = where dq is summed (1: in the kernel's LDS, M <= 4; 0: by the separate dq kernel); qm =
+// query staging (0: four-row groups, 1: groups and full rows for M <= 8, 2: the selected-query read
+// with M slots per token over E <= 16 bank rows).
+const void* multi_bwd_mfma_kernel_ptr(int nt, int dqm, bool full, bool acc, int qm);
 const void* multi_dq_mfma_kernel_ptr();
 const void* stream_probe_kernel_ptr(int cpt);
-size_t multi_bwd_mfma_lds(int nt, int dqm, int M, bool sel, int E);
+size_t multi_bwd_mfma_lds(int nt, int dqm, int M, int qm, int E);
 const void* sel_bwd_kernel_ptr_bf16(int ch, int sb, bool full, bool acc, int mq);
 const void* sel_bwd_kernel_ptr_f32(int ch, int sb, bool full, bool acc, int mq);
 const void* ticket_reset_kernel_ptr();

@@ -132,27 +132,33 @@ constexpr int dq_stride(int nt, int dqm) { return dqm ? kMfmaWaves * nt * 32 + 8
 }  // namespace
 
 // LDS of the per-token kernel: the dq sums (dqm = 1), the staged queries as four-row groups per
-// column (M rows; selected read: the E bank rows, plus the bank as E + 1 row-major rows, the last
-// zero, and the token's slot ids), the waves' exchange, p and a, and the B partial sums.
-size_t multi_bwd_mfma_lds(int nt, int dqm, int M, bool sel, int E) {
+// column (M rows; selected read, qm = 2: the E bank rows), with qm >= 1 also as full-width rows
+// plus a zero row and the token's slot ids, the waves' exchange, p and a, and the B partial sums.
+size_t multi_bwd_mfma_lds(int nt, int dqm, int M, int qm, int E) {
   const size_t D = (size_t)nt * kMfmaWaves * 32;
-  const int rows = sel ? E : M;
+  const int rows = qm == 2 ? E : M;
   size_t b = ((size_t)dq_rows(dqm) * dq_stride(nt, dqm) + (size_t)kMfmaWaves * kXchFloats + 512 +
               64) * sizeof(float) + D * ((rows + 3) / 4) * 8;
-  if (sel) b += (size_t)(E + 1) * D * 2 + 16 * sizeof(int);
+  if (qm >= 1) b += (size_t)(rows + 1) * D * 2 + 16 * sizeof(int);
   return b;
 }
 
-// SEL: the selected-query read. Token n's query m is bank row ids[n, m] (M = slots per token);
-// the score operands come from the bank's row-major copy in LDS, the q term of dv and dq (here
-// dbank) take the token's a_{m,s} summed per bank row. dq is always formed by the dq kernel.
-template <int NT, bool FULL, bool ACC, int DQM, bool SEL>
+// QM: how the queries are staged. 0: only as four-row groups per column (the score operand is
+// their transpose); 1: also as M + 1 full-width rows (the last zero), the score operand read
+// directly (M <= 8); 2: the selected-query read: token n's query m is bank row ids[n, m] (M =
+// slots per token), the bank staged both ways (E rows), the q term of dv and dq (here dbank)
+// taking the token's a_{m,s} summed per bank row; dq is formed by the dq kernel.
+template <int NT, bool FULL, bool ACC, int DQM, int QM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 8)))
 void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
+  constexpr bool SEL = QM == 2;
+  constexpr bool QROWS = QM >= 1;
   static_assert(!SEL || DQM == 0, "the selected read forms dbank in the dq kernel");
   constexpr int W = kMfmaWaves;
   constexpr int D = NT * W * 32;          // the row width this kernel is built for
-  constexpr int LAG = NT >= 8 ? 4 : 2;    // the next token's contractions trail its loads
+  // the next token's contractions trail its loads by LAG tiles (2 for the widest rows with the
+  // transposed score operand: its registers, else spilled)
+  constexpr int LAG = NT >= 8 ? (QM == 0 && NT == 16 ? 2 : 4) : 2;
   constexpr int DQR = dq_rows(DQM);
   constexpr int DQS = dq_stride(NT, DQM);
   extern __shared__ float lds[];
@@ -163,8 +169,8 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   float* xch = lds + DQR * DQS + D * QG * 2;                 // [W][kXchFloats]
   float* pa = xch + W * kXchFloats;                          // p[16][16], a[16][16]
   float* bpart = pa + 512;                                   // [4][16] partial B sums
-  char* bankl = reinterpret_cast<char*>(bpart + 64);         // SEL: [E + 1][D] bf16 bank rows
-  int* sid = reinterpret_cast<int*>(bankl + (SEL ? (size_t)(a.E + 1) * D * 2 : 0));  // [16]
+  char* bankl = reinterpret_cast<char*>(bpart + 64);         // QROWS: [QR + 1][D] bf16 rows
+  int* sid = reinterpret_cast<int*>(bankl + (QROWS ? (size_t)(QR + 1) * D * 2 : 0));  // [16]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
   const mb_u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -224,24 +230,29 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
     }
     *reinterpret_cast<mb_u32x2*>(qtl + (size_t)idx * 8) = mb_u32x2{w2[0], w2[1]};
   }
-  if constexpr (SEL) {
-    // the bank as full-width rows (zero before the key slice), row E zero for ids out of range
-    for (int idx = tid; idx < (a.E + 1) * (D / 8); idx += W * 64) {
+  if constexpr (QROWS) {
+    // the queries (the bank) as full-width rows (zero before the key slice); row QR zero, for
+    // absent slots and ids out of range
+    for (int idx = tid; idx < (QR + 1) * (D / 8); idx += W * 64) {
       const int e = idx / (D / 8), j = 8 * (idx - e * (D / 8));
       mb_u32x4 v = zero4;
-      if (e < a.E && j >= a.lo)
+      if (e < QR && j >= a.lo)
         v = *reinterpret_cast<const mb_u32x4*>(static_cast<const char*>(a.query) +
                                                 ((int64_t)e * a.R + (j - a.lo)) * 2);
       *reinterpret_cast<mb_u32x4*>(bankl + ((size_t)e * D + j) * 2) = v;
     }
   }
-  // SEL: the staged row of slot c's query for token n (row E, zero, for ids outside [0, E) and
-  // for the lanes of absent slots)
+  // QROWS: the staged row of query (slot) c for token n: c itself, or the bank row its id names
+  // (row QR, zero, for ids outside [0, E) and for the lanes of absent queries)
   auto slot_row = [&](int64_t n) {
-    int r = a.E;
-    if (SEL && qlive) {
-      const int64_t id = a.ids[n * a.M + c];
-      r = (id >= 0 && id < a.E) ? (int)id : a.E;
+    int r = QR;
+    if (qlive) {
+      if constexpr (SEL) {
+        const int64_t id = a.ids[n * a.M + c];
+        r = (id >= 0 && id < a.E) ? (int)id : a.E;
+      } else {
+        r = c;
+      }
     }
     return r;
   };
@@ -253,9 +264,10 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
     return qgl ? x : mb_u32x2{0u, 0u};
   };
 
-  // identity B operand of the transposes: lane (g, c) holds I[4g + i][c]
-  mb_u32x2 ident = {0u, 0u};
-  if ((c >> 2) == g) ident[(c >> 1) & 1] = (c & 1) ? 0x3F800000u : 0x00003F80u;
+  // identity B operand of the transposes: lane (g, c) holds I[4g + i][c] (bf16 1.0 in slot c % 4
+  // when c / 4 == g)
+  const uint32_t one_bf = ((c >> 2) == g) ? ((c & 1) ? 0x3F800000u : 0x00003F80u) : 0u;
+  const mb_u32x2 ident = {(c & 2) ? 0u : one_bf, (c & 2) ? one_bf : 0u};
 
   if constexpr (DQM != 0) {
     for (int i = tid; i < DQR * DQS; i += W * 64) dql[i] = 0.f;
@@ -266,10 +278,10 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   mb_float4 tsc, tdp, tss;
   // scores, dp and sums of squares of tile t (lane (g, c) ends with rows 4g + i, column c); the
   // score operand is query c at the tile's eight columns 8g .. 8g+7, the transpose of its groups
-  int qrow = 0;  // SEL: the bank row slot c reads for the token being contracted
+  int qrow = 0;  // QROWS: the staged row query (slot) c reads for the token being contracted
   auto contract = [&](int t) {
     mb_u32x4 qop;
-    if constexpr (SEL) {
+    if constexpr (QROWS) {
       qop = *reinterpret_cast<const mb_u32x4*>(bankl + ((size_t)qrow * D + col_w + 32 * t) * 2);
     } else {
       const mb_u32x2 q0 = tr2(ld_qt(t, 0), ident);
@@ -325,6 +337,7 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   {
     const float lse_t = load_lse(n);
     if constexpr (SEL) qrow = slot_row(n);
+    else if constexpr (QROWS) qrow = qlive ? c : QR;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       V[t] = ld_v(t, n);
@@ -344,7 +357,7 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
     const bool more = next < a.N;
     const int64_t ln = more ? next : n;  // rows loaded behind this token (unused after the last)
     const float lse_next = more ? load_lse(next) : 0.f;
-    if constexpr (SEL) qrow = slot_row(ln);
+    if constexpr (SEL) qrow = slot_row(ln);  // (fixed per lane for the multi-query read)
 
     // this token's coefficient operands: lane (g, c) pairs p and a of queries 4g .. 4g+3 with
     // source c (hi and lo terms), and B_c
@@ -540,34 +553,28 @@ __global__ __launch_bounds__(512) void multi_dq_mfma_kernel(const MfmaDqArgs a) 
   }
 }
 
-#define ATTNRES_MFMA_BWD_K(NT, DQM, SEL)                                                     \
-  (acc ? (full ? (const void*)&multi_bwd_mfma_kernel<NT, true, true, DQM, SEL>                      \
-               : (const void*)&multi_bwd_mfma_kernel<NT, false, true, DQM, SEL>)                    \
-       : (full ? (const void*)&multi_bwd_mfma_kernel<NT, true, false, DQM, SEL>                     \
-               : (const void*)&multi_bwd_mfma_kernel<NT, false, false, DQM, SEL>))
+#define ATTNRES_MFMA_BWD_K(NT, DQM, QM)                                                       \
+  (acc ? (full ? (const void*)&multi_bwd_mfma_kernel<NT, true, true, DQM, QM>                       \
+               : (const void*)&multi_bwd_mfma_kernel<NT, false, true, DQM, QM>)                     \
+       : (full ? (const void*)&multi_bwd_mfma_kernel<NT, true, false, DQM, QM>                      \
+               : (const void*)&multi_bwd_mfma_kernel<NT, false, false, DQM, QM>))
 
-// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); dqm = 1: dq summed in LDS (M <= 4),
-// 0: coefficients to the workspace for the dq kernel; sel: the selected-query read (dqm = 0)
-const void* multi_bwd_mfma_kernel_ptr(int nt, int dqm, bool full, bool acc, bool sel) {
-  if (sel) {
-    if (dqm != 0) return nullptr;
-    switch (nt) {
-      case 4: return ATTNRES_MFMA_BWD_K(4, 0, true);
-      case 8: return ATTNRES_MFMA_BWD_K(8, 0, true);
-      case 12: return ATTNRES_MFMA_BWD_K(12, 0, true);
-      case 16: return ATTNRES_MFMA_BWD_K(16, 0, true);
-      default: return nullptr;
+#define ATTNRES_MFMA_BWD_NT(NT)                                                                   \
+  case NT:                                                                                        \
+    switch (dqm * 4 + qm) {                                                                       \
+      case 1 * 4 + 1: return ATTNRES_MFMA_BWD_K(NT, 1, 1);                                       \
+      case 0 * 4 + 1: return ATTNRES_MFMA_BWD_K(NT, 0, 1);                                       \
+      case 0 * 4 + 0: return ATTNRES_MFMA_BWD_K(NT, 0, 0);                                       \
+      case 0 * 4 + 2: return ATTNRES_MFMA_BWD_K(NT, 0, 2);                                       \
+      default: return nullptr;                                                                    \
     }
-  }
-  switch (nt * 4 + dqm) {
-    case 4 * 4 + 1: return ATTNRES_MFMA_BWD_K(4, 1, false);
-    case 4 * 4 + 0: return ATTNRES_MFMA_BWD_K(4, 0, false);
-    case 8 * 4 + 1: return ATTNRES_MFMA_BWD_K(8, 1, false);
-    case 8 * 4 + 0: return ATTNRES_MFMA_BWD_K(8, 0, false);
-    case 12 * 4 + 1: return ATTNRES_MFMA_BWD_K(12, 1, false);
-    case 12 * 4 + 0: return ATTNRES_MFMA_BWD_K(12, 0, false);
-    case 16 * 4 + 1: return ATTNRES_MFMA_BWD_K(16, 1, false);
-    case 16 * 4 + 0: return ATTNRES_MFMA_BWD_K(16, 0, false);
+
+// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); dqm = 1: dq summed in LDS (M <= 4,
+// with qm = 1), 0: coefficients to the workspace for the dq kernel; qm = query staging (0: groups
+// only, 1: groups and rows, M <= 8; 2: the selected read)
+const void* multi_bwd_mfma_kernel_ptr(int nt, int dqm, bool full, bool acc, int qm) {
+  switch (nt) {
+    ATTNRES_MFMA_BWD_NT(4) ATTNRES_MFMA_BWD_NT(8) ATTNRES_MFMA_BWD_NT(12) ATTNRES_MFMA_BWD_NT(16)
     default: break;
   }
   return nullptr;
