@@ -68,15 +68,19 @@ typedef struct {
                               workgroups finish (faster). The token-resident backward adds each
                               batch's q/w gradient into exact FP64 bins (a multiple of 2^-20 and
                               a remainder rounded to 2^-53, each summed exactly while per-batch
-                              contributions stay below 2^31 in magnitude and a call has fewer than
-                              2^21 tokens per workgroup), so the sums do not depend on which
+                              contributions stay below 2^31 in magnitude, a workgroup's 2^-20 bin
+                              below 2^33 and it bins fewer than 2^20 batches; data outside these
+                              bounds loses the guarantee), so the sums do not depend on which
                               workgroup took which batch; the streaming backward gives each
                               workgroup a fixed share and each counter batch of the last quarter
                               its own partial row.
                               1: a static token split (no counter).
                               The two modes may differ from each other in the last bits of
-                              dq/dw/dow. Multi- and selected-query reads: 0 reproduces dq/dbank
-                              to FP32 rounding only; 1 is a static split, bitwise reproducible. */
+                              dq/dw/dow. Multi- and selected-query reads: their one-pass
+                              matrix-core backward (three or more bf16 queries or slots, see
+                              attnres_multi_bwd) always splits statically, bitwise reproducible;
+                              their query-group kernels with 0 reproduce dq/dbank to FP32
+                              rounding only, with 1 a static split, bitwise reproducible. */
   int32_t accumulate_dvalues; /* backward only. 0: dvalues are overwritten with this read's
                               gradient. 1: the gradient is added to the existing dvalues (read,
                               summed in FP32, rounded once to storage), so a source shared by
@@ -181,9 +185,13 @@ attnres_status attnres_bwd_noalloc(const attnres_desc* desc, const attnres_sourc
  * entry points return ATTNRES_ERR_UNSUPPORTED otherwise; at D = 4096, bf16, S <= 24). The forward of
  * 3 <= M <= 16 bf16 queries over 2 <= S <= 16 sources with D <= 4096 runs in one pass on matrix cores
  * (tokens strided over the grid; with 9 to 16 queries and the optional forward workspace they come
- * from its counter instead; outputs are the same either way, bit for bit); otherwise, and
- * always in the backward, queries run in groups of at most four, each group reading the sources
- * again (later backward groups add into dvalues).
+ * from its counter instead; outputs are the same either way, bit for bit); otherwise queries run
+ * in groups of at most four, each group reading the sources again. The backward of 3 <= M <= 16
+ * bf16 queries over 2 <= S <= 16 sources with D = 1024, 2048, 3072 or 4096, R and the row strides
+ * multiples of 8 and 16-byte aligned queries, runs in one pass on matrix cores (dvalues written and
+ * rounded once; a second pass over the key slice forms dq unless M <= 4), except M <= 4 with
+ * S <= 12, which is one launch of the query-group kernel; otherwise backward groups after the first
+ * add into dvalues. ATTNRES_MULTI_MFMA=0 (read once) turns the matrix-core kernels off.
  * Layout of y, dout [.., D] and lse: ATTNRES_QUERY_MAJOR = [M, N] rows (the page's default),
  * ATTNRES_TOKEN_MAJOR = [N, M] rows (the page's output_layout="token_major"). */
 typedef enum { ATTNRES_QUERY_MAJOR = 0, ATTNRES_TOKEN_MAJOR = 1 } attnres_layout;
@@ -202,8 +210,9 @@ typedef struct {
 /* Bytes of the optional forward workspace (a token counter): 256. */
 attnres_status attnres_multi_fwd_workspace_bytes(const attnres_multi_desc* desc, size_t* bytes);
 
-/* Bytes of the backward workspace (a token counter and FP32 partial dq rows). No initialisation
- * needed. */
+/* Bytes of the backward workspace (counter words, per-token coefficients and FP32 partial dq
+ * rows), enough for either backward kernel. Its first 256 bytes must be zero when the workspace is
+ * first used; the calls leave them zero. */
 attnres_status attnres_multi_workspace_bytes(const attnres_multi_desc* desc, size_t* bytes);
 
 /* Forward. queries [M, R] contiguous; y [M, N, D] or [N, M, D] contiguous (layout); lse [M, N] or
@@ -230,11 +239,15 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* desc, const attnres_s
  * with one or two chunks per thread (D <= 8192 bf16 / 4096 f32). The forward of 3 <= K <= 16 bf16
  * slots over 2 <= S <= 16 sources with D <= 4096 runs in one pass on matrix cores when the bank
  * (E + 1 rows of D bf16) fits in a workgroup's LDS (the optional forward workspace holds the token
- * counter of 9 to 16 slots, as in the multi-query read); otherwise, and in the backward, slots run
- * in groups of at most four.
+ * counter of 9 to 16 slots, as in the multi-query read); otherwise slots run in groups of at most
+ * four. The backward of 3 <= K <= 16 bf16 slots runs in one pass on matrix cores under the
+ * multi-query read's conditions when E <= 16 and the bank fits in a workgroup's LDS (as E + 1 rows
+ * and as transposed groups of four: E <= 8 at D = 4096), dbank formed by a second pass over the key
+ * slice; otherwise in slot groups (later groups add into dvalues).
  * The bank gradient goes through per-workgroup FP32 partial rows of the whole bank (the workspace
- * is 256 + P * E * R * 4 bytes, P = backward workgroups), so a large bank costs workspace and
- * traffic; E * R * 4 must stay below 2 GiB (else ATTNRES_ERR_UNSUPPORTED). */
+ * is 256 + P * E * R * 4 bytes, P = backward workgroups, or the matrix-core backward's
+ * coefficients and partial rows), so a large bank costs workspace and traffic; E * R * 4 must stay
+ * below 2 GiB (else ATTNRES_ERR_UNSUPPORTED). */
 typedef struct {
   int32_t S, D, R;
   int32_t E;               /* bank rows, >= 1 */
