@@ -5,8 +5,8 @@
 namespace attnres {
 
 #define ATTNRES_CASE(CH, SB) \
-  case SB: return full ? (const void*)&bwd_resident_kernel<true, CH, SB, true, true> \
-                       : (const void*)&bwd_resident_kernel<true, CH, SB, false, true>;
+  case SB: return full ? (const void*)&bwd_resident_kernel<true, CH, SB, true, true, true> \
+                       : (const void*)&bwd_resident_kernel<true, CH, SB, false, true, true>;
 
 const void* bwd_resident_acc_kernel_ptr_bf16(int ch, int sb, bool full) {
   switch (ch) {

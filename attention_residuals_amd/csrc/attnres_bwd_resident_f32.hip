@@ -5,8 +5,8 @@
 namespace attnres {
 
 #define ATTNRES_CASE(CH, SB) \
-  case SB: return full ? (const void*)&bwd_resident_kernel<false, CH, SB, true, false> \
-                       : (const void*)&bwd_resident_kernel<false, CH, SB, false, false>;
+  case SB: return full ? (const void*)&bwd_resident_kernel<false, CH, SB, true, false, true> \
+                       : (const void*)&bwd_resident_kernel<false, CH, SB, false, false, true>;
 
 const void* bwd_resident_kernel_ptr_f32(int ch, int sb, bool full) {
   switch (ch) {

@@ -48,6 +48,7 @@ inline constexpr int64_t kMaxTicketTokens = int64_t(1) << 31;
 const void* fwd_kernel_ptr_bf16(int ch, int sb, bool full, bool one_block);
 const void* fwd_kernel_ptr_f32(int ch, int sb, bool full, bool one_block);
 const void* bwd_resident_kernel_ptr_bf16(int ch, int sb, bool full);
+const void* bwd_resident_rows_kernel_ptr_bf16(int ch, int sb, bool full);  // FP32 rows, no bins
 const void* bwd_resident_kernel_ptr_f32(int ch, int sb, bool full);
 const void* bwd_resident_acc_kernel_ptr_bf16(int ch, int sb, bool full);
 const void* bwd_resident_acc_kernel_ptr_f32(int ch, int sb, bool full);

@@ -861,7 +861,10 @@ __device__ __forceinline__ void store_bins(const BwdArgs& a, const Cols<BF16, CH
 // are prefetched one token ahead like the source rows and added before the store).
 // Two waves per SIMD: the grid holds two 4-wave workgroups per CU (more measured slower), and the
 // row slab, the exact FP64 bins and the pipelined loads need the registers of that occupancy.
-template <bool BF16, int CH, int SB, bool FULL, bool ACC>
+// BIN: the q/w gradient sums go through exact FP64 bins per batch (the same bits whatever tokens
+// the counter hands out); without it the workgroup keeps one FP32 running sum over all its tokens
+// and writes it as an FP32 row (faster; bitwise reproducible only under a static split).
+template <bool BF16, int CH, int SB, bool FULL, bool ACC, bool BIN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void bwd_resident_kernel(const BwdArgs a) {
   constexpr int VEC = Fmt<BF16>::VEC;
@@ -906,10 +909,12 @@ void bwd_resident_kernel(const BwdArgs a) {
   // exact bins of this workgroup's q/w gradient sums (kBinMagicA/B): whatever tokens the counter
   // hands this workgroup, the merged sums are the same
   double ba[CH][VEC], bb[CH][VEC];
+  if constexpr (BIN) {
 #pragma unroll
-  for (int j = 0; j < CH; ++j)
+    for (int j = 0; j < CH; ++j)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) ba[j][e] = bb[j][e] = 0.0;
+      for (int e = 0; e < VEC; ++e) ba[j][e] = bb[j][e] = 0.0;
+  }
   // lse of the current token; the next one is loaded with the next token's rows (a vector load
   // waited for at its use would otherwise also drain every store issued before it)
   float lse = n0 < a.N ? a.lse[n0] : 0.f;
@@ -1031,7 +1036,9 @@ void bwd_resident_kernel(const BwdArgs a) {
     }
     if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     // a batch is a fixed token set summed in token order, so its FP32 sum is binned once
-    if (last_tok) bin_token<CH, VEC>(du, ba, bb);
+    if constexpr (BIN) {
+      if (last_tok) bin_token<CH, VEC>(du, ba, bb);
+    }
     if (last_tok) {
       b = b_next;
       batch_end = min(next + a.tpt, a.N);
@@ -1039,7 +1046,8 @@ void bwd_resident_kernel(const BwdArgs a) {
     lse = lse_next;
     n = next;
   }
-  store_bins<BF16, CH, FULL>(a, cs, ba, bb, blockIdx.x);
+  if constexpr (BIN) store_bins<BF16, CH, FULL>(a, cs, ba, bb, blockIdx.x);
+  else store_row<BF16, CH, FULL>(a, cs, du, dow, blockIdx.x, false);
 }
 
 // ------------------------------------------------------------------ backward, streaming

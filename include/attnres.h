@@ -62,19 +62,22 @@ typedef struct {
   int32_t has_norm_weight; /* key-norm weight w[R] present */
   int32_t out_norm;        /* output RMSNorm after the mixture */
   int32_t has_out_weight;  /* output-norm weight ow[D] present (requires out_norm) */
-  int32_t deterministic;   /* Backward token schedule. Single-query read: every output is
-                              bitwise reproducible across calls in both modes.
-                              0: tokens go out in batches through a device-wide counter as
-                              workgroups finish (faster). The token-resident backward adds each
-                              batch's q/w gradient into exact FP64 bins (a multiple of 2^-20 and
-                              a remainder rounded to 2^-53, each summed exactly while per-batch
-                              contributions stay below 2^31 in magnitude, a workgroup's 2^-20 bin
-                              below 2^33 and it bins fewer than 2^20 batches; data outside these
-                              bounds loses the guarantee), so the sums do not depend on which
-                              workgroup took which batch; the streaming backward gives each
-                              workgroup a fixed share and each counter batch of the last quarter
-                              its own partial row.
-                              1: a static token split (no counter).
+  int32_t deterministic;   /* Backward reductions. Tokens go out in batches through a
+                              device-wide counter as workgroups finish in both modes (a static
+                              split when N is below twice the workgroup count); y, lse and
+                              dvalues are bitwise reproducible in both.
+                              1: dq/dw/dow bitwise reproducible across calls. The token-resident
+                              backward adds each batch's q/w gradient into exact FP64 bins (a
+                              multiple of 2^-20 and a remainder rounded to 2^-53, each summed
+                              exactly while per-batch contributions stay below 2^31 in magnitude,
+                              a workgroup's 2^-20 bin below 2^33 and it bins fewer than 2^20
+                              batches; data outside these bounds loses the guarantee), so the sums
+                              do not depend on which workgroup took which batch; the streaming
+                              backward gives each workgroup a fixed share and each counter batch
+                              of the last quarter its own partial row.
+                              0 (default): the same, except that the bf16 token-resident backward
+                              without accumulation keeps one FP32 running sum per workgroup (about
+                              1.6% faster), so its dq/dw reproduce to FP32 rounding only.
                               The two modes may differ from each other in the last bits of
                               dq/dw/dow. Multi- and selected-query reads: their one-pass
                               matrix-core backward (three or more bf16 queries or slots, see
@@ -150,7 +153,8 @@ attnres_status attnres_fwd(const attnres_desc* desc, const attnres_sources* valu
  *                   with any concurrent call.
  * Two kernel launches: the backward, then a finaliser that sums each column's partial rows in a
  * fixed order, writes dq, dw and dow and returns the workspace's counters to zero, so repeated
- * calls give bitwise-identical results in both schedules (desc->deterministic). */
+ * calls give bitwise-identical results with desc->deterministic = 1 (dq/dw/dow to FP32 rounding
+ * with 0, every other output bitwise). */
 attnres_status attnres_bwd(const attnres_desc* desc, const attnres_sources* values,
                            const void* query, const void* norm_w, const void* out_w,
                            const float* lse, const float* out_rstd, const float* o32,
