@@ -829,9 +829,57 @@ attnres_status try_mfma_fwd(int S, int D, int R, int M, float eps, float scale, 
   *used = false;
   const char* e = std::getenv("ATTNRES_MULTI_MFMA");
   if (e && e[0] == '0') return ATTNRES_OK;
+  const bool sel = ids != nullptr;
+  // rows of D = 256 nt columns, five or more queries (or the selected read): the forward in the
+  // matrix-core backward's operand layout, two tokens in flight; with three or four queries the
+  // kernel below is as fast (ATTNRES_MULTI_TILE_FWD=0 keeps it for every shape)
+  {
+    static const char* te = std::getenv("ATTNRES_MULTI_TILE_FWD");
+    const int nt = D / 256;
+    const int rows = sel ? E : M;
+    const size_t lds = multi_fwd_tile_lds(nt, rows);
+    bool al = aligned(queries, 16) && aligned(y, 16) && y_sm % 8 == 0 && y_sn % 8 == 0;
+    for (int s = 0; s < S && s < 16; ++s) al = al && aligned(src[s], 16);
+    if (!(te && te[0] == '0') && al && bf16 && S >= 2 && S <= 16 && M >= (sel ? 3 : 5) &&
+        M <= 16 &&
+        D % 256 == 0 && (nt == 4 || nt == 8 || nt == 12 || nt == 16) && R % 8 == 0 &&
+        row_stride % 8 == 0 && lds <= (size_t)f.lds_per_block) {
+      const void* fn = multi_fwd_tile_kernel_ptr(nt, R == D, sel);
+      if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no tile multi-query forward kernel");
+      int per_cu = 0;
+      attnres_status st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu);
+      if (st != ATTNRES_OK) return st;
+      MfmaFwdArgs ta;
+      std::memset(&ta, 0, sizeof ta);
+      for (int s = 0; s < S; ++s) ta.src[s] = src[s];
+      ta.row_stride = row_stride;
+      ta.N = N;
+      ta.S = S;
+      ta.D = D;
+      ta.R = R;
+      ta.lo = D - R;
+      ta.M = M;
+      ta.eps = eps;
+      ta.scale = scale;
+      ta.inv_R = 1.0f / (float)R;
+      ta.query = queries;
+      ta.y = y;
+      ta.y_sm = y_sm;
+      ta.y_sn = y_sn;
+      ta.lse = lse;
+      ta.l_sm = l_sm;
+      ta.l_sn = l_sn;
+      ta.ids = ids;
+      ta.E = E;
+      ta.id_flag = (sel && workspace) ? static_cast<uint32_t*>(workspace) + kCtrIdFlag : nullptr;
+      *used = true;
+      const int grid = (int)std::min<int64_t>(N, (int64_t)f.cus * per_cu);
+      return launch(fn, grid, 1, 64 * kMfmaWaves, lds, &ta, stream,
+                    "tile multi-query forward launch");
+    }
+  }
   const int cgw = (D + 1023) / 1024;
   const int mq = M <= 4 ? 4 : (M <= 8 ? 8 : 16);
-  const bool sel = ids != nullptr;
   const size_t lds = multi_fwd_mfma_lds(cgw, mq, sel ? E + 1 : mq);
   if (!bf16 || S < 2 || S > 16 || M < 3 || M > 16 || cgw > 4 || lds > (size_t)f.lds_per_block)
     return ATTNRES_OK;

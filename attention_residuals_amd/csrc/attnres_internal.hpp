@@ -73,6 +73,10 @@ size_t multi_fwd_mfma_lds(int cgw, int mq, int qrows);
 // with M slots per token over E <= 16 bank rows).
 const void* multi_bwd_mfma_kernel_ptr(int nt, int dqm, bool full, bool acc, int qm);
 const void* multi_dq_mfma_kernel_ptr();
+// Multi- and selected-query forward in the same operand layout (8 waves, D = 256 nt), two tokens
+// in flight; LDS for `rows` staged rows (M queries or E bank rows).
+const void* multi_fwd_tile_kernel_ptr(int nt, bool full, bool sel);
+size_t multi_fwd_tile_lds(int nt, int rows);
 const void* stream_probe_kernel_ptr(int cpt);
 size_t multi_bwd_mfma_lds(int nt, int dqm, int M, int qm, int E);
 const void* sel_bwd_kernel_ptr_bf16(int ch, int sb, bool full, bool acc, int mq);

@@ -34,93 +34,12 @@
 // range per workgroup (16x16x16 MFMAs with the sources as the contraction index).
 #include "attnres_internal.hpp"
 #include "attnres_kernels.hpp"
+#include "attnres_mfma_tiles.hpp"
 
 namespace attnres {
 namespace {
 
-typedef short mb_short4 __attribute__((ext_vector_type(4)));
-typedef float mb_float4 __attribute__((ext_vector_type(4)));
-typedef uint32_t mb_u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t mb_u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 mb_bf16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ Chunk bnt_load16(const char* p) {
-  return __builtin_bit_cast(Chunk,
-                            __builtin_nontemporal_load(reinterpret_cast<const mb_u32x4*>(p)));
-}
-__device__ __forceinline__ mb_u32x4 nt_ld(const char* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const mb_u32x4*>(p));
-}
-__device__ __forceinline__ void nt_st(char* p, const mb_u32x4& v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<mb_u32x4*>(p));
-}
-
-// {a.low, b.low} / {a.high, b.high} of two words (v_perm_b32)
-__device__ __forceinline__ uint32_t bpair_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t bpair_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
-// B operand of element e of a chunk from four rows (k = row, 4 bf16 per lane)
-__device__ __forceinline__ mb_short4 gather_e(const Chunk (&r)[4], int e) {
-  const int wi = e >> 1;
-  const uint32_t b0 = (e & 1) ? bpair_hi(r[0].w[wi], r[1].w[wi]) : bpair_lo(r[0].w[wi], r[1].w[wi]);
-  const uint32_t b1 = (e & 1) ? bpair_hi(r[2].w[wi], r[3].w[wi]) : bpair_lo(r[2].w[wi], r[3].w[wi]);
-  return __builtin_bit_cast(mb_short4, mb_u32x2{b0, b1});
-}
-
-// Four FP32 weights as two bf16 terms (w = hi + lo, ~16 bits kept), each packed as 4 bf16
-__device__ __forceinline__ void split4(const float (&w)[4], mb_u32x2& hi, mb_u32x2& lo) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    hi[i] = pack_bf16x2(w[2 * i], w[2 * i + 1]);
-    lo[i] = pack_bf16x2(w[2 * i] - lo_f(hi[i]), w[2 * i + 1] - hi_f(hi[i]));
-  }
-}
-__device__ __forceinline__ void split_a(const float (&w)[4], mb_short4& hi, mb_short4& lo) {
-  mb_u32x2 h, l;
-  split4(w, h, l);
-  hi = __builtin_bit_cast(mb_short4, h);
-  lo = __builtin_bit_cast(mb_short4, l);
-}
-
-__device__ __forceinline__ mb_float4 mfma_k32(const mb_u32x4& a, const mb_u32x4& b,
-                                              const mb_float4& acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mb_bf16x8, a),
-                                                 __builtin_bit_cast(mb_bf16x8, b), acc, 0, 0, 0);
-}
-__device__ __forceinline__ mb_float4 mfma_k16(const mb_u32x2& a, const mb_u32x2& b,
-                                              const mb_float4& acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mb_short4, a),
-                                                   __builtin_bit_cast(mb_short4, b), acc, 0, 0, 0);
-}
-
-// Transpose of half h of a tile held in operand layout (lane (g, c): row c, columns 8g .. 8g+7 in
-// x's eight bf16 slots). The 16x16x16 A operand takes slots 4h .. 4h+3 (columns 8g + 4h + i as
-// k = 4g + i); against the identity the product is that block itself in the output layout, so
-// lane (g, c) receives rows 4g .. 4g+3 at column 8(c/4) + 4h + c%4 of the tile, exact in FP32,
-// and the high halves of the FP32 words are those bf16 values again.
-__device__ __forceinline__ mb_u32x2 tr_half(const mb_u32x4& x, int h, const mb_u32x2& ident) {
-  const mb_u32x2 a = h ? mb_u32x2{x[2], x[3]} : mb_u32x2{x[0], x[1]};
-  const mb_float4 t = mfma_k16(a, ident, mb_float4{0.f, 0.f, 0.f, 0.f});
-  return mb_u32x2{bpair_hi(f_bits(t[0]), f_bits(t[1])), bpair_hi(f_bits(t[2]), f_bits(t[3]))};
-}
-
-// The same transpose of a block already in the 16x16x16 A layout (four bf16 per lane).
-__device__ __forceinline__ mb_u32x2 tr2(const mb_u32x2& a, const mb_u32x2& ident) {
-  const mb_float4 t = mfma_k16(a, ident, mb_float4{0.f, 0.f, 0.f, 0.f});
-  return mb_u32x2{bpair_hi(f_bits(t[0]), f_bits(t[1])), bpair_hi(f_bits(t[2]), f_bits(t[3]))};
-}
-
-// Sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the same lane of the wave's four DPP rows).
-__device__ __forceinline__ float rows4_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);
-  x = bits_f(a[0]) + bits_f(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
-  return bits_f(b[0]) + bits_f(b[1]);
-}
+using namespace tiles;
 
 constexpr int kXchFloats = 2 * 256 + 16;  // a wave's score and dp tiles and its 16 sums of squares
 
@@ -139,7 +58,7 @@ size_t multi_bwd_mfma_lds(int nt, int dqm, int M, int qm, int E) {
   const int rows = qm == 2 ? E : M;
   size_t b = ((size_t)dq_rows(dqm) * dq_stride(nt, dqm) + (size_t)kMfmaWaves * kXchFloats + 512 +
               64) * sizeof(float) + D * ((rows + 3) / 4) * 8;
-  if (qm >= 1) b += (size_t)(rows + 1) * D * 2 + 16 * sizeof(int);
+  if (qm >= 1) b += (size_t)(rows + 1) * (D + tiles::kRowPad) * 2 + 16 * sizeof(int);
   return b;
 }
 
@@ -169,8 +88,9 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   float* xch = lds + DQR * DQS + D * QG * 2;                 // [W][kXchFloats]
   float* pa = xch + W * kXchFloats;                          // p[16][16], a[16][16]
   float* bpart = pa + 512;                                   // [4][16] partial B sums
-  char* bankl = reinterpret_cast<char*>(bpart + 64);         // QROWS: [QR + 1][D] bf16 rows
-  int* sid = reinterpret_cast<int*>(bankl + (QROWS ? (size_t)(QR + 1) * D * 2 : 0));  // [16]
+  constexpr int QP = D + kRowPad;                            // staged row pitch
+  char* bankl = reinterpret_cast<char*>(bpart + 64);         // QROWS: [QR + 1][QP] bf16 rows
+  int* sid = reinterpret_cast<int*>(bankl + (QROWS ? (size_t)(QR + 1) * QP * 2 : 0));  // [16]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
   const mb_u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -197,15 +117,15 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   const char* gsrc = static_cast<const char*>(a.dout) + ((qlive ? c * a.g_sm : 0) + col_w) * 2;
 
   auto ld_v = [&](int t, int64_t n) {
-    const mb_u32x4 x = nt_ld(vsrc + n * a.row_stride * 2 + 64 * t);
+    const mb_u32x4 x = ld16(vsrc + n * a.row_stride * 2 + 64 * t);
     return vlive ? x : zero4;
   };
   auto ld_y = [&](int t, int64_t n) {
-    const mb_u32x4 x = nt_ld(gsrc + n * a.g_sn * 2 + 64 * t);
+    const mb_u32x4 x = ld16(gsrc + n * a.g_sn * 2 + 64 * t);
     return qlive ? x : zero4;
   };
   auto ld_old = [&](int t, int64_t n) {
-    const mb_u32x4 x = nt_ld(vdst + n * a.drow_stride * 2 + 64 * t);
+    const mb_u32x4 x = ld16(vdst + n * a.drow_stride * 2 + 64 * t);
     return vlive ? x : zero4;
   };
 
@@ -239,7 +159,7 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
       if (e < QR && j >= a.lo)
         v = *reinterpret_cast<const mb_u32x4*>(static_cast<const char*>(a.query) +
                                                 ((int64_t)e * a.R + (j - a.lo)) * 2);
-      *reinterpret_cast<mb_u32x4*>(bankl + ((size_t)e * D + j) * 2) = v;
+      *reinterpret_cast<mb_u32x4*>(bankl + ((size_t)e * QP + j) * 2) = v;
     }
   }
   // QROWS: the staged row of query (slot) c for token n: c itself, or the bank row its id names
@@ -282,7 +202,7 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
   auto contract = [&](int t) {
     mb_u32x4 qop;
     if constexpr (QROWS) {
-      qop = *reinterpret_cast<const mb_u32x4*>(bankl + ((size_t)qrow * D + col_w + 32 * t) * 2);
+      qop = *reinterpret_cast<const mb_u32x4*>(bankl + ((size_t)qrow * QP + col_w + 32 * t) * 2);
     } else {
       const mb_u32x2 q0 = tr2(ld_qt(t, 0), ident);
       const mb_u32x2 q1 = tr2(ld_qt(t, 1), ident);
@@ -466,7 +386,7 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
       V[t] = ld_v(t, ln);
       Y[t] = ld_y(t, ln);
       if (vlive)
-        nt_st(vdst + n * a.drow_stride * 2 + 64 * t,
+        st16(vdst + n * a.drow_stride * 2 + 64 * t,
               mb_u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
                        pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])});
       if (t >= LAG) contract(t - LAG);

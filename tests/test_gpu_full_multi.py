@@ -59,8 +59,8 @@ def test_multi_query_full_size(M, layout):
 
 
 def test_multi_query_full_size_forward_sixteen_slots():
-    # the sixteen-slot matrix-core forward with its token counter, as `bench.py --queries 16`
-    # runs it (outputs and lse of sampled tokens)
+    # the sixteen-query tile forward (sixteen staged rows, static stride), as
+    # `bench.py --queries 16` runs it (outputs and lse of sampled tokens)
     import attention_residuals_amd as A
     w, M, layout = HEADLINE, 16, "query_major"
     print(f"[case] full multi forward M={M} {layout}", flush=True)

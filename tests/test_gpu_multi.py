@@ -18,7 +18,7 @@ import torch
 import attnres_workloads as W
 import oracle
 from parity import (TOL_F32, assert_ok, compare_rows, compare_stat, compare_vec, gpu_available,
-                    half_ulp_bf16, multi_bwd_groups, to_f64)
+                    half_ulp_bf16, multi_bwd_groups, tile_fwd, to_f64)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
@@ -276,9 +276,11 @@ def _fwd_counter_case(fwd, ref, N, label, uses_counter):
 
 
 @pytest.mark.parametrize("M,S,D,R,layout", [
-    (16, 10, 1024, 1024, "query_major"),  # sixteen slots: the next token's rows loaded in place
-    (12, 7, 3072, 768, "token_major"),    # padded to sixteen slots, sliced key, three groups
-    (4, 10, 1024, 1024, "token_major"),   # four slots: static stride with or without workspace
+    (16, 10, 1280, 1280, "query_major"),  # older forward, sixteen slots: rows loaded in place
+    (12, 7, 2560, 768, "token_major"),    # older forward, padded to sixteen slots, sliced key
+    (4, 10, 1280, 1280, "token_major"),   # older forward, four slots: static stride
+    (16, 10, 1024, 1024, "query_major"),  # tile forward: static stride, workspace untouched
+    (12, 7, 3072, 768, "token_major"),    # tile forward, sliced key
 ])
 def test_matrix_core_forward_token_counter(M, S, D, R, layout):
     # enough tokens for at least two per resident workgroup, so the counter schedule runs
@@ -293,12 +295,14 @@ def test_matrix_core_forward_token_counter(M, S, D, R, layout):
         return _from_layout(y, layout), _from_layout(lse, layout)
 
     ref = oracle.run_multi(V, Q, want=("y", "lse"))
-    _fwd_counter_case(fwd, ref, N, f"matrix-core forward counter M={M} {layout}", M > 8)
+    _fwd_counter_case(fwd, ref, N, f"matrix-core forward counter M={M} {layout}",
+                      M > 8 and not tile_fwd(S, D, M, "bf16", R=R))
 
 
-def test_matrix_core_selected_forward_token_counter():
+@pytest.mark.parametrize("D", [1280, 1024])  # older forward (counter), tile forward (none)
+def test_matrix_core_selected_forward_token_counter(D):
     import attention_residuals_amd as A
-    S, N, D, E, K = 10, 2 * 4 * 256 + 37, 1024, 8, 12
+    S, N, E, K = 10, 2 * 4 * 256 + 37, 8, 12
     print(f"[case] matrix-core selected forward counter E={E} K={K} N={N}", flush=True)
     g = torch.Generator().manual_seed(4200)
     V = torch.randn((S, N, D), generator=g).to(torch.bfloat16)
@@ -310,4 +314,5 @@ def test_matrix_core_selected_forward_token_counter():
         return A.attnres_selected_fwd(Vg, bg, ig, dynamic=dynamic, workspace=ws)
 
     ref = oracle.run_selected(V, bank, ids, want=("y", "lse"))
-    _fwd_counter_case(fwd, ref, N, "matrix-core selected forward counter", True)
+    _fwd_counter_case(fwd, ref, N, f"matrix-core selected forward counter D={D}",
+                      not tile_fwd(S, D, K, "bf16", E=E))
