@@ -169,15 +169,16 @@ def roofline_for(kernel: str, bwd_bytes: int, fwd_bytes: int, bwd_ms: float, fwd
     return out
 
 
-def load_traffic(workload: str, launches_bytes: int):
+def load_traffic(workload: str, scope: str = "single"):
     """HBM traffic of the backward call from committed rocprofv3 counter summaries, if they were
-    taken on the current kernel sources (same source hash); else None."""
+    taken on the current kernel sources (same source hash over `scope`, as kernel_source_hash);
+    else None."""
     path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(scope):
         return None
     return rec.get("bwd_call_hbm_bytes")
 
@@ -347,7 +348,7 @@ def main() -> int:
         ceiling = stream_ceiling((vs, [y]), (vs + [x["dout"]], [dv[s] for s in range(S)]),
                                  fwd_bytes, bwd_bytes)
         ceiling["value_frac"] = round(value / ceiling["step_GBps"], 4)
-    traffic = None if args.accumulate else load_traffic(w.name, bwd_bytes)
+    traffic = None if args.accumulate else load_traffic(w.name)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -487,7 +488,9 @@ def run_multi(args, w) -> int:
                    "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 1),
                    "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4)},
         "roofline": roofline_for("attnres_multi_bwd (backward kernels + finaliser)", bwd_bytes,
-                                 fwd_bytes, bwd_ms, fwd_ms, f"{w.name}_multi_m{M}_{args.layout}"),
+                                 fwd_bytes, bwd_ms, fwd_ms, f"{w.name}_multi_m{M}_{args.layout}",
+                                 None if args.accumulate else
+                                 load_traffic(f"{w.name}_multi_m{M}_{args.layout}", "all")),
         "cpu_baseline": None,
         "parity_check": check,
         "source_hash": kernel_source_hash("all"),
@@ -575,7 +578,9 @@ def run_selected(args, w) -> int:
                    "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 1),
                    "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4)},
         "roofline": roofline_for("attnres_selected_bwd (backward kernels + finaliser)", bwd_bytes,
-                                 fwd_bytes, bwd_ms, fwd_ms, f"{w.name}_selected_e{E}_k{K}"),
+                                 fwd_bytes, bwd_ms, fwd_ms, f"{w.name}_selected_e{E}_k{K}",
+                                 None if args.accumulate else
+                                 load_traffic(f"{w.name}_selected_e{E}_k{K}", "all")),
         "cpu_baseline": None,
         "parity_check": check,
         "source_hash": kernel_source_hash("all"),
