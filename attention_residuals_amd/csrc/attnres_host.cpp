@@ -169,13 +169,16 @@ const void* fwd_ptr(const Shape& sh) {
                  : fwd_kernel_ptr_f32(sh.ch, sh.sb_fwd, sh.full, sh.fwd_one);
 }
 
-// binned: the token-resident kernel with exact FP64 bins (always for accumulation and FP32
-// storage; the bf16 overwrite kernel also comes with FP32 rows)
+// binned: the token-resident kernel with exact FP64 bins (always for FP32 storage; the bf16
+// kernels, overwriting or accumulating, also come with FP32 rows)
 const void* bwd_ptr(const Shape& sh, bool acc, bool binned = true) {
   if (sh.resident) {
-    if (acc)
+    if (acc) {
+      if (!binned && sh.bf16)
+        return bwd_resident_acc_rows_kernel_ptr_bf16(sh.ch, sh.sb_bwd, sh.full);
       return sh.bf16 ? bwd_resident_acc_kernel_ptr_bf16(sh.ch, sh.sb_bwd, sh.full)
                      : bwd_resident_acc_kernel_ptr_f32(sh.ch, sh.sb_bwd, sh.full);
+    }
     if (!binned && sh.bf16) return bwd_resident_rows_kernel_ptr_bf16(sh.ch, sh.sb_bwd, sh.full);
     return sh.bf16 ? bwd_resident_kernel_ptr_bf16(sh.ch, sh.sb_bwd, sh.full)
                    : bwd_resident_kernel_ptr_f32(sh.ch, sh.sb_bwd, sh.full);
@@ -301,10 +304,11 @@ attnres_status bwd_grid(const attnres_desc* d, const Shape& sh, bool binned, int
 // fit, and ATTNRES_ERR_WORKSPACE is returned when even one row per workgroup does not.
 attnres_status plan_bwd(const attnres_desc* d, const Shape& sh, BwdPlan* pl, size_t budget = 0) {
   // The token-resident kernel sums the q/w gradients into exact bins when the result must not
-  // depend on the schedule (deterministic; and always for accumulation and FP32 storage, which
-  // have no row variant); the default bf16 overwrite keeps FP32 rows, 1.6% faster at the
-  // headline shape (backward 1.017 -> 1.002 ms), reproducible to FP32 rounding under tickets.
-  const bool binned = sh.resident && (d->deterministic || d->accumulate_dvalues || !sh.bf16);
+  // depend on the schedule (deterministic; and always for FP32 storage, which has no row
+  // variant); the default bf16 backward keeps FP32 rows, 1.6% faster at the headline shape
+  // (backward 1.017 -> 1.002 ms) and without the bins' spills when accumulating into dvalues,
+  // reproducible to FP32 rounding under tickets.
+  const bool binned = sh.resident && (d->deterministic || !sh.bf16);
   int64_t cap = 0;
   attnres_status st = bwd_grid(d, sh, binned, &cap);
   if (st != ATTNRES_OK) return st;

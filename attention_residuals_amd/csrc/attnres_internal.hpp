@@ -51,6 +51,7 @@ const void* bwd_resident_kernel_ptr_bf16(int ch, int sb, bool full);
 const void* bwd_resident_rows_kernel_ptr_bf16(int ch, int sb, bool full);  // FP32 rows, no bins
 const void* bwd_resident_kernel_ptr_f32(int ch, int sb, bool full);
 const void* bwd_resident_acc_kernel_ptr_bf16(int ch, int sb, bool full);
+const void* bwd_resident_acc_rows_kernel_ptr_bf16(int ch, int sb, bool full);  // FP32 rows
 const void* bwd_resident_acc_kernel_ptr_f32(int ch, int sb, bool full);
 const void* bwd_stream_kernel_ptr(bool bf16, int ch, int sb, bool full, bool acc);
 const void* finalize_kernel_ptr(bool bf16);

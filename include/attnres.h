@@ -76,8 +76,9 @@ typedef struct {
                               backward gives each workgroup a fixed share and each counter batch
                               of the last quarter its own partial row.
                               0 (default): the same, except that the bf16 token-resident backward
-                              without accumulation keeps one FP32 running sum per workgroup (about
-                              1.6% faster), so its dq/dw reproduce to FP32 rounding only.
+                              keeps one FP32 running sum per workgroup (about 1.6% faster; when
+                              accumulating into dvalues the binned kernel spills and runs ~13%
+                              slower), so its dq/dw reproduce to FP32 rounding only.
                               The two modes may differ from each other in the last bits of
                               dq/dw/dow. Multi- and selected-query reads: their one-pass
                               matrix-core backward (three or more bf16 queries or slots, see

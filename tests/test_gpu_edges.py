@@ -289,6 +289,27 @@ def test_accumulate_into_existing_dvalues(S, N, D, R, dtype, out_norm, packed):
     assert_ok(check_all(w, got, ref), f"accumulate S={S} N={N} D={D} R={R} {dtype}")
 
 
+@pytest.mark.parametrize("S,N,D,R", [(10, 3001, 4096, 4096), (24, 2001, 2048, 512)])
+def test_accumulate_deterministic_repeats_bitwise(S, N, D, R):
+    # accumulating bf16 backward with deterministic = 1: the exact-bin kernel under the ticket
+    # schedule (the default mode keeps FP32 rows); parity with the oracle, and two calls from the
+    # same existing dvalues agree bit for bit
+    w = _wl(S, N, D, R, seed=1750 + S)
+    xc = W.generate(w)
+    init = (3.0 * torch.randn((S, N, D), generator=torch.Generator().manual_seed(1751))).to(
+        w.torch_dtype)
+    print(f"[case] deterministic accumulate S={S} N={N} D={D} R={R}", flush=True)
+    xg = inputs_on(xc, "cuda")
+    got = [run_gpu(w, xg, dvalues=init.to("cuda"), accumulate=True, deterministic=True)
+           for _ in range(2)]
+    torch.cuda.synchronize()
+    for k in ("dvalues", "dq", "dw"):
+        assert torch.equal(got[0][k], got[1][k]), k
+    ref = run_oracle(w, xc)
+    ref["dvalues"] = ref["dvalues"] + init.double().numpy()
+    assert_ok(check_all(w, got[0], ref), f"deterministic accumulate S={S} N={N} D={D} R={R}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_block_schedule_reads_share_completed_sources(dtype):
     # fast-attnres page, "Full and Block schedules": a Block read takes the embedding and the
