@@ -368,6 +368,10 @@ def main() -> int:
                    "algorithmic_bytes": algo, "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 1),
                    "fwd_ms": round(fwd_avg, 4), "bwd_ms": round(bwd_avg, 4),
                    "event_ms_per_step": round(float(np.mean(ev_step)), 4),
+                   # per-step HIP-event times of fwd + bwd: median and 10th / 90th percentiles
+                   "event_ms_step_median": round(float(np.median(ev_step)), 4),
+                   "event_ms_step_p10": round(float(np.percentile(ev_step, 10)), 4),
+                   "event_ms_step_p90": round(float(np.percentile(ev_step, 90)), 4),
                    "b200_ms_context": B200_MS.get(w.name)},
         "roofline": roofline_for("attnres_bwd (backward kernel + finaliser)", bwd_bytes, fwd_bytes,
                                  bwd_avg, fwd_avg,
