@@ -169,6 +169,14 @@ def roofline_for(kernel: str, bwd_bytes: int, fwd_bytes: int, bwd_ms: float, fwd
     return out
 
 
+def input_checksums(x: dict) -> dict:
+    """FP64 sum of every input tensor (taken after the timed steps): identifies the synthetic
+    inputs a line was measured on."""
+    import torch
+    return {k: float(torch.sum(v, dtype=torch.float64).item()) for k, v in x.items()
+            if v is not None}
+
+
 def load_traffic(workload: str, scope: str = "single"):
     """HBM traffic of the backward call from committed rocprofv3 counter summaries, if they were
     taken on the current kernel sources (same source hash over `scope`, as kernel_source_hash);
@@ -372,7 +380,8 @@ def main() -> int:
                    "event_ms_step_median": round(float(np.median(ev_step)), 4),
                    "event_ms_step_p10": round(float(np.percentile(ev_step, 10)), 4),
                    "event_ms_step_p90": round(float(np.percentile(ev_step, 90)), 4),
-                   "b200_ms_context": B200_MS.get(w.name)},
+                   "b200_ms_context": B200_MS.get(w.name),
+                   "input_checksums_f64": input_checksums(x)},
         "roofline": roofline_for("attnres_bwd (backward kernel + finaliser)", bwd_bytes, fwd_bytes,
                                  bwd_avg, fwd_avg,
                                  w.name + ("_accumulate" if args.accumulate else ""), traffic,
