@@ -1055,8 +1055,8 @@ attnres_status plan_multi_bwd_mfma(const attnres_multi_desc* m, const MultiShape
                                    int64_t row_stride, int64_t drow_stride, MultiBwdPlan* pl) {
   pl->mfma = false;
   // up to four queries with S <= 12 (and D <= 4096) are one launch of the query-group kernel,
-  // which measured faster there (M = 3, 4 at S = 10, N = 32768, D = 4096: 1.42 / 1.69 ms against
-  // 1.85 / 1.90 ms); it rounds dvalues once as well
+  // which measured faster there or the same (M = 3, 4 at S = 10, N = 32768, D = 4096: 1.44 / 1.66
+  // ms against 1.64 / 1.65 ms); it rounds dvalues once as well
   if (!ms.base.bf16 || (m->M <= 4 && m->S <= 12)) return ATTNRES_OK;
   return plan_mfma_bwd(m->S, m->D, m->R, m->M, false, 0, m->N, m->accumulate_dvalues != 0,
                        row_stride, drow_stride, pl);
@@ -1733,9 +1733,10 @@ attnres_status attnres_selected_bwd(const attnres_selected_desc* d, const attnre
 
   char* ws = static_cast<char*>(workspace);
   // three or more bf16 slots: one pass on matrix cores when the shape and the bank fit (dvalues
-  // rounded once; the query-group kernels take slots in pairs)
+  // rounded once). Three slots that the slot-group kernel takes in one launch stay there: it
+  // measured faster (S = 10, N = 32768, D = 4096, E = 4 / 8: backward 1.70 ms against 2.10 / 2.12)
   MultiBwdPlan mp;
-  if (N > 0 && ms.base.bf16 && K >= 3 && aligned(bank, 16)) {
+  if (N > 0 && ms.base.bf16 && (K >= 4 || (K == 3 && ms.mq_max < 3)) && aligned(bank, 16)) {
     st = plan_mfma_bwd(d->S, d->D, d->R, (int)K, true, d->E, N, d->accumulate_dvalues != 0,
                        values->row_stride, dvalues->row_stride, &mp);
     if (st != ATTNRES_OK) return st;

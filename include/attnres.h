@@ -187,13 +187,14 @@ attnres_status attnres_bwd_noalloc(const attnres_desc* desc, const attnres_sourc
  * written: no key-norm weight and no output norm. The backward returns dvalues summed over the
  * queries and dq [M, R], each row summed over all tokens.
  * Token-resident only: a token's S rows must fit on chip (attnres_multi_*_workspace_bytes and the
- * entry points return ATTNRES_ERR_UNSUPPORTED otherwise; at D = 4096, bf16, S <= 24). The forward of
- * 3 <= M <= 16 bf16 queries over 2 <= S <= 16 sources with D <= 4096 runs in one pass on matrix cores
- * (tokens strided over the grid). With 5 <= M, D = 1024, 2048, 3072 or 4096, R and the row stride
- * multiples of 8, and queries, sources and y 16-byte aligned (y strides multiples of 8 elements),
- * that pass runs in the backward's tile layout; otherwise, with 9 to 16 queries and the optional
- * forward workspace, tokens come from its counter (outputs are the same either way, bit for bit).
- * Other shapes run queries in groups of at most four, each group reading the sources again. The backward of 3 <= M <= 16
+ * entry points return ATTNRES_ERR_UNSUPPORTED otherwise; at D = 4096, bf16, S <= 24). The forward
+ * of 3 <= M <= 16 bf16 queries over 2 <= S <= 16 sources with D <= 4096 runs in one pass on matrix
+ * cores (tokens strided over the grid). With 5 <= M, D = 1024, 2048, 3072 or 4096, R and the row
+ * stride multiples of 8, and queries, sources and y 16-byte aligned (y strides multiples of 8
+ * elements), that pass runs in the backward's tile layout; otherwise, with 9 to 16 queries and the
+ * optional forward workspace, tokens come from its counter (outputs are the same either way, bit
+ * for bit). Other shapes run queries in groups of at most four, each group reading the sources
+ * again. The backward of 3 <= M <= 16
  * bf16 queries over 2 <= S <= 16 sources with D = 1024, 2048, 3072 or 4096, R and the row strides
  * multiples of 8 and 16-byte aligned queries, runs in one pass on matrix cores (dvalues written and
  * rounded once; a second pass over the key slice forms dq unless M <= 4), except M <= 4 with
@@ -247,10 +248,13 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* desc, const attnres_s
  * slots over 2 <= S <= 16 sources with D <= 4096 runs in one pass on matrix cores when the bank
  * (E + 1 rows of D bf16) fits in a workgroup's LDS (in the tile layout under the multi-query read's
  * conditions for it; else the optional forward workspace holds the token counter of 9 to 16 slots,
- * as in the multi-query read); otherwise slots run in groups of at most four. The backward of 3 <= K <= 16 bf16 slots runs in one pass on matrix cores under the
- * multi-query read's conditions when E <= 16 and the bank fits in a workgroup's LDS (as E + 1 rows
- * and as transposed groups of four: E <= 8 at D = 4096), dbank formed by a second pass over the key
- * slice; otherwise in slot groups (later groups add into dvalues).
+ * as in the multi-query read); otherwise slots run in groups of at most four. The backward of
+ * 4 <= K <= 16 bf16 slots (K = 3 too when the slot-group kernel would need two launches: S > 10 or
+ * two chunks per thread) runs in one pass on matrix cores under the multi-query read's conditions
+ * when E <= 16 and the bank fits in a workgroup's LDS (as E + 1 rows and as transposed groups of
+ * four: E <= 8 at D = 4096), dbank formed by a second pass over the key slice; otherwise in slot
+ * groups of at most four (two with S > 10 or two chunks per thread; later groups add into
+ * dvalues).
  * The bank gradient goes through per-workgroup FP32 partial rows of the whole bank (the workspace
  * is 256 + P * E * R * 4 bytes, P = backward workgroups, or the matrix-core backward's
  * coefficients and partial rows), so a large bank costs workspace and traffic; E * R * 4 must stay

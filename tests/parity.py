@@ -234,15 +234,24 @@ def tile_fwd(S: int, D: int, M: int, dtype: str, R=None, row_stride=None, E=None
             and lds <= LDS_PER_BLOCK)
 
 
+def sel_slots_per_launch(S: int, D: int, dtype: str) -> int:
+    """Slots per launch of the selected read's slot-group backward: four with one 16-byte chunk
+    per thread (D <= 512 chunks at eight waves) and S <= 10, else two."""
+    return 4 if (D // (8 if dtype == "bf16" else 4) <= 512 and S <= 10) else 2
+
+
 def sel_mfma_bwd(S: int, D: int, K: int, E: int, dtype: str, R=None, row_stride=None) -> bool:
-    """True when the selected-query backward runs in one pass on matrix cores: bf16, 3 <= K <= 16,
-    2 <= S <= 16, D in (1024, 2048, 3072, 4096), R and the row stride multiples of 8 elements,
-    E <= 16 and the staged bank (E + 1 row-major rows and the transposed four-row groups) within
-    the workgroup's LDS beside the exchange."""
+    """True when the selected-query backward runs in one pass on matrix cores: bf16, 3 <= K <= 16
+    (K = 3 only where the slot-group kernel would need two launches), 2 <= S <= 16, D in (1024,
+    2048, 3072, 4096), R and the row stride multiples of 8 elements, E <= 16 and the staged bank
+    (E + 1 row-major rows and the transposed four-row groups) within the workgroup's LDS beside
+    the exchange."""
     R = D if R is None else R
     row_stride = D if row_stride is None else row_stride
     if not (dtype == "bf16" and 3 <= K <= 16 and 2 <= S <= 16 and D in (1024, 2048, 3072, 4096)
             and R % 8 == 0 and row_stride % 8 == 0 and 1 <= E <= 16):
+        return False
+    if K == 3 and sel_slots_per_launch(S, D, dtype) >= 3:
         return False
     lds = (E + 1) * (D + 8) * 2 + 16 * 4 + -(-E // 4) * D * 8 + (8 * (2 * 256 + 16) + 512 + 64) * 4
     return lds <= LDS_PER_BLOCK
@@ -253,14 +262,18 @@ def multi_bwd_groups(S: int, D: int, M: int, dtype: str, selected: bool = False,
     """Backward launch groups (first query, count) of the multi- and selected-query reads as the
     library plans them: one pass on matrix cores where multi_mfma_bwd (multi-query read) or
     sel_mfma_bwd (selected read, E bank rows) holds, else up to four queries per launch with one
-    16-byte chunk per thread (D <= 512 chunks at eight waves) and S <= 12, else two, sized as evenly
+    16-byte chunk per thread (D <= 512 chunks at eight waves) and S <= 12 (selected read: S <= 10),
+    else two, sized as evenly
     as possible (larger groups first). Each launch after the first adds into dvalues, rounding the
     running sum to storage again."""
     if not selected and multi_mfma_bwd(S, D, M, dtype, R, row_stride):
         return [(0, M)]
     if selected and E is not None and sel_mfma_bwd(S, D, M, E, dtype, R, row_stride):
         return [(0, M)]
-    per = 4 if (D // (8 if dtype == "bf16" else 4) <= 512 and S <= 12) else 2
+    if selected:
+        per = sel_slots_per_launch(S, D, dtype)
+    else:
+        per = 4 if (D // (8 if dtype == "bf16" else 4) <= 512 and S <= 12) else 2
     n = -(-M // per)
     out, m0 = [], 0
     for i in range(n):

@@ -87,7 +87,7 @@ def _check(V, bank, ids, G, label, dtype, init=None, ref_bank=None, ref_ids=None
 @pytest.mark.parametrize("S,N,D,R,E,K,dtype", [
     (10, 701, 4096, 4096, 8, 2, "bf16"),    # partial bank in LDS where a workgroup may hold 160 KiB
     (10, 301, 4096, 4096, 16, 2, "bf16"),   # partial bank in global blocks
-    (8, 513, 2048, 512, 16, 3, "bf16"),     # LDS bank, two groups
+    (8, 513, 2048, 512, 16, 3, "bf16"),     # LDS bank, three slots in one slot-group launch
     (6, 257, 1024, 1024, 4, 1, "f32"),      # LDS bank, a padded slot
     (4, 300, 8192, 8192, 3, 2, "bf16"),     # two chunks per thread
     (5, 129, 256, 5, 3, 5, "f32"),          # slice start not a multiple of four, three groups
@@ -99,8 +99,10 @@ def _check(V, bank, ids, G, label, dtype, init=None, ref_bank=None, ref_ids=None
     (8, 257, 1024, 1024, 4, 4, "f32"),      # four slots, FP32
     (10, 211, 2048, 2048, 24, 7, "bf16"),   # seven slots: groups of four and three, global blocks
     (6, 149, 2048, 2048, 40, 4, "bf16"),    # a bank too large to stage: the slot-group forward
-    # the one-pass matrix-core backward (3 <= K <= 16 bf16 slots, E <= 16, D = 256 nt)
+    # the one-pass matrix-core backward (3 <= K <= 16 bf16 slots, E <= 16, D = 256 nt; three
+    # slots only where the slot-group kernel would need two launches: S > 10)
     (16, 257, 4096, 4096, 6, 16, "bf16"),   # sixteen slots and sources
+    (12, 211, 2048, 2048, 8, 3, "bf16"),    # three slots, twelve sources
     (5, 300, 3072, 1024, 3, 9, "bf16"),     # twelve column tiles per wave, sliced key
     (12, 150, 1024, 1024, 16, 5, "bf16"),   # sixteen bank rows
 ])
