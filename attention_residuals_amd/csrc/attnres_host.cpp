@@ -1732,11 +1732,12 @@ attnres_status attnres_selected_bwd(const attnres_selected_desc* d, const attnre
   if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
 
   char* ws = static_cast<char*>(workspace);
-  // three or more bf16 slots: one pass on matrix cores when the shape and the bank fit (dvalues
-  // rounded once). Three slots that the slot-group kernel takes in one launch stay there: it
-  // measured faster (S = 10, N = 32768, D = 4096, E = 4 / 8: backward 1.70 ms against 2.10 / 2.12)
+  // bf16 slots that the slot-group kernel would take in two or more launches: one pass on matrix
+  // cores when the shape and the bank fit (dvalues rounded once). Slots it takes in one launch
+  // stay there, measured faster (S = 10, N = 32768, D = 4096, E = 8: backward 1.70 / 2.09 ms for
+  // three / four slots against 2.12 / 2.13 ms on matrix cores)
   MultiBwdPlan mp;
-  if (N > 0 && ms.base.bf16 && (K >= 4 || (K == 3 && ms.mq_max < 3)) && aligned(bank, 16)) {
+  if (N > 0 && ms.base.bf16 && K > ms.mq_max && aligned(bank, 16)) {
     st = plan_mfma_bwd(d->S, d->D, d->R, (int)K, true, d->E, N, d->accumulate_dvalues != 0,
                        values->row_stride, dvalues->row_stride, &mp);
     if (st != ATTNRES_OK) return st;

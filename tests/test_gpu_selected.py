@@ -99,8 +99,8 @@ def _check(V, bank, ids, G, label, dtype, init=None, ref_bank=None, ref_ids=None
     (8, 257, 1024, 1024, 4, 4, "f32"),      # four slots, FP32
     (10, 211, 2048, 2048, 24, 7, "bf16"),   # seven slots: groups of four and three, global blocks
     (6, 149, 2048, 2048, 40, 4, "bf16"),    # a bank too large to stage: the slot-group forward
-    # the one-pass matrix-core backward (3 <= K <= 16 bf16 slots, E <= 16, D = 256 nt; three
-    # slots only where the slot-group kernel would need two launches: S > 10)
+    # the one-pass matrix-core backward (bf16 slots beyond one slot-group launch: K > 4, or K > 2
+    # with S > 10; E <= 16, D = 256 nt)
     (16, 257, 4096, 4096, 6, 16, "bf16"),   # sixteen slots and sources
     (12, 211, 2048, 2048, 8, 3, "bf16"),    # three slots, twelve sources
     (5, 300, 3072, 1024, 3, 9, "bf16"),     # twelve column tiles per wave, sliced key
