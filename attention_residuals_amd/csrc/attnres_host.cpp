@@ -1514,7 +1514,7 @@ attnres_status attnres_selected_workspace_bytes(const attnres_selected_desc* d, 
   if ((st = plan_sel_bwd(d, ms, &pl)) != ATTNRES_OK) return st;
   *bytes = pl.bytes;
   // or the matrix-core backward's, when it may serve the call (dense rows assumed here)
-  if (ms.base.bf16 && d->K >= 3 && d->N > 0) {
+  if (ms.base.bf16 && d->K > ms.mq_max && d->N > 0) {
     MultiBwdPlan mp;
     if (plan_mfma_bwd(d->S, d->D, d->R, d->K, true, d->E, d->N, d->accumulate_dvalues != 0, d->D,
                       d->D, &mp) == ATTNRES_OK &&

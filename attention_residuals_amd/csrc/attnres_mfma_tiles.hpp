@@ -11,8 +11,8 @@ namespace attnres {
 namespace tiles {
 
 // bf16 elements of padding after each row staged in LDS: row r starts 16 r bytes further round the
-// 64 banks, so the 16 lanes of a four-lane group reading 16 bytes of rows 0..15 at one column fall
-// in distinct banks instead of all in the same four
+// 64 banks, so the 16 lanes of one lane group g, which read 16 bytes of rows 0..15 at the same
+// column, fall in distinct banks instead of all in the same four
 constexpr int kRowPad = 8;
 
 

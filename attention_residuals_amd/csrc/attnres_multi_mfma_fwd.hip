@@ -11,10 +11,10 @@
 // the column, so per tile one MFMA gives the scores Q V^T (queries, or the bank, staged as full
 // rows in LDS) and one the key sums of squares diag(V V^T). The 8 waves' tiles meet in LDS and 256
 // threads finish one (query, source) pair each: routing weight, row maximum and sum over the
-// sources by DPP, lse. The mixture runs transposed, y^T = V^T P^T, per 16-column half-tile: two
-// identity MFMAs put the sources in the k slots and one 16x16x32 MFMA takes the weights as two bf16
-// terms (hi in slots 0-3, lo in 4-7), leaving lane (g, c) with query c's output at eight
-// consecutive columns: one 16-byte store.
+// sources by DPP, lse. The mixture runs transposed, y^T = V^T P^T: each 16-column half of a tile
+// takes one identity MFMA (the sources into the k slots) and one 16x16x32 MFMA with the weights as
+// two bf16 terms (hi in slots 0-3, lo in 4-7); the two halves leave lane (g, c) with query c's
+// output at eight consecutive columns: one 16-byte store per tile.
 // Two tokens in flight: each token's rows are loaded into a second register set at the start of
 // the previous token, so they arrive while that token's mixture is computed and stored.
 #include "attnres_internal.hpp"
