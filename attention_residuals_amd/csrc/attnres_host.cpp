@@ -983,6 +983,7 @@ struct MultiBwdPlan {
   size_t off_part = 256, bytes = 256;
   // one-pass matrix-core backward (bf16, 3 <= M <= 16, 2 <= S <= 16, D <= 4096)
   bool mfma = false;
+  bool compact = false;  // sources and dY rows in one 16-row tile (S + M <= 16)
   int nt = 0, dqm = 0, qm = 0, grid = 0, tiles = 0, ranges = 0, chunk0 = 0;
   int64_t tpr = 0;
   size_t lds = 0, off_coef = 0;
@@ -1013,20 +1014,34 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
   DevFacts f;
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
-  // the queries also as full rows where they fit (M <= 8): the score operand without transposes
-  int qm = sel ? 2 : (M <= 8 ? 1 : 0);
-  size_t lds = multi_bwd_mfma_lds(nt, dqm, M, qm, E);
-  if (qm == 1 && lds > (size_t)f.lds_per_block && dqm == 0) {
-    qm = 0;
-    lds = multi_bwd_mfma_lds(nt, dqm, M, qm, E);
+  // sources and dY rows together in one 16-row tile when they fit (S + M <= 16; the multi-query
+  // read): half the row registers, two tokens in flight (ATTNRES_MULTI_COMPACT=0 turns it off)
+  static const char* ce = std::getenv("ATTNRES_MULTI_COMPACT");
+  bool compact = !sel && S + M <= 16 && !(ce && ce[0] == '0');
+  int qm = 0;
+  size_t lds = 0;
+  if (compact) {
+    lds = multi_bwd_compact_lds(nt, dqm != 0, M);
+    compact = lds <= (size_t)f.lds_per_block;
   }
-  if (lds > (size_t)f.lds_per_block) return ATTNRES_OK;
-  const void* fn = multi_bwd_mfma_kernel_ptr(nt, dqm, R == D, acc, qm);
+  if (!compact) {
+    // the queries also as full rows where they fit (M <= 8): the score operand without transposes
+    qm = sel ? 2 : (M <= 8 ? 1 : 0);
+    lds = multi_bwd_mfma_lds(nt, dqm, M, qm, E);
+    if (qm == 1 && lds > (size_t)f.lds_per_block && dqm == 0) {
+      qm = 0;
+      lds = multi_bwd_mfma_lds(nt, dqm, M, qm, E);
+    }
+    if (lds > (size_t)f.lds_per_block) return ATTNRES_OK;
+  }
+  const void* fn = compact ? multi_bwd_compact_kernel_ptr(nt, dqm != 0, R == D, acc)
+                           : multi_bwd_mfma_kernel_ptr(nt, dqm, R == D, acc, qm);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query backward kernel");
   int per_cu = 0;
   if ((st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu)) != ATTNRES_OK) return st;
   const int rows = sel ? E : M;  // rows of the reduced gradient (dq or dbank)
   pl->mfma = true;
+  pl->compact = compact;
   pl->nt = nt;
   pl->dqm = dqm;
   pl->qm = qm;
@@ -1054,10 +1069,11 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
 attnres_status plan_multi_bwd_mfma(const attnres_multi_desc* m, const MultiShape& ms,
                                    int64_t row_stride, int64_t drow_stride, MultiBwdPlan* pl) {
   pl->mfma = false;
-  // up to four queries with S <= 12 (and D <= 4096) are one launch of the query-group kernel,
-  // which measured faster there or the same (M = 3, 4 at S = 10, N = 32768, D = 4096: 1.44 / 1.66
-  // ms against 1.64 / 1.65 ms); it rounds dvalues once as well
-  if (!ms.base.bf16 || (m->M <= 4 && m->S <= 12)) return ATTNRES_OK;
+  // up to three queries with S <= 12 (and D <= 4096) are one launch of the query-group kernel,
+  // which measured faster there (M = 3 at S = 10, N = 32768, D = 4096: 1.38 ms against 1.50 ms for
+  // the compact matrix-core kernel); it rounds dvalues once as well. Four queries: the compact
+  // kernel, 1.53 against 1.66 ms
+  if (!ms.base.bf16 || (m->M <= 3 && m->S <= 12)) return ATTNRES_OK;
   return plan_mfma_bwd(m->S, m->D, m->R, m->M, false, 0, m->N, m->accumulate_dvalues != 0,
                        row_stride, drow_stride, pl);
 }
@@ -1068,7 +1084,8 @@ attnres_status launch_mfma_bwd(const MultiBwdPlan& pl, MfmaBwdArgs& b, bool sel,
                                char* ws, void* stream) {
   if (pl.dqm == 0) b.coef = reinterpret_cast<float*>(ws + pl.off_coef);
   else b.part = reinterpret_cast<float*>(ws + pl.off_part);
-  const void* fn = multi_bwd_mfma_kernel_ptr(pl.nt, pl.dqm, b.R == b.D, acc, pl.qm);
+  const void* fn = pl.compact ? multi_bwd_compact_kernel_ptr(pl.nt, pl.dqm != 0, b.R == b.D, acc)
+                              : multi_bwd_mfma_kernel_ptr(pl.nt, pl.dqm, b.R == b.D, acc, pl.qm);
   attnres_status st = launch(fn, pl.grid, 1, 64 * kMfmaWaves, pl.lds, &b, stream,
                              "matrix-core multi-query backward launch");
   if (st != ATTNRES_OK || pl.dqm != 0) return st;

@@ -194,12 +194,13 @@ attnres_status attnres_bwd_noalloc(const attnres_desc* desc, const attnres_sourc
  * elements), that pass runs in the backward's tile layout; otherwise, with 9 to 16 queries and the
  * optional forward workspace, tokens come from its counter (outputs are the same either way, bit
  * for bit). Other shapes run queries in groups of at most four, each group reading the sources
- * again. The backward of 3 <= M <= 16
- * bf16 queries over 2 <= S <= 16 sources with D = 1024, 2048, 3072 or 4096, R and the row strides
- * multiples of 8 and 16-byte aligned queries, runs in one pass on matrix cores (dvalues written and
- * rounded once; a second pass over the key slice forms dq unless M <= 4), except M <= 4 with
- * S <= 12, which is one launch of the query-group kernel; otherwise backward groups after the first
- * add into dvalues. ATTNRES_MULTI_MFMA=0 (read once) turns the matrix-core kernels off.
+ * again. The backward of 3 <= M <= 16 bf16 queries over 2 <= S <= 16 sources with D = 1024, 2048,
+ * 3072 or 4096, R and the row strides multiples of 8 and 16-byte aligned queries, runs in one pass
+ * on matrix cores (dvalues written and rounded once; with S + M <= 16 the sources and dY rows share
+ * one register tile and two tokens are in flight; a second pass over the key slice forms dq unless
+ * M <= 4), except M = 3 with S <= 12, which is one launch of the query-group kernel; otherwise
+ * backward groups after the first add into dvalues. ATTNRES_MULTI_MFMA=0 (read once) turns the
+ * matrix-core kernels off.
  * Layout of y, dout [.., D] and lse: ATTNRES_QUERY_MAJOR = [M, N] rows (the page's default),
  * ATTNRES_TOKEN_MAJOR = [N, M] rows (the page's output_layout="token_major"). */
 typedef enum { ATTNRES_QUERY_MAJOR = 0, ATTNRES_TOKEN_MAJOR = 1 } attnres_layout;
