@@ -1014,14 +1014,14 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
   DevFacts f;
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
-  // sources and dY rows together in one 16-row tile when they fit (S + M <= 16; the multi-query
-  // read): half the row registers, two tokens in flight (ATTNRES_MULTI_COMPACT=0 turns it off)
+  // sources and dY rows together in one 16-row tile when they fit (S + M <= 16): half the row
+  // registers, two tokens in flight (ATTNRES_MULTI_COMPACT=0 turns it off)
   static const char* ce = std::getenv("ATTNRES_MULTI_COMPACT");
-  bool compact = !sel && S + M <= 16 && !(ce && ce[0] == '0');
+  bool compact = S + M <= 16 && !(ce && ce[0] == '0');
   int qm = 0;
   size_t lds = 0;
   if (compact) {
-    lds = multi_bwd_compact_lds(nt, dqm != 0, M);
+    lds = multi_bwd_compact_lds(nt, dqm != 0, sel ? E : M);
     compact = lds <= (size_t)f.lds_per_block;
   }
   if (!compact) {
@@ -1034,7 +1034,7 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
     }
     if (lds > (size_t)f.lds_per_block) return ATTNRES_OK;
   }
-  const void* fn = compact ? multi_bwd_compact_kernel_ptr(nt, dqm != 0, R == D, acc)
+  const void* fn = compact ? multi_bwd_compact_kernel_ptr(nt, dqm != 0, R == D, acc, sel)
                            : multi_bwd_mfma_kernel_ptr(nt, dqm, R == D, acc, qm);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query backward kernel");
   int per_cu = 0;
@@ -1084,8 +1084,9 @@ attnres_status launch_mfma_bwd(const MultiBwdPlan& pl, MfmaBwdArgs& b, bool sel,
                                char* ws, void* stream) {
   if (pl.dqm == 0) b.coef = reinterpret_cast<float*>(ws + pl.off_coef);
   else b.part = reinterpret_cast<float*>(ws + pl.off_part);
-  const void* fn = pl.compact ? multi_bwd_compact_kernel_ptr(pl.nt, pl.dqm != 0, b.R == b.D, acc)
-                              : multi_bwd_mfma_kernel_ptr(pl.nt, pl.dqm, b.R == b.D, acc, pl.qm);
+  const void* fn =
+      pl.compact ? multi_bwd_compact_kernel_ptr(pl.nt, pl.dqm != 0, b.R == b.D, acc, sel)
+                 : multi_bwd_mfma_kernel_ptr(pl.nt, pl.dqm, b.R == b.D, acc, pl.qm);
   attnres_status st = launch(fn, pl.grid, 1, 64 * kMfmaWaves, pl.lds, &b, stream,
                              "matrix-core multi-query backward launch");
   if (st != ATTNRES_OK || pl.dqm != 0) return st;
@@ -1506,6 +1507,11 @@ attnres_status check_ids(const int64_t* ids, int64_t N) {
   return ATTNRES_OK;
 }
 
+// Slot counts for which the selected backward tries the matrix-core kernels (see its dispatch).
+bool sel_mfma_slots(const attnres_selected_desc* d, const MultiShape& ms) {
+  return d->K > ms.mq_max || (d->K >= 4 && d->S + d->K <= 16);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1531,7 +1537,7 @@ attnres_status attnres_selected_workspace_bytes(const attnres_selected_desc* d, 
   if ((st = plan_sel_bwd(d, ms, &pl)) != ATTNRES_OK) return st;
   *bytes = pl.bytes;
   // or the matrix-core backward's, when it may serve the call (dense rows assumed here)
-  if (ms.base.bf16 && d->K > ms.mq_max && d->N > 0) {
+  if (ms.base.bf16 && sel_mfma_slots(d, ms) && d->N > 0) {
     MultiBwdPlan mp;
     if (plan_mfma_bwd(d->S, d->D, d->R, d->K, true, d->E, d->N, d->accumulate_dvalues != 0, d->D,
                       d->D, &mp) == ATTNRES_OK &&
@@ -1749,12 +1755,13 @@ attnres_status attnres_selected_bwd(const attnres_selected_desc* d, const attnre
   if ((st = check_disjoint(outs, ins)) != ATTNRES_OK) return st;
 
   char* ws = static_cast<char*>(workspace);
-  // bf16 slots that the slot-group kernel would take in two or more launches: one pass on matrix
-  // cores when the shape and the bank fit (dvalues rounded once). Slots it takes in one launch
-  // stay there, measured faster (S = 10, N = 32768, D = 4096, E = 8: backward 1.70 / 2.09 ms for
-  // three / four slots against 2.12 / 2.13 ms on matrix cores)
+  // one pass on matrix cores (dvalues rounded once) for bf16 slots that the slot-group kernel
+  // would take in two or more launches, and for four or more slots that fit the compact tile with
+  // the sources (S + K <= 16), when the shape and the bank fit. Measured at S = 10, N = 32768,
+  // D = 4096, E = 8 (backward ms, slot groups / compact tile): three slots 1.70 / 1.82, four 2.09 /
+  // 1.87; six 1.95 compact against 2.21 for the separate-tile kernel
   MultiBwdPlan mp;
-  if (N > 0 && ms.base.bf16 && K > ms.mq_max && aligned(bank, 16)) {
+  if (N > 0 && ms.base.bf16 && sel_mfma_slots(d, ms) && aligned(bank, 16)) {
     st = plan_mfma_bwd(d->S, d->D, d->R, (int)K, true, d->E, N, d->accumulate_dvalues != 0,
                        values->row_stride, dvalues->row_stride, &mp);
     if (st != ATTNRES_OK) return st;

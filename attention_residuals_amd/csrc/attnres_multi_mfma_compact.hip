@@ -34,40 +34,46 @@ constexpr int kCompactDqRows = 4;          // fused dq: at most four queries
 
 }  // namespace
 
-// LDS: the dq sums ([4][D + 8] FP32, with dq), the queries as M + 1 padded rows (the last zero),
-// the waves' exchange, p and a, and the B partial sums.
-size_t multi_bwd_compact_lds(int nt, bool dq, int M) {
+// LDS: the dq sums ([4][D + 8] FP32, with dq), the queries (selected read: the bank) as rows + 1
+// padded rows (the last zero), the waves' exchange, p and a, the B partial sums and the slots'
+// bank rows.
+size_t multi_bwd_compact_lds(int nt, bool dq, int rows) {
   const size_t D = (size_t)nt * kMfmaWaves * 32;
   return (dq ? (size_t)kCompactDqRows * (D + 8) * sizeof(float) : 0) +
-         (size_t)(M + 1) * (D + tiles::kRowPad) * 2 +
-         ((size_t)kMfmaWaves * kCompactXch + 512 + 64) * sizeof(float);
+         (size_t)(rows + 1) * (D + tiles::kRowPad) * 2 +
+         ((size_t)kMfmaWaves * kCompactXch + 512 + 64 + 16) * sizeof(float);
 }
 
-template <int NT, bool FULL, bool ACC, bool DQ>
+// SEL: the selected read (M = slots per token; slot m of token n reads bank row ids[n, m], a zero
+// row for ids outside [0, E)); the dq kernel then forms dbank from a summed per bank row.
+template <int NT, bool FULL, bool ACC, bool DQ, bool SEL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 8)))
 void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
+  static_assert(!SEL || !DQ, "the selected read forms dbank in the dq kernel");
   constexpr int W = kMfmaWaves;
   constexpr int D = NT * W * 32;
   constexpr int QP = D + kRowPad;  // staged row pitch (bf16 elements)
   constexpr int DQS = D + 8;       // dq row stride (floats)
   extern __shared__ float lds[];
   const int M = a.M, S = a.S;
+  const int QR = SEL ? a.E : M;  // staged rows
   float* dql = lds;                                                            // DQ: [4][DQS]
-  char* qrows = reinterpret_cast<char*>(lds + (DQ ? kCompactDqRows * DQS : 0));  // [M + 1][QP]
-  float* xch = reinterpret_cast<float*>(qrows + (size_t)(M + 1) * QP * 2);     // [W][kCompactXch]
+  char* qrows = reinterpret_cast<char*>(lds + (DQ ? kCompactDqRows * DQS : 0));  // [QR + 1][QP]
+  float* xch = reinterpret_cast<float*>(qrows + (size_t)(QR + 1) * QP * 2);    // [W][kCompactXch]
   float* pa = xch + W * kCompactXch;                                           // p, a [16][16]
   float* bpart = pa + 512;                                                     // [4][16]
+  int* sid = reinterpret_cast<int*>(bpart + 64);                               // SEL: [16]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
   const mb_u32x4 zero4 = {0u, 0u, 0u, 0u};
   const int col_w = wave * NT * 32 + 8 * g;
   auto keyok = [&](int t) { return FULL || col_w + 32 * t >= a.lo; };
 
-  // the queries as full-width rows, zero before the key slice; row M zero
-  for (int idx = tid; idx < (M + 1) * (D / 8); idx += W * 64) {
+  // the queries (the bank) as full-width rows, zero before the key slice; row QR zero
+  for (int idx = tid; idx < (QR + 1) * (D / 8); idx += W * 64) {
     const int e = idx / (D / 8), j = 8 * (idx - e * (D / 8));
     mb_u32x4 v = zero4;
-    if (e < M && j >= a.lo)
+    if (e < QR && j >= a.lo)
       v = *reinterpret_cast<const mb_u32x4*>(static_cast<const char*>(a.query) +
                                               ((int64_t)e * a.R + (j - a.lo)) * 2);
     *reinterpret_cast<mb_u32x4*>(qrows + ((size_t)e * QP + j) * 2) = v;
@@ -102,9 +108,20 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
     const mb_u32x4 x = ld16(vdst + n * a.drow_stride * 2 + 64 * t);
     return vrow ? x : zero4;
   };
-  // query c at the lane's eight columns of tile t (the zero row for lanes past M)
-  const int qrow = c < M ? c : M;
-  auto ld_q = [&](int t) {
+  // the staged row query (slot) c reads for token n: c itself, or the bank row its id names (row
+  // QR, zero, for lanes past M and ids outside [0, E))
+  const int fixed_row = c < M ? c : QR;
+  auto slot_row = [&](int64_t n) {
+    if constexpr (!SEL) return fixed_row;
+    int r = QR;
+    if (c < M) {
+      const int64_t id = a.ids[n * M + c];
+      r = (id >= 0 && id < a.E) ? (int)id : a.E;
+    }
+    return r;
+  };
+  // that row at the lane's eight columns of tile t
+  auto ld_q = [&](int t, int qrow) {
     return *reinterpret_cast<const mb_u32x4*>(qrows + ((size_t)qrow * QP + col_w + 32 * t) * 2);
   };
   const mb_u32x2 ident = identity_operand(g, c);
@@ -113,11 +130,11 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
   mb_float4 tsc, tg, tk;
   // scores, Gram matrix and key sums of squares of a token's rows X (after the exchange barrier
   // the 8 waves' tiles sit in LDS)
-  auto contract = [&](const mb_u32x4 (&X)[NT]) {
+  auto contract = [&](const mb_u32x4 (&X)[NT], int qrow) {
     tsc = tg = tk = mb_float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      tsc = mfma_k32(ld_q(t), X[t], tsc);
+      tsc = mfma_k32(ld_q(t, qrow), X[t], tsc);
       tg = mfma_k32(X[t], X[t], tg);
       if constexpr (!FULL) {
         const mb_u32x4 xm = keyok(t) ? X[t] : zero4;
@@ -134,7 +151,8 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
   };
   const int pm = tid >> 4, ps = tid & 15;  // (query, source) finished by thread tid < 256
   // the pairs of token n: routing weight, delta, a and the B terms into LDS
-  auto pairs = [&](int64_t n, float lse_t) {
+  auto pairs = [&](int64_t n, float lse_t, int qrow) {
+    if (SEL && tid < 16) sid[tid] = qrow;  // lanes 0 .. 15 of wave 0 hold slots 0 .. 15
     if (tid < 256) {
       const int drow = S + pm < 16 ? S + pm : 15;  // X row of query pm's dY
       float sc = 0.f, dpv = 0.f, ss = 0.f;
@@ -153,7 +171,7 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
       const float bt = valid ? -av * scv.rho * scv.rho * sc * a.inv_R : 0.f;
       pa[pm * 16 + ps] = p;
       pa[256 + pm * 16 + ps] = av;
-      if constexpr (!DQ) a.coef[n * 256 + tid] = av;
+      if constexpr (!DQ && !SEL) a.coef[n * 256 + tid] = av;
       const float bs = rows4_sum(bt);  // over this wave's four queries
       if (lane < 16) bpart[wave * 16 + ps] = bs;
     }
@@ -163,7 +181,7 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
   };
 
   // dv of token n from its rows X (weights in LDS)
-  auto dv = [&](const mb_u32x4 (&X)[NT], int64_t n) {
+  auto dv = [&](const mb_u32x4 (&X)[NT], int64_t n, int qrow) {
     // B operands (k = rows of X, then queries): lane (g, c) holds the weights of rows 4g .. 4g+3
     // for output source c, p of the dY rows (zero for the source rows) and a of the queries
     mb_u32x2 py_hi, py_lo, aq_hi, aq_lo;
@@ -177,6 +195,22 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
       }
       split4(pv, py_hi, py_lo);
       split4(av, aq_hi, aq_lo);
+    }
+    if constexpr (SEL) {
+      // the dq kernel's coefficients: a of bank rows 4g .. 4g+3 with source c, the token's slots
+      // summed per bank row in slot order (slots reading no bank row add to none)
+      float ab[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < M; ++k) {
+        const int e = sid[k] - 4 * g;
+        const float ak = pa[256 + k * 16 + c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (e == i && sid[k] < a.E) ab[i] += ak;
+      }
+      if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.coef[n * 256 + (4 * g + i) * 16 + c] = ab[i];
+      }
     }
     const float bsrc = ((bpart[c] + bpart[16 + c]) + bpart[32 + c]) + bpart[48 + c];
     // dq A operands: output row r = m + 8h (m = r % 8) takes a[m][4g + i] in slots 4h .. 4h+3
@@ -206,7 +240,7 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
       if constexpr (ACC) {
         if (t + 2 < NT) old[t + 2] = ld_old(t + 2, n);
       }
-      const mb_u32x4 qop = ld_q(t);
+      const mb_u32x4 qop = ld_q(t, qrow);
       float f[8];
       mb_u32x2 xt[2];
 #pragma unroll
@@ -254,17 +288,19 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
   };
 
   mb_u32x4 XA[NT], XB[NT];
+  int qa = 0, qb = 0;  // the staged rows the tokens in XA and XB read
   int64_t n = blockIdx.x;
   const float lse0 = load_lse(n);
+  qa = slot_row(n);
 #pragma unroll
   for (int t = 0; t < NT; ++t) XA[t] = ld_x(t, n);
-  contract(XA);
+  contract(XA, qa);
   __syncthreads();
-  pairs(n, lse0);
+  pairs(n, lse0, qa);
   __syncthreads();
   // one token: the next token's rows go into the other set first, then this token's dv, then the
   // next token's contractions and pairs; false when there is no next token
-  auto step = [&](const mb_u32x4 (&Xc)[NT], mb_u32x4 (&Xn)[NT]) {
+  auto step = [&](const mb_u32x4 (&Xc)[NT], int qc, mb_u32x4 (&Xn)[NT], int& qn) {
     const int64_t next = n + gridDim.x;
     const bool more = next < a.N;
     float lse_n = 0.f;
@@ -272,17 +308,18 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) Xn[t] = ld_x(t, next);
       lse_n = load_lse(next);
+      qn = slot_row(next);
     }
-    dv(Xc, n);
+    dv(Xc, n, qc);
     if (!more) return false;
-    contract(Xn);
+    contract(Xn, qn);
     __syncthreads();
-    pairs(next, lse_n);
+    pairs(next, lse_n, qn);
     __syncthreads();
     n = next;
     return true;
   };
-  while (step(XA, XB) && step(XB, XA)) {
+  while (step(XA, qa, XB, qb) && step(XB, qb, XA, qa)) {
   }
 
   // this workgroup's dq partial row [M][R] (key columns)
@@ -296,17 +333,21 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
   }
 }
 
-#define ATTNRES_COMPACT_K(NT, DQ)                                                                \
-  (acc ? (full ? (const void*)&multi_bwd_compact_kernel<NT, true, true, DQ>                      \
-               : (const void*)&multi_bwd_compact_kernel<NT, false, true, DQ>)                    \
-       : (full ? (const void*)&multi_bwd_compact_kernel<NT, true, false, DQ>                     \
-               : (const void*)&multi_bwd_compact_kernel<NT, false, false, DQ>))
+#define ATTNRES_COMPACT_K(NT, DQ, SEL)                                                           \
+  (acc ? (full ? (const void*)&multi_bwd_compact_kernel<NT, true, true, DQ, SEL>                 \
+               : (const void*)&multi_bwd_compact_kernel<NT, false, true, DQ, SEL>)               \
+       : (full ? (const void*)&multi_bwd_compact_kernel<NT, true, false, DQ, SEL>                \
+               : (const void*)&multi_bwd_compact_kernel<NT, false, false, DQ, SEL>))
 
-#define ATTNRES_COMPACT_NT(NT) \
-  case NT: return dq ? ATTNRES_COMPACT_K(NT, true) : ATTNRES_COMPACT_K(NT, false);
+#define ATTNRES_COMPACT_NT(NT)                                                                   \
+  case NT:                                                                                       \
+    return sel ? ATTNRES_COMPACT_K(NT, false, true)                                              \
+               : (dq ? ATTNRES_COMPACT_K(NT, true, false) : ATTNRES_COMPACT_K(NT, false, false));
 
-// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); dq: dq summed in LDS (M <= 4)
-const void* multi_bwd_compact_kernel_ptr(int nt, bool dq, bool full, bool acc) {
+// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); dq: dq summed in LDS (M <= 4, not
+// with sel); sel: the selected read
+const void* multi_bwd_compact_kernel_ptr(int nt, bool dq, bool full, bool acc, bool sel) {
+  if (sel && dq) return nullptr;
   switch (nt) {
     ATTNRES_COMPACT_NT(4) ATTNRES_COMPACT_NT(8) ATTNRES_COMPACT_NT(12) ATTNRES_COMPACT_NT(16)
     default: break;

@@ -251,10 +251,11 @@ attnres_status attnres_multi_bwd(const attnres_multi_desc* desc, const attnres_s
  * conditions for it; else the optional forward workspace holds the token counter of 9 to 16 slots,
  * as in the multi-query read); otherwise slots run in groups of at most four. The backward runs
  * slots in groups of at most four (two with S > 10 or two chunks per thread); when that takes two
- * or more groups, 3 <= K <= 16 bf16 slots instead run in one pass on matrix cores under the
- * multi-query read's conditions when E <= 16 and the bank fits in a workgroup's LDS (as E + 1 rows
- * and as transposed groups of four: E <= 8 at D = 4096), dbank formed by a second pass over the
- * key slice; otherwise later groups add into dvalues.
+ * or more groups, or with 4 <= K and S + K <= 16, bf16 slots instead run in one pass on matrix
+ * cores under the multi-query read's conditions when E <= 16 and the bank fits in a workgroup's
+ * LDS (as E + 1 rows, and unless S + K <= 16 also as transposed groups of four: E <= 8 at
+ * D = 4096), dbank formed by a second pass over the key slice; otherwise later groups add into
+ * dvalues.
  * The bank gradient goes through per-workgroup FP32 partial rows of the whole bank (the workspace
  * is 256 + P * E * R * 4 bytes, P = backward workgroups, or the matrix-core backward's
  * coefficients and partial rows), so a large bank costs workspace and traffic; E * R * 4 must stay

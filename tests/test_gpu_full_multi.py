@@ -81,7 +81,7 @@ def test_multi_query_full_size_forward_sixteen_slots():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("E,K", [(8, 2), (8, 4), (8, 8)])  # slot groups; K = 8: matrix cores
+@pytest.mark.parametrize("E,K", [(8, 2), (8, 4), (8, 8)])  # slot groups, compact tile, separate tiles
 def test_selected_query_full_size(E, K):
     import attention_residuals_amd as A
     w = HEADLINE

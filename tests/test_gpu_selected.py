@@ -95,12 +95,12 @@ def _check(V, bank, ids, G, label, dtype, init=None, ref_bank=None, ref_ids=None
     (24, 199, 2048, 640, 5, 2, "bf16"),
     (4, 200, 512, 512, 1, 3, "bf16"),       # every slot names the same row
     (12, 333, 1024, 1024, 40, 2, "bf16"),   # many rows (global blocks)
-    (10, 301, 4096, 4096, 8, 4, "bf16"),    # four slots in one backward launch, LDS bank
+    (10, 301, 4096, 4096, 8, 4, "bf16"),    # four slots: the compact matrix-core backward
     (8, 257, 1024, 1024, 4, 4, "f32"),      # four slots, FP32
     (10, 211, 2048, 2048, 24, 7, "bf16"),   # seven slots: groups of four and three, global blocks
     (6, 149, 2048, 2048, 40, 4, "bf16"),    # a bank too large to stage: the slot-group forward
     # the one-pass matrix-core backward (bf16 slots beyond one slot-group launch: K > 4, or K > 2
-    # with S > 10; E <= 16, D = 256 nt)
+    # with S > 10; or 4 <= K with S + K <= 16, the compact tile; E <= 16, D = 256 nt)
     (16, 257, 4096, 4096, 6, 16, "bf16"),   # sixteen slots and sources
     (12, 211, 2048, 2048, 8, 3, "bf16"),    # three slots, twelve sources
     (5, 300, 3072, 1024, 3, 9, "bf16"),     # twelve column tiles per wave, sliced key
@@ -112,7 +112,8 @@ def test_selected_parity(S, N, D, R, E, K, dtype):
     _check(V, bank, ids, G, f"selected S={S} N={N} D={D} R={R} E={E} K={K} {dtype}", dtype)
 
 
-@pytest.mark.parametrize("K,dynamic", [(2, False), (2, True), (3, True), (4, False), (4, True)])
+@pytest.mark.parametrize("K,dynamic", [(2, False), (2, True), (3, True), (4, False), (4, True),
+                                       (6, True)])  # six slots: the compact matrix-core backward
 def test_selected_several_tokens_per_workgroup(K, dynamic):
     # every workgroup reads several tokens (static grid of 8x the resident count, or tickets), so
     # the next token's ids, bank rows and source rows loaded one token ahead are checked
@@ -161,7 +162,7 @@ def test_selected_ids_outside_the_bank_set_the_workspace_flag(K):
     assert A.attnres_selected_ids_flag(ws)
 
 
-@pytest.mark.parametrize("K,packed", [(2, True), (3, False), (4, True)])
+@pytest.mark.parametrize("K,packed", [(2, True), (3, False), (4, True), (6, False)])
 def test_selected_accumulate_into_dvalues(K, packed):
     S, N, D, R, E = 6, 301, 2048, 2048, 6
     print(f"[case] selected accumulate K={K} packed={packed}", flush=True)
