@@ -62,12 +62,15 @@ def _replay_and_compare(capture_step, eager_step, bufs, inputs, outs, reduced, d
         check_oracle(xin)
 
 
-# M = 5: the matrix-core forward's eight-slot kernel (static stride); M = 12: its sixteen-slot
-# kernel, which takes tokens from the forward workspace's counter unless deterministic
-@pytest.mark.parametrize("M,deterministic", [(5, True), (5, False), (12, True), (12, False)])
-def test_multi_query_graph_replay(M, deterministic):
+# D = 2048: the tile forward, and the compact (M = 5) or separate-tile (M = 12) matrix-core
+# backward; D = 1280: the older matrix-core forward, whose sixteen-slot kernel takes tokens from the
+# forward workspace's counter unless deterministic, and the query-group backward
+@pytest.mark.parametrize("M,D,deterministic", [(5, 2048, True), (5, 2048, False), (12, 2048, True),
+                                               (12, 2048, False), (12, 1280, True),
+                                               (12, 1280, False)])
+def test_multi_query_graph_replay(M, D, deterministic):
     import attention_residuals_amd as A
-    S, N, D = 6, 1531, 2048
+    S, N = 6, 1531
     inputs = []
     for seed in (21, 22):
         V, g = _sources(S, N, D, seed)
@@ -116,13 +119,15 @@ def test_multi_query_graph_replay(M, deterministic):
             res[f"dq{m}"] = compare_vec(to_f64(dq[m]), ref["dq"][m], "bf16")
         assert_ok(res, f"multi graph replay M={M} deterministic={deterministic}")
 
-    print(f"[case] multi graph M={M} deterministic={deterministic}", flush=True)
+    print(f"[case] multi graph M={M} D={D} deterministic={deterministic}", flush=True)
     _replay_and_compare(step, eager, bufs, inputs, {"y": y, "lse": lse, "dv": dv}, {"dq": dq},
                         deterministic, check)
 
 
+# K = 3: the slot-group backward; K = 6: the compact matrix-core backward; K = 12: the
+# separate-tile one
 @pytest.mark.parametrize("E,K,deterministic", [(6, 3, True), (6, 3, False), (48, 3, False),
-                                               (6, 12, False)])
+                                               (6, 6, False), (6, 12, False)])
 def test_selected_query_graph_replay(E, K, deterministic):
     import attention_residuals_amd as A
     S, N, D = 6, 1531, 2048
