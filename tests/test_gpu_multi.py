@@ -119,7 +119,11 @@ def _check(V, Q, G, label, dtype, init=None, f32_tol=None, **kw):
     # its own LDS (no second pass over the sources)
     (14, 300, 2048, 2048, 4, "bf16", "token_major"),
     (16, 201, 1024, 512, 3, "bf16", "query_major"),
-    (13, 150, 3072, 3072, 3, "bf16", "query_major"),
+    (13, 150, 3072, 3072, 3, "bf16", "query_major"),   # compact tile (S + M = 16), dq in LDS
+    # sources and dY rows in one tile (S + M <= 16) with dq formed by the dq kernel
+    (9, 257, 4096, 1024, 7, "bf16", "query_major"),    # sliced key, sixteen rows
+    (4, 300, 1024, 1024, 12, "bf16", "token_major"),
+    (2, 199, 3072, 3072, 14, "bf16", "query_major"),
 ])
 def test_multi_query_parity(S, N, D, R, M, dtype, layout):
     V, Q, G = _inputs(S, N, D, R, M, dtype, seed=2000 + S * M + D)

@@ -102,7 +102,9 @@ def _check(V, bank, ids, G, label, dtype, init=None, ref_bank=None, ref_ids=None
     # the one-pass matrix-core backward (bf16 slots beyond one slot-group launch: K > 4, or K > 2
     # with S > 10; or 4 <= K with S + K <= 16, the compact tile; E <= 16, D = 256 nt)
     (16, 257, 4096, 4096, 6, 16, "bf16"),   # sixteen slots and sources
-    (12, 211, 2048, 2048, 8, 3, "bf16"),    # three slots, twelve sources
+    (12, 211, 2048, 2048, 8, 3, "bf16"),    # three slots, twelve sources (compact tile)
+    (4, 200, 1024, 256, 8, 6, "bf16"),      # compact tile, sliced key
+    (9, 129, 4096, 4096, 7, 7, "bf16"),     # compact tile, sixteen rows
     (5, 300, 3072, 1024, 3, 9, "bf16"),     # twelve column tiles per wave, sliced key
     (12, 150, 1024, 1024, 16, 5, "bf16"),   # sixteen bank rows
 ])
