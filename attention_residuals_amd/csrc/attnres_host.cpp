@@ -991,8 +991,9 @@ struct MultiBwdPlan {
 
 // The one-pass matrix-core backward: every query's gradient in one pass over the sources, so
 // dvalues are written (and rounded) once. One workgroup per CU over a static token stride, the
-// queries staged in its LDS. With M <= 4 each workgroup also sums dq for its tokens in LDS and
-// writes one [M * R] partial row; otherwise the per-token coefficients a_{m,s} go to the workspace
+// queries staged in its LDS. With M <= 4 (the compact tile: M <= 8 where the sums fit its LDS) each
+// workgroup also sums dq for its tokens in LDS and writes one [M * R] partial row; otherwise the
+// per-token coefficients a_{m,s} go to the workspace
 // ([N][16][16] FP32) and the dq kernel reads the key slice of the sources again over static token
 // ranges (about two workgroups per CU). The finaliser adds the partial rows in a fixed order.
 // Rows of D = 256 nt columns (nt = 4, 8, 12 or 16 tiles of 32 columns per wave), R and the row
@@ -1010,7 +1011,7 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
       (nt != 4 && nt != 8 && nt != 12 && nt != 16) || R % 8 != 0 || row_stride % 8 != 0 ||
       drow_stride % 8 != 0 || (sel && (E < 1 || E > 16)))
     return ATTNRES_OK;
-  const int dqm = (!sel && M <= 4) ? 1 : 0;
+  int dqm = (!sel && M <= 4) ? 1 : 0;
   DevFacts f;
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
@@ -1021,8 +1022,14 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
   int qm = 0;
   size_t lds = 0;
   if (compact) {
-    lds = multi_bwd_compact_lds(nt, dqm != 0, sel ? E : M);
+    // dq summed in the kernel's LDS for up to eight queries where the sums fit beside the staged
+    // queries (backward call at S = 10, N = 32768, D = 4096: M = 6 1.99 ms with the dq pass over
+    // the sources, 1.75 ms with the sums in LDS; M = 5 1.86 / 1.62 ms)
+    const bool cdq =
+        !sel && M <= 8 && multi_bwd_compact_lds(nt, true, M, M) <= (size_t)f.lds_per_block;
+    lds = multi_bwd_compact_lds(nt, cdq, sel ? E : M, M);
     compact = lds <= (size_t)f.lds_per_block;
+    if (compact) dqm = cdq ? 1 : 0;
   }
   if (!compact) {
     // the queries also as full rows where they fit (M <= 8): the score operand without transposes

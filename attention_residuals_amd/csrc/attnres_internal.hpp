@@ -82,7 +82,7 @@ const void* stream_probe_kernel_ptr(int cpt);
 size_t multi_bwd_mfma_lds(int nt, int dqm, int M, int qm, int E);
 // The multi-query backward with the sources and dY rows in one 16-row tile (S + M <= 16).
 const void* multi_bwd_compact_kernel_ptr(int nt, bool dq, bool full, bool acc, bool sel);
-size_t multi_bwd_compact_lds(int nt, bool dq, int rows);
+size_t multi_bwd_compact_lds(int nt, bool dq, int rows, int M);
 const void* sel_bwd_kernel_ptr_bf16(int ch, int sb, bool full, bool acc, int mq);
 const void* sel_bwd_kernel_ptr_f32(int ch, int sb, bool full, bool acc, int mq);
 const void* ticket_reset_kernel_ptr();

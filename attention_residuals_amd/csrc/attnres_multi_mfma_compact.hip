@@ -17,9 +17,9 @@
 //   * dv^T per 16-column half: an identity MFMA transposes X (its rows into the k slots) for two
 //     16x16x16 MFMAs with p as two bf16 terms (zero for the source rows); another transposes the
 //     query rows for two with a; B_s t_s is added on the vector ALU and each dv chunk rounded once.
-//   * dq with M <= 4: summed per workgroup in LDS from the same transposed X (a is zero past the
-//     source rows) and written as one partial row; otherwise the token's a_{m,s} go to the
-//     workspace and the dq kernel forms dq.
+//   * dq with M <= 8 where the sums fit the LDS: summed per workgroup in LDS from the same
+//     transposed X (a is zero past the source rows) and written as one partial row; otherwise the
+//     token's a_{m,s} go to the workspace and the dq kernel forms dq.
 #include "attnres_internal.hpp"
 #include "attnres_kernels.hpp"
 #include "attnres_mfma_tiles.hpp"
@@ -29,19 +29,22 @@ namespace {
 
 using namespace tiles;
 
-constexpr int kCompactXch = 2 * 256 + 16;  // a wave's score and Gram tiles and 16 sums of squares
-constexpr int kCompactDqRows = 4;          // fused dq: at most four queries
+// a wave's exchange (FP32): the score rows of up to QX queries (slots), the dY-by-source rows of
+// its Gram tile for those queries and 16 sums of squares; QX = 8 with dq summed in LDS (M <= 8),
+// else 16
+constexpr int compact_qx(bool dq) { return dq ? 8 : 16; }
+constexpr int compact_xch(bool dq) { return 2 * compact_qx(dq) * 16 + 16; }
 
 }  // namespace
 
-// LDS: the dq sums ([4][D + 8] FP32, with dq), the queries (selected read: the bank) as rows + 1
-// padded rows (the last zero), the waves' exchange, p and a, the B partial sums and the slots'
-// bank rows.
-size_t multi_bwd_compact_lds(int nt, bool dq, int rows) {
+// LDS: the dq sums ([M][D + 8] FP32, with dq) and a scratch row for the rows past M of a lane's
+// group of four ([32 nt + 32] FP32), the queries (selected read: the bank) as padded rows, the
+// waves' exchange, p and a, the B partial sums and the slots' bank rows.
+size_t multi_bwd_compact_lds(int nt, bool dq, int rows, int M) {
   const size_t D = (size_t)nt * kMfmaWaves * 32;
-  return (dq ? (size_t)kCompactDqRows * (D + 8) * sizeof(float) : 0) +
-         (size_t)(rows + 1) * (D + tiles::kRowPad) * 2 +
-         ((size_t)kMfmaWaves * kCompactXch + 512 + 64 + 16) * sizeof(float);
+  return (dq ? ((size_t)M * (D + 8) + 32 * nt + 32) * sizeof(float) : 0) +
+         (size_t)rows * (D + tiles::kRowPad) * 2 +
+         ((size_t)kMfmaWaves * compact_xch(dq) + 512 + 64 + 16) * sizeof(float);
 }
 
 // SEL: the selected read (M = slots per token; slot m of token n reads bank row ids[n, m], a zero
@@ -57,10 +60,12 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
   extern __shared__ float lds[];
   const int M = a.M, S = a.S;
   const int QR = SEL ? a.E : M;  // staged rows
-  float* dql = lds;                                                            // DQ: [4][DQS]
-  char* qrows = reinterpret_cast<char*>(lds + (DQ ? kCompactDqRows * DQS : 0));  // [QR + 1][QP]
-  float* xch = reinterpret_cast<float*>(qrows + (size_t)(QR + 1) * QP * 2);    // [W][kCompactXch]
-  float* pa = xch + W * kCompactXch;                                           // p, a [16][16]
+  constexpr int QX = compact_qx(DQ), XS = compact_xch(DQ);
+  float* dql = lds;                                                    // DQ: [M][DQS]
+  float* dqx = dql + M * DQS;                                          // DQ: [32 NT + 32]
+  char* qrows = reinterpret_cast<char*>(lds + (DQ ? M * DQS + 32 * NT + 32 : 0));  // [QR][QP]
+  float* xch = reinterpret_cast<float*>(qrows + (size_t)QR * QP * 2);         // [W][XS]
+  float* pa = xch + W * XS;                                                   // p, a [16][16]
   float* bpart = pa + 512;                                                     // [4][16]
   int* sid = reinterpret_cast<int*>(bpart + 64);                               // SEL: [16]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -69,17 +74,17 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
   const int col_w = wave * NT * 32 + 8 * g;
   auto keyok = [&](int t) { return FULL || col_w + 32 * t >= a.lo; };
 
-  // the queries (the bank) as full-width rows, zero before the key slice; row QR zero
-  for (int idx = tid; idx < (QR + 1) * (D / 8); idx += W * 64) {
+  // the queries (the bank) as full-width rows, zero before the key slice
+  for (int idx = tid; idx < QR * (D / 8); idx += W * 64) {
     const int e = idx / (D / 8), j = 8 * (idx - e * (D / 8));
     mb_u32x4 v = zero4;
-    if (e < QR && j >= a.lo)
+    if (j >= a.lo)
       v = *reinterpret_cast<const mb_u32x4*>(static_cast<const char*>(a.query) +
                                               ((int64_t)e * a.R + (j - a.lo)) * 2);
     *reinterpret_cast<mb_u32x4*>(qrows + ((size_t)e * QP + j) * 2) = v;
   }
   if constexpr (DQ) {
-    for (int i = tid; i < kCompactDqRows * DQS; i += W * 64) dql[i] = 0.f;
+    for (int i = tid; i < M * DQS; i += W * 64) dql[i] = 0.f;
   }
 
   // lane (g, c) streams row c of X: source c, or the dY row of query c - S; lanes past S + M read
@@ -108,9 +113,10 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
     const mb_u32x4 x = ld16(vdst + n * a.drow_stride * 2 + 64 * t);
     return vrow ? x : zero4;
   };
-  // the staged row query (slot) c reads for token n: c itself, or the bank row its id names (row
-  // QR, zero, for lanes past M and ids outside [0, E))
-  const int fixed_row = c < M ? c : QR;
+  // the staged row query (slot) c reads for token n: c itself (lanes past M: the last query, since
+  // their score rows are never used and their weights a are zero), or the bank row its id names
+  // (QR, read as zeros, for lanes past M and ids outside [0, E))
+  const int fixed_row = c < M ? c : M - 1;
   auto slot_row = [&](int64_t n) {
     if constexpr (!SEL) return fixed_row;
     int r = QR;
@@ -120,11 +126,22 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
     }
     return r;
   };
-  // that row at the lane's eight columns of tile t
+  // that row at the lane's eight columns of tile t (row QR of the selected read: zeros)
   auto ld_q = [&](int t, int qrow) {
-    return *reinterpret_cast<const mb_u32x4*>(qrows + ((size_t)qrow * QP + col_w + 32 * t) * 2);
+    const int r = (SEL && qrow >= QR) ? 0 : qrow;
+    const mb_u32x4 v =
+        *reinterpret_cast<const mb_u32x4*>(qrows + ((size_t)r * QP + col_w + 32 * t) * 2);
+    if constexpr (SEL) return qrow < QR ? v : zero4;
+    return v;
   };
   const mb_u32x2 ident = identity_operand(g, c);
+  // the dq sums of this lane, rows m0 + i = 4(g % 2) + i at its column of tile 0 (tile t adds 32 t
+  // floats); rows past M go to the scratch row, whose contents are never used
+  const int m0 = 4 * (g & 1), dcol = 8 * (c >> 2) + (c & 3) + 4 * (g >> 1);
+  float* dqp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dqp[i] = (m0 + i < M) ? dql + (m0 + i) * DQS + wave * NT * 32 + dcol : dqx + dcol;
   __syncthreads();
 
   mb_float4 tsc, tg, tk;
@@ -141,12 +158,13 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
         tk = mfma_k32(xm, xm, tk);
       }
     }
-    float* xw = xch + wave * kCompactXch;
+    float* xw = xch + wave * XS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xw[(4 * g + i) * 16 + c] = tsc[i];       // score of query 4g + i with row c
-      xw[256 + (4 * g + i) * 16 + c] = tg[i];  // <row 4g + i, row c>
-      if (4 * g + i == c) xw[512 + c] = FULL ? tg[i] : tk[i];
+      const int r = 4 * g + i;
+      if (r < QX) xw[r * 16 + c] = tsc[i];  // score of query r with row c
+      if (r >= S && r < S + M) xw[(QX + r - S) * 16 + c] = tg[i];  // <dY row of query r - S, row c>
+      if (r == c) xw[2 * QX * 16 + c] = FULL ? tg[i] : tk[i];
     }
   };
   const int pm = tid >> 4, ps = tid & 15;  // (query, source) finished by thread tid < 256
@@ -154,14 +172,14 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
   auto pairs = [&](int64_t n, float lse_t, int qrow) {
     if (SEL && tid < 16) sid[tid] = qrow;  // lanes 0 .. 15 of wave 0 hold slots 0 .. 15
     if (tid < 256) {
-      const int drow = S + pm < 16 ? S + pm : 15;  // X row of query pm's dY
+      const int qm = pm < M ? pm : 0;  // exchange row read (queries past M are masked below)
       float sc = 0.f, dpv = 0.f, ss = 0.f;
 #pragma unroll
       for (int w = 0; w < W; ++w) {  // wave order: a fixed summation order
-        const float* x = xch + w * kCompactXch;
-        sc += x[pm * 16 + ps];
-        dpv += x[256 + drow * 16 + ps];
-        ss += x[512 + ps];
+        const float* x = xch + w * XS;
+        sc += x[qm * 16 + ps];
+        dpv += x[(QX + qm) * 16 + ps];
+        ss += x[2 * QX * 16 + ps];
       }
       const bool valid = pm < M && ps < S;
       const Score scv = source_score(ss, sc, a.inv_R, a.eps, a.scale);
@@ -265,19 +283,19 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
       }
       if constexpr (DQ) {
         // the sources in the k slots (a is zero past them); output row 4g + i is query
-        // 4(g % 2) + i of half g / 2 (rows of queries 4 .. 7 are zero)
+        // m0 + i = 4(g % 2) + i of half g / 2 (queries past M have zero rows; lanes whose four
+        // queries are all past M skip the sums)
         const mb_u32x4 b = {xt[0][0], xt[0][1], xt[1][0], xt[1][1]};
         mb_float4 acc = {0.f, 0.f, 0.f, 0.f};
-        float* acc_p = dql + (wave * NT + t) * 32 + 8 * (c >> 2) + (c & 3) + 4 * (g >> 1);
-        if (!(g & 1)) {
+        if (m0 < M) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = acc_p[i * DQS];
+          for (int i = 0; i < 4; ++i) acc[i] = dqp[i][32 * t];
         }
         acc = mfma_k32(dqa_hi, b, acc);
         acc = mfma_k32(dqa_lo, b, acc);
-        if (!(g & 1)) {
+        if (m0 < M) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc_p[i * DQS] = acc[i];
+          for (int i = 0; i < 4; ++i) dqp[i][32 * t] = acc[i];
         }
       }
       if (vrow)
@@ -344,7 +362,7 @@ void multi_bwd_compact_kernel(const MfmaBwdArgs a) {
     return sel ? ATTNRES_COMPACT_K(NT, false, true)                                              \
                : (dq ? ATTNRES_COMPACT_K(NT, true, false) : ATTNRES_COMPACT_K(NT, false, false));
 
-// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); dq: dq summed in LDS (M <= 4, not
+// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); dq: dq summed in LDS (M <= 8, not
 // with sel); sel: the selected read
 const void* multi_bwd_compact_kernel_ptr(int nt, bool dq, bool full, bool acc, bool sel) {
   if (sel && dq) return nullptr;

@@ -120,6 +120,10 @@ def _check(V, Q, G, label, dtype, init=None, f32_tol=None, **kw):
     (14, 300, 2048, 2048, 4, "bf16", "token_major"),
     (16, 201, 1024, 512, 3, "bf16", "query_major"),
     (13, 150, 3072, 3072, 3, "bf16", "query_major"),   # compact tile (S + M = 16), dq in LDS
+    # sources and dY rows in one tile (S + M <= 16), five to eight queries with dq summed in LDS
+    (10, 257, 4096, 4096, 6, "bf16", "query_major"),   # the largest that fits (~155 KiB)
+    (8, 300, 2048, 2048, 8, "bf16", "token_major"),
+    (11, 211, 3072, 1024, 5, "bf16", "token_major"),   # sliced key
     # sources and dY rows in one tile (S + M <= 16) with dq formed by the dq kernel
     (9, 257, 4096, 1024, 7, "bf16", "query_major"),    # sliced key, sixteen rows
     (4, 300, 1024, 1024, 12, "bf16", "token_major"),
