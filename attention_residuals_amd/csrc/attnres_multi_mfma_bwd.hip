@@ -25,11 +25,10 @@
 //   * As soon as a tile's dv is written, its registers take the next token's rows, and the next
 //     token's score contractions run a few tiles behind those loads, so the loads overlap the
 //     current token's work.
-//   * dq: with M <= 8 the partial sums over the workgroup's tokens sit in LDS ([8][columns] FP32,
-//     two half-tiles stacked into one 16x16x32 MFMA per term); with M <= 16 and rows of at most
-//     2048 columns, [16][columns]. Otherwise the per-token a_{m,s} go to the workspace and kernel 2
-//     forms dq. Either way one FP32 partial row per workgroup or range, summed by the finaliser in
-//     a fixed order.
+//   * dq: with M <= 4 the partial sums over the workgroup's tokens sit in LDS ([4][columns] FP32,
+//     two half-tiles stacked into one 16x16x32 MFMA per term). Otherwise the per-token a_{m,s} go
+//     to the workspace and kernel 2 forms dq. Either way one FP32 partial row per workgroup or
+//     range, summed by the finaliser in a fixed order.
 // Kernel 2 (multi_dq_mfma_kernel): dq_m[j] = sum_n sum_s a_{m,s,n} t_{s,n}[j] over a static token
 // range per workgroup (16x16x16 MFMAs with the sources as the contraction index).
 #include "attnres_internal.hpp"

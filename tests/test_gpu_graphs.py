@@ -62,8 +62,8 @@ def _replay_and_compare(capture_step, eager_step, bufs, inputs, outs, reduced, d
         check_oracle(xin)
 
 
-# D = 2048: the tile forward, and the compact (M = 5) or separate-tile (M = 12) matrix-core
-# backward; D = 1280: the older matrix-core forward, whose sixteen-slot kernel takes tokens from the
+# D = 2048: the tile forward, and the compact (M = 5, dq summed in LDS) or separate-tile (M = 12,
+# with the dq pass) matrix-core backward; D = 1280: the older matrix-core forward, whose sixteen-slot kernel takes tokens from the
 # forward workspace's counter unless deterministic, and the query-group backward
 @pytest.mark.parametrize("M,D,deterministic", [(5, 2048, True), (5, 2048, False), (12, 2048, True),
                                                (12, 2048, False), (12, 1280, True),

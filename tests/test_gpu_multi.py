@@ -155,9 +155,11 @@ def test_multi_query_several_tokens_per_workgroup(M, dynamic):
            deterministic=not dynamic)
 
 
-@pytest.mark.parametrize("S,M,packed", [(6, 2, True), (6, 6, False), (14, 3, True)])
-def test_multi_query_accumulate_into_dvalues(S, M, packed):
-    N, D, R = 301, 2048, 2048
+# (6, 6) and (10, 6) at D = 4096: the compact tile summing dq in LDS beside the accumulated rows
+@pytest.mark.parametrize("S,M,packed,D", [(6, 2, True, 2048), (6, 6, False, 2048),
+                                          (14, 3, True, 2048), (10, 6, True, 4096)])
+def test_multi_query_accumulate_into_dvalues(S, M, packed, D):
+    N, R = 301, D
     V, Q, G = _inputs(S, N, D, R, M, "bf16", seed=2100 + M)
     init = (2.0 * torch.randn((S, N, D), generator=torch.Generator().manual_seed(5))).to(V.dtype)
     _check(V, Q, G, f"multi accumulate M={M}", "bf16", init=init, accumulate=True, packed=packed)
