@@ -124,6 +124,7 @@ def _check(V, Q, G, label, dtype, init=None, f32_tol=None, **kw):
     (10, 257, 4096, 4096, 6, "bf16", "query_major"),   # the largest that fits (~155 KiB)
     (8, 300, 2048, 2048, 8, "bf16", "token_major"),
     (11, 211, 3072, 1024, 5, "bf16", "token_major"),   # sliced key
+    (9, 211, 2048, 2048, 7, "bf16", "query_major"),    # second group of four cut after three
     # sources and dY rows in one tile (S + M <= 16) with dq formed by the dq kernel
     (9, 257, 4096, 1024, 7, "bf16", "query_major"),    # sliced key, sixteen rows
     (4, 300, 1024, 1024, 12, "bf16", "token_major"),
