@@ -841,14 +841,16 @@ attnres_status try_mfma_fwd(int S, int D, int R, int M, float eps, float scale, 
     static const char* te = std::getenv("ATTNRES_MULTI_TILE_FWD");
     const int nt = D / 256;
     const int rows = sel ? E : M;
-    const size_t lds = multi_fwd_tile_lds(nt, rows);
+    // eight or more queries: outputs staged through LDS and stored as whole lines
+    const bool stg = !sel && M >= 8;
+    const size_t lds = multi_fwd_tile_lds(nt, rows, sel, stg);
     bool al = aligned(queries, 16) && aligned(y, 16) && y_sm % 8 == 0 && y_sn % 8 == 0;
     for (int s = 0; s < S && s < 16; ++s) al = al && aligned(src[s], 16);
     if (!(te && te[0] == '0') && al && bf16 && S >= 2 && S <= 16 && M >= (sel ? 3 : 5) &&
         M <= 16 &&
         D % 256 == 0 && (nt == 4 || nt == 8 || nt == 12 || nt == 16) && R % 8 == 0 &&
         row_stride % 8 == 0 && lds <= (size_t)f.lds_per_block) {
-      const void* fn = multi_fwd_tile_kernel_ptr(nt, R == D, sel);
+      const void* fn = multi_fwd_tile_kernel_ptr(nt, R == D, sel, stg);
       if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no tile multi-query forward kernel");
       int per_cu = 0;
       attnres_status st = blocks_per_cu(fn, 64 * kMfmaWaves, lds, &per_cu);

@@ -14,7 +14,11 @@
 // sources by DPP, lse. The mixture runs transposed, y^T = V^T P^T: each 16-column half of a tile
 // takes one identity MFMA (the sources into the k slots) and one 16x16x32 MFMA with the weights as
 // two bf16 terms (hi in slots 0-3, lo in 4-7); the two halves leave lane (g, c) with query c's
-// output at eight consecutive columns: one 16-byte store per tile.
+// output at eight consecutive columns: one 16-byte store per tile, half of a 128-byte line. With
+// eight or more queries (STG) two tiles' outputs pass through a 2 KiB block of the wave's LDS
+// instead and go out as whole lines (8 rows x 128 bytes per store) with the streaming hint (forward
+// at S = 10, N = 32768, D = 4096: M = 8 0.99 -> 0.94 ms, M = 16 1.48 -> 1.44 ms; with fewer rows
+// the staging, which moves all 16 rows, costs more than it saves: M = 5 0.854 -> 0.867 ms).
 // Two tokens in flight: each token's rows are loaded into a second register set at the start of
 // the previous token, so they arrive while that token's mixture is computed and stored.
 #include "attnres_internal.hpp"
@@ -27,37 +31,47 @@ namespace {
 using namespace tiles;
 
 constexpr int kFwdXch = 256 + 16;  // a wave's score tile and its 16 sums of squares
+constexpr int kFwdStage = 2048;     // a wave's output staging block: 16 rows x 128 bytes
+
+// byte offset of 16-byte chunk b (0 .. 7) of row r (0 .. 15) in a staging block; the XOR spreads
+// both the operand-layout writes (16 rows, one chunk each) and the row-major reads (8 rows of 8
+// chunks) over all 64 banks per 16 lanes
+__device__ __forceinline__ int stage_off(int r, int b) { return (r * 8 + (b ^ ((r >> 1) & 7))) * 16; }
 
 }  // namespace
 
-// LDS of the tile forward: the staged rows (rows + 1, the last zero, padded), the waves' exchange
-// and the routing weights.
-size_t multi_fwd_tile_lds(int nt, int rows) {
+// LDS of the tile forward: the staged rows (padded; the selected read adds a zero row), the waves'
+// exchange, the routing weights and, with stg, the waves' output staging blocks.
+size_t multi_fwd_tile_lds(int nt, int rows, bool sel, bool stg) {
   const size_t D = (size_t)nt * kMfmaWaves * 32;
-  return (size_t)(rows + 1) * (D + tiles::kRowPad) * 2 +
-         ((size_t)kMfmaWaves * kFwdXch + 256) * sizeof(float);
+  return (size_t)(rows + (sel ? 1 : 0)) * (D + tiles::kRowPad) * 2 +
+         ((size_t)kMfmaWaves * kFwdXch + 256) * sizeof(float) +
+         (stg ? (size_t)kMfmaWaves * kFwdStage : 0);
 }
 
-template <int NT, bool FULL, bool SEL>
+template <int NT, bool FULL, bool SEL, bool STG>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 8)))
 void multi_fwd_tile_kernel(const MfmaFwdArgs a) {
   constexpr int W = kMfmaWaves;
   constexpr int D = NT * W * 32;
   extern __shared__ float lds[];
+  static_assert(!(SEL && STG), "the selected read stores from the operand layout");
   const int QR = SEL ? a.E : a.M;  // staged rows (queries or bank rows)
+  const int QA = SEL ? QR + 1 : QR;  // allocated rows: the selected read's last one zero
   constexpr int QP = D + kRowPad;                                   // staged row pitch
-  char* qrows = reinterpret_cast<char*>(lds);                      // [QR + 1][QP] bf16
-  float* xch = reinterpret_cast<float*>(qrows + (size_t)(QR + 1) * QP * 2);  // [W][kFwdXch]
+  char* qrows = reinterpret_cast<char*>(lds);                      // [QA][QP] bf16
+  float* xch = reinterpret_cast<float*>(qrows + (size_t)QA * QP * 2);  // [W][kFwdXch]
   float* pa = xch + W * kFwdXch;                                   // p[16][16]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  char* stg = reinterpret_cast<char*>(pa + 256) + wave * kFwdStage;  // this wave's staging block
   const int g = lane >> 4, c = lane & 15;
   const mb_u32x4 zero4 = {0u, 0u, 0u, 0u};
   const int col_w = wave * NT * 32 + 8 * g;
   auto keyok = [&](int t) { return FULL || col_w + 32 * t >= a.lo; };
 
-  // the rows as full-width rows, zero before the key slice; row QR zero (absent queries and ids
+  // the rows as full-width rows, zero before the key slice (row QR of the selected read zero: ids
   // outside [0, E))
-  for (int idx = tid; idx < (QR + 1) * (D / 8); idx += W * 64) {
+  for (int idx = tid; idx < QA * (D / 8); idx += W * 64) {
     const int e = idx / (D / 8), j = 8 * (idx - e * (D / 8));
     mb_u32x4 v = zero4;
     if (e < QR && j >= a.lo)
@@ -74,13 +88,22 @@ void multi_fwd_tile_kernel(const MfmaFwdArgs a) {
     if (s == c && vlive) vsrc = static_cast<const char*>(a.src[s]);
   vsrc += col_w * 2;
   char* ybase = static_cast<char*>(a.y) + ((qlive ? c * a.y_sm : 0) + col_w) * 2;
+  // STG: the output rows this lane stores from the staging block, queries yr and 8 + yr, 16 bytes
+  // at column 8 yb of each 64-column tile pair
+  const int yr = lane >> 3, yb = lane & 7;
+  const bool ylive0 = yr < a.M, ylive1 = 8 + yr < a.M;
+  char* yrow0 =
+      static_cast<char*>(a.y) + ((ylive0 ? yr * a.y_sm : 0) + wave * NT * 32 + 8 * yb) * 2;
+  char* yrow1 =
+      static_cast<char*>(a.y) + ((ylive1 ? (8 + yr) * a.y_sm : 0) + wave * NT * 32 + 8 * yb) * 2;
   auto ld_v = [&](int t, int64_t n) {
     const mb_u32x4 x = ld16(vsrc + n * a.row_stride * 2 + 64 * t);
     return vlive ? x : zero4;
   };
-  // the staged row query (slot) c reads for token n: c itself, or the bank row its id names (row
-  // QR, zero, for absent queries and ids outside [0, E))
-  const int fixed_row = qlive ? c : QR;
+  // the staged row query (slot) c reads for token n: c itself (lanes past M: the last query, whose
+  // score rows there are never used), or the bank row its id names (row QR, zero, for absent slots
+  // and ids outside [0, E))
+  const int fixed_row = qlive ? c : a.M - 1;
   auto slot_row = [&](int64_t n) {
     if constexpr (!SEL) return fixed_row;
     int r = QR;
@@ -143,21 +166,55 @@ void multi_fwd_tile_kernel(const MfmaFwdArgs a) {
       split4(pv, hi, lo);
       bp = mb_u32x4{hi[0], hi[1], lo[0], lo[1]};
     }
+    if constexpr (!STG) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float f[8];
+      for (int t = 0; t < NT; ++t) {
+        float f[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const mb_u32x2 vt = tr_half(V[t], h, ident);  // sources 4g .. 4g+3 at one column
-        const mb_float4 d = mfma_k32(mb_u32x4{vt[0], vt[1], vt[0], vt[1]}, bp,
-                                     mb_float4{0.f, 0.f, 0.f, 0.f});
+        for (int h = 0; h < 2; ++h) {
+          const mb_u32x2 vt = tr_half(V[t], h, ident);  // sources 4g .. 4g+3 at one column
+          const mb_float4 d = mfma_k32(mb_u32x4{vt[0], vt[1], vt[0], vt[1]}, bp,
+                                       mb_float4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[4 * h + i] = d[i];  // query c, column 8g + 4h + i
+          for (int i = 0; i < 4; ++i) f[4 * h + i] = d[i];  // query c, column 8g + 4h + i
+        }
+        if (qlive)
+          st16(ybase + n * a.y_sn * 2 + 64 * t,
+               mb_u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                        pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])});
       }
-      if (qlive)
-        st16(ybase + n * a.y_sn * 2 + 64 * t,
-              mb_u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                       pack_bf16x2(f[6], f[7])});
+      return;
+    }
+    const int64_t yoff = n * a.y_sn * 2;
+#pragma unroll
+    for (int u = 0; u < NT / 2; ++u) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int t = 2 * u + k;
+        float f[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const mb_u32x2 vt = tr_half(V[t], h, ident);  // sources 4g .. 4g+3 at one column
+          const mb_float4 d = mfma_k32(mb_u32x4{vt[0], vt[1], vt[0], vt[1]}, bp,
+                                       mb_float4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) f[4 * h + i] = d[i];  // query c, column 8g + 4h + i
+        }
+        // row c, chunk 4k + g of the tile pair (zeros for lanes past M)
+        *reinterpret_cast<mb_u32x4*>(stg + stage_off(c, 4 * k + g)) =
+            mb_u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                     pack_bf16x2(f[6], f[7])};
+      }
+      // the other lanes' chunks: LDS operations of one wave complete in order, the fences keep the
+      // compiler from reusing an earlier read of the block or moving the next pair's writes ahead
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const mb_u32x4 r0 = *reinterpret_cast<const mb_u32x4*>(stg + stage_off(yr, yb));
+      const mb_u32x4 r1 = *reinterpret_cast<const mb_u32x4*>(stg + stage_off(8 + yr, yb));
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (ylive0)
+        __builtin_nontemporal_store(r0, reinterpret_cast<mb_u32x4*>(yrow0 + yoff + 128 * u));
+      if (ylive1)
+        __builtin_nontemporal_store(r1, reinterpret_cast<mb_u32x4*>(yrow1 + yoff + 128 * u));
     }
   };
 
@@ -195,13 +252,17 @@ void multi_fwd_tile_kernel(const MfmaFwdArgs a) {
 
 #define ATTNRES_FWD_TILE(NT)                                                                 \
   case NT:                                                                                   \
-    return sel ? (full ? (const void*)&multi_fwd_tile_kernel<NT, true, true>                 \
-                       : (const void*)&multi_fwd_tile_kernel<NT, false, true>)               \
-               : (full ? (const void*)&multi_fwd_tile_kernel<NT, true, false>                \
-                       : (const void*)&multi_fwd_tile_kernel<NT, false, false>);
+    return sel ? (full ? (const void*)&multi_fwd_tile_kernel<NT, true, true, false>          \
+                       : (const void*)&multi_fwd_tile_kernel<NT, false, true, false>)        \
+               : stg ? (full ? (const void*)&multi_fwd_tile_kernel<NT, true, false, true>    \
+                             : (const void*)&multi_fwd_tile_kernel<NT, false, false, true>)  \
+                     : (full ? (const void*)&multi_fwd_tile_kernel<NT, true, false, false>   \
+                             : (const void*)&multi_fwd_tile_kernel<NT, false, false, false>);
 
-// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16)
-const void* multi_fwd_tile_kernel_ptr(int nt, bool full, bool sel) {
+// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); stg: outputs staged through LDS
+// (not with sel)
+const void* multi_fwd_tile_kernel_ptr(int nt, bool full, bool sel, bool stg) {
+  if (sel && stg) return nullptr;
   switch (nt) {
     ATTNRES_FWD_TILE(4) ATTNRES_FWD_TILE(8) ATTNRES_FWD_TILE(12) ATTNRES_FWD_TILE(16)
     default: break;

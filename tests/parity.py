@@ -222,13 +222,15 @@ LDS_PER_BLOCK = 160 * 1024  # gfx950
 def tile_fwd(S: int, D: int, M: int, dtype: str, R=None, row_stride=None, E=None) -> bool:
     """True when the multi-query (or, with E, selected-query) forward runs in the tile kernel with
     a static token stride: bf16, 5 <= M <= 16 (3 <= M for the selected read), 2 <= S <= 16, D in (1024, 2048, 3072, 4096), R and
-    the row stride multiples of 8 elements, and the staged rows (M, or E, plus a zero row) within
-    the workgroup's LDS beside the exchange. Other shapes take the older forward, whose
-    sixteen-slot kernels draw tokens from a counter in the workspace."""
+    the row stride multiples of 8 elements, and the staged rows (M; or E plus a zero row) within the
+    workgroup's LDS beside the exchange (and, with eight or more queries, the output staging
+    blocks). Other shapes take the older forward, whose sixteen-slot kernels draw tokens from a
+    counter in the workspace."""
     R = D if R is None else R
     row_stride = D if row_stride is None else row_stride
-    rows = M if E is None else E
-    lds = (rows + 1) * (D + 8) * 2 + (8 * (256 + 16) + 256) * 4
+    rows = M if E is None else E + 1
+    stage = 8 * 2048 if (E is None and M >= 8) else 0
+    lds = rows * (D + 8) * 2 + (8 * (256 + 16) + 256) * 4 + stage
     return (dtype == "bf16" and (5 if E is None else 3) <= M <= 16 and 2 <= S <= 16
             and D in (1024, 2048, 3072, 4096) and R % 8 == 0 and row_stride % 8 == 0
             and lds <= LDS_PER_BLOCK)
