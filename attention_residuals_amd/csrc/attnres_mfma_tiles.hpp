@@ -39,6 +39,12 @@ __device__ __forceinline__ void st16(char* p, const mb_u32x4& v) {
   *reinterpret_cast<mb_u32x4*>(p) = v;
 }
 
+// Byte offset of 16-byte chunk b (0 .. 7) of row r (0 .. 15) in a 2 KiB staging block that turns
+// two operand-layout tiles (lane (g, c): row c, 16 bytes at column 8g of each) into whole 128-byte
+// row segments: the XOR spreads both the tile writes (16 rows, one chunk each) and the row reads
+// (8 rows of 8 chunks) over all 64 banks per 16 lanes.
+__device__ __forceinline__ int stage_off(int r, int b) { return (r * 8 + (b ^ ((r >> 1) & 7))) * 16; }
+
 // {a.low, b.low} / {a.high, b.high} of two words (v_perm_b32)
 __device__ __forceinline__ uint32_t bpair_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

@@ -113,6 +113,23 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
     }
   vsrc += col_w * 2;
   vdst += col_w * 2;
+  // dv goes out as whole 128-byte row segments: each tile pair's outputs pass through this wave's
+  // exchange block (free during the dv loop: every wave read it before the barrier that precedes
+  // the loop, and this wave writes it again only after), then lane l stores 16 bytes of sources
+  // dr and 8 + dr at column 8 db of the pair, with the streaming hint
+  char* stg = reinterpret_cast<char*>(xch + wave * kXchFloats);
+  const int dr = lane >> 3, db = lane & 7;
+  const bool dlive0 = dr < a.S, dlive1 = 8 + dr < a.S;
+  char* dvr0 = static_cast<char*>(a.dsrc[0]);
+  char* dvr1 = static_cast<char*>(a.dsrc[0]);
+#pragma unroll
+  for (int s = 1; s < 8; ++s)
+    if (s == dr && dlive0) dvr0 = static_cast<char*>(a.dsrc[s]);
+#pragma unroll
+  for (int s = 8; s < 16; ++s)
+    if (s == 8 + dr && dlive1) dvr1 = static_cast<char*>(a.dsrc[s]);
+  dvr0 += (wave * NT * 32 + 8 * db) * 2;
+  dvr1 += (wave * NT * 32 + 8 * db) * 2;
   const char* gsrc = static_cast<const char*>(a.dout) + ((qlive ? c * a.g_sm : 0) + col_w) * 2;
 
   auto ld_v = [&](int t, int64_t n) {
@@ -384,10 +401,21 @@ void multi_bwd_mfma_kernel(const MfmaBwdArgs a) {
       // the tile's registers take the next token's rows
       V[t] = ld_v(t, ln);
       Y[t] = ld_y(t, ln);
-      if (vlive)
-        st16(vdst + n * a.drow_stride * 2 + 64 * t,
-              mb_u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])});
+      // row c, chunk 4(t % 2) + g of the tile pair (zeros for lanes past S)
+      *reinterpret_cast<mb_u32x4*>(stg + stage_off(c, 4 * (t & 1) + g)) =
+          mb_u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                   pack_bf16x2(f[6], f[7])};
+      if (t & 1) {
+        // the other lanes' chunks (a wave's LDS operations complete in order; the fences keep
+        // the compiler from reusing an earlier read or moving the next pair's writes ahead)
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const mb_u32x4 r0 = *reinterpret_cast<const mb_u32x4*>(stg + stage_off(dr, db));
+        const mb_u32x4 r1 = *reinterpret_cast<const mb_u32x4*>(stg + stage_off(8 + dr, db));
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const int64_t off = n * a.drow_stride * 2 + 128 * (t >> 1);
+        if (dlive0) __builtin_nontemporal_store(r0, reinterpret_cast<mb_u32x4*>(dvr0 + off));
+        if (dlive1) __builtin_nontemporal_store(r1, reinterpret_cast<mb_u32x4*>(dvr1 + off));
+      }
       if (t >= LAG) contract(t - LAG);
     }
 #pragma unroll

@@ -33,11 +33,6 @@ using namespace tiles;
 constexpr int kFwdXch = 256 + 16;  // a wave's score tile and its 16 sums of squares
 constexpr int kFwdStage = 2048;     // a wave's output staging block: 16 rows x 128 bytes
 
-// byte offset of 16-byte chunk b (0 .. 7) of row r (0 .. 15) in a staging block; the XOR spreads
-// both the operand-layout writes (16 rows, one chunk each) and the row-major reads (8 rows of 8
-// chunks) over all 64 banks per 16 lanes
-__device__ __forceinline__ int stage_off(int r, int b) { return (r * 8 + (b ^ ((r >> 1) & 7))) * 16; }
-
 }  // namespace
 
 // LDS of the tile forward: the staged rows (padded; the selected read adds a zero row), the waves'
