@@ -841,8 +841,12 @@ attnres_status try_mfma_fwd(int S, int D, int R, int M, float eps, float scale, 
     static const char* te = std::getenv("ATTNRES_MULTI_TILE_FWD");
     const int nt = D / 256;
     const int rows = sel ? E : M;
-    // eight or more queries: outputs staged through LDS and stored as whole lines
-    const bool stg = !sel && M >= 8;
+    // outputs staged through LDS and stored as whole lines: five to eight rows in the exchange
+    // blocks, more in staging blocks of their own where they fit; fewer rows are stored from the
+    // operand layout (forward at S = 10, N = 32768, D = 4096, direct / staged, ms: M = 6 0.887 /
+    // 0.871, M = 8 0.943 / 0.924, selected K = 3 0.809 / 0.838, K = 4 0.828 / 0.852)
+    int stg = M > 8 ? (sel ? 0 : 16) : (M >= 5 ? 8 : 0);
+    if (stg == 16 && multi_fwd_tile_lds(nt, rows, sel, 16) > (size_t)f.lds_per_block) stg = 0;
     const size_t lds = multi_fwd_tile_lds(nt, rows, sel, stg);
     bool al = aligned(queries, 16) && aligned(y, 16) && y_sm % 8 == 0 && y_sn % 8 == 0;
     for (int s = 0; s < S && s < 16; ++s) al = al && aligned(src[s], 16);

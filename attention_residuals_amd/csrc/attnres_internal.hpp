@@ -76,8 +76,8 @@ const void* multi_bwd_mfma_kernel_ptr(int nt, int dqm, bool full, bool acc, int 
 const void* multi_dq_mfma_kernel_ptr();
 // Multi- and selected-query forward in the same operand layout (8 waves, D = 256 nt), two tokens
 // in flight; LDS for `rows` staged rows (M queries or E bank rows).
-const void* multi_fwd_tile_kernel_ptr(int nt, bool full, bool sel, bool stg);
-size_t multi_fwd_tile_lds(int nt, int rows, bool sel, bool stg);
+const void* multi_fwd_tile_kernel_ptr(int nt, bool full, bool sel, int stg);
+size_t multi_fwd_tile_lds(int nt, int rows, bool sel, int stg);
 const void* stream_probe_kernel_ptr(int cpt);
 size_t multi_bwd_mfma_lds(int nt, int dqm, int M, int qm, int E);
 // The multi-query backward with the sources and dY rows in one 16-row tile (S + M <= 16).

@@ -14,11 +14,11 @@
 // sources by DPP, lse. The mixture runs transposed, y^T = V^T P^T: each 16-column half of a tile
 // takes one identity MFMA (the sources into the k slots) and one 16x16x32 MFMA with the weights as
 // two bf16 terms (hi in slots 0-3, lo in 4-7); the two halves leave lane (g, c) with query c's
-// output at eight consecutive columns: one 16-byte store per tile, half of a 128-byte line. With
-// eight or more queries (STG) two tiles' outputs pass through a 2 KiB block of the wave's LDS
-// instead and go out as whole lines (8 rows x 128 bytes per store) with the streaming hint (forward
-// at S = 10, N = 32768, D = 4096: M = 8 0.99 -> 0.94 ms, M = 16 1.48 -> 1.44 ms; with fewer rows
-// the staging, which moves all 16 rows, costs more than it saves: M = 5 0.854 -> 0.867 ms).
+// output at eight consecutive columns, half of a 128-byte line. With five or more rows two tiles'
+// outputs pass through LDS instead and go out as whole lines (8 rows x 128 bytes per store) with
+// the streaming hint: up to 8 rows (STG = 8) through the wave's own exchange block, idle during
+// the mixture; more (STG = 16) through a 2 KiB block per wave of their own. STG = 0 stores from
+// the operand layout (fewer rows, where the staging costs more than it saves).
 // Two tokens in flight: each token's rows are loaded into a second register set at the start of
 // the previous token, so they arrive while that token's mixture is computed and stored.
 #include "attnres_internal.hpp"
@@ -36,21 +36,21 @@ constexpr int kFwdStage = 2048;     // a wave's output staging block: 16 rows x 
 }  // namespace
 
 // LDS of the tile forward: the staged rows (padded; the selected read adds a zero row), the waves'
-// exchange, the routing weights and, with stg, the waves' output staging blocks.
-size_t multi_fwd_tile_lds(int nt, int rows, bool sel, bool stg) {
+// exchange, the routing weights and, with stg = 16, the waves' output staging blocks.
+size_t multi_fwd_tile_lds(int nt, int rows, bool sel, int stg) {
   const size_t D = (size_t)nt * kMfmaWaves * 32;
   return (size_t)(rows + (sel ? 1 : 0)) * (D + tiles::kRowPad) * 2 +
          ((size_t)kMfmaWaves * kFwdXch + 256) * sizeof(float) +
-         (stg ? (size_t)kMfmaWaves * kFwdStage : 0);
+         (stg == 16 ? (size_t)kMfmaWaves * kFwdStage : 0);
 }
 
-template <int NT, bool FULL, bool SEL, bool STG>
+template <int NT, bool FULL, bool SEL, int STG>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 8)))
 void multi_fwd_tile_kernel(const MfmaFwdArgs a) {
   constexpr int W = kMfmaWaves;
   constexpr int D = NT * W * 32;
   extern __shared__ float lds[];
-  static_assert(!(SEL && STG), "the selected read stores from the operand layout");
+  static_assert(!(SEL && STG == 16), "the selected read has no staging blocks of its own");
   const int QR = SEL ? a.E : a.M;  // staged rows (queries or bank rows)
   const int QA = SEL ? QR + 1 : QR;  // allocated rows: the selected read's last one zero
   constexpr int QP = D + kRowPad;                                   // staged row pitch
@@ -58,7 +58,9 @@ void multi_fwd_tile_kernel(const MfmaFwdArgs a) {
   float* xch = reinterpret_cast<float*>(qrows + (size_t)QA * QP * 2);  // [W][kFwdXch]
   float* pa = xch + W * kFwdXch;                                   // p[16][16]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  char* stg = reinterpret_cast<char*>(pa + 256) + wave * kFwdStage;  // this wave's staging block
+  // this wave's staging block (STG = 8: its exchange block, 1088 bytes)
+  char* stg = STG == 16 ? reinterpret_cast<char*>(pa + 256) + wave * kFwdStage
+                        : reinterpret_cast<char*>(xch + wave * kFwdXch);
   const int g = lane >> 4, c = lane & 15;
   const mb_u32x4 zero4 = {0u, 0u, 0u, 0u};
   const int col_w = wave * NT * 32 + 8 * g;
@@ -83,8 +85,8 @@ void multi_fwd_tile_kernel(const MfmaFwdArgs a) {
     if (s == c && vlive) vsrc = static_cast<const char*>(a.src[s]);
   vsrc += col_w * 2;
   char* ybase = static_cast<char*>(a.y) + ((qlive ? c * a.y_sm : 0) + col_w) * 2;
-  // STG: the output rows this lane stores from the staging block, queries yr and 8 + yr, 16 bytes
-  // at column 8 yb of each 64-column tile pair
+  // STG: the output rows this lane stores from the staging block, queries (slots) yr and, with
+  // STG = 16, 8 + yr, 16 bytes at column 8 yb of each 64-column tile pair
   const int yr = lane >> 3, yb = lane & 7;
   const bool ylive0 = yr < a.M, ylive1 = 8 + yr < a.M;
   char* yrow0 =
@@ -161,7 +163,7 @@ void multi_fwd_tile_kernel(const MfmaFwdArgs a) {
       split4(pv, hi, lo);
       bp = mb_u32x4{hi[0], hi[1], lo[0], lo[1]};
     }
-    if constexpr (!STG) {
+    if constexpr (STG == 0) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         float f[8];
@@ -195,20 +197,22 @@ void multi_fwd_tile_kernel(const MfmaFwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) f[4 * h + i] = d[i];  // query c, column 8g + 4h + i
         }
-        // row c, chunk 4k + g of the tile pair (zeros for lanes past M)
-        *reinterpret_cast<mb_u32x4*>(stg + stage_off(c, 4 * k + g)) =
-            mb_u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                     pack_bf16x2(f[6], f[7])};
+        // row c, chunk 4k + g of the tile pair (zeros for lanes past M; STG = 8: rows 0 .. 7)
+        if (STG == 16 || c < 8)
+          *reinterpret_cast<mb_u32x4*>(stg + stage_off(c, 4 * k + g)) =
+              mb_u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
       }
       // the other lanes' chunks: LDS operations of one wave complete in order, the fences keep the
       // compiler from reusing an earlier read of the block or moving the next pair's writes ahead
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       const mb_u32x4 r0 = *reinterpret_cast<const mb_u32x4*>(stg + stage_off(yr, yb));
-      const mb_u32x4 r1 = *reinterpret_cast<const mb_u32x4*>(stg + stage_off(8 + yr, yb));
+      mb_u32x4 r1 = zero4;
+      if constexpr (STG == 16) r1 = *reinterpret_cast<const mb_u32x4*>(stg + stage_off(8 + yr, yb));
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       if (ylive0)
         __builtin_nontemporal_store(r0, reinterpret_cast<mb_u32x4*>(yrow0 + yoff + 128 * u));
-      if (ylive1)
+      if (STG == 16 && ylive1)
         __builtin_nontemporal_store(r1, reinterpret_cast<mb_u32x4*>(yrow1 + yoff + 128 * u));
     }
   };
@@ -245,19 +249,21 @@ void multi_fwd_tile_kernel(const MfmaFwdArgs a) {
   }
 }
 
+#define ATTNRES_FWD_TILE_S(NT, SEL, STG)                                                     \
+  (full ? (const void*)&multi_fwd_tile_kernel<NT, true, SEL, STG>                            \
+        : (const void*)&multi_fwd_tile_kernel<NT, false, SEL, STG>)
 #define ATTNRES_FWD_TILE(NT)                                                                 \
   case NT:                                                                                   \
-    return sel ? (full ? (const void*)&multi_fwd_tile_kernel<NT, true, true, false>          \
-                       : (const void*)&multi_fwd_tile_kernel<NT, false, true, false>)        \
-               : stg ? (full ? (const void*)&multi_fwd_tile_kernel<NT, true, false, true>    \
-                             : (const void*)&multi_fwd_tile_kernel<NT, false, false, true>)  \
-                     : (full ? (const void*)&multi_fwd_tile_kernel<NT, true, false, false>   \
-                             : (const void*)&multi_fwd_tile_kernel<NT, false, false, false>);
+    return sel ? (stg == 8 ? ATTNRES_FWD_TILE_S(NT, true, 8) : ATTNRES_FWD_TILE_S(NT, true, 0)) \
+               : (stg == 16 ? ATTNRES_FWD_TILE_S(NT, false, 16)                              \
+                            : stg == 8 ? ATTNRES_FWD_TILE_S(NT, false, 8)                    \
+                                       : ATTNRES_FWD_TILE_S(NT, false, 0));
 
-// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); stg: outputs staged through LDS
-// (not with sel)
-const void* multi_fwd_tile_kernel_ptr(int nt, bool full, bool sel, bool stg) {
-  if (sel && stg) return nullptr;
+// nt = 32-column tiles per wave (D = 256 nt: 4, 8, 12 or 16); stg: outputs stored from the
+// operand layout (0) or staged through LDS, up to 8 rows in the exchange block (8) or 16 in blocks
+// of their own (16, not with sel)
+const void* multi_fwd_tile_kernel_ptr(int nt, bool full, bool sel, int stg) {
+  if ((sel && stg == 16) || (stg != 0 && stg != 8 && stg != 16)) return nullptr;
   switch (nt) {
     ATTNRES_FWD_TILE(4) ATTNRES_FWD_TILE(8) ATTNRES_FWD_TILE(12) ATTNRES_FWD_TILE(16)
     default: break;

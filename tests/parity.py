@@ -223,14 +223,15 @@ def tile_fwd(S: int, D: int, M: int, dtype: str, R=None, row_stride=None, E=None
     """True when the multi-query (or, with E, selected-query) forward runs in the tile kernel with
     a static token stride: bf16, 5 <= M <= 16 (3 <= M for the selected read), 2 <= S <= 16, D in (1024, 2048, 3072, 4096), R and
     the row stride multiples of 8 elements, and the staged rows (M; or E plus a zero row) within the
-    workgroup's LDS beside the exchange (and, with eight or more queries, the output staging
-    blocks). Other shapes take the older forward, whose sixteen-slot kernels draw tokens from a
-    counter in the workspace."""
+    workgroup's LDS beside the exchange (with more than eight queries also the output staging
+    blocks, where they fit). Other shapes take the older forward, whose sixteen-slot kernels draw
+    tokens from a counter in the workspace."""
     R = D if R is None else R
     row_stride = D if row_stride is None else row_stride
     rows = M if E is None else E + 1
-    stage = 8 * 2048 if (E is None and M >= 8) else 0
-    lds = rows * (D + 8) * 2 + (8 * (256 + 16) + 256) * 4 + stage
+    lds = rows * (D + 8) * 2 + (8 * (256 + 16) + 256) * 4
+    if E is None and M > 8 and lds + 8 * 2048 <= LDS_PER_BLOCK:
+        lds += 8 * 2048
     return (dtype == "bf16" and (5 if E is None else 3) <= M <= 16 and 2 <= S <= 16
             and D in (1024, 2048, 3072, 4096) and R % 8 == 0 and row_stride % 8 == 0
             and lds <= LDS_PER_BLOCK)
