@@ -21,7 +21,8 @@
 //   * dv^T = dY^T P + Q^T A per 16-column half-tile: one K = 32 operand carries four queries' dY
 //     and q values, the other the matching p and a values, as two bf16 terms (hi, then lo, in two
 //     MFMAs); B_s t_s is added on the vector ALU and each dv row chunk is rounded once to bf16
-//     (with accumulate: added to the existing row first).
+//     (with accumulate: added to the existing row first). Each tile pair's chunks then pass
+//     through the wave's exchange block and go out as whole 128-byte row segments.
 //   * As soon as a tile's dv is written, its registers take the next token's rows, and the next
 //     token's score contractions run a few tiles behind those loads, so the loads overlap the
 //     current token's work.

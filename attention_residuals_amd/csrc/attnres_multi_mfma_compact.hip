@@ -16,7 +16,9 @@
 //     staged as rows in LDS.
 //   * dv^T per 16-column half: an identity MFMA transposes X (its rows into the k slots) for two
 //     16x16x16 MFMAs with p as two bf16 terms (zero for the source rows); another transposes the
-//     query rows for two with a; B_s t_s is added on the vector ALU and each dv chunk rounded once.
+//     query rows for two with a; B_s t_s is added on the vector ALU and each dv chunk rounded once
+//     (without the dq sums in LDS, each tile pair's chunks then go out as whole 128-byte row
+//     segments through the wave's exchange block).
 //   * dq with M <= 8 where the sums fit the LDS: summed per workgroup in LDS from the same
 //     transposed X (a is zero past the source rows) and written as one partial row; otherwise the
 //     token's a_{m,s} go to the workspace and the dq kernel forms dq.
