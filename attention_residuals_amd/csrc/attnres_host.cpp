@@ -1024,7 +1024,10 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
   // sources and dY rows together in one 16-row tile when they fit (S + M <= 16): half the row
   // registers, two tokens in flight (ATTNRES_MULTI_COMPACT=0 turns it off)
   static const char* ce = std::getenv("ATTNRES_MULTI_COMPACT");
-  bool compact = S + M <= 16 && !(ce && ce[0] == '0');
+  // up to four queries the separate tiles sum dq in LDS too and measured faster (backward call at
+  // S = 10, N = 32768, D = 4096, M = 4: 1.32 ms against 1.60 ms for the compact tile; accumulating
+  // 2.01 against 2.12 ms)
+  bool compact = S + M <= 16 && !(ce && ce[0] == '0') && (sel || M > 4);
   int qm = 0;
   size_t lds = 0;
   if (compact) {
@@ -1082,11 +1085,11 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
 attnres_status plan_multi_bwd_mfma(const attnres_multi_desc* m, const MultiShape& ms,
                                    int64_t row_stride, int64_t drow_stride, MultiBwdPlan* pl) {
   pl->mfma = false;
-  // up to three queries with S <= 12 (and D <= 4096) are one launch of the query-group kernel,
-  // which measured faster there (M = 3 at S = 10, N = 32768, D = 4096: 1.38 ms against 1.50 ms for
-  // the compact matrix-core kernel); it rounds dvalues once as well. Four queries: the compact
-  // kernel, 1.53 against 1.66 ms
-  if (!ms.base.bf16 || (m->M <= 3 && m->S <= 12)) return ATTNRES_OK;
+  // accumulating into dvalues, up to three queries with S <= 12 are one launch of the query-group
+  // kernel, which rounds dvalues once as well and measured faster there (M = 3 at S = 10,
+  // N = 32768, D = 4096: 1.81 ms against 1.96 ms); overwriting, the separate-tile kernel is faster
+  // (1.29 against 1.39 ms)
+  if (!ms.base.bf16 || (m->accumulate_dvalues && m->M <= 3 && m->S <= 12)) return ATTNRES_OK;
   return plan_mfma_bwd(m->S, m->D, m->R, m->M, false, 0, m->N, m->accumulate_dvalues != 0,
                        row_stride, drow_stride, pl);
 }

@@ -197,10 +197,10 @@ attnres_status attnres_bwd_noalloc(const attnres_desc* desc, const attnres_sourc
  * again. The backward of 3 <= M <= 16 bf16 queries over 2 <= S <= 16 sources with D = 1024, 2048,
  * 3072 or 4096, R and the row strides multiples of 8 and 16-byte aligned queries, runs in one pass
  * on matrix cores (dvalues written and rounded once; with S + M <= 16 the sources and dY rows share
- * one register tile and two tokens are in flight; a second pass over the key slice forms dq unless
- * M <= 4, or, in the shared tile, M <= 8 with the dq sums fitting the workgroup's LDS beside the
- * queries: M <= 6 at D = 4096), except M = 3 with S <= 12, which is one launch of the query-group
- * kernel; otherwise
+ * one register tile (used from five queries on) and two tokens are in flight; a second pass over
+ * the key slice forms dq unless M <= 4, or, in the shared tile, M <= 8 with the dq sums fitting the
+ * workgroup's LDS beside the queries: M <= 6 at D = 4096), except M = 3 with S <= 12 accumulating
+ * into dvalues, which is one launch of the query-group kernel; otherwise
  * backward groups after the first add into dvalues. ATTNRES_MULTI_MFMA=0 (read once) turns the
  * matrix-core kernels off.
  * Layout of y, dout [.., D] and lse: ATTNRES_QUERY_MAJOR = [M, N] rows (the page's default),

@@ -206,12 +206,11 @@ def assert_ok(res: dict, label: str) -> None:
 
 def multi_mfma_bwd(S: int, D: int, M: int, dtype: str, R=None, row_stride=None) -> bool:
     """True when the multi-query backward runs in one pass on matrix cores: bf16, 3 <= M <= 16,
-    2 <= S <= 16, D in (1024, 2048, 3072, 4096), R and the row stride multiples of 8 elements,
-    and not M <= 3 with S <= 12 (one launch of the query-group kernel there)."""
+    2 <= S <= 16, D in (1024, 2048, 3072, 4096), R and the row stride multiples of 8 elements
+    (accumulating into dvalues, M = 3 with S <= 12 runs the query-group kernel instead: one launch,
+    one pass as well, so the launch groups are the same)."""
     R = D if R is None else R
     row_stride = D if row_stride is None else row_stride
-    if M <= 3 and S <= 12:
-        return False
     return (dtype == "bf16" and 3 <= M <= 16 and 2 <= S <= 16 and D in (1024, 2048, 3072, 4096)
             and R % 8 == 0 and row_stride % 8 == 0)
 

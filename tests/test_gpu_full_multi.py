@@ -26,8 +26,9 @@ def _groups(w, M, selected, E=None):
     return multi_bwd_passes(w.S, w.D, M, w.dtype, selected, R=w.R, E=E)
 
 
-# M = 2: the query-group kernels; M = 4 and 6: the compact matrix-core backward (sources and dY
-# rows in one tile, dq summed in LDS); M = 8: the separate-tile matrix-core backward and its dq pass
+# M = 2: the query-group kernels; M = 4: the separate-tile matrix-core backward with dq summed in
+# LDS; M = 6: the compact one (sources and dY rows in one tile, dq summed in LDS); M = 8: the
+# separate-tile backward and its dq pass
 @pytest.mark.parametrize("M,layout", [(2, "query_major"), (4, "token_major"), (6, "query_major"),
                                       (8, "token_major")])
 def test_multi_query_full_size(M, layout):

@@ -119,7 +119,7 @@ def _check(V, Q, G, label, dtype, init=None, f32_tol=None, **kw):
     # its own LDS (no second pass over the sources)
     (14, 300, 2048, 2048, 4, "bf16", "token_major"),
     (16, 201, 1024, 512, 3, "bf16", "query_major"),
-    (13, 150, 3072, 3072, 3, "bf16", "query_major"),   # compact tile (S + M = 16), dq in LDS
+    (13, 150, 3072, 3072, 3, "bf16", "query_major"),   # separate tiles, S + M = 16, dq in LDS
     # sources and dY rows in one tile (S + M <= 16), five to eight queries with dq summed in LDS
     (10, 257, 4096, 4096, 6, "bf16", "query_major"),   # the largest that fits (~155 KiB)
     (8, 300, 2048, 2048, 8, "bf16", "token_major"),
