@@ -1021,12 +1021,12 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
   DevFacts f;
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
-  // sources and dY rows together in one 16-row tile when they fit (S + M <= 16): half the row
-  // registers, two tokens in flight (ATTNRES_MULTI_COMPACT=0 turns it off)
+  // sources and dY rows together in one 16-row tile when they fit (S + M <= 16; from five queries
+  // on, or the selected read): half the row registers, two tokens in flight
+  // (ATTNRES_MULTI_COMPACT=0 turns it off). Up to four queries the separate tiles sum dq in LDS
+  // too and measured faster (backward call at S = 10, N = 32768, D = 4096, M = 4: 1.32 ms against
+  // 1.60 ms for the compact tile; accumulating 2.01 against 2.12 ms)
   static const char* ce = std::getenv("ATTNRES_MULTI_COMPACT");
-  // up to four queries the separate tiles sum dq in LDS too and measured faster (backward call at
-  // S = 10, N = 32768, D = 4096, M = 4: 1.32 ms against 1.60 ms for the compact tile; accumulating
-  // 2.01 against 2.12 ms)
   bool compact = S + M <= 16 && !(ce && ce[0] == '0') && (sel || M > 4);
   int qm = 0;
   size_t lds = 0;
