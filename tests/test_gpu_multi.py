@@ -156,14 +156,26 @@ def test_multi_query_several_tokens_per_workgroup(M, dynamic):
            deterministic=not dynamic)
 
 
-# (6, 6) and (10, 6) at D = 4096: the compact tile summing dq in LDS beside the accumulated rows
+# (6, 6) and (10, 6) at D = 4096: the compact tile summing dq in LDS beside the accumulated rows;
+# (14, 3) as a list: the separate tiles' whole-line dv stores into separate allocations
 @pytest.mark.parametrize("S,M,packed,D", [(6, 2, True, 2048), (6, 6, False, 2048),
-                                          (14, 3, True, 2048), (10, 6, True, 4096)])
+                                          (14, 3, True, 2048), (10, 6, True, 4096),
+                                          (14, 3, False, 2048)])
 def test_multi_query_accumulate_into_dvalues(S, M, packed, D):
     N, R = 301, D
     V, Q, G = _inputs(S, N, D, R, M, "bf16", seed=2100 + M)
     init = (2.0 * torch.randn((S, N, D), generator=torch.Generator().manual_seed(5))).to(V.dtype)
     _check(V, Q, G, f"multi accumulate M={M}", "bf16", init=init, accumulate=True, packed=packed)
+
+
+@pytest.mark.parametrize("S,M", [(6, 4), (10, 12), (16, 9)])
+def test_separate_tiles_with_list_sources(S, M):
+    # the separate-tile backward (M <= 4, or S + M > 16) with sources as a list: each lane's two
+    # whole-line dv stores pick their rows' allocations from the pointer table
+    N, D, R = 301, 2048, 2048
+    V, Q, G = _inputs(S, N, D, R, M, "bf16", seed=2150 + S * M)
+    print(f"[case] separate tiles, list sources S={S} M={M}", flush=True)
+    _check(V, Q, G, f"multi list S={S} M={M}", "bf16", packed=False)
 
 
 @pytest.mark.parametrize("S,N,D,R,M", [(10, 3001, 4096, 4096, 4), (5, 999, 2048, 640, 11)])
