@@ -1021,15 +1021,29 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
   DevFacts f;
   attnres_status st = device_facts(&f);
   if (st != ATTNRES_OK) return st;
-  // sources and dY rows together in one 16-row tile when they fit (S + M <= 16; from five queries
-  // on, or the selected read): half the row registers, two tokens in flight
-  // (ATTNRES_MULTI_COMPACT=0 turns it off). Up to four queries the separate tiles sum dq in LDS
-  // too and measured faster (backward call at S = 10, N = 32768, D = 4096, M = 4: 1.32 ms against
-  // 1.60 ms for the compact tile; accumulating 2.01 against 2.12 ms)
-  static const char* ce = std::getenv("ATTNRES_MULTI_COMPACT");
-  bool compact = S + M <= 16 && !(ce && ce[0] == '0') && (sel || M > 4);
+  // the separate tiles' staged queries (full rows where they fit, M <= 8: the score operand
+  // without transposes); false when they do not fit the LDS
   int qm = 0;
   size_t lds = 0;
+  auto separate_fits = [&](int* qm_out, size_t* lds_out) {
+    int q = sel ? 2 : (M <= 8 ? 1 : 0);
+    size_t b = multi_bwd_mfma_lds(nt, dqm, M, q, E);
+    if (q == 1 && b > (size_t)f.lds_per_block && dqm == 0) {
+      q = 0;
+      b = multi_bwd_mfma_lds(nt, dqm, M, q, E);
+    }
+    *qm_out = q;
+    *lds_out = b;
+    return b <= (size_t)f.lds_per_block;
+  };
+  // sources and dY rows together in one 16-row tile when they fit (S + M <= 16): half the row
+  // registers, two tokens in flight (ATTNRES_MULTI_COMPACT=0 turns it off). Up to four queries
+  // (slots) the separate tiles are faster where they fit (backward call at S = 10, N = 32768,
+  // D = 4096, M = 4: 1.32 ms against 1.60 ms for the compact tile, accumulating 2.01 against
+  // 2.12 ms, both with dq in LDS; selected E = 8, K = 4: 1.85 against 1.90 ms)
+  static const char* ce = std::getenv("ATTNRES_MULTI_COMPACT");
+  bool compact = S + M <= 16 && !(ce && ce[0] == '0');
+  if (compact && M <= 4 && separate_fits(&qm, &lds)) compact = false;
   if (compact) {
     // dq summed in the kernel's LDS for up to eight queries where the sums fit beside the staged
     // queries (backward call at S = 10, N = 32768, D = 4096: M = 6 1.99 ms with the dq pass over
@@ -1040,16 +1054,7 @@ attnres_status plan_mfma_bwd(int S, int D, int R, int M, bool sel, int E, int64_
     compact = lds <= (size_t)f.lds_per_block;
     if (compact) dqm = cdq ? 1 : 0;
   }
-  if (!compact) {
-    // the queries also as full rows where they fit (M <= 8): the score operand without transposes
-    qm = sel ? 2 : (M <= 8 ? 1 : 0);
-    lds = multi_bwd_mfma_lds(nt, dqm, M, qm, E);
-    if (qm == 1 && lds > (size_t)f.lds_per_block && dqm == 0) {
-      qm = 0;
-      lds = multi_bwd_mfma_lds(nt, dqm, M, qm, E);
-    }
-    if (lds > (size_t)f.lds_per_block) return ATTNRES_OK;
-  }
+  if (!compact && !separate_fits(&qm, &lds)) return ATTNRES_OK;
   const void* fn = compact ? multi_bwd_compact_kernel_ptr(nt, dqm != 0, R == D, acc, sel)
                            : multi_bwd_mfma_kernel_ptr(nt, dqm, R == D, acc, qm);
   if (!fn) return fail(ATTNRES_ERR_UNSUPPORTED, "no matrix-core multi-query backward kernel");

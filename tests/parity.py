@@ -247,7 +247,8 @@ def sel_mfma_bwd(S: int, D: int, K: int, E: int, dtype: str, R=None, row_stride=
     and more slots than the slot-group kernel takes in one launch (sel_slots_per_launch), or
     K >= 4 with S + K <= 16 (the compact tile); 2 <= S <= 16, D in (1024, 2048, 3072, 4096), R and
     the row stride multiples of 8 elements, E <= 16 and the staged bank within the workgroup's LDS
-    beside the exchange (the compact tile: E rows; else E + 1 and the transposed four-row groups)."""
+    beside the exchange (the compact tile: E rows; the separate tiles: E + 1 and the transposed
+    four-row groups)."""
     R = D if R is None else R
     row_stride = D if row_stride is None else row_stride
     if not (dtype == "bf16" and 3 <= K <= 16 and 2 <= S <= 16 and D in (1024, 2048, 3072, 4096)
@@ -256,11 +257,12 @@ def sel_mfma_bwd(S: int, D: int, K: int, E: int, dtype: str, R=None, row_stride=
     compact = S + K <= 16
     if K <= sel_slots_per_launch(S, D, dtype) and not (K >= 4 and compact):
         return False
-    if compact:
-        lds = E * (D + 8) * 2 + (8 * (2 * 256 + 16) + 512 + 64 + 16) * 4
-    else:
-        lds = (E + 1) * (D + 8) * 2 + 16 * 4 + -(-E // 4) * D * 8 + (8 * (2 * 256 + 16) + 512 + 64) * 4
-    return lds <= LDS_PER_BLOCK
+    # the compact tile (the bank as E rows) or the separate tiles (E + 1 rows and the transposed
+    # four-row groups), whichever fits (up to four slots the separate tiles are preferred)
+    compact_lds = E * (D + 8) * 2 + (8 * (2 * 256 + 16) + 512 + 64 + 16) * 4
+    separate_lds = ((E + 1) * (D + 8) * 2 + 16 * 4 + -(-E // 4) * D * 8
+                    + (8 * (2 * 256 + 16) + 512 + 64) * 4)
+    return (compact and compact_lds <= LDS_PER_BLOCK) or separate_lds <= LDS_PER_BLOCK
 
 
 def multi_bwd_groups(S: int, D: int, M: int, dtype: str, selected: bool = False, R=None,

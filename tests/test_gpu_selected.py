@@ -95,15 +95,16 @@ def _check(V, bank, ids, G, label, dtype, init=None, ref_bank=None, ref_ids=None
     (24, 199, 2048, 640, 5, 2, "bf16"),
     (4, 200, 512, 512, 1, 3, "bf16"),       # every slot names the same row
     (12, 333, 1024, 1024, 40, 2, "bf16"),   # many rows (global blocks)
-    (10, 301, 4096, 4096, 8, 4, "bf16"),    # four slots: the compact matrix-core backward
+    (10, 301, 4096, 4096, 8, 4, "bf16"),    # four slots: the separate-tile matrix-core backward
     (8, 257, 1024, 1024, 4, 4, "f32"),      # four slots, FP32
     (10, 211, 2048, 2048, 24, 7, "bf16"),   # seven slots: groups of four and three, global blocks
     (6, 149, 2048, 2048, 40, 4, "bf16"),    # a bank too large to stage: the slot-group forward
     # the one-pass matrix-core backward (bf16 slots beyond one slot-group launch: K > 4, or K > 2
     # with S > 10; or 4 <= K with S + K <= 16, the compact tile; E <= 16, D = 256 nt)
     (16, 257, 4096, 4096, 6, 16, "bf16"),   # sixteen slots and sources
-    (12, 211, 2048, 2048, 8, 3, "bf16"),    # three slots, twelve sources (compact tile)
+    (12, 211, 2048, 2048, 8, 3, "bf16"),    # three slots, twelve sources (separate tiles)
     (4, 200, 1024, 256, 8, 6, "bf16"),      # compact tile, sliced key
+    (10, 201, 4096, 4096, 16, 4, "bf16"),   # four slots, a bank only the compact tile fits
     (9, 129, 4096, 4096, 7, 7, "bf16"),     # compact tile, sixteen rows
     (5, 300, 3072, 1024, 3, 9, "bf16"),     # twelve column tiles per wave, sliced key
     (12, 150, 1024, 1024, 16, 5, "bf16"),   # sixteen bank rows
